@@ -1,0 +1,125 @@
+// kvq_internal.h -- device helpers and launch parameter blocks shared by the
+// library's HIP sources (not installed; the public interface is include/kvq.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+constexpr int D = 128;        // head_dim supported by the kernels
+constexpr int VT = KVQ_VTILE; // tokens per V code tile
+constexpr int MAX_GQ = 8;     // q-heads per kv-head handled by one attention block
+
+// ------------------------------------------------------------ binary16 bits
+__device__ __forceinline__ uint16_t h2bits(_Float16 h) { return __builtin_bit_cast(uint16_t, h); }
+__device__ __forceinline__ float bits2f(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// binary16 of x rounded toward -inf: convert to nearest-even, then step one
+// binary16 value down if that overshot x.
+__device__ __forceinline__ uint16_t f16_down(float x) {
+  uint16_t b = h2bits((_Float16)x);
+  if (bits2f(b) > x) b = (b & 0x8000u) ? (uint16_t)(b + 1) : (b == 0 ? (uint16_t)0x8001 : (uint16_t)(b - 1));
+  if ((b & 0x7FFFu) == 0) b = 0;   // store zero as +0
+  return b;
+}
+
+// binary16 of x rounded toward +inf.
+__device__ __forceinline__ uint16_t f16_up(float x) {
+  uint16_t b = h2bits((_Float16)x);
+  if (bits2f(b) < x) b = (b & 0x8000u) ? (b == 0x8000u ? (uint16_t)1 : (uint16_t)(b - 1)) : (uint16_t)(b + 1);
+  if ((b & 0x7FFFu) == 0) b = 0;
+  return b;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+// Load channel d of row `row` of an input tensor (fp32 or bf16).
+__device__ __forceinline__ float load_in(const void* p, int64_t idx, int bf16) {
+  return bf16 ? bf16_to_f32(((const uint16_t*)p)[idx]) : ((const float*)p)[idx];
+}
+
+// ------------------------------------------------------------ wave reductions
+template <int W>
+__device__ __forceinline__ float wmax(float v) {
+#pragma unroll
+  for (int o = 1; o < W; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+template <int W>
+__device__ __forceinline__ float wmin(float v) {
+#pragma unroll
+  for (int o = 1; o < W; o <<= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wmax_n(float v, int w) {
+  for (int o = 1; o < w; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wmin_n(float v, int w) {
+  for (int o = 1; o < w; o <<= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ uint32_t wor_n(uint32_t v, int w) {
+  for (int o = 1; o < w; o <<= 1) v |= __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ------------------------------------------------------------ launch blocks
+struct Regions {
+  uint8_t* codes[2];
+  uint32_t* sz[2];      // [U][tcap][NG] packed (s | z << 16)
+  uint8_t* idx[2];
+  uint16_t* t16[2];
+  float* tab[2];
+  float* win[2];
+  float* ws;
+};
+
+struct EncodeArgs {
+  Regions r;
+  const void* src[2];   // [U][src_rows][D]; this launch reads rows 0..n_new-1
+  int src_rows;
+  int n_new, t0, tcap, ngroups, group, bits, bf16, mode;
+  int n_pat, max_pat;
+  float rho;            // V threshold constant; < 0 disables
+  int tiles_per_block;  // V code tiles handled by one block
+  int win_update;       // accumulate the Chebyshev window over these tokens
+  int win_close;        // this call ends a window
+  int close_slot;       // table slot for the new centre, -1 = dropped
+};
+
+struct AttnArgs {
+  Regions r;
+  const void* q;        // [B][Hq][D]
+  float* out;           // [B][Hq][D]
+  int B, Hq, Hkv, gq, T, tcap, ngroups, group, bits, bf16, mode;
+  int n_pat, max_pat;
+  int splits, chunk;    // tokens per split (multiple of 64)
+  float qscale;         // sm_scale * log2(e)
+};
+
+struct DequantArgs {
+  Regions r;
+  float* out;           // [U][n][D]
+  int which, tok0, n, tcap, ngroups, group, bits, mode, max_pat;
+};
+
+// Host launchers (each returns the hipError_t of its launch).
+hipError_t launch_fill(float* p, float value, int64_t n, hipStream_t s);
+hipError_t launch_window_reset(float* win_k, float* win_v, int units, hipStream_t s);
+hipError_t launch_encode(const EncodeArgs& a, int units, int n_blocks_x, hipStream_t s);
+hipError_t launch_dequant(const DequantArgs& a, int units, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+hipError_t launch_kmeans_pair(const void* xk, const void* xv, int bf16, int n_tok, int k,
+                              float* tab_k, float* tab_v, int max_pat, int units, uint8_t* assign,
+                              hipStream_t s);
+hipError_t launch_chan_scale_pair(const void* xk, const void* xv, int bf16, int n_tok, float* sk,
+                                  float* sv, int units, hipStream_t s);
+
+}  // namespace kvq

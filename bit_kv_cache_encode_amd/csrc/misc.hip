@@ -1,0 +1,252 @@
+// misc.hip -- dequant readback, state fills and the prefill init kernels.
+//
+// Dequant: PatternKV section 3.2 (index restore after the Eq 1 inverse);
+// KVarN-style inverse (channel and token scale, inverse Hadamard rotation).
+// Init: PatternKV section 3.1 Eq 4 (per-head k-means over the prefill) and
+// the channel axis of KVarN's dual-axis normalisation.
+#include "kvq_internal.h"
+
+namespace kvq {
+
+// ------------------------------------------------------------ fills
+__global__ void fill_kernel(float* p, float v, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+hipError_t launch_fill(float* p, float value, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t want = (n + 255) / 256;
+  int blocks = (int)(want < 4096 ? want : 4096);
+  hipLaunchKernelGGL(fill_kernel, dim3(blocks), dim3(256), 0, s, p, value, n);
+  return hipGetLastError();
+}
+
+// Window state [U][2][D]: min row = +inf, max row = -inf.
+__global__ void window_reset_kernel(float* wk, float* wv, int units) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= units * 2 * D) return;
+  float v = ((i / D) & 1) ? -INFINITY : INFINITY;
+  wk[i] = v;
+  wv[i] = v;
+}
+
+hipError_t launch_window_reset(float* wk, float* wv, int units, hipStream_t s) {
+  int n = units * 2 * D;
+  hipLaunchKernelGGL(window_reset_kernel, dim3((n + 255) / 256), dim3(256), 0, s, wk, wv, units);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ dequant
+__device__ __forceinline__ uint32_t read_code(const uint8_t* codes, int which, int64_t u, int t,
+                                              int d, int tcap, int bits) {
+  int64_t byte;
+  int sh;
+  if (which == 0) {
+    int64_t bit = (int64_t)d * bits;
+    byte = (u * tcap + t) * (D * bits / 8) + bit / 8;
+    sh = (int)(bit & 7);
+  } else {
+    int64_t bit = (int64_t)(t % VT) * bits;
+    byte = (u * (tcap / VT) + t / VT) * (VT * D * bits / 8) + (int64_t)d * 4 * bits + bit / 8;
+    sh = (int)(bit & 7);
+  }
+  return (codes[byte] >> sh) & ((1u << bits) - 1u);
+}
+
+// One wave per (token, unit); lane l holds channels l and l+64.
+__global__ void __launch_bounds__(64) dequant_kernel(DequantArgs a) {
+  const int lane = threadIdx.x;
+  const int j = blockIdx.x, t = a.tok0 + j;
+  const int64_t u = blockIdx.y;
+  const int w = a.which;
+  const uint32_t* sz = a.r.sz[w] + (u * a.tcap + t) * a.ngroups;
+  float v[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    int d = lane + 64 * k;
+    uint32_t p = sz[d / a.group];
+    float s = bits2f((uint16_t)(p & 0xFFFF)), z = bits2f((uint16_t)(p >> 16));
+    float q = (float)read_code(a.r.codes[w], w, u, t, d, a.tcap, a.bits);
+    v[k] = __builtin_fmaf(q, s, z);
+  }
+  float* out = a.out + (u * a.n + j) * D;
+  if (a.mode == KVQ_MODE_PATTERN) {
+    int k = a.r.idx[w][u * a.tcap + t];
+    if (k != KVQ_INDEX_NONE) {
+      const float* m = a.r.tab[w] + (u * a.max_pat + k) * D;
+      v[0] = v[0] + m[lane];
+      v[1] = v[1] + m[lane + 64];
+    }
+    out[lane] = v[0];
+    out[lane + 64] = v[1];
+    return;
+  }
+  // KVarN inverse: y^ = fl(fl(w * t) * c); x^ = FWHT(y^) * fp32(1/sqrt(D)).
+  const float tf = bits2f(a.r.t16[w][u * a.tcap + t]);
+  const float* c = a.r.tab[w] + u * D;
+  float x0 = v[0] * tf, x1 = v[1] * tf;
+  x0 = x0 * c[lane];
+  x1 = x1 * c[lane + 64];
+#pragma unroll
+  for (int h = 1; h < 64; h <<= 1) {
+    float p0 = __shfl_xor(x0, h, 64), p1 = __shfl_xor(x1, h, 64);
+    if (lane & h) { x0 = p0 - x0; x1 = p1 - x1; }
+    else { x0 = x0 + p0; x1 = x1 + p1; }
+  }
+  float a0 = x0 + x1, a1 = x0 - x1;
+  const float isd = (float)(1.0 / __builtin_sqrt(128.0));
+  out[lane] = a0 * isd;
+  out[lane + 64] = a1 * isd;
+}
+
+hipError_t launch_dequant(const DequantArgs& a, int units, hipStream_t s) {
+  if (a.n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(dequant_kernel, dim3(a.n, units), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ k-means (Eq 4)
+// One block per (unit, kind).  Arithmetic mirrors the definition step by step
+// in binary64: distance = sum over channels, in channel order, of diff*diff;
+// strict '<' keeps the lowest index; centroid = member sum in token order
+// divided by the member count; empty clusters keep their centroid.
+constexpr int KM_THREADS = 256;
+constexpr int KM_MAXK = 64;
+constexpr int KM_ITERS = 50;
+
+struct KmShared {
+  double cent[KM_MAXK][D];
+  double sums[KM_MAXK][D];
+  int cnt[KM_MAXK];
+  int changed;
+};
+
+__global__ void __launch_bounds__(KM_THREADS) kmeans_kernel(const void* xk, const void* xv,
+                                                             int bf16, int n, int k, float* tab_k,
+                                                             float* tab_v, int max_pat,
+                                                             uint8_t* assign) {
+  extern __shared__ unsigned char km_raw[];
+  KmShared& sh = *reinterpret_cast<KmShared*>(km_raw);
+  const int kind = blockIdx.y;
+  const int64_t u = blockIdx.x;
+  const void* x = kind ? xv : xk;
+  float* tab = (kind ? tab_v : tab_k) + u * max_pat * D;
+  uint8_t* a = assign + ((int64_t)kind * gridDim.x + u) * n;
+  const int64_t xrow0 = u * (int64_t)n;
+
+  for (int i = threadIdx.x; i < k * D; i += KM_THREADS) {
+    int j = i / D, d = i % D;
+    int64_t row = (int64_t)j * n / k;
+    sh.cent[j][d] = (double)load_in(x, (xrow0 + row) * D + d, bf16);
+  }
+  __syncthreads();
+  for (int it = 0; it < KM_ITERS; ++it) {
+    if (threadIdx.x == 0) sh.changed = 0;
+    __syncthreads();
+    int changed = 0;
+    for (int t = threadIdx.x; t < n; t += KM_THREADS) {
+      float xr[D];
+      for (int d = 0; d < D; ++d) xr[d] = load_in(x, (xrow0 + t) * D + d, bf16);
+      int best = 0;
+      double bd = INFINITY;
+      for (int j = 0; j < k; ++j) {
+        double dist = 0.0;
+        for (int d = 0; d < D; ++d) {
+          double diff = (double)xr[d] - sh.cent[j][d];
+          dist = dist + diff * diff;
+        }
+        if (dist < bd) { bd = dist; best = j; }
+      }
+      if (it == 0 || a[t] != (uint8_t)best) changed = 1;
+      a[t] = (uint8_t)best;
+    }
+    if (changed) atomicOr(&sh.changed, 1);
+    __threadfence_block();
+    __syncthreads();
+    if (it > 0 && sh.changed == 0) break;
+    // update: thread d owns column d of the sums; tokens in order
+    for (int i = threadIdx.x; i < k * D; i += KM_THREADS) sh.sums[i / D][i % D] = 0.0;
+    if (threadIdx.x < KM_MAXK) sh.cnt[threadIdx.x] = 0;
+    __syncthreads();
+    if (threadIdx.x < D) {
+      const int d = threadIdx.x;
+      for (int t = 0; t < n; ++t) {
+        int j = a[t];
+        sh.sums[j][d] = sh.sums[j][d] + (double)load_in(x, (xrow0 + t) * D + d, bf16);
+        if (d == 0) sh.cnt[j] += 1;
+      }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < k * D; i += KM_THREADS) {
+      int j = i / D, d = i % D;
+      if (sh.cnt[j] > 0) sh.cent[j][d] = sh.sums[j][d] / (double)sh.cnt[j];
+    }
+    __syncthreads();
+  }
+  for (int i = threadIdx.x; i < k * D; i += KM_THREADS) tab[i] = (float)sh.cent[i / D][i % D];
+}
+
+hipError_t launch_kmeans_pair(const void* xk, const void* xv, int bf16, int n_tok, int k,
+                              float* tab_k, float* tab_v, int max_pat, int units, uint8_t* assign,
+                              hipStream_t s) {
+  size_t lds = sizeof(KmShared);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kmeans_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kmeans_kernel, dim3(units, 2), dim3(KM_THREADS), lds, s, xk, xv, bf16,
+                     n_tok, k, tab_k, tab_v, max_pat, assign);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ KVarN channel scale
+// c_j = sqrt(mean over prefix tokens of (y_j / rms(y))^2), y = FWHT(x)/sqrt(D),
+// in binary64; 0 becomes 1.  One block of 128 threads per (unit, kind).
+__global__ void __launch_bounds__(D) chan_scale_kernel(const void* xk, const void* xv, int bf16,
+                                                       int n, float* sk, float* sv) {
+  __shared__ double buf[D];
+  __shared__ double red[D];
+  const int kind = blockIdx.y, d = threadIdx.x;
+  const int64_t u = blockIdx.x;
+  const void* x = kind ? xv : xk;
+  double acc = 0.0;
+  int cnt = 0;
+  for (int t = 0; t < n; ++t) {
+    buf[d] = (double)load_in(x, (u * n + t) * D + d, bf16);
+    __syncthreads();
+    for (int h = 1; h < D; h <<= 1) {
+      double mine = buf[d], other = buf[d ^ h];
+      __syncthreads();
+      buf[d] = (d & h) ? other - mine : mine + other;
+      __syncthreads();
+    }
+    double y = buf[d] / sqrt((double)D);
+    red[d] = y * y;
+    __syncthreads();
+    for (int h = D / 2; h >= 1; h >>= 1) {
+      if (d < h) red[d] += red[d + h];
+      __syncthreads();
+    }
+    double r = sqrt(red[0] / (double)D);
+    __syncthreads();
+    if (r > 0.0) {
+      acc += (y / r) * (y / r);
+      cnt++;
+    }
+  }
+  float c = cnt ? (float)sqrt(acc / (double)cnt) : 1.0f;
+  (kind ? sv : sk)[u * D + d] = (c == 0.0f) ? 1.0f : c;
+}
+
+hipError_t launch_chan_scale_pair(const void* xk, const void* xv, int bf16, int n_tok, float* sk,
+                                  float* sv, int units, hipStream_t s) {
+  hipLaunchKernelGGL(chan_scale_kernel, dim3(units, 2), dim3(D), 0, s, xk, xv, bf16, n_tok, sk, sv);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,181 @@
+/*
+ * kvq.h -- low-bit (2/4-bit) KV-cache encode and single-query decode
+ * attention over the packed cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The method is PatternKV's pattern-aligned residual quantization
+ * (arXiv 2510.05176v2, "PatternKV: Flattening KV Representation Expands
+ * Quantization Headroom"), with a KVarN-style second encode mode (arXiv
+ * 2606.03458, Hadamard rotation plus variance normalisation over both axes;
+ * NSNQuant, arXiv 2505.18231, token-wise normalisation with a Hadamard
+ * transform).
+ *
+ * Conventions shared by every call
+ *  - Return 0 (KVQ_OK) or a negative status.  Every argument is validated on
+ *    the host before anything is launched, so a call that fails leaves the
+ *    cache and all outputs untouched.  No exception crosses this interface.
+ *  - Tensor pointers are DEVICE pointers, 16-byte aligned, row-major and
+ *    contiguous in the shapes stated.  Inputs are binary32 (KVQ_F32) or
+ *    bfloat16 (KVQ_BF16) as the cache's in_dtype says; outputs are binary32.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *    work on it and never synchronise or copy device data to the host.
+ *  - A cache must not be used from two streams or two threads at once.
+ *  - The library never allocates device memory: the caller owns one device
+ *    buffer per cache (kvq_layout_of().total bytes, 256-byte aligned) and
+ *    frees it.  The split-K workspace of the attention lives in that buffer.
+ *  - Supported shapes: head_dim 128; bits 2 or 4; group divides 128 and is a
+ *    multiple of 8; max_patterns <= 255; n_q_heads a multiple of
+ *    n_kv_heads with at most 8 q-heads per kv-head.
+ *  - Domain: finite inputs with |x| < 16384.  Outside it codes and scales are
+ *    unspecified (no error is raised; checking would need a device sync).
+ *
+ * Stored format (per (batch, kv-head) "unit", for K and for V alike unless
+ * noted; T = token capacity rounded up to 32):
+ *  - codes: T * 128 * bits / 8 bytes.  K is token-major: channel d of a token
+ *    sits at bit bits*d of the token's record (little-endian).  V is stored
+ *    in tiles of 32 tokens, channel-major: channel d of a tile owns 4*bits
+ *    bytes and token i of the tile sits at bit bits*i.
+ *  - sz: per token and group, the binary16 scale s then the binary16 zero z
+ *    (Eq 1: x^ = s*q + z).  z is the group minimum rounded toward -inf, s is
+ *    (max - z)/(2^bits - 1) rounded toward +inf; codes are
+ *    clamp(rint((r - z) * fl(1/s)), 0, 2^bits - 1), 0 when s == 0.
+ *  - idx (PATTERN): one byte per token, the stored pattern index k* of
+ *    section 3.2, 0xFF when the raw vector was quantized.
+ *  - t16 (KVARN): one binary16 token scale per token.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_OK 0
+#define KVQ_EINVAL (-1)     /* bad argument or configuration */
+#define KVQ_ECAPACITY (-2)  /* append would exceed max_tokens */
+#define KVQ_ESTATE (-3)     /* call not valid in the cache's state */
+#define KVQ_EDEVICE (-4)    /* a HIP launch or runtime call failed */
+
+#define KVQ_MODE_PATTERN 0  /* PatternKV residual encode */
+#define KVQ_MODE_KVARN 1    /* Hadamard + dual-axis normalisation encode */
+#define KVQ_F32 0
+#define KVQ_BF16 1
+#define KVQ_INDEX_NONE 0xFF
+#define KVQ_VTILE 32
+
+typedef struct {
+  int32_t batch;          /* B */
+  int32_t n_q_heads;      /* Hq */
+  int32_t n_kv_heads;     /* Hkv; q-head hq attends to kv-head hq / (Hq/Hkv) */
+  int32_t head_dim;       /* D, must be 128 */
+  int32_t max_tokens;     /* token capacity per unit */
+  int32_t bits;           /* 2 or 4 */
+  int32_t group;          /* channels per quantization group (Eq 1 scope) */
+  int32_t mode;           /* KVQ_MODE_PATTERN or KVQ_MODE_KVARN */
+  int32_t max_patterns;   /* pattern table capacity per unit and kind, <= 255 */
+  int32_t pattern_window; /* G_pattern of Eq 5 (0 = no decode-time patterns) */
+  float v_alpha;          /* z-test level of section 3.3; <= 0 disables it */
+  int32_t in_dtype;       /* KVQ_F32 or KVQ_BF16 for k, v and q inputs */
+  int32_t max_splits;     /* split-K workspace capacity; 0 = derived */
+} kvq_config;
+
+/* Byte offsets (from the cache base) and sizes of every region. */
+typedef struct {
+  uint64_t k_codes, v_codes, k_sz, v_sz, k_idx, v_idx, k_t16, v_t16;
+  uint64_t k_tab, v_tab;  /* PATTERN: fp32 [U][max_patterns][D]; KVARN: fp32 [U][D] */
+  uint64_t k_win, v_win;  /* PATTERN window state: fp32 [U][2][D] (min, max) */
+  uint64_t ws;            /* split-K partials */
+  uint64_t codes_bytes, sz_bytes, idx_bytes, t16_bytes, tab_bytes, win_bytes, ws_bytes;
+  uint64_t total;
+  int32_t token_cap;      /* max_tokens rounded up to KVQ_VTILE */
+  int32_t n_groups;       /* head_dim / group */
+  int32_t record_bytes;   /* stored bytes per token per unit and kind */
+  int32_t max_splits;
+} kvq_layout;
+
+typedef struct {
+  kvq_config cfg;
+  void* base;             /* device buffer of layout.total bytes */
+  int32_t n_tokens;       /* tokens stored per unit */
+  int32_t n_patterns;     /* patterns in every unit's table */
+  int32_t win_count;      /* decode appends in the open Chebyshev window */
+  int32_t dropped;        /* window centres dropped because the table was full */
+  float rho;              /* binary32 rho*(head_dim, v_alpha) of Eq 10 */
+} kvq_cache;
+
+/* Layout of a cache for `cfg`.  Host only; touches no device.
+ * KVQ_EINVAL if the configuration is not supported. */
+int kvq_layout_of(const kvq_config* cfg, kvq_layout* out);
+
+/* Bind `cache` to a caller-allocated device buffer of `bytes` bytes
+ * (>= layout.total, 256-byte aligned) and reset it: no tokens, no patterns,
+ * empty Chebyshev window (launches one fill kernel on `stream`).
+ * KVQ_EINVAL on a bad config, size or alignment. */
+int kvq_cache_init(kvq_cache* cache, const kvq_config* cfg, void* base, uint64_t bytes,
+                   void* stream);
+
+/* Prefill pattern mining (PatternKV section 3.1, Eq 4): for every unit and for
+ * K and V separately, Euclidean k-means over the n_tok prefix vectors
+ * (k: [B][Hkv][n_tok][D], v likewise) into n_patterns centroids: centroid j
+ * starts at prefix row floor(j*n_tok/n_patterns); Lloyd iterations run until
+ * no assignment changes (at most 50), ties go to the lowest index, an empty
+ * cluster keeps its centroid; binary64 arithmetic, stored as fp32.
+ * KVARN mode instead sets each unit's per-channel scale c_j to the root mean
+ * square over the prefix of (y_j / rms(y)) with y the orthonormal Hadamard
+ * rotation of the token (0 becomes 1): the channel axis of KVarN's dual-axis
+ * normalisation (arXiv 2606.03458, abstract).  Resets the Chebyshev window.
+ * KVQ_EINVAL if n_tok < 1 or n_patterns > max_patterns. */
+int kvq_init_patterns(kvq_cache* cache, const void* k, const void* v, int32_t n_tok,
+                      int32_t n_patterns, void* stream);
+
+/* Upload pattern tables mined elsewhere: k_tab and v_tab are fp32 device
+ * arrays [B][Hkv][n][D] (PATTERN, n <= max_patterns) or per-channel scales
+ * [B][Hkv][D] (KVARN, n ignored).  Resets the Chebyshev window.
+ * KVQ_EINVAL on a bad n or null pointer. */
+int kvq_set_patterns(kvq_cache* cache, const float* k_tab, const float* v_tab, int32_t n,
+                     void* stream);
+
+/* Encode n_new tokens per unit (k_new, v_new: [B][Hkv][n_new][D]) and append
+ * them at position n_tokens.
+ * PATTERN (section 3.2, Eq 6 and Eq 1): each vector takes its nearest pattern
+ * under d_mm(x, m) = max_i(x_i - m_i) - min_j(x_j - m_j) (lowest index on
+ * ties), subtracts it and quantizes the residual per group; a V vector keeps
+ * its pattern only if R_flat <= rho* R_raw (section 3.3, Eq 10), else it
+ * stores index 0xFF and quantizes the raw vector.  update_patterns != 0 marks
+ * decode-stage appends: they feed the Chebyshev window (Eq 5) whose centre
+ * fl(fl(min + max) * 0.5) joins the table after every pattern_window-th such
+ * token and serves the tokens after it.
+ * KVARN: y = Hadamard(x)/sqrt(D), y~ = y / c, t = rms(y~) stored as binary16,
+ * u = y~ / t quantized per group (update_patterns is ignored).
+ * KVQ_ECAPACITY if n_tokens + n_new > max_tokens; KVQ_EINVAL on null inputs
+ * or n_new < 0. */
+int kvq_encode_append(kvq_cache* cache, const void* k_new, const void* v_new, int32_t n_new,
+                      int32_t update_patterns, void* stream);
+
+/* Single-query decode attention over all n_tokens cached tokens, reading the
+ * packed cache directly (PatternKV section 3.4: pattern restore, dequant and
+ * the QK product fused; dequant, pattern restore and the attention-weighted
+ * sum over V fused).  q: [B][Hq][D] in in_dtype; out: fp32 [B][Hq][D];
+ * out = softmax(sm_scale * q . k^) v^ with k^, v^ the dequantized cache
+ * (sm_scale <= 0 means 1/sqrt(D)).  Split-K over tokens with a combine pass.
+ * KVQ_ESTATE if the cache is empty; KVQ_EINVAL on null pointers. */
+int kvq_attn_decode(kvq_cache* cache, const void* q, float* out, float sm_scale, void* stream);
+
+/* Dequantize tokens tok0 .. tok0+n-1 of K (which = 0) or V (which = 1) into
+ * fp32 out [B][Hkv][n][D]: PATTERN x^ = fl(fmaf(q, s, z) + M_k*) (the index
+ * restore of section 3.2), or fmaf(q, s, z) alone for index 0xFF; KVARN
+ * x^ = Hadamard(fl(fl(fmaf(q, s, z) * t) * c)) / sqrt(D).
+ * KVQ_EINVAL on a bad `which` or a span outside [0, n_tokens). */
+int kvq_dequant(const kvq_cache* cache, int32_t which, int32_t tok0, int32_t n, float* out,
+                void* stream);
+
+/* Message for a status code (static storage). */
+const char* kvq_strerror(int status);
+
+/* The HIP error code behind the most recent KVQ_EDEVICE on this thread. */
+int kvq_last_device_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

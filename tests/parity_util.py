@@ -1,0 +1,104 @@
+"""Helpers shared by the GPU parity tests: build matching oracle / GPU caches
+from the same seeded inputs and compare their stored bytes.
+
+The oracle never receives anything produced by the GPU: both sides get the
+same synthetic inputs (and the oracle computes its own pattern tables).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+from bit_kv_cache_encode_amd import synth
+
+ATTN_TOL = 2e-3        # absolute, attention outputs (bf16 inputs)
+DEQ_RTOL = 1e-6        # relative, dequantised values
+
+
+def to_dev(x: np.ndarray, dtype: torch.dtype, device="cuda") -> torch.Tensor:
+    """fp32 numpy -> device tensor of `dtype` (bf16 by nearest-even)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(dtype).to(device).contiguous()
+
+
+def to_oracle(x: np.ndarray, bf16: bool) -> np.ndarray:
+    """The same values as the oracle receives them (bf16 as bit patterns)."""
+    return synth.f32_to_bf16_bits(x) if bf16 else np.ascontiguousarray(x, dtype=np.float32)
+
+
+def dev_to_oracle(t: torch.Tensor) -> np.ndarray:
+    """A device input tensor as oracle input (bf16 -> uint16 bits)."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.float().cpu().numpy()
+
+
+def gpu_sz(cache, which: int) -> np.ndarray:
+    L = cache.layout
+    a = cache.region("kv"[which] + "_sz").cpu().numpy().view(np.uint16)
+    return a.reshape(cache.cfg.batch * cache.cfg.n_kv_heads, L.token_cap, L.n_groups, 2)
+
+
+def gpu_idx(cache, which: int) -> np.ndarray:
+    L = cache.layout
+    return cache.region("kv"[which] + "_idx").cpu().numpy().reshape(-1, L.token_cap)
+
+
+def gpu_t16(cache, which: int) -> np.ndarray:
+    L = cache.layout
+    return cache.region("kv"[which] + "_t16").cpu().numpy().view(np.uint16).reshape(-1, L.token_cap)
+
+
+def gpu_codes(cache, which: int, T: int) -> np.ndarray:
+    c = cache.cfg
+    packed = cache.region("kv"[which] + "_codes").cpu().numpy().reshape(c.batch * c.n_kv_heads, -1)
+    return O.unpack_codes(packed, which, T, c.head_dim, c.bits)
+
+
+def gpu_tab(cache, which: int) -> np.ndarray:
+    c = cache.cfg
+    a = cache.region("kv"[which] + "_tab").cpu().numpy().view(np.float32)
+    U = c.batch * c.n_kv_heads
+    return a.reshape(U, c.max_patterns, c.head_dim) if cache.mode == "pattern" else a.reshape(U, c.head_dim)
+
+
+def assert_same_encode(ref: "O.RefCache", cache, T: int, units=None, ref_units=None) -> None:
+    """Codes, scales, indices (and t16) bit-exact for tokens < T.
+
+    units: GPU unit indices to compare; ref_units: matching oracle units."""
+    c = cache.cfg
+    U = c.batch * c.n_kv_heads
+    units = list(range(U)) if units is None else list(units)
+    ref_units = units if ref_units is None else list(ref_units)
+    for which in (0, 1):
+        gc = gpu_codes(cache, which, T)[units]
+        rc = O.unpack_codes(ref.codes(which), which, T, c.head_dim, c.bits)[ref_units]
+        bad = gc != rc
+        assert not bad.any(), (f"{'KV'[which]} codes differ at {np.argwhere(bad)[:5]} "
+                               f"(ties there: {ref.ties(which)[ref_units][:, :T][bad][:5]})")
+        gs = gpu_sz(cache, which)[units, :T]
+        rs = ref.sz(which)[ref_units, :T]
+        assert np.array_equal(gs, rs), f"{'KV'[which]} scales differ at {np.argwhere(gs != rs)[:5]}"
+        if cache.mode == "pattern":
+            gi = gpu_idx(cache, which)[units, :T]
+            ri = ref.idx(which)[ref_units, :T]
+            assert np.array_equal(gi, ri), f"{'KV'[which]} idx differ at {np.argwhere(gi != ri)[:5]}"
+        else:
+            gt = gpu_t16(cache, which)[units, :T]
+            rt = ref.t16(which)[ref_units, :T]
+            assert np.array_equal(gt, rt), f"{'KV'[which]} t16 differ at {np.argwhere(gt != rt)[:5]}"
+
+
+def make_pair(B, Hq, Hkv, max_tokens, *, bits=2, group=32, mode="pattern", max_patterns=32,
+              pattern_window=128, v_alpha=0.05, bf16=True):
+    from bit_kv_cache_encode_amd import KVCache
+    dt = torch.bfloat16 if bf16 else torch.float32
+    gpu = KVCache(B, Hq, Hkv, max_tokens, bits=bits, group=group, mode=mode,
+                  max_patterns=max_patterns, pattern_window=pattern_window, v_alpha=v_alpha,
+                  in_dtype=dt)
+    ref = O.RefCache(B, Hq, Hkv, 128, max_tokens, bits=bits, group=group,
+                     mode=O.PATTERN if mode == "pattern" else O.KVARN,
+                     max_patterns=max_patterns, pattern_window=pattern_window, v_alpha=v_alpha,
+                     in_dtype=O.IN_BF16 if bf16 else O.IN_F32)
+    return gpu, ref, dt

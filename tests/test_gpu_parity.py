@@ -1,0 +1,198 @@
+"""GPU parity: the HIP path (through the C-ABI) against the CPU oracle.
+
+Bar: codes, scales, pattern indices and token scales bit-exact; dequantised
+values within 1e-6 relative; attention within 2e-3 absolute.  Sizes span
+several 32/64-token tiles with ragged tails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from bit_kv_cache_encode_amd import synth
+from parity_util import (ATTN_TOL, DEQ_RTOL, assert_same_encode, gpu_tab, make_pair, to_dev,
+                         to_oracle)
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(B, H, T, seed_off=0):
+    k = synth.k_vectors(B, H, T, 128, seed=synth.seed_for("k") + seed_off)
+    v = synth.v_vectors(B, H, T, 128, seed=synth.seed_for("v") + seed_off)
+    return k, v
+
+
+def _check_dequant(ref, gpu, T):
+    for which in (0, 1):
+        g = gpu.dequant(which, 0, T).cpu().numpy()
+        r = ref.dequant(which, 0, T)
+        np.testing.assert_allclose(g, r, rtol=DEQ_RTOL, atol=1e-7)
+
+
+def _check_attn(ref, gpu, q_np, bf16):
+    dt = torch.bfloat16 if bf16 else torch.float32
+    out = gpu.attn_decode(to_dev(q_np, dt)).cpu().numpy()
+    want = ref.attn_decode(to_oracle(q_np, bf16))
+    err = np.abs(out - want).max()
+    assert err <= ATTN_TOL, f"attention max abs err {err}"
+    return err
+
+
+def test_tiny_reference_config():
+    """1 KV head, T=256, fp32, 8 k-means patterns, 2-bit, group 32."""
+    B, Hq, H, T = 1, 1, 1, 256
+    gpu, ref, dt = make_pair(B, Hq, H, T, max_patterns=8, bf16=False)
+    k, v = _inputs(B, H, T)
+    assert ref.init_patterns(k, v, 8) == 0
+    gpu.init_patterns(to_dev(k, dt), to_dev(v, dt), 8)
+    torch.cuda.synchronize()
+    for which in (0, 1):
+        assert np.array_equal(gpu_tab(gpu, which)[:, :8], ref.patterns(which)[:, :8])
+    assert ref.encode_append(k, v) == 0
+    gpu.encode_append(to_dev(k, dt), to_dev(v, dt))
+    assert_same_encode(ref, gpu, T)
+    _check_dequant(ref, gpu, T)
+    _check_attn(ref, gpu, synth.queries(B, Hq, 128), bf16=False)
+
+
+@pytest.mark.parametrize("T", [1, 31, 64, 300])
+def test_llama_shape_encode_attend(T):
+    """Llama-3-8B head geometry (32 q / 8 kv, GQA 4), bf16, 32 patterns."""
+    B, Hq, H = 2, 8, 2
+    gpu, ref, dt = make_pair(B, Hq, H, 512, max_patterns=32)
+    kp, vp = _inputs(B, H, 200, seed_off=5)
+    ref.init_patterns(to_oracle(kp, True), to_oracle(vp, True), 32)
+    gpu.init_patterns(to_dev(kp, dt), to_dev(vp, dt), 32)
+    k, v = _inputs(B, H, T)
+    ref.encode_append(to_oracle(k, True), to_oracle(v, True))
+    gpu.encode_append(to_dev(k, dt), to_dev(v, dt))
+    assert_same_encode(ref, gpu, T)
+    _check_dequant(ref, gpu, T)
+    _check_attn(ref, gpu, synth.queries(B, Hq, 128), bf16=True)
+
+
+@pytest.mark.parametrize("bits,group,gq,npat", [(4, 64, 4, 64), (2, 32, 7, 64), (2, 64, 1, 16),
+                                                 (4, 32, 2, 0), (2, 128, 8, 255)])
+def test_shape_variants(bits, group, gq, npat):
+    B, H, T = 1, 2, 333
+    gpu, ref, dt = make_pair(B, gq * H, H, 400, bits=bits, group=group, max_patterns=max(npat, 1))
+    if npat:
+        rng = np.random.default_rng(npat)
+        tk = rng.standard_normal((B, H, npat, 128)).astype(np.float32)
+        tv = rng.standard_normal((B, H, npat, 128)).astype(np.float32)
+        ref.set_patterns(tk, tv)
+        gpu.set_patterns(torch.from_numpy(tk).cuda(), torch.from_numpy(tv).cuda())
+    k, v = _inputs(B, H, T, seed_off=bits)
+    ref.encode_append(to_oracle(k, True), to_oracle(v, True))
+    gpu.encode_append(to_dev(k, dt), to_dev(v, dt))
+    assert_same_encode(ref, gpu, T)
+    _check_dequant(ref, gpu, T)
+    _check_attn(ref, gpu, synth.queries(B, gq * H, 128, step=3), bf16=True)
+
+
+def test_kvarn_mode():
+    """Hadamard + dual-axis normalisation encode, with oracle channel scales."""
+    B, Hq, H, T = 2, 8, 2, 150
+    gpu, ref, dt = make_pair(B, Hq, H, 256, mode="kvarn", max_patterns=0)
+    kp, vp = _inputs(B, H, 64, seed_off=9)
+    ref.init_patterns(to_oracle(kp, True), to_oracle(vp, True), 0)
+    cs_k, cs_v = ref.scales(0).reshape(B, H, 128), ref.scales(1).reshape(B, H, 128)
+    # GPU channel scales agree with the oracle's within rounding (binary64 sums
+    # in a different order), then the oracle's are uploaded so the encode is
+    # compared on identical inputs.
+    gpu.init_patterns(to_dev(kp, dt), to_dev(vp, dt), 0)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(gpu_tab(gpu, 0).reshape(B, H, 128), cs_k, rtol=1e-6)
+    np.testing.assert_allclose(gpu_tab(gpu, 1).reshape(B, H, 128), cs_v, rtol=1e-6)
+    gpu.set_patterns(torch.from_numpy(np.ascontiguousarray(cs_k)).cuda(),
+                     torch.from_numpy(np.ascontiguousarray(cs_v)).cuda())
+    k, v = _inputs(B, H, T)
+    ref.encode_append(to_oracle(k, True), to_oracle(v, True))
+    gpu.encode_append(to_dev(k, dt), to_dev(v, dt))
+    assert_same_encode(ref, gpu, T)
+    _check_dequant(ref, gpu, T)
+    _check_attn(ref, gpu, synth.queries(B, Hq, 128), bf16=True)
+
+
+def test_chunked_appends_equal_bulk():
+    """Appending in ragged pieces stores the same bytes as one bulk append
+    (V tiles shared between calls keep the other calls' bits)."""
+    B, Hq, H, T = 1, 4, 1, 250
+    k, v = _inputs(B, H, T)
+    a, ref, dt = make_pair(B, Hq, H, 256)
+    b, _, _ = make_pair(B, Hq, H, 256)
+    kd, vd = to_dev(k, dt), to_dev(v, dt)
+    for c in (a, b):
+        c.init_patterns(kd[:, :, :128].contiguous(), vd[:, :, :128].contiguous(), 16)
+    a.encode_append(kd, vd)
+    pos = 0
+    for n in (3, 29, 1, 64, 5, 100, 48):
+        b.encode_append(kd[:, :, pos:pos + n].contiguous(), vd[:, :, pos:pos + n].contiguous())
+        pos += n
+    assert pos == T
+    torch.cuda.synchronize()
+    for name in ("k_codes", "k_sz", "k_idx", "v_sz", "v_idx"):
+        L = a.layout
+        per = {"k_codes": 32, "k_sz": 16, "k_idx": 1, "v_sz": 16, "v_idx": 1}[name]
+        assert torch.equal(a.region(name)[:T * per], b.region(name)[:T * per]), name
+    assert torch.equal(a.region("v_codes")[:T // 32 * 1024], b.region("v_codes")[:T // 32 * 1024])
+    ga = a.dequant(1, 0, T)
+    gb = b.dequant(1, 0, T)
+    assert torch.equal(ga, gb)
+
+
+def test_streaming_chebyshev_window():
+    """Decode appends one token at a time: a Chebyshev centre joins the table
+    after every window; later tokens use it; GPU and oracle agree bit for bit."""
+    B, Hq, H, W = 2, 8, 2, 16
+    gpu, ref, dt = make_pair(B, Hq, H, 256, max_patterns=6, pattern_window=W)
+    kp, vp = _inputs(B, H, 64, seed_off=11)
+    ref.init_patterns(to_oracle(kp, True), to_oracle(vp, True), 4)
+    gpu.init_patterns(to_dev(kp, dt), to_dev(vp, dt), 4)
+    ref.encode_append(to_oracle(kp, True), to_oracle(vp, True))
+    gpu.encode_append(to_dev(kp, dt), to_dev(vp, dt))
+    k, v = _inputs(B, H, 3 * W + 7, seed_off=12)
+    drift = synth.drift_dirs(B, H, 128)
+    k = k + 0.5 * np.arange(k.shape[2], dtype=np.float32)[None, None, :, None] * drift[:, :, None, :]
+    for t in range(k.shape[2]):
+        kt, vt = k[:, :, t:t + 1], v[:, :, t:t + 1]
+        ref.encode_append(to_oracle(kt, True), to_oracle(vt, True), update=1)
+        gpu.encode_append(to_dev(kt, dt), to_dev(vt, dt), update_patterns=True)
+        assert gpu.n_patterns == ref.n_patterns and gpu.win_count == ref.win_count
+    assert ref.n_patterns == 6 and ref.dropped == 1
+    T = ref.n_tokens
+    assert_same_encode(ref, gpu, T)
+    for which in (0, 1):
+        assert np.array_equal(gpu_tab(gpu, which)[:, :6], ref.patterns(which)[:, :6])
+    _check_attn(ref, gpu, synth.queries(B, Hq, 128, step=1), bf16=True)
+    # a multi-token decode append crossing a window boundary is split there
+    k2, v2 = _inputs(B, H, 2 * W + 3, seed_off=13)
+    ref.encode_append(to_oracle(k2, True), to_oracle(v2, True), update=1)
+    gpu.encode_append(to_dev(k2, dt), to_dev(v2, dt), update_patterns=True)
+    assert gpu.n_patterns == ref.n_patterns and gpu.dropped == ref.dropped
+    assert_same_encode(ref, gpu, ref.n_tokens)
+
+
+def test_determinism_and_checkpoint():
+    """Two runs give byte-identical caches; a snapshot restored into a fresh
+    buffer continues identically."""
+    B, Hq, H, T = 2, 8, 2, 200
+    k, v = _inputs(B, H, T)
+    caches = []
+    for _ in range(2):
+        g, _, dt = make_pair(B, Hq, H, 512)
+        g.init_patterns(to_dev(k, dt), to_dev(v, dt), 8)
+        g.encode_append(to_dev(k, dt), to_dev(v, dt))
+        caches.append(g)
+    torch.cuda.synchronize()
+    assert torch.equal(caches[0].buf[:caches[0].layout.ws], caches[1].buf[:caches[1].layout.ws])
+    snap = caches[0].snapshot()
+    fresh, _, dt = make_pair(B, Hq, H, 512)
+    fresh.restore(snap)
+    k2, v2 = _inputs(B, H, 40, seed_off=3)
+    for c in (caches[0], fresh):
+        c.encode_append(to_dev(k2, dt), to_dev(v2, dt), update_patterns=True)
+    q = to_dev(synth.queries(B, Hq, 128), dt)
+    assert torch.equal(caches[0].attn_decode(q), fresh.attn_decode(q))
+    torch.cuda.synchronize()
+    assert torch.equal(caches[0].buf[:caches[0].layout.ws], fresh.buf[:fresh.layout.ws])
