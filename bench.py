@@ -1,0 +1,232 @@
+"""Benchmark: decode steps over a 2-bit PatternKV-packed KV cache on one MI355X.
+
+Workload (the Llama-3-8B-shaped 32k-context decode configuration): batch 8,
+32 q-heads / 8 kv-heads (GQA 4), head_dim 128, bf16 K/V/q, 2-bit codes in
+groups of 32 channels, 32 k-means patterns per head, V threshold alpha 0.05,
+Chebyshev window 128, context 32768.  One step is one decode step of a
+32-layer stack: for every layer, encode-append the new token's K and V
+(update_patterns on) and run single-query decode attention over the packed
+cache.  The 32 layer caches (6.9 GB) are distinct buffers, so the 256 MB
+Infinity Cache cannot hold them.
+
+value = algorithmic bytes of a step / step time (effective GB/s); the bytes
+are the packed cache records read by attention, the pattern tables read by
+attention and encode, the new K/V read and records written by encode, q and
+the outputs.  The roofline object covers the attention kernel alone, timed
+with events on the stream it runs on.  A bulk (prefill-style) encode rate is
+reported as encode tokens/s.  The CPU oracle is timed on a bounded sample.
+
+Usage: python bench.py [--steps K] [--warmup W] [--context T] [--layers L]
+       [--no-cpu-baseline] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn effective GB/s over 2-bit packed KV (% of HBM peak); encode tok/s"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attention.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--context", type=int, default=32768)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--batch", type=int, default=8)
+    ap.add_argument("--kmeans-tokens", type=int, default=2048)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--attn-only", type=int, default=0,
+                    help="profiling aid: run N attention calls on the layer caches and exit")
+    return ap.parse_args()
+
+
+def attn_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("attn.hip", "attn_mfma.hip", "kvq_internal.h"):
+        p = os.path.join(ROOT, "bit_kv_cache_encode_amd", "csrc", f)
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the decode path shards by (batch, kv-head) with no communication; see "
+              "DESIGN.md for the multi-GPU layout)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from bit_kv_cache_encode_amd import KVCache, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    B, Hq, H, D, T0, L = args.batch, 32, 8, 128, args.context, args.layers
+    P, W = 32, 128
+    n_steps = args.warmup + args.steps
+    max_tokens = T0 + n_steps + 64
+    U = B * H
+
+    # ---- setup (untimed): one layer mined + bulk-encoded, then replicated
+    k, v = synth.device_kv(B, H, T0, D, layer=0, device=dev)
+    base = KVCache(B, Hq, H, max_tokens, bits=2, group=32, mode="pattern", max_patterns=P,
+                   pattern_window=W, v_alpha=0.05, in_dtype=torch.bfloat16, device=dev)
+    nk = min(args.kmeans_tokens, T0)
+    base.init_patterns(k[:, :, :nk].contiguous(), v[:, :, :nk].contiguous(), P)
+    torch.cuda.synchronize()
+    # bulk encode rate: the whole prefix in one append (prefill-style)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    base.encode_append(k, v)
+    e1.record()
+    torch.cuda.synchronize()
+    bulk_ms = e0.elapsed_time(e1)
+    # repeat the bulk encode on a scratch cache to get a warm measurement
+    scratch = KVCache(B, Hq, H, T0, bits=2, group=32, mode="pattern", max_patterns=P,
+                      pattern_window=W, v_alpha=0.05, in_dtype=torch.bfloat16, device=dev)
+    scratch.set_patterns(base.region("k_tab").view(torch.float32).view(B, H, P, D).clone(),
+                         base.region("v_tab").view(torch.float32).view(B, H, P, D).clone())
+    e0.record()
+    scratch.encode_append(k, v)
+    e1.record()
+    torch.cuda.synchronize()
+    bulk_ms = min(bulk_ms, e0.elapsed_time(e1))
+    del scratch, k, v
+    layers = [base] + [base.clone() for _ in range(L - 1)]
+    torch.cuda.synchronize()
+
+    # per-step inputs: new K/V token per layer, one query per layer
+    kn, vn = synth.device_kv(B, H, n_steps * L, D, layer=1, device=dev)
+    kn = kn.view(B, H, n_steps, L, D).permute(2, 3, 0, 1, 4).contiguous()
+    vn = vn.view(B, H, n_steps, L, D).permute(2, 3, 0, 1, 4).contiguous()
+    qs = [synth.device_queries(B, Hq, D, step=s, device=dev) for s in range(L)]
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+
+    if args.attn_only:
+        for i in range(args.attn_only):
+            layers[i % L].attn_decode(qs[i % L], out=out)
+        torch.cuda.synchronize()
+        print(f"attn-only: {args.attn_only} calls done")
+        return
+
+    rec = base.layout.record_bytes
+    in_b = 2
+
+    def attn_bytes(T):
+        return 2 * U * T * rec + 2 * U * P * D * 4 + B * Hq * D * (in_b + 4)
+
+    enc_bytes = 2 * U * D * in_b + 2 * U * rec + 2 * U * P * D * 4
+
+    def step(s, ev=None):
+        for li, c in enumerate(layers):
+            c.encode_append(kn[s, li][:, :, None, :], vn[s, li][:, :, None, :],
+                            update_patterns=True)
+            if ev is not None:
+                ev[li][0].record()
+            c.attn_decode(qs[li], out=out)
+            if ev is not None:
+                ev[li][1].record()
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    T_start = layers[0].n_tokens
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in range(L)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(args.warmup + s, evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    attn_ms = [e[0].elapsed_time(e[1]) for st in evs for e in st]
+    attn_avg_us = 1e3 * sum(attn_ms) / len(attn_ms)
+    T_mid = T_start + args.steps // 2 + 1
+    step_bytes = L * (attn_bytes(T_mid) + enc_bytes)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = attn_bytes(T_mid) / (attn_avg_us * 1e-6) / 1e9
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tr = json.load(open(TRAFFIC_FILE))
+        if tr.get("source_hash") == attn_source_hash():
+            traffic = tr.get("bytes_per_launch")
+
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": (f"decode step of a {L}-layer Llama-3-8B-shaped stack: batch {B}, "
+                                f"{Hq} q / {H} kv heads, head_dim {D}, context {T0}, bf16 in, "
+                                f"2-bit PatternKV codes (group 32, {P} patterns, alpha 0.05, "
+                                f"window {W}); per layer encode-append 1 token + decode attention"),
+                   "batch": B, "context": T0, "layers": L, "n_q_heads": Hq, "n_kv_heads": H,
+                   "head_dim": D, "bits": 2, "group": 32, "patterns": P},
+        "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "attention (split + combine)",
+                     "avg_launch_us": round(attn_avg_us, 3),
+                     "algorithmic_bytes_per_launch": attn_bytes(T_mid)},
+        "encode": {"bulk_tok_s": round(B * T0 / (bulk_ms * 1e-3), 1),
+                   "bulk_tokens": B * T0, "bulk_ms": round(bulk_ms, 3),
+                   "token": "one position's K and V for all 8 kv-heads of one layer"},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args, T0, P, W, attn_bytes, enc_bytes, U)
+    print(json.dumps(res))
+
+
+def cpu_baseline(args, T0, P, W, attn_bytes, enc_bytes, U):
+    """The oracle, as it stands, on a bounded sample of the same workload: one
+    (batch, kv-head) unit at the same context, decode steps (encode 1 token
+    with the Chebyshev window on + 4-q-head attention) repeated until the time
+    budget is spent."""
+    import oracle as O
+    from bit_kv_cache_encode_amd import synth
+
+    D, rep = 128, 4
+    n_max = 4096
+    k = synth.k_vectors(1, 1, T0 + n_max, D)
+    v = synth.v_vectors(1, 1, T0 + n_max, D)
+    kb, vb = synth.f32_to_bf16_bits(k), synth.f32_to_bf16_bits(v)
+    q = synth.f32_to_bf16_bits(synth.queries(1, rep, D))
+    r = O.RefCache(1, rep, 1, D, T0 + n_max, max_patterns=P, pattern_window=W,
+                   in_dtype=O.IN_BF16)
+    nk = min(args.kmeans_tokens, T0)
+    r.init_patterns(kb[:, :, :nk], vb[:, :, :nk], P)
+    r.encode_append(kb[:, :, :T0], vb[:, :, :T0])
+    steps, secs, nbytes = 0, 0.0, 0.0
+    while secs < args.cpu_seconds and steps < n_max:
+        t = T0 + steps
+        t_start = time.perf_counter()
+        r.encode_append(kb[:, :, t:t + 1], vb[:, :, t:t + 1], update=1)
+        r.attn_decode(q)
+        secs += time.perf_counter() - t_start
+        nbytes += (attn_bytes(t + 1) + enc_bytes) / U
+        steps += 1
+    return {"value": round(nbytes / secs / 1e9, 5), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": (f"{steps} decode steps (encode 1 token + 4-q-head attention) on one of "
+                       f"the {U} (batch, kv-head) units at context {T0}; single-threaded C "
+                       f"oracle, {secs:.1f} s timed; bytes counted as in value")}
+
+
+if __name__ == "__main__":
+    main()

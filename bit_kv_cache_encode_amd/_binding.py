@@ -34,9 +34,9 @@ class kvq_config(C.Structure):
 class kvq_layout(C.Structure):
     _fields_ = [(n, C.c_uint64) for n in (
         "k_codes", "v_codes", "k_sz", "v_sz", "k_idx", "v_idx", "k_t16", "v_t16",
-        "k_tab", "v_tab", "k_win", "v_win", "ws",
+        "k_tab", "v_tab", "k_win", "v_win", "ws", "cnt",
         "codes_bytes", "sz_bytes", "idx_bytes", "t16_bytes", "tab_bytes", "win_bytes",
-        "ws_bytes", "total")] + [(n, C.c_int32) for n in (
+        "ws_bytes", "cnt_bytes", "total")] + [(n, C.c_int32) for n in (
         "token_cap", "n_groups", "record_bytes", "max_splits")]
 
 

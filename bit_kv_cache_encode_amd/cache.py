@@ -142,9 +142,20 @@ class KVCache:
                 "v_sz": L.sz_bytes, "k_idx": L.idx_bytes, "v_idx": L.idx_bytes,
                 "k_t16": L.t16_bytes, "v_t16": L.t16_bytes, "k_tab": L.tab_bytes,
                 "v_tab": L.tab_bytes, "k_win": L.win_bytes, "v_win": L.win_bytes,
-                "ws": L.ws_bytes}[name]
+                "ws": L.ws_bytes, "cnt": L.cnt_bytes}[name]
         off = getattr(L, name)
         return self.buf[off:off + size]
+
+    def clone(self) -> "KVCache":
+        """An independent cache with a copy of this one's buffer and state."""
+        other = KVCache.__new__(KVCache)
+        other.cfg, other.layout, other.device = self.cfg, self.layout, self.device
+        other.in_dtype, other.mode = self.in_dtype, self.mode
+        other.buf = self.buf.clone()
+        other.c = B.kvq_cache()
+        C.memmove(C.addressof(other.c), C.addressof(self.c), C.sizeof(B.kvq_cache))
+        other.c.base = other.buf.data_ptr()
+        return other
 
     def state_bytes(self) -> int:
         """Bytes a checkpoint needs: the whole buffer."""

@@ -2,6 +2,7 @@
 // cache layout, host-side state (token, pattern and window counters) and
 // kernel launches.  Every check runs before the first launch of a call.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "kvq_internal.h"
@@ -114,6 +115,7 @@ Regions regions_of(const kvq_cache* c, const kvq_layout& L) {
   r.win[0] = (float*)(base + L.k_win);
   r.win[1] = (float*)(base + L.v_win);
   r.ws = (float*)(base + L.ws);
+  r.cnt = (uint32_t*)(base + L.cnt);
   return r;
 }
 
@@ -128,7 +130,7 @@ int kvq_layout_of(const kvq_config* cfg, kvq_layout* out) {
   kvq_layout L;
   memset(&L, 0, sizeof(L));
   const uint64_t U = (uint64_t)cfg->batch * cfg->n_kv_heads;
-  const int tcap = (cfg->max_tokens + VT - 1) / VT * VT;
+  const int tcap = (cfg->max_tokens + 63) / 64 * 64;
   const bool pattern = cfg->mode == KVQ_MODE_PATTERN;
   L.token_cap = tcap;
   L.n_groups = D / cfg->group;
@@ -158,6 +160,8 @@ int kvq_layout_of(const kvq_config* cfg, kvq_layout* out) {
   L.k_win = place(L.win_bytes);
   L.v_win = place(L.win_bytes);
   L.ws = place(L.ws_bytes);
+  L.cnt_bytes = U * 4;
+  L.cnt = place(L.cnt_bytes);
   L.total = off;
   *out = L;
   return KVQ_OK;
@@ -174,6 +178,8 @@ int kvq_cache_init(kvq_cache* cache, const kvq_config* cfg, void* base, uint64_t
   cache->rho = cfg->v_alpha > 0.0f ? rho_star(D, cfg->v_alpha) : -1.0f;
   hipStream_t s = (hipStream_t)stream;
   Regions r = regions_of(cache, L);
+  hipError_t ec = launch_fill((float*)r.cnt, 0.0f, (int64_t)(L.cnt_bytes / 4), s);
+  if (ec != hipSuccess) return dev_fail(ec);
   if (cfg->mode == KVQ_MODE_PATTERN) {
     hipError_t e = launch_window_reset(r.win[0], r.win[1], cfg->batch * cfg->n_kv_heads, s);
     if (e != hipSuccess) return dev_fail(e);
@@ -346,13 +352,28 @@ int kvq_attn_decode(kvq_cache* cache, const void* q, float* out, float sm_scale,
   const float sm = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)D);
   a.qscale = sm * 1.4426950408889634f;
   const int units = c.batch * c.n_kv_heads;
-  int want = (ATTN_TARGET_BLOCKS + units - 1) / units;
+  // Kernel choice: the MFMA kernel covers groups of 32 / 64 channels with up
+  // to 16/(128/group) q-heads per kv-head; KVQ_ATTN_KERNEL=valu forces the
+  // VALU kernel (used to cross-check both).  KVQ_ATTN_BLOCKS sets the target
+  // grid size of the MFMA kernel.
+  const char* kenv = getenv("KVQ_ATTN_KERNEL");
+  const bool use_mfma = mfma_attention_supported(c.bits, c.group, a.gq) &&
+                        !(kenv && strcmp(kenv, "valu") == 0);
+  int target = use_mfma ? 512 : ATTN_TARGET_BLOCKS;
+  const char* benv = getenv("KVQ_ATTN_BLOCKS");
+  if (benv && atoi(benv) > 0) target = atoi(benv);
+  int want = (target + units - 1) / units;
   if (want > L.max_splits) want = L.max_splits;
   if (want < 1) want = 1;
   int chunk = (a.T + want - 1) / want;
   chunk = (chunk + ATTN_MIN_CHUNK - 1) / ATTN_MIN_CHUNK * ATTN_MIN_CHUNK;
   a.chunk = chunk;
   a.splits = (a.T + chunk - 1) / chunk;
+  if (use_mfma) {
+    hipError_t e = launch_attention_mfma(a, (hipStream_t)stream);
+    if (e != hipSuccess) return dev_fail(e);
+    return KVQ_OK;
+  }
   hipError_t e = launch_attention(a, (hipStream_t)stream);
   if (e != hipSuccess) return dev_fail(e);
   return KVQ_OK;

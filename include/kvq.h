@@ -25,11 +25,12 @@
  *  - Supported shapes: head_dim 128; bits 2 or 4; group divides 128 and is a
  *    multiple of 8; max_patterns <= 255; n_q_heads a multiple of
  *    n_kv_heads with at most 8 q-heads per kv-head.
- *  - Domain: finite inputs with |x| < 16384.  Outside it codes and scales are
- *    unspecified (no error is raised; checking would need a device sync).
+ *  - Domain: finite K/V inputs with |x| < 4096 and queries with
+ *    |q| * sm_scale < 40.  Outside it results are unspecified (no error is
+ *    raised; checking would need a device sync).
  *
  * Stored format (per (batch, kv-head) "unit", for K and for V alike unless
- * noted; T = token capacity rounded up to 32):
+ * noted; T = token capacity, max_tokens rounded up to a multiple of 64):
  *  - codes: T * 128 * bits / 8 bytes.  K is token-major: channel d of a token
  *    sits at bit bits*d of the token's record (little-endian).  V is stored
  *    in tiles of 32 tokens, channel-major: channel d of a tile owns 4*bits
@@ -85,9 +86,11 @@ typedef struct {
   uint64_t k_tab, v_tab;  /* PATTERN: fp32 [U][max_patterns][D]; KVARN: fp32 [U][D] */
   uint64_t k_win, v_win;  /* PATTERN window state: fp32 [U][2][D] (min, max) */
   uint64_t ws;            /* split-K partials */
+  uint64_t cnt;           /* split-K arrival counters, uint32 [U], zero between calls */
   uint64_t codes_bytes, sz_bytes, idx_bytes, t16_bytes, tab_bytes, win_bytes, ws_bytes;
+  uint64_t cnt_bytes;
   uint64_t total;
-  int32_t token_cap;      /* max_tokens rounded up to KVQ_VTILE */
+  int32_t token_cap;      /* max_tokens rounded up to a multiple of 64 */
   int32_t n_groups;       /* head_dim / group */
   int32_t record_bytes;   /* stored bytes per token per unit and kind */
   int32_t max_splits;

@@ -196,3 +196,57 @@ def test_determinism_and_checkpoint():
     assert torch.equal(caches[0].attn_decode(q), fresh.attn_decode(q))
     torch.cuda.synchronize()
     assert torch.equal(caches[0].buf[:caches[0].layout.ws], fresh.buf[:fresh.layout.ws])
+
+
+@pytest.mark.parametrize("bits,group,gq,mode", [
+    (2, 32, 4, "pattern"), (2, 32, 1, "pattern"), (4, 64, 4, "pattern"), (4, 64, 8, "pattern"),
+    (2, 64, 2, "pattern"), (4, 32, 3, "pattern"), (2, 32, 4, "kvarn"), (4, 64, 8, "kvarn")])
+@pytest.mark.parametrize("blocks", [1, 40, 4096])
+def test_attention_kernels_agree(monkeypatch, bits, group, gq, mode, blocks):
+    """The MFMA kernel (fused split-K combine) and the VALU kernel both match
+    the oracle, for one block per unit up to many splits, ragged lengths."""
+    B, H, T = 2, 2, 1000
+    gpu, ref, dt = make_pair(B, gq * H, H, 1024, bits=bits, group=group, mode=mode,
+                             max_patterns=24)
+    k, v = _inputs(B, H, T, seed_off=bits + gq)
+    if mode == "pattern":
+        ref.init_patterns(to_oracle(k[:, :, :256], True), to_oracle(v[:, :, :256], True), 24)
+        gpu.init_patterns(to_dev(k[:, :, :256], dt), to_dev(v[:, :, :256], dt), 24)
+    else:
+        ref.init_patterns(to_oracle(k[:, :, :256], True), to_oracle(v[:, :, :256], True), 0)
+        gpu.set_patterns(torch.from_numpy(ref.scales(0).reshape(B, H, 128).copy()).cuda(),
+                         torch.from_numpy(ref.scales(1).reshape(B, H, 128).copy()).cuda())
+    ref.encode_append(to_oracle(k, True), to_oracle(v, True))
+    gpu.encode_append(to_dev(k, dt), to_dev(v, dt))
+    monkeypatch.setenv("KVQ_ATTN_BLOCKS", str(blocks))
+    for step, qmul in ((0, 1.0), (1, 6.0)):          # flat and peaked softmax
+        q = synth.queries(B, gq * H, 128, step=step) * np.float32(qmul)
+        want = ref.attn_decode(to_oracle(q, True))
+        monkeypatch.delenv("KVQ_ATTN_KERNEL", raising=False)
+        got_m = gpu.attn_decode(to_dev(q, dt)).cpu().numpy()
+        monkeypatch.setenv("KVQ_ATTN_KERNEL", "valu")
+        got_v = gpu.attn_decode(to_dev(q, dt)).cpu().numpy()
+        em, ev = np.abs(got_m - want).max(), np.abs(got_v - want).max()
+        assert em <= ATTN_TOL and ev <= ATTN_TOL, (em, ev)
+
+
+def test_attention_repeated_calls_reset_counters(monkeypatch):
+    """The fused combine's arrival counters return to zero after each call, so
+    repeated calls (and calls after appends) keep matching the oracle."""
+    B, Hq, H = 2, 8, 2
+    gpu, ref, dt = make_pair(B, Hq, H, 4096)
+    k, v = _inputs(B, H, 3000)
+    ref.init_patterns(to_oracle(k[:, :, :512], True), to_oracle(v[:, :, :512], True), 16)
+    gpu.init_patterns(to_dev(k[:, :, :512], dt), to_dev(v[:, :, :512], dt), 16)
+    monkeypatch.setenv("KVQ_ATTN_BLOCKS", "64")
+    pos = 0
+    for n in (1000, 1, 999, 1000):
+        ref.encode_append(to_oracle(k[:, :, pos:pos + n], True), to_oracle(v[:, :, pos:pos + n], True))
+        gpu.encode_append(to_dev(k[:, :, pos:pos + n], dt), to_dev(v[:, :, pos:pos + n], dt))
+        pos += n
+        q = synth.queries(B, Hq, 128, step=pos)
+        want = ref.attn_decode(to_oracle(q, True))
+        for _ in range(3):
+            got = gpu.attn_decode(to_dev(q, dt)).cpu().numpy()
+            assert np.abs(got - want).max() <= ATTN_TOL
+    assert int(gpu.region("cnt").view(torch.int32).abs().sum()) == 0
