@@ -185,10 +185,10 @@ __global__ void __launch_bounds__(AT_THREADS) attn_split_kernel(AttnArgs a) {
       const int g = d / G;
       for (int j = 0; j < nvalid; ++j) {
         const int t = tok0 + j;
-        const uint8_t* vt = a.r.codes[1] + ((u * (a.tcap / VT)) + t / VT) * (VT * D * bits / 8) +
-                            (int64_t)d * 4 * bits;
-        const int bit = (t % VT) * bits;
-        const uint32_t c = (vt[bit >> 3] >> (bit & 7)) & ((1u << bits) - 1u);
+        const int per = 32 / bits, i = t % VT;
+        const uint32_t* vt = (const uint32_t*)(a.r.codes[1] + ((u * (a.tcap / VT)) + t / VT) *
+                                                                  (VT * D * bits / 8));
+        const uint32_t c = (vt[(i / per) * D + d] >> ((i % per) * bits)) & ((1u << bits) - 1u);
         const uint32_t p = sh.vsz[j][g];
         float vv = __builtin_fmaf((float)c, bits2f((uint16_t)(p & 0xFFFF)), bits2f((uint16_t)(p >> 16)));
         vv *= sh.tv[j];
@@ -254,12 +254,16 @@ __global__ void __launch_bounds__(D) attn_combine_kernel(AttnArgs a) {
   a.out[(int64_t)row0 * D + d] = buf[d] * (float)(1.0 / __builtin_sqrt(128.0));
 }
 
+hipError_t launch_attention_combine(const AttnArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(a.B * a.Hq), dim3(D), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(attn_split_kernel, dim3(a.splits, a.B * a.Hkv), dim3(AT_THREADS), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(a.B * a.Hq), dim3(D), 0, s, a);
-  return hipGetLastError();
+  return launch_attention_combine(a, s);
 }
 
 }  // namespace kvq

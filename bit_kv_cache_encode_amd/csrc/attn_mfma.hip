@@ -21,6 +21,8 @@
 // carries the inverse power, so unpacking a pair of codes is one AND.  q and
 // p*s are split into binary16 hi + lo parts (two MFMAs), so products keep
 // about 22 bits; accumulation is fp32.
+#include <type_traits>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -101,35 +103,82 @@ __device__ __forceinline__ u32x4 unpack_v(uint32_t w, int j) {
   return r;
 }
 
-template <int NG>
-struct MfShared {
-  static constexpr int HB = 16 / NG;
-  float q[HB][D];                 // q' = q * sm_scale * log2(e) (KVarN: rotated, * c_K)
-  float qm[HB][MAXP];             // q' . M^K_j
-  float ps[MF_WAVES][HB][TILE];   // p * 2^(EP - code power) (* t_V) per wave
-  _Float16 vs[MF_WAVES][NG][TILE];// V group scales s per wave
-  float w[MF_WAVES][HB][MAXP];    // V pattern mass per wave
-  float alpha[MF_WAVES][HB];
-  float m[MF_WAVES][HB];
-  float o[HB][D];                 // merged o
-  float z[HB][NG];                // merged sum p z
-  float l[HB];
-  float wsum[HB][MAXP];
-  float M[HB];
-  int last;
+// Per-wave LDS copy of one 64-token tile, byte offsets.  Every segment is
+// contiguous in the cache and 16-byte aligned, so the copy is plain 16-byte
+// loads per lane.
+template <int BITS, int NG, bool KVARN>
+struct TileShape {
+  static constexpr int KREC = D * BITS / 8;
+  static constexpr int KC = TILE * KREC;            // K codes
+  static constexpr int KS = TILE * NG * 4;          // K (s, z) words
+  static constexpr int VC = 2 * VT * D * BITS / 8;  // two V code tiles
+  static constexpr int VS = TILE * NG * 4;          // V (s, z) words
+  static constexpr int IX = KVARN ? 2 * TILE : TILE;// K idx or t16; V likewise
+  static constexpr int O_KC = 0, O_KS = KC, O_VC = O_KS + KS, O_VS = O_VC + VC;
+  static constexpr int O_KI = O_VS + VS, O_VI = O_KI + IX;
+  static constexpr int BYTES = O_VI + IX;
+  static constexpr int R_KC = KC / 16 / 64, R_VC = VC / 16 / 64;   // pieces per lane
+  static constexpr int P_KS = KS / 16, P_IX = IX / 16;              // pieces (<= 64)
 };
 
+// Row offset (floats) of head h in a wave's p table.  Rows hold 64 tokens;
+// within each group of four rows the offsets are 0, 72, 168, 240 (banks
+// skewed by 0, 8, 40, 48 words) so that the four rows a lane group reads hit
+// different LDS banks; groups of four rows are 320 floats apart.
+__host__ __device__ inline int ps_row(int h) {
+  return (h >> 2) * 320 + (h & 3) * 72 + ((h & 2) ? 24 : 0);
+}
+constexpr int PS_FLOATS = 2 * 320;   // 8 rows
+
+// Dynamic LDS layout of a block (bytes); npat = padded pattern count.
+struct MfLds {
+  int q, qsum, qm, ps, vs, w, alpha, m, o, z, l, wsum, M, last, f, tiles, total;
+};
+__host__ __device__ inline int al16(int x) { return (x + 15) & ~15; }
+__host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes, int splits) {
+  MfLds L;
+  int o = 0;
+  L.q = o; o = al16(o + HB * D * 4);
+  L.qsum = o; o = al16(o + HB * NG * 4);
+  L.qm = o; o = al16(o + HB * npat * 4);
+  L.ps = o; o = al16(o + MF_WAVES * PS_FLOATS * 4);
+  L.vs = o; o = al16(o + MF_WAVES * NG * TILE * 2);
+  L.w = o; o = al16(o + MF_WAVES * HB * npat * 4);
+  L.alpha = o; o = al16(o + MF_WAVES * HB * 4);
+  L.m = o; o = al16(o + MF_WAVES * HB * 4);
+  L.o = o; o = al16(o + HB * D * 4);
+  L.z = o; o = al16(o + HB * NG * 4);
+  L.l = o; o = al16(o + HB * 4);
+  L.wsum = o; o = al16(o + HB * npat * 4);
+  L.M = o; o = al16(o + HB * 4);
+  L.last = o; o = al16(o + 16);
+  L.f = o; o = al16(o + HB * splits * 4);
+  L.tiles = o; o = al16(o + MF_WAVES * tile_bytes);
+  L.total = o;
+  return L;
+}
+__host__ __device__ inline int pad_pat(int n) { return n < 4 ? 4 : (n + 3) & ~3; }
+
+// Two fp32 values -> packed binary16 hi parts and lo residuals (both rounded
+// toward zero; hi + lo keeps ~21 significant bits).
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  auto h = __builtin_amdgcn_cvt_pkrtz(a, b);
+  hi = __builtin_bit_cast(uint32_t, h);
+  auto l = __builtin_amdgcn_cvt_pkrtz(a - (float)h[0], b - (float)h[1]);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
 template <int BITS, int NG, bool KVARN>
-__global__ void __launch_bounds__(MF_THREADS) attn_mfma_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_mfma_kernel(AttnArgs a) {
+  using TS = TileShape<BITS, NG, KVARN>;
   constexpr int G = D / NG;            // channels per group
   constexpr int HB = 16 / NG;          // heads per row block
   constexpr int CPG = 16 / NG;         // PV columns per group
-  constexpr int SPL = 4 / NG;          // heads per lane in the 16x16 output
-  constexpr int KREC = D * BITS / 8;   // K record bytes
+  constexpr int SPL = 4 / NG;          // heads per lane in a 16x16 output
   constexpr int KW = BITS;             // dwords of a lane's 32-channel K slice
   constexpr int VTB = VT * D * BITS / 8;
-  extern __shared__ unsigned char mf_raw[];
-  MfShared<NG>& sh = *reinterpret_cast<MfShared<NG>*>(mf_raw);
+  extern __shared__ __attribute__((aligned(16))) unsigned char mf_raw[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane >> 4, n16 = lane & 15;
@@ -137,38 +186,92 @@ __global__ void __launch_bounds__(MF_THREADS) attn_mfma_kernel(AttnArgs a) {
   const int u = blockIdx.x % U, split = blockIdx.x / U;
   const int b = u / a.Hkv, hk = u % a.Hkv, hq0 = hk * a.gq;
   const int t_begin = split * a.chunk, t_end = min(a.T, t_begin + a.chunk);
-  const int T = a.T;
   const int n_pat = KVARN ? 0 : a.n_pat;
+  const int npat = pad_pat(n_pat);
+  const MfLds Lo = mf_lds(HB, NG, npat, TS::BYTES, a.splits);
+  float* s_q = (float*)(mf_raw + Lo.q);            // [HB][D]
+  float* s_qsum = (float*)(mf_raw + Lo.qsum);      // [HB][NG]
+  float* s_qm = (float*)(mf_raw + Lo.qm);          // [HB][npat]
+  float* s_ps = (float*)(mf_raw + Lo.ps) + wave * PS_FLOATS;
+  _Float16* s_vs = (_Float16*)(mf_raw + Lo.vs) + wave * NG * TILE;
+  float* s_w = (float*)(mf_raw + Lo.w);            // [WAVES][HB][npat]
+  float* s_alpha = (float*)(mf_raw + Lo.alpha);    // [WAVES][HB]
+  float* s_m = (float*)(mf_raw + Lo.m);            // [WAVES][HB]
+  float* s_o = (float*)(mf_raw + Lo.o);            // [HB][D]
+  float* s_z = (float*)(mf_raw + Lo.z);            // [HB][NG]
+  float* s_l = (float*)(mf_raw + Lo.l);            // [HB]
+  float* s_wsum = (float*)(mf_raw + Lo.wsum);      // [HB][npat]
+  float* s_M = (float*)(mf_raw + Lo.M);            // [HB]
+  int* s_last = (int*)(mf_raw + Lo.last);
+  unsigned char* tb = mf_raw + Lo.tiles + wave * TS::BYTES;
+  float* wrow = s_w + wave * HB * npat;
+
+  const uint8_t* kcodes = a.r.codes[0] + (int64_t)u * a.tcap * TS::KREC;
+  const uint8_t* vcodes = a.r.codes[1] + (int64_t)u * a.tcap * TS::KREC;
+  const uint8_t* ksz = (const uint8_t*)(a.r.sz[0] + (int64_t)u * a.tcap * NG);
+  const uint8_t* vsz = (const uint8_t*)(a.r.sz[1] + (int64_t)u * a.tcap * NG);
+  const uint8_t* kix_src = KVARN ? (const uint8_t*)(a.r.t16[0] + (int64_t)u * a.tcap)
+                                 : a.r.idx[0] + (int64_t)u * a.tcap;
+  const uint8_t* vix_src = KVARN ? (const uint8_t*)(a.r.t16[1] + (int64_t)u * a.tcap)
+                                 : a.r.idx[1] + (int64_t)u * a.tcap;
+
+  // ---------------------------------------------------------------- tile copy
+  u32x4 rkc[TS::R_KC], rvc[TS::R_VC], rks, rvs, rix;
+  auto issue = [&](int tile) {
+    const u32x4* kc = (const u32x4*)(kcodes + (int64_t)tile * TS::KREC);
+    const u32x4* vc = (const u32x4*)(vcodes + (int64_t)(tile >> 5) * VTB);
+#pragma unroll
+    for (int r = 0; r < TS::R_KC; ++r) rkc[r] = kc[lane + 64 * r];
+#pragma unroll
+    for (int r = 0; r < TS::R_VC; ++r) rvc[r] = vc[lane + 64 * r];
+    if (lane < TS::P_KS) {
+      rks = ((const u32x4*)(ksz + (int64_t)tile * NG * 4))[lane];
+      rvs = ((const u32x4*)(vsz + (int64_t)tile * NG * 4))[lane];
+    }
+    const int ix_bytes = KVARN ? 2 : 1;
+    if (lane < TS::P_IX) rix = ((const u32x4*)(kix_src + (int64_t)tile * ix_bytes))[lane];
+    else if (lane < 2 * TS::P_IX)
+      rix = ((const u32x4*)(vix_src + (int64_t)tile * ix_bytes))[lane - TS::P_IX];
+  };
+  auto commit = [&]() {
+    u32x4* t4 = (u32x4*)tb;
+#pragma unroll
+    for (int r = 0; r < TS::R_KC; ++r) t4[TS::O_KC / 16 + lane + 64 * r] = rkc[r];
+#pragma unroll
+    for (int r = 0; r < TS::R_VC; ++r) t4[TS::O_VC / 16 + lane + 64 * r] = rvc[r];
+    if (lane < TS::P_KS) {
+      t4[TS::O_KS / 16 + lane] = rks;
+      t4[TS::O_VS / 16 + lane] = rvs;
+    }
+    if (lane < 2 * TS::P_IX) t4[TS::O_KI / 16 + lane] = rix;
+  };
+
+  // the first tile's loads are in flight while the prologue runs
+  if (t_begin + TILE * wave < t_end) issue(t_begin + TILE * wave);
 
   // ---------------------------------------------------------------- prologue
   for (int i = tid; i < HB * D; i += MF_THREADS) {
     const int h = i / D, d = i % D;
-    sh.q[h][d] = h < a.gq ? load_in(a.q, ((int64_t)b * a.Hq + hq0 + h) * D + d, a.bf16) : 0.0f;
-    sh.o[h][d] = 0.0f;
+    s_q[i] = h < a.gq ? load_in(a.q, ((int64_t)b * a.Hq + hq0 + h) * D + d, a.bf16) : 0.0f;
+    s_o[i] = 0.0f;
   }
-  for (int i = tid; i < MF_WAVES * HB * MAXP; i += MF_THREADS) (&sh.w[0][0][0])[i] = 0.0f;
-  for (int i = tid; i < HB * MAXP; i += MF_THREADS) {
-    (&sh.wsum[0][0])[i] = 0.0f;
-    (&sh.qm[0][0])[i] = 0.0f;
-  }
-  if (tid < HB * NG) (&sh.z[0][0])[tid] = 0.0f;
-  if (tid < HB) sh.l[tid] = 0.0f;
+  for (int i = tid; i < MF_WAVES * HB * npat; i += MF_THREADS) s_w[i] = 0.0f;
+  for (int i = tid; i < HB * npat; i += MF_THREADS) { s_wsum[i] = 0.0f; s_qm[i] = 0.0f; }
+  if (tid < HB * NG) s_z[tid] = 0.0f;
+  if (tid < HB) s_l[tid] = 0.0f;
   __syncthreads();
   if (KVARN) {
     for (int hs = 1; hs < D; hs <<= 1) {
       float v[HB * D / MF_THREADS];
 #pragma unroll
       for (int k = 0; k < HB * D / MF_THREADS; ++k) {
-        const int i = tid + k * MF_THREADS, h = i / D, d = i % D;
-        const float mine = sh.q[h][d], other = sh.q[h][d ^ hs];
+        const int i = tid + k * MF_THREADS, d = i % D;
+        const float mine = s_q[i], other = s_q[i ^ hs];
         v[k] = (d & hs) ? other - mine : mine + other;
       }
       __syncthreads();
 #pragma unroll
-      for (int k = 0; k < HB * D / MF_THREADS; ++k) {
-        const int i = tid + k * MF_THREADS;
-        sh.q[i / D][i % D] = v[k];
-      }
+      for (int k = 0; k < HB * D / MF_THREADS; ++k) s_q[tid + k * MF_THREADS] = v[k];
       __syncthreads();
     }
   }
@@ -176,20 +279,41 @@ __global__ void __launch_bounds__(MF_THREADS) attn_mfma_kernel(AttnArgs a) {
     const float isd = (float)(1.0 / __builtin_sqrt(128.0));
     const float* ck = a.r.tab[0] + (int64_t)u * D;
     for (int i = tid; i < HB * D; i += MF_THREADS) {
-      const int d = i % D;
-      float v = (&sh.q[0][0])[i];
-      if (KVARN) v = v * isd * ck[d];
-      (&sh.q[0][0])[i] = v * a.qscale;
+      float v = s_q[i];
+      if (KVARN) v = v * isd * ck[i % D];
+      s_q[i] = v * a.qscale;
     }
   }
   __syncthreads();
-  if (!KVARN) {
+  // per-group sums of q': thread (h = tid/32) adds 4 channels, then lanes of a
+  // group reduce (G/4 lanes per group)
+  {
+    const int h = tid >> 5, c0 = (tid & 31) * 4;
+    float s = 0.0f;
+    if (h < HB) s = (s_q[h * D + c0] + s_q[h * D + c0 + 1]) + (s_q[h * D + c0 + 2] + s_q[h * D + c0 + 3]);
+#pragma unroll
+    for (int o = 1; o < G / 4; o <<= 1) s += __shfl_xor(s, o, 64);
+    if (h < HB && ((tid & 31) % (G / 4)) == 0) s_qsum[h * NG + c0 / G] = s;
+  }
+  // q' . M^K_j: four threads per (h, j), 32 channels each
+  if (!KVARN && n_pat > 0) {
     const float* mk = a.r.tab[0] + (int64_t)u * a.max_pat * D;
-    for (int i = tid; i < a.gq * n_pat; i += MF_THREADS) {
-      const int h = i / n_pat, jj = i % n_pat;
+    for (int i = tid; i < 4 * a.gq * n_pat; i += MF_THREADS) {
+      const int part = i & 3, pj = i >> 2, h = pj / n_pat, jj = pj % n_pat;
+      const float4* m4 = (const float4*)(mk + (int64_t)jj * D + part * 32);
+      const float* qh = s_q + h * D + part * 32;
       float s = 0.0f;
-      for (int d = 0; d < D; ++d) s = __builtin_fmaf(sh.q[h][d], mk[(int64_t)jj * D + d], s);
-      sh.qm[h][jj] = s;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float4 m = m4[k];
+        s = __builtin_fmaf(qh[4 * k], m.x, s);
+        s = __builtin_fmaf(qh[4 * k + 1], m.y, s);
+        s = __builtin_fmaf(qh[4 * k + 2], m.z, s);
+        s = __builtin_fmaf(qh[4 * k + 3], m.w, s);
+      }
+      s += __shfl_xor(s, 1, 64);
+      s += __shfl_xor(s, 2, 64);
+      if (part == 0) s_qm[h * npat + jj] = s;
     }
   }
   __syncthreads();
@@ -200,29 +324,27 @@ __global__ void __launch_bounds__(MF_THREADS) attn_mfma_kernel(AttnArgs a) {
     const int h = n16 / NG, g = n16 % NG;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      float v[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int ch = qk_channel<BITS>(j, c, i);
-        v[i] = (ch / G == g) ? ldexpf(sh.q[h][ch], EQ - code_shift<BITS>(i)) : 0.0f;
+      for (int p = 0; p < 4; ++p) {
+        float v2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int i = 2 * p + e, ch = qk_channel<BITS>(j, c, i);
+          v2[e] = (ch / G == g) ? ldexpf(s_q[h * D + ch], EQ - code_shift<BITS>(i)) : 0.0f;
+        }
+        uint32_t hi, lo;
+        split2(v2[0], v2[1], hi, lo);
+        aq_hi[c][p] = hi;
+        aq_lo[c][p] = lo;
       }
-      split_pack(v, aq_hi[c], aq_lo[c]);
     }
   }
-  // Per-lane constants of the QK output layout: register r <-> row
-  // 4j + r = (head hq_r, group r % NG).
+  // QK output register r <-> row 4j + r = (head 4j/NG + r/NG, group r % NG)
   float qsum[4];
-  int head_r[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int m = 4 * j + r, h = m / NG, g = m % NG;
-    head_r[r] = h;
-    float s = 0.0f;
-    for (int d = g * G; d < (g + 1) * G; ++d) s += sh.q[h][d];
-    qsum[r] = s;
-  }
+  for (int r = 0; r < 4; ++r) qsum[r] = s_qsum[((4 * j + r) / NG) * NG + r % NG];
+  const int head0 = (4 * j) / NG;   // head of register slot s is head0 + s
 
-  // running state per head slot (SPL heads per lane)
   float m_run[SPL], l_run[SPL], zacc[4];
 #pragma unroll
   for (int s = 0; s < SPL; ++s) { m_run[s] = -INFINITY; l_run[s] = 0.0f; }
@@ -232,83 +354,88 @@ __global__ void __launch_bounds__(MF_THREADS) attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
   for (int bb = 0; bb < 8; ++bb) oacc[bb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const uint8_t* kcodes = a.r.codes[0] + (int64_t)u * a.tcap * KREC;
-  const uint8_t* vcodes = a.r.codes[1] + (int64_t)u * a.tcap * KREC;
-  const uint32_t* ksz = a.r.sz[0] + (int64_t)u * a.tcap * NG;
-  const uint32_t* vsz = a.r.sz[1] + (int64_t)u * a.tcap * NG;
-  const uint8_t* kidx = a.r.idx[0] + (int64_t)u * a.tcap;
-  const uint8_t* vidx = a.r.idx[1] + (int64_t)u * a.tcap;
-  const uint16_t* kt16 = a.r.t16[0] + (int64_t)u * a.tcap;
-  const uint16_t* vt16 = a.r.t16[1] + (int64_t)u * a.tcap;
-  float* wrow = &sh.w[wave][0][0];
+  int tile = t_begin + TILE * wave;
+  for (; tile < t_end; tile += TILE * MF_WAVES) {
+    __builtin_amdgcn_wave_barrier();
+    commit();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (tile + TILE * MF_WAVES < t_end) issue(tile + TILE * MF_WAVES);
+    const int nvalid = t_end - tile;
+    auto tile_body = [&](auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value;
 
-  // ---------------------------------------------------------------- tiles
-  for (int tile = t_begin + TILE * wave; tile < t_end; tile += TILE * MF_WAVES) {
-    // ---- loads (token indices clamped into the stored range)
-    uint32_t kw[4][KW];
-    uint32_t kszw[4][NG], vszw[4][NG];
-    int kix[4], vix[4];
-    float tk[4], tv[4];
+    // ---- QK: four independent accumulators (one per 16-token column block)
+    // so consecutive MFMAs never wait on each other.
+    f32x4 C[4];
+    {
+      uint32_t kw[4][KW];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int tc = min(tile + 16 * nb + n16, T - 1);
-      const uint32_t* kp = (const uint32_t*)(kcodes + (int64_t)tc * KREC) + j * KW;
+      for (int nb = 0; nb < 4; ++nb) {
+        const int t64 = 16 * nb + n16;
+        if (KW == 2) {
+          const uint2 w = *(const uint2*)(tb + TS::O_KC + t64 * TS::KREC + j * 8);
+          kw[nb][0] = w.x; kw[nb][1 % KW] = w.y;
+        } else {
+          const u32x4 w = *(const u32x4*)(tb + TS::O_KC + t64 * TS::KREC + j * 16);
 #pragma unroll
-      for (int w = 0; w < KW; ++w) kw[nb][w] = kp[w];
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        kszw[nb][g] = ksz[(int64_t)tc * NG + g];
-        vszw[nb][g] = vsz[(int64_t)tc * NG + g];
+          for (int q = 0; q < KW; ++q) kw[nb][q] = w[q];
+        }
+        C[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       }
-      if (KVARN) {
-        tk[nb] = bits2f(kt16[tc]);
-        tv[nb] = bits2f(vt16[tc]);
-        kix[nb] = vix[nb] = KVQ_INDEX_NONE;
-      } else {
-        kix[nb] = kidx[tc];
-        vix[nb] = vidx[tc];
-        tk[nb] = tv[nb] = 1.0f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        u32x4 B[4];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) B[nb] = unpack_k<BITS>(kw[nb], c);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) C[nb] = mfma16(aq_hi[c], B[nb], C[nb]);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) C[nb] = mfma16(aq_lo[c], B[nb], C[nb]);
       }
     }
-    uint32_t vw[2][8];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const uint8_t* vt = vcodes + (int64_t)((tile >> 5) + kb) * VTB;
-#pragma unroll
-      for (int bb = 0; bb < 8; ++bb) {
-        const int ch = G * (n16 / CPG) + CPG * bb + (n16 % CPG);
-        vw[kb][bb] = BITS == 2 ? *(const uint32_t*)(vt + ch * 8 + 4 * (j >> 1))
-                               : *(const uint32_t*)(vt + ch * 16 + 4 * j);
-      }
-    }
-
-    // ---- QK scores: sc[nb][s] for head slot s of this lane
     float sc[4][SPL];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      f32x4 C = {0.0f, 0.0f, 0.0f, 0.0f};
+      const int t64 = 16 * nb + n16;
+      const bool valid = FULL || t64 < nvalid;
+      uint32_t kszw[NG];
+      {
+        const uint32_t* kszp = (const uint32_t*)(tb + TS::O_KS) + t64 * NG;
+        if (NG == 4) {
+          const u32x4 k4 = *(const u32x4*)kszp;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const u32x4 B = unpack_k<BITS>(kw[nb], c);
-        C = mfma16(aq_hi[c], B, C);
-        C = mfma16(aq_lo[c], B, C);
+          for (int g = 0; g < NG; ++g) kszw[g] = k4[g];
+        } else {
+          const uint2 k2 = *(const uint2*)kszp;
+          kszw[0] = k2.x; kszw[1 % NG] = k2.y;
+        }
       }
-      const bool valid = tile + 16 * nb + n16 < t_end;
+      float tk = 1.0f;
+      int kix = KVQ_INDEX_NONE;
+      if (KVARN) {
+        tk = bits2f(((const uint16_t*)(tb + TS::O_KI))[t64]);
+      } else {
+        const int ki = tb[TS::O_KI + t64];
+        kix = valid ? ki : KVQ_INDEX_NONE;
+      }
 #pragma unroll
       for (int s = 0; s < SPL; ++s) {
         float dot = 0.0f, zt = 0.0f;
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
           const int r = s * NG + g;
-          const uint32_t w = kszw[nb][g];
-          dot = __builtin_fmaf(bits2f((uint16_t)(w & 0xFFFFu)), C[r], dot);
-          zt = __builtin_fmaf(bits2f((uint16_t)(w >> 16)), qsum[r], zt);
+          dot = __builtin_fmaf(bits2f((uint16_t)(kszw[g] & 0xFFFFu)), C[nb][r], dot);
+          zt = __builtin_fmaf(bits2f((uint16_t)(kszw[g] >> 16)), qsum[r], zt);
         }
         float v = __builtin_fmaf(dot, (float)(1 << (24 - EQ)), zt);
         if (!KVARN) {
-          if (kix[nb] != KVQ_INDEX_NONE) v += sh.qm[head_r[s * NG]][kix[nb]];
+          const bool has = kix != KVQ_INDEX_NONE;
+          const float qm = s_qm[(head0 + s) * npat + (has ? kix : 0)];
+          v += has ? qm : 0.0f;
         } else {
-          v *= tk[nb];
+          v *= tk;
         }
         sc[nb][s] = valid ? v : -INFINITY;
       }
@@ -328,7 +455,7 @@ __global__ void __launch_bounds__(MF_THREADS) attn_mfma_kernel(AttnArgs a) {
       float al[SPL];
 #pragma unroll
       for (int s = 0; s < SPL; ++s) {
-        al[s] = exp2f(m_run[s] - mnew[s]);
+        al[s] = __builtin_amdgcn_exp2f(m_run[s] - mnew[s]);
         l_run[s] *= al[s];
         m_run[s] = mnew[s];
       }
@@ -341,14 +468,11 @@ __global__ void __launch_bounds__(MF_THREADS) attn_mfma_kernel(AttnArgs a) {
       if (!KVARN && n_pat > 0) {
         if (n16 == 0)
 #pragma unroll
-          for (int s = 0; s < SPL; ++s) sh.alpha[wave][head_r[s * NG]] = al[s];
+          for (int s = 0; s < SPL; ++s) s_alpha[wave * HB + head0 + s] = al[s];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        for (int e = lane; e < a.gq * n_pat; e += 64) {
-          const int h = e / n_pat;
-          wrow[h * MAXP + (e % n_pat)] *= sh.alpha[wave][h];
-        }
+        for (int e = lane; e < a.gq * npat; e += 64) wrow[e] *= s_alpha[wave * HB + e / npat];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -357,158 +481,232 @@ __global__ void __launch_bounds__(MF_THREADS) attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int t64 = 16 * nb + n16;
+      const bool valid = FULL || t64 < nvalid;
+      uint32_t vszz[NG];
+      {
+        const uint32_t* vszp = (const uint32_t*)(tb + TS::O_VS) + t64 * NG;
+        if (NG == 4) {
+          const u32x4 v4 = *(const u32x4*)vszp;
+#pragma unroll
+          for (int g = 0; g < NG; ++g) vszz[g] = valid ? v4[g] : 0u;
+        } else {
+          const uint2 v2 = *(const uint2*)vszp;
+          vszz[0] = valid ? v2.x : 0u;
+          vszz[1 % NG] = valid ? v2.y : 0u;
+        }
+      }
+      float tv = 1.0f;
+      int vix = KVQ_INDEX_NONE;
+      if (KVARN) {
+        const float t = bits2f(((const uint16_t*)(tb + TS::O_VI))[t64]);
+        tv = valid ? t : 0.0f;
+      } else {
+        const int vi = tb[TS::O_VI + t64];
+        vix = valid ? vi : KVQ_INDEX_NONE;
+      }
 #pragma unroll
       for (int s = 0; s < SPL; ++s) {
-        const float p = exp2f(sc[nb][s] - m_run[s]);
+        const float p = __builtin_amdgcn_exp2f(sc[nb][s] - m_run[s]);
         l_run[s] += p;
-        const int h = head_r[s * NG];
-        const float pt = p * tv[nb];          // KVarN: v^ carries the token scale t
+        const float pt = p * tv;              // KVarN: v^ carries the token scale t
 #pragma unroll
         for (int g = 0; g < NG; ++g)
-          zacc[s * NG + g] = __builtin_fmaf(pt, bits2f((uint16_t)(vszw[nb][g] >> 16)), zacc[s * NG + g]);
-        if (!KVARN && vix[nb] != KVQ_INDEX_NONE && p != 0.0f && h < a.gq)
-          atomicAdd(&wrow[h * MAXP + vix[nb]], p);
-        sh.ps[wave][h][t64] = ldexpf(pt, EP - pv_shift<BITS>(t64 & 31));
+          zacc[s * NG + g] = __builtin_fmaf(pt, bits2f((uint16_t)(vszz[g] >> 16)), zacc[s * NG + g]);
+        if (!KVARN && vix != KVQ_INDEX_NONE && head0 + s < a.gq)
+          atomicAdd(&wrow[(head0 + s) * npat + vix], p);
+        s_ps[ps_row(head0 + s) + t64] = ldexpf(pt, EP - pv_shift<BITS>(t64 & 31));
       }
-      if (j < NG) sh.vs[wave][j][t64] = __builtin_bit_cast(_Float16, (uint16_t)(vszw[nb][j] & 0xFFFFu));
+      // V group scale of this token for group j (lanes j < NG)
+      uint32_t sw = vszz[0];
+#pragma unroll
+      for (int g = 1; g < NG; ++g) sw = (j == g) ? vszz[g] : sw;
+      if (j < NG) s_vs[j * TILE + t64] = __builtin_bit_cast(_Float16, (uint16_t)(sw & 0xFFFFu));
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // ---- PV over the two 32-token V tiles of this iteration
+    // ---- PV over the two 32-token V tiles
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       u32x4 ahi, alo;
       {
         const int h = n16 / NG, g = n16 % NG;
-        float v[8];
+        const bool live = h < a.gq;
+        // element (p, e) of this lane reads token base + p + e*off: two runs of
+        // four consecutive tokens
+        const int base = 32 * kb + pv_token<BITS>(j, 0), off = pv_token<BITS>(j, 1) - pv_token<BITS>(j, 0);
+        const float4 p0 = *(const float4*)(s_ps + ps_row(h) + base);
+        const float4 p1 = *(const float4*)(s_ps + ps_row(h) + base + off);
+        const uint2 v0 = *(const uint2*)(s_vs + g * TILE + base);
+        const uint2 v1 = *(const uint2*)(s_vs + g * TILE + base + off);
+        const float pa[4] = {p0.x, p0.y, p0.z, p0.w}, pb[4] = {p1.x, p1.y, p1.z, p1.w};
+        const uint32_t va[2] = {v0.x, v0.y}, vb[2] = {v1.x, v1.y};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int t64 = 32 * kb + pv_token<BITS>(j, i);
-          v[i] = h < a.gq ? sh.ps[wave][h][t64] * (float)sh.vs[wave][g][t64] : 0.0f;
+        for (int p = 0; p < 4; ++p) {
+          const float s0 = bits2f((uint16_t)(va[p >> 1] >> (16 * (p & 1))));
+          const float s1 = bits2f((uint16_t)(vb[p >> 1] >> (16 * (p & 1))));
+          const float x0 = live ? pa[p] * s0 : 0.0f;
+          const float x1 = live ? pb[p] * s1 : 0.0f;
+          uint32_t hi, lo;
+          split2(x0, x1, hi, lo);
+          ahi[p] = hi;
+          alo[p] = lo;
         }
-        split_pack(v, ahi, alo);
       }
+      // this lane's word of channels 8*n16 .. 8*n16+7 (word-major V tile)
+      const int word = BITS == 2 ? (j >> 1) : j;
+      const u32x4* vp = (const u32x4*)(tb + TS::O_VC + kb * VTB + (word * D + 8 * n16) * 4);
+      const u32x4 w0 = vp[0], w1 = vp[1];
+      u32x4 B[8];
 #pragma unroll
-      for (int bb = 0; bb < 8; ++bb) {
-        const u32x4 B = unpack_v<BITS>(vw[kb][bb], j);
-        oacc[bb] = mfma16(ahi, B, oacc[bb]);
-        oacc[bb] = mfma16(alo, B, oacc[bb]);
-      }
+      for (int bb = 0; bb < 8; ++bb) B[bb] = unpack_v<BITS>(bb < 4 ? w0[bb] : w1[bb - 4], j);
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb) oacc[bb] = mfma16(ahi, B[bb], oacc[bb]);
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb) oacc[bb] = mfma16(alo, B[bb], oacc[bb]);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      };
+    if (nvalid >= TILE) tile_body(std::true_type{});
+    else tile_body(std::false_type{});
   }
 
   // ---------------------------------------------------------------- merge waves
 #pragma unroll
-  for (int s = 0; s < SPL; ++s) {
-    l_run[s] = l_run[s] + __shfl_xor(l_run[s], 1, 64);
-    l_run[s] = l_run[s] + __shfl_xor(l_run[s], 2, 64);
-    l_run[s] = l_run[s] + __shfl_xor(l_run[s], 4, 64);
-    l_run[s] = l_run[s] + __shfl_xor(l_run[s], 8, 64);
-  }
+  for (int s = 0; s < SPL; ++s)
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) l_run[s] += __shfl_xor(l_run[s], o, 64);
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) zacc[r] += __shfl_xor(zacc[r], o, 64);
   if (n16 == 0)
 #pragma unroll
-    for (int s = 0; s < SPL; ++s) sh.m[wave][head_r[s * NG]] = m_run[s];
+    for (int s = 0; s < SPL; ++s) s_m[wave * HB + head0 + s] = m_run[s];
   __syncthreads();
   if (tid < HB) {
     float M = -INFINITY;
-    for (int w = 0; w < MF_WAVES; ++w) M = fmaxf(M, sh.m[w][tid]);
-    sh.M[tid] = M;
+    for (int w = 0; w < MF_WAVES; ++w) M = fmaxf(M, s_m[w * HB + tid]);
+    s_M[tid] = M;
   }
   __syncthreads();
   float f[SPL];
 #pragma unroll
-  for (int s = 0; s < SPL; ++s) {
-    const int h = head_r[s * NG];
-    f[s] = (m_run[s] == -INFINITY) ? 0.0f : exp2f(m_run[s] - sh.M[h]);
-  }
+  for (int s = 0; s < SPL; ++s)
+    f[s] = (m_run[s] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run[s] - s_M[head0 + s]);
   if (n16 == 0) {
 #pragma unroll
     for (int s = 0; s < SPL; ++s) {
-      const int h = head_r[s * NG];
-      atomicAdd(&sh.l[h], f[s] * l_run[s]);
+      atomicAdd(&s_l[head0 + s], f[s] * l_run[s]);
 #pragma unroll
-      for (int g = 0; g < NG; ++g) atomicAdd(&sh.z[h][g], f[s] * zacc[s * NG + g]);
+      for (int g = 0; g < NG; ++g) atomicAdd(&s_z[(head0 + s) * NG + g], f[s] * zacc[s * NG + g]);
     }
   }
   {
     const float oscale = (float)(1 << (24 - EP));
+    const int gcol = n16 / CPG;
 #pragma unroll
     for (int bb = 0; bb < 8; ++bb) {
-      const int ch = G * (n16 / CPG) + CPG * bb + (n16 % CPG);
-      const int gcol = n16 / CPG;
+      const int ch = 8 * n16 + bb;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if (r % NG != gcol) continue;
-        const int s = r / NG, h = head_r[r];
-        if (h < a.gq) atomicAdd(&sh.o[h][ch], oacc[bb][r] * oscale * f[s]);
+        const int s = r / NG, h = head0 + s;
+        if (h < a.gq) atomicAdd(&s_o[h * D + ch], oacc[bb][r] * oscale * f[s]);
       }
     }
   }
   if (!KVARN && n_pat > 0) {
-    // per-wave pattern mass scaled by that wave's factor for each head
     if (n16 == 0)
 #pragma unroll
-      for (int s = 0; s < SPL; ++s) sh.alpha[wave][head_r[s * NG]] = f[s];
+      for (int s = 0; s < SPL; ++s) s_alpha[wave * HB + head0 + s] = f[s];
     __syncthreads();
-    for (int e = tid; e < a.gq * n_pat; e += MF_THREADS) {
-      const int h = e / n_pat, jj = e % n_pat;
+    for (int e = tid; e < a.gq * npat; e += MF_THREADS) {
+      const int h = e / npat;
       float acc = 0.0f;
-      for (int w = 0; w < MF_WAVES; ++w) acc = __builtin_fmaf(sh.alpha[w][h], sh.w[w][h][jj], acc);
-      sh.wsum[h][jj] = acc;
+#pragma unroll
+      for (int w = 0; w < MF_WAVES; ++w)
+        acc = __builtin_fmaf(s_alpha[w * HB + h], s_w[(w * HB) * npat + e], acc);
+      s_wsum[e] = acc;
     }
   }
   __syncthreads();
 
   // ---------------------------------------------------------------- partial out
+  // o (without the pattern term), running max M, sum l and the per-pattern
+  // mass w of this split, all relative to M.
   const int S = a.splits;
-  float* ml = a.r.ws + (int64_t)a.B * a.Hq * S * D;
-  const float* mv = a.r.tab[1] + (int64_t)u * a.max_pat * D;
+  const int64_t rows = (int64_t)a.B * a.Hq * S;
+  float* ml = a.r.ws + rows * D;
+  float* wp = ml + rows * 2;
   for (int i = tid; i < a.gq * D; i += MF_THREADS) {
     const int h = i / D, d = i % D;
-    float o = sh.o[h][d] + sh.z[h][d / G];
-    if (!KVARN)
-      for (int jj = 0; jj < n_pat; ++jj) o = __builtin_fmaf(sh.wsum[h][jj], mv[(int64_t)jj * D + d], o);
     const int64_t row = ((int64_t)b * a.Hq + hq0 + h) * S + split;
-    a.r.ws[row * D + d] = o;
+    a.r.ws[row * D + d] = s_o[i] + s_z[h * NG + d / G];
     if (d == 0) {
-      ml[row * 2] = sh.M[h];
-      ml[row * 2 + 1] = sh.l[h];
+      ml[row * 2] = s_M[h];
+      ml[row * 2 + 1] = s_l[h];
     }
   }
+  if (!KVARN)
+    for (int i = tid; i < a.gq * n_pat; i += MF_THREADS) {
+      const int h = i / n_pat, jj = i % n_pat;
+      const int64_t row = ((int64_t)b * a.Hq + hq0 + h) * S + split;
+      wp[row * a.max_pat + jj] = s_wsum[h * npat + jj];
+    }
   // ---------------------------------------------------------------- fused combine
-  __threadfence();
+  // Every thread's partial stores complete before the barrier; thread 0's
+  // release-acquire increment (agent scope) publishes them, and the block
+  // that arrives last merges all splits of the unit.
   __syncthreads();
   if (tid == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(&a.r.cnt[u], 1u, __ATOMIC_ACQ_REL,
                                                  __HIP_MEMORY_SCOPE_AGENT);
-    sh.last = prev == (uint32_t)(S - 1);
+    *s_last = prev == (uint32_t)(S - 1);
   }
   __syncthreads();
-  if (!sh.last) return;
-  __threadfence();
+  if (!*s_last) return;
+  // split factors f_s = 2^(m_s - M) per head, kept in LDS (s_w is free now)
+  float* s_f = (float*)(mf_raw + Lo.f);     // [HB][S] split factors 2^(m_s - M)
+  if (tid < a.gq) {
+    const int64_t row0 = ((int64_t)b * a.Hq + hq0 + tid) * S;
+    float M = -INFINITY;
+    for (int sp = 0; sp < S; ++sp) M = fmaxf(M, ml[(row0 + sp) * 2]);
+    float L = 0.0f;
+    for (int sp = 0; sp < S; ++sp) {
+      const float fs = __builtin_amdgcn_exp2f(ml[(row0 + sp) * 2] - M);
+      s_f[tid * S + sp] = fs;
+      L = __builtin_fmaf(ml[(row0 + sp) * 2 + 1], fs, L);
+    }
+    s_l[tid] = L;
+  }
+  __syncthreads();
+  if (!KVARN && n_pat > 0) {
+    for (int i = tid; i < a.gq * n_pat; i += MF_THREADS) {
+      const int h = i / n_pat, jj = i % n_pat;
+      const int64_t row0 = ((int64_t)b * a.Hq + hq0 + h) * S;
+      float w = 0.0f;
+      for (int sp = 0; sp < S; ++sp) w = __builtin_fmaf(wp[(row0 + sp) * a.max_pat + jj], s_f[h * S + sp], w);
+      s_wsum[h * npat + jj] = w;
+    }
+    __syncthreads();
+  }
+  const float* mv = a.r.tab[1] + (int64_t)u * a.max_pat * D;
   for (int i = tid; i < a.gq * D; i += MF_THREADS) {
     const int h = i / D, d = i % D;
     const int64_t row0 = ((int64_t)b * a.Hq + hq0 + h) * S;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[(row0 + s) * 2]);
-    float L = 0.0f, o = 0.0f;
-    for (int s = 0; s < S; ++s) {
-      const float fs = exp2f(ml[(row0 + s) * 2] - M);
-      L = __builtin_fmaf(ml[(row0 + s) * 2 + 1], fs, L);
-      o = __builtin_fmaf(a.r.ws[(row0 + s) * D + d], fs, o);
-    }
-    const float r = o / L;
+    float o = 0.0f;
+#pragma unroll 4
+    for (int sp = 0; sp < S; ++sp) o = __builtin_fmaf(a.r.ws[(row0 + sp) * D + d], s_f[h * S + sp], o);
+    if (!KVARN)
+#pragma unroll 8
+      for (int jj = 0; jj < n_pat; ++jj) o = __builtin_fmaf(s_wsum[h * npat + jj], mv[(int64_t)jj * D + d], o);
+    const float r = o / s_l[h];
     if (!KVARN) a.out[((int64_t)b * a.Hq + hq0 + h) * D + d] = r;
-    else sh.o[h][d] = r * a.r.tab[1][(int64_t)u * D + d];
+    else s_o[i] = r * a.r.tab[1][(int64_t)u * D + d];
   }
   if (KVARN) {
     __syncthreads();
@@ -516,39 +714,36 @@ __global__ void __launch_bounds__(MF_THREADS) attn_mfma_kernel(AttnArgs a) {
       float v[HB * D / MF_THREADS];
 #pragma unroll
       for (int k = 0; k < HB * D / MF_THREADS; ++k) {
-        const int i = tid + k * MF_THREADS, h = i / D, d = i % D;
-        const float mine = sh.o[h][d], other = sh.o[h][d ^ hs];
+        const int i = tid + k * MF_THREADS, d = i % D;
+        const float mine = s_o[i], other = s_o[i ^ hs];
         v[k] = (d & hs) ? other - mine : mine + other;
       }
       __syncthreads();
 #pragma unroll
-      for (int k = 0; k < HB * D / MF_THREADS; ++k) {
-        const int i = tid + k * MF_THREADS;
-        sh.o[i / D][i % D] = v[k];
-      }
+      for (int k = 0; k < HB * D / MF_THREADS; ++k) s_o[tid + k * MF_THREADS] = v[k];
       __syncthreads();
     }
     const float isd = (float)(1.0 / __builtin_sqrt(128.0));
-    for (int i = tid; i < a.gq * D; i += MF_THREADS) {
-      const int h = i / D, d = i % D;
-      a.out[((int64_t)b * a.Hq + hq0 + h) * D + d] = sh.o[h][d] * isd;
-    }
+    for (int i = tid; i < a.gq * D; i += MF_THREADS)
+      a.out[((int64_t)b * a.Hq + hq0) * D + i] = s_o[i] * isd;
   }
   if (tid == 0) a.r.cnt[u] = 0;   // ready for the next call (stream-ordered)
 }
 
 template <int BITS, int NG, bool KVARN>
 static hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
-  const size_t lds = sizeof(MfShared<NG>);
-  static bool attr = false;
-  if (!attr) {
+  constexpr int HB = 16 / NG;
+  const int npat = pad_pat(KVARN ? 0 : a.n_pat);
+  const MfLds L = mf_lds(HB, NG, npat, TileShape<BITS, NG, KVARN>::BYTES, a.splits);
+  static int attr = 0;
+  if (L.total > attr) {
     hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel<BITS, NG, KVARN>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, L.total);
     if (e != hipSuccess) return e;
-    attr = true;
+    attr = L.total;
   }
   hipLaunchKernelGGL((attn_mfma_kernel<BITS, NG, KVARN>), dim3(a.B * a.Hkv * a.splits),
-                     dim3(MF_THREADS), lds, s, a);
+                     dim3(MF_THREADS), L.total, s, a);
   return hipGetLastError();
 }
 

@@ -10,7 +10,7 @@
 // waves encode the tile's new tokens one vector per wave; lane l holds
 // channels l and l+64.  Pattern distances use a lane-per-pattern mapping over
 // an LDS copy of the table.  K records (token-major) are written directly;
-// V codes are staged in LDS and written channel-major once per tile, merging
+// V codes are staged in LDS and written word by word once per tile, merging
 // with the bits of tokens outside this call at the tile's edges.
 #include "kvq_internal.h"
 
@@ -219,14 +219,14 @@ __global__ void __launch_bounds__(ENC_THREADS) encode_kernel(EncodeArgs a) {
       }
     }
     if (kind == 1) {
-      // Pack the V tile channel-major: channel d owns 4*bits bytes; each
-      // 32-bit word holds 32/bits consecutive tokens.
+      // Pack the V tile: 32-bit word (wi, d) holds tokens wi*per .. +per-1
+      // of channel d and sits at word index wi*D + d of the tile.
       __syncthreads();
       const int per = 32 / a.bits;                    // tokens per word
       const int words = D * a.bits;                   // words per tile (VT*D*bits/32)
       uint32_t* tile_out = (uint32_t*)(a.r.codes[1] + ((u * (a.tcap / VT)) + tile) * (VT * D * a.bits / 8));
       for (int w = threadIdx.x; w < words; w += ENC_THREADS) {
-        const int d = w / (VT / per), tok0 = (w % (VT / per)) * per;
+        const int d = w % D, tok0 = (w / D) * per;
         uint32_t word = 0, keep = 0;
         for (int i = 0; i < per; ++i) {
           const int t = tile * VT + tok0 + i;

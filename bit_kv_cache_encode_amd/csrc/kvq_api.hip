@@ -141,7 +141,9 @@ int kvq_layout_of(const kvq_config* cfg, kvq_layout* out) {
   L.t16_bytes = pattern ? 0 : U * tcap * 2;
   L.tab_bytes = pattern ? U * (uint64_t)cfg->max_patterns * D * 4 : U * D * 4;
   L.win_bytes = pattern ? U * 2 * D * 4 : 0;
-  uint64_t ws_attn = (uint64_t)cfg->batch * cfg->n_q_heads * L.max_splits * (D + 2) * 4;
+  // split-K partials: o[D], (m, l) and the per-pattern mass w[max_patterns]
+  uint64_t ws_attn = (uint64_t)cfg->batch * cfg->n_q_heads * L.max_splits *
+                     (D + 2 + (uint64_t)cfg->max_patterns) * 4;
   uint64_t ws_init = 2 * U * (uint64_t)tcap;       // k-means assignments (one byte per token)
   L.ws_bytes = ws_attn > ws_init ? ws_attn : ws_init;
   L.record_bytes = (int)(D * cfg->bits / 8 + L.n_groups * 4 + (pattern ? 1 : 2));

@@ -117,6 +117,7 @@ hipError_t launch_window_reset(float* win_k, float* win_v, int units, hipStream_
 hipError_t launch_encode(const EncodeArgs& a, int units, int n_blocks_x, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, int units, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attention_combine(const AttnArgs& a, hipStream_t s);
 bool mfma_attention_supported(int bits, int group, int gq);
 hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t s);
 hipError_t launch_kmeans_pair(const void* xk, const void* xv, int bf16, int n_tok, int k,

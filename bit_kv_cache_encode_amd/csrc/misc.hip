@@ -48,8 +48,9 @@ __device__ __forceinline__ uint32_t read_code(const uint8_t* codes, int which, i
     byte = (u * tcap + t) * (D * bits / 8) + bit / 8;
     sh = (int)(bit & 7);
   } else {
-    int64_t bit = (int64_t)(t % VT) * bits;
-    byte = (u * (tcap / VT) + t / VT) * (VT * D * bits / 8) + (int64_t)d * 4 * bits + bit / 8;
+    const int per = 32 / bits, i = t % VT;
+    const int64_t bit = (int64_t)(i % per) * bits;
+    byte = (u * (tcap / VT) + t / VT) * (VT * D * bits / 8) + ((int64_t)(i / per) * D + d) * 4 + bit / 8;
     sh = (int)(bit & 7);
   }
   return (codes[byte] >> sh) & ((1u << bits) - 1u);

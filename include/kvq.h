@@ -33,8 +33,9 @@
  * noted; T = token capacity, max_tokens rounded up to a multiple of 64):
  *  - codes: T * 128 * bits / 8 bytes.  K is token-major: channel d of a token
  *    sits at bit bits*d of the token's record (little-endian).  V is stored
- *    in tiles of 32 tokens, channel-major: channel d of a tile owns 4*bits
- *    bytes and token i of the tile sits at bit bits*i.
+ *    in tiles of 32 tokens; a tile is made of 32-bit words, each holding
+ *    32/bits consecutive tokens of one channel (token k of the word at bit
+ *    bits*k), word w of channel d at byte (w*128 + d)*4 of the tile.
  *  - sz: per token and group, the binary16 scale s then the binary16 zero z
  *    (Eq 1: x^ = s*q + z).  z is the group minimum rounded toward -inf, s is
  *    (max - z)/(2^bits - 1) rounded toward +inf; codes are

@@ -266,7 +266,7 @@ def attn_exact(k, v, q, n_q_heads, sm_scale=0.0):
 
 def unpack_codes(packed: np.ndarray, which: int, T: int, D: int, bits: int) -> np.ndarray:
     """Codes [U][T][D] from the stored byte layout (K token-major; V 32-token
-    tiles, channel-major).  Pure index arithmetic."""
+    tiles of 32-bit words, word-major then channel).  Pure index arithmetic."""
     U = packed.shape[0]
     per = 8 // bits
     mask = (1 << bits) - 1
@@ -275,5 +275,6 @@ def unpack_codes(packed: np.ndarray, which: int, T: int, D: int, bits: int) -> n
     vals = ((b[..., None] >> sh) & mask).reshape(U, -1)   # code stream in bit order
     if which == 0:
         return vals.reshape(U, -1, D)[:, :T]
-    tiles = vals.reshape(U, -1, D, VTILE)                 # [U][tile][d][i]
-    return tiles.transpose(0, 1, 3, 2).reshape(U, -1, D)[:, :T]
+    per_word = 32 // bits
+    tiles = vals.reshape(U, -1, bits, D, per_word)        # [U][tile][word][d][k]
+    return tiles.transpose(0, 1, 2, 4, 3).reshape(U, -1, D)[:, :T]

@@ -48,8 +48,10 @@
  *      hq reading kv-head hq / (Hq/Hkv), evaluated in binary64 over the
  *      dequantised cache and rounded to fp32.
  *  R15 Code layout: K codes token-major, channel d at bit n*d of the token's
- *      record (little-endian); V codes in tiles of 32 tokens, channel-major:
- *      channel d of the tile owns 4n bytes, token i of the tile at bit n*i.
+ *      record (little-endian); V codes in tiles of 32 tokens made of 32-bit
+ *      words, each holding 32/n consecutive tokens of one channel (token k of
+ *      the word at bit n*k); word w of channel d sits at (w*D + d)*4 bytes
+ *      of the tile (all channels' first words, then their second words...).
  */
 #include "kvqref.h"
 
@@ -360,9 +362,10 @@ static int64_t code_byte(const kvqref_cache* c, int kind, int64_t u, int32_t t, 
     return (u * c->tcap + t) * c->kbytes + bit / 8;
   }
   int64_t tile = t / KVQREF_VTILE, i = t % KVQREF_VTILE;
-  int64_t bit = i * bits;
+  int64_t per_word = 32 / bits;              /* tokens per 32-bit word */
+  int64_t word = i / per_word, bit = (i % per_word) * bits;
   *shift = (int)(bit & 7);
-  return (u * (c->tcap / KVQREF_VTILE) + tile) * c->vtile + (int64_t)d * 4 * bits + bit / 8;
+  return (u * (c->tcap / KVQREF_VTILE) + tile) * c->vtile + (word * c->D + d) * 4 + bit / 8;
 }
 
 static void put_code(kvqref_cache* c, int kind, int64_t u, int32_t t, int32_t d, unsigned q) {

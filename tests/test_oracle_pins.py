@@ -233,7 +233,7 @@ def test_golden_pattern_2bit(ref):
     assert list(c.sz(0)[0, :2].ravel()) == [int(v, 16) for v in g["k_sz"]]
     assert list(c.sz(1)[0, :2].ravel()) == [int(v, 16) for v in g["v_sz"]]
     vb = c.codes(1)[0]
-    assert [vb[8 * d] for d in range(8)] == [int(v, 16) for v in g["v_chan_byte0"]]
+    assert [vb[4 * d] for d in range(8)] == [int(v, 16) for v in g["v_chan_byte0"]]
     assert list(c.ties(0)[0, 1]) == [int(v) for v in g["k_ties_t1"]]
     deq = c.dequant(0, 0, 2)[0, 0]
     assert list(deq[0]) == [float(v) for v in g["k_dequant_t0"]]
