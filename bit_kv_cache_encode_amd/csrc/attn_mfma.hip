@@ -12,8 +12,13 @@
 //       the VALU then applies s_g, z_g and the pattern term (q . M^K)[k*].
 //  PV:  rows = (head, group), columns = 16 channels, reduction = 32 tokens of
 //       one V code tile.  Row (h, g) carries p_h * s_g per token; a column
-//       only keeps the row of its own group.  z and pattern terms are summed
-//       on the side (sum p z per group; a per-head histogram of p over k*).
+//       only keeps the row of its own group.  z is summed on the side
+//       (sum p z per group).
+//  V pattern mass  w_j = sum_t p_t [k*_t = j]  is a third product: rows =
+//       (head, part) with part 0/1 = binary16 hi/lo of p, columns = 16
+//       patterns, reduction = 32 tokens, B = the one-hot matrix of the
+//       tokens' pattern indices.  For more than 64 patterns it falls back to
+//       LDS atomics.
 //
 // Codes enter the MFMA as binary16 subnormals: a 2-bit (4-bit) field masked
 // in place inside a 32-bit word is the integer code times 2^-24 times a power
@@ -30,13 +35,13 @@ namespace kvq {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int MF_WAVES = 4;
 constexpr int MF_THREADS = MF_WAVES * 64;
 constexpr int TILE = 64;         // tokens per wave iteration (4 QK column blocks, 2 V tiles)
 constexpr int EQ = 10;           // q operand carries 2^EQ
 constexpr int EP = 4;            // p*s operand carries 2^EP
-constexpr int MAXP = 256;
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a),
@@ -130,18 +135,25 @@ __host__ __device__ inline int ps_row(int h) {
 }
 constexpr int PS_FLOATS = 2 * 320;   // 8 rows
 
+// Row offset (words) of head h in a wave's packed (hi | lo << 16) p table;
+// 68-word rows put the 16-byte reads of different heads on different banks.
+__host__ __device__ inline int ph_row(int h) { return h * 68; }
+constexpr int PH_WORDS = 8 * 68;
+
 // Dynamic LDS layout of a block (bytes); npat = padded pattern count.
 struct MfLds {
-  int q, qsum, qm, ps, vs, w, alpha, m, o, z, l, wsum, M, last, f, tiles, total;
+  int q, qsum, qm, ps, ph, vs, w, alpha, m, o, z, l, wsum, M, last, f, tiles, total;
 };
 __host__ __device__ inline int al16(int x) { return (x + 15) & ~15; }
-__host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes, int splits) {
+__host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes, int splits,
+                                        bool hist_mfma) {
   MfLds L;
   int o = 0;
   L.q = o; o = al16(o + HB * D * 4);
   L.qsum = o; o = al16(o + HB * NG * 4);
   L.qm = o; o = al16(o + HB * npat * 4);
   L.ps = o; o = al16(o + MF_WAVES * PS_FLOATS * 4);
+  L.ph = o; o = al16(o + (hist_mfma ? MF_WAVES * PH_WORDS * 4 : 0));
   L.vs = o; o = al16(o + MF_WAVES * NG * TILE * 2);
   L.w = o; o = al16(o + MF_WAVES * HB * npat * 4);
   L.alpha = o; o = al16(o + MF_WAVES * HB * 4);
@@ -168,9 +180,12 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t&
   lo = __builtin_bit_cast(uint32_t, l);
 }
 
-template <int BITS, int NG, bool KVARN>
+// Pattern-mass path: NPB > 0 -> one-hot MFMA over NPB blocks of 16 patterns;
+// NPB == 0 -> LDS atomics (or no pattern term at all for KVarN).
+template <int BITS, int NG, bool KVARN, int NPB>
 __global__ void __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_mfma_kernel(AttnArgs a) {
+  static_assert(!(KVARN && NPB), "KVarN has no pattern term");
   using TS = TileShape<BITS, NG, KVARN>;
   constexpr int G = D / NG;            // channels per group
   constexpr int HB = 16 / NG;          // heads per row block
@@ -188,11 +203,12 @@ attn_mfma_kernel(AttnArgs a) {
   const int t_begin = split * a.chunk, t_end = min(a.T, t_begin + a.chunk);
   const int n_pat = KVARN ? 0 : a.n_pat;
   const int npat = pad_pat(n_pat);
-  const MfLds Lo = mf_lds(HB, NG, npat, TS::BYTES, a.splits);
+  const MfLds Lo = mf_lds(HB, NG, npat, TS::BYTES, a.splits, NPB > 0);
   float* s_q = (float*)(mf_raw + Lo.q);            // [HB][D]
   float* s_qsum = (float*)(mf_raw + Lo.qsum);      // [HB][NG]
   float* s_qm = (float*)(mf_raw + Lo.qm);          // [HB][npat]
   float* s_ps = (float*)(mf_raw + Lo.ps) + wave * PS_FLOATS;
+  uint32_t* s_ph = (uint32_t*)(mf_raw + Lo.ph) + wave * PH_WORDS;
   _Float16* s_vs = (_Float16*)(mf_raw + Lo.vs) + wave * NG * TILE;
   float* s_w = (float*)(mf_raw + Lo.w);            // [WAVES][HB][npat]
   float* s_alpha = (float*)(mf_raw + Lo.alpha);    // [WAVES][HB]
@@ -353,6 +369,14 @@ attn_mfma_kernel(AttnArgs a) {
   f32x4 oacc[8];
 #pragma unroll
   for (int bb = 0; bb < 8; ++bb) oacc[bb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // pattern-mass accumulators: row 4j + r = (head head0 + r / NG, part r % NG)
+  f32x4 hacc[NPB > 0 ? NPB : 1];
+#pragma unroll
+  for (int cb = 0; cb < (NPB > 0 ? NPB : 1); ++cb) hacc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // hist A: this lane's row (head n16 / NG, part n16 % NG) takes the low
+  // (part 0) or high (part 1) binary16 of each packed word; other rows are 0
+  const uint32_t hsel = (n16 / NG >= a.gq || n16 % NG > 1) ? 0x0C0C0C0Cu
+                        : (n16 % NG == 0 ? 0x05040100u : 0x07060302u);
 
   int tile = t_begin + TILE * wave;
   for (; tile < t_end; tile += TILE * MF_WAVES) {
@@ -385,15 +409,13 @@ attn_mfma_kernel(AttnArgs a) {
         C[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       }
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        u32x4 B[4];
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) B[nb] = unpack_k<BITS>(kw[nb], c);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) C[nb] = mfma16(aq_hi[c], B[nb], C[nb]);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) C[nb] = mfma16(aq_lo[c], B[nb], C[nb]);
-      }
+        for (int nb = 0; nb < 4; ++nb) {
+          const u32x4 B = unpack_k<BITS>(kw[nb], c);
+          C[nb] = mfma16(aq_hi[c], B, C[nb]);
+          C[nb] = mfma16(aq_lo[c], B, C[nb]);
+        }
     }
     float sc[4][SPL];
 #pragma unroll
@@ -465,7 +487,12 @@ attn_mfma_kernel(AttnArgs a) {
       for (int bb = 0; bb < 8; ++bb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) oacc[bb][r] *= al[r / NG];
-      if (!KVARN && n_pat > 0) {
+      if constexpr (NPB > 0) {
+#pragma unroll
+        for (int cb = 0; cb < NPB; ++cb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) hacc[cb][r] *= al[r / NG];
+      } else if (!KVARN && n_pat > 0) {
         if (n16 == 0)
 #pragma unroll
           for (int s = 0; s < SPL; ++s) s_alpha[wave * HB + head0 + s] = al[s];
@@ -478,6 +505,8 @@ attn_mfma_kernel(AttnArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
     }
+    float pk[4][SPL];
+    int vk[4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int t64 = 16 * nb + n16;
@@ -512,15 +541,32 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
         for (int g = 0; g < NG; ++g)
           zacc[s * NG + g] = __builtin_fmaf(pt, bits2f((uint16_t)(vszz[g] >> 16)), zacc[s * NG + g]);
-        if (!KVARN && vix != KVQ_INDEX_NONE && head0 + s < a.gq)
-          atomicAdd(&wrow[(head0 + s) * npat + vix], p);
+        pk[nb][s] = p;
         s_ps[ps_row(head0 + s) + t64] = ldexpf(pt, EP - pv_shift<BITS>(t64 & 31));
+        if constexpr (NPB > 0) {
+          // p * 2^15 <= 2^15 as binary16 hi + lo (round to nearest even)
+          const float x = p * 32768.0f;
+          const _Float16 hi = (_Float16)x;
+          const _Float16 lo = (_Float16)(x - (float)hi);
+          s_ph[ph_row(head0 + s) + t64] = (uint32_t)h2bits(hi) | ((uint32_t)h2bits(lo) << 16);
+        }
       }
+      vk[nb] = vix;
       // V group scale of this token for group j (lanes j < NG)
       uint32_t sw = vszz[0];
 #pragma unroll
       for (int g = 1; g < NG; ++g) sw = (j == g) ? vszz[g] : sw;
       if (j < NG) s_vs[j * TILE + t64] = __builtin_bit_cast(_Float16, (uint16_t)(sw & 0xFFFFu));
+    }
+    // V pattern mass: the tile's LDS adds are issued back to back so their
+    // latencies overlap (nothing reads LDS between them)
+    if (!KVARN && NPB == 0 && n_pat > 0) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int s = 0; s < SPL; ++s)
+          if (vk[nb] != KVQ_INDEX_NONE && head0 + s < a.gq)
+            atomicAdd(&wrow[(head0 + s) * npat + vk[nb]], pk[nb][s]);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -554,17 +600,46 @@ attn_mfma_kernel(AttnArgs a) {
           alo[p] = lo;
         }
       }
+      if constexpr (NPB > 0) {
+        // element i = 2p + e of lane group j <-> token 32 kb + 8 j + i
+        const u32x4 h0 = *(const u32x4*)(s_ph + ph_row(n16 / NG) + 32 * kb + 8 * j);
+        const u32x4 h1 = *(const u32x4*)(s_ph + ph_row(n16 / NG) + 32 * kb + 8 * j + 4);
+        u32x4 ah;
+        ah[0] = __builtin_amdgcn_perm(h0[1], h0[0], hsel);
+        ah[1] = __builtin_amdgcn_perm(h0[3], h0[2], hsel);
+        ah[2] = __builtin_amdgcn_perm(h1[1], h1[0], hsel);
+        ah[3] = __builtin_amdgcn_perm(h1[3], h1[2], hsel);
+        // pattern indices of tokens 2p, 2p + 1 in the two 16-bit halves
+        const uint2 vw = *(const uint2*)(tb + TS::O_VI + 32 * kb + 8 * j);
+        uint32_t pr[4];
+        pr[0] = __builtin_amdgcn_perm(0u, vw.x, 0x0C010C00u);
+        pr[1] = __builtin_amdgcn_perm(0u, vw.x, 0x0C030C02u);
+        pr[2] = __builtin_amdgcn_perm(0u, vw.y, 0x0C010C00u);
+        pr[3] = __builtin_amdgcn_perm(0u, vw.y, 0x0C030C02u);
+#pragma unroll
+        for (int cb = 0; cb < NPB; ++cb) {
+          // B = 2^-24 (binary16 0x0001) where the index equals this column's
+          // pattern, else 0
+          const u16x2 tgt = u16x2{(uint16_t)(16 * cb + n16), (uint16_t)(16 * cb + n16)};
+          u32x4 B;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const u16x2 d = __builtin_bit_cast(u16x2, pr[q]) ^ tgt;
+            B[q] = __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(u16x2{1, 1}, d));
+          }
+          hacc[cb] = mfma16(ah, B, hacc[cb]);
+        }
+      }
       // this lane's word of channels 8*n16 .. 8*n16+7 (word-major V tile)
       const int word = BITS == 2 ? (j >> 1) : j;
       const u32x4* vp = (const u32x4*)(tb + TS::O_VC + kb * VTB + (word * D + 8 * n16) * 4);
       const u32x4 w0 = vp[0], w1 = vp[1];
-      u32x4 B[8];
 #pragma unroll
-      for (int bb = 0; bb < 8; ++bb) B[bb] = unpack_v<BITS>(bb < 4 ? w0[bb] : w1[bb - 4], j);
-#pragma unroll
-      for (int bb = 0; bb < 8; ++bb) oacc[bb] = mfma16(ahi, B[bb], oacc[bb]);
-#pragma unroll
-      for (int bb = 0; bb < 8; ++bb) oacc[bb] = mfma16(alo, B[bb], oacc[bb]);
+      for (int bb = 0; bb < 8; ++bb) {
+        const u32x4 B = unpack_v<BITS>(bb < 4 ? w0[bb] : w1[bb - 4], j);
+        oacc[bb] = mfma16(ahi, B, oacc[bb]);
+        oacc[bb] = mfma16(alo, B, oacc[bb]);
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -617,6 +692,16 @@ attn_mfma_kernel(AttnArgs a) {
         const int s = r / NG, h = head0 + s;
         if (h < a.gq) atomicAdd(&s_o[h * D + ch], oacc[bb][r] * oscale * f[s]);
       }
+    }
+  }
+  if constexpr (NPB > 0) {
+    // w = (hi + lo rows) * 2^-15 / 2^-24
+#pragma unroll
+    for (int cb = 0; cb < NPB; ++cb) {
+      const int pat = 16 * cb + n16;
+#pragma unroll
+      for (int s = 0; s < SPL; ++s)
+        if (pat < npat) wrow[(head0 + s) * npat + pat] = (hacc[cb][s * NG] + hacc[cb][s * NG + 1]) * 512.0f;
     }
   }
   if (!KVARN && n_pat > 0) {
@@ -730,21 +815,31 @@ attn_mfma_kernel(AttnArgs a) {
   if (tid == 0) a.r.cnt[u] = 0;   // ready for the next call (stream-ordered)
 }
 
-template <int BITS, int NG, bool KVARN>
+template <int BITS, int NG, bool KVARN, int NPB>
 static hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
   constexpr int HB = 16 / NG;
   const int npat = pad_pat(KVARN ? 0 : a.n_pat);
-  const MfLds L = mf_lds(HB, NG, npat, TileShape<BITS, NG, KVARN>::BYTES, a.splits);
+  const MfLds L = mf_lds(HB, NG, npat, TileShape<BITS, NG, KVARN>::BYTES, a.splits, NPB > 0);
   static int attr = 0;
   if (L.total > attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel<BITS, NG, KVARN>,
+    hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel<BITS, NG, KVARN, NPB>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, L.total);
     if (e != hipSuccess) return e;
     attr = L.total;
   }
-  hipLaunchKernelGGL((attn_mfma_kernel<BITS, NG, KVARN>), dim3(a.B * a.Hkv * a.splits),
+  hipLaunchKernelGGL((attn_mfma_kernel<BITS, NG, KVARN, NPB>), dim3(a.B * a.Hkv * a.splits),
                      dim3(MF_THREADS), L.total, s, a);
   return hipGetLastError();
+}
+
+template <int BITS, int NG>
+static hipError_t launch_bits_group(const AttnArgs& a, hipStream_t s) {
+  if (a.mode == KVQ_MODE_KVARN) return launch_one<BITS, NG, true, 0>(a, s);
+  if (a.n_pat <= 0) return launch_one<BITS, NG, false, 0>(a, s);
+  if (a.n_pat <= 16) return launch_one<BITS, NG, false, 1>(a, s);
+  if (a.n_pat <= 32) return launch_one<BITS, NG, false, 2>(a, s);
+  if (a.n_pat <= 64) return launch_one<BITS, NG, false, 4>(a, s);
+  return launch_one<BITS, NG, false, 0>(a, s);
 }
 
 bool mfma_attention_supported(int bits, int group, int gq) {
@@ -755,13 +850,8 @@ bool mfma_attention_supported(int bits, int group, int gq) {
 }
 
 hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t s) {
-  const bool kv = a.mode == KVQ_MODE_KVARN;
-  if (a.group == 32) {
-    if (a.bits == 2) return kv ? launch_one<2, 4, true>(a, s) : launch_one<2, 4, false>(a, s);
-    return kv ? launch_one<4, 4, true>(a, s) : launch_one<4, 4, false>(a, s);
-  }
-  if (a.bits == 2) return kv ? launch_one<2, 2, true>(a, s) : launch_one<2, 2, false>(a, s);
-  return kv ? launch_one<4, 2, true>(a, s) : launch_one<4, 2, false>(a, s);
+  if (a.group == 32) return a.bits == 2 ? launch_bits_group<2, 4>(a, s) : launch_bits_group<4, 4>(a, s);
+  return a.bits == 2 ? launch_bits_group<2, 2>(a, s) : launch_bits_group<4, 2>(a, s);
 }
 
 }  // namespace kvq
