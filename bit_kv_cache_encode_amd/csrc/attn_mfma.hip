@@ -142,11 +142,10 @@ constexpr int PH_WORDS = 8 * 68;
 
 // Dynamic LDS layout of a block (bytes); npat = padded pattern count.
 struct MfLds {
-  int q, qsum, qm, ps, ph, vs, w, alpha, m, o, z, l, wsum, M, last, f, tiles, total;
+  int q, qsum, qm, ps, ph, vs, w, alpha, m, o, z, l, wsum, M, last, tiles, total;
 };
 __host__ __device__ inline int al16(int x) { return (x + 15) & ~15; }
-__host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes, int splits,
-                                        bool hist_mfma) {
+__host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes, bool hist_mfma) {
   MfLds L;
   int o = 0;
   L.q = o; o = al16(o + HB * D * 4);
@@ -164,8 +163,9 @@ __host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes
   L.wsum = o; o = al16(o + HB * npat * 4);
   L.M = o; o = al16(o + HB * 4);
   L.last = o; o = al16(o + 16);
-  L.f = o; o = al16(o + HB * splits * 4);
-  L.tiles = o; o = al16(o + MF_WAVES * tile_bytes);
+  // the tile buffers, reused after the loop for per-wave o[HB][D] and (l, z[NG])
+  const int part_bytes = MF_WAVES * HB * (D + 1 + NG) * 4;
+  L.tiles = o; o = al16(o + (MF_WAVES * tile_bytes > part_bytes ? MF_WAVES * tile_bytes : part_bytes));
   L.total = o;
   return L;
 }
@@ -203,7 +203,7 @@ attn_mfma_kernel(AttnArgs a) {
   const int t_begin = split * a.chunk, t_end = min(a.T, t_begin + a.chunk);
   const int n_pat = KVARN ? 0 : a.n_pat;
   const int npat = pad_pat(n_pat);
-  const MfLds Lo = mf_lds(HB, NG, npat, TS::BYTES, a.splits, NPB > 0);
+  const MfLds Lo = mf_lds(HB, NG, npat, TS::BYTES, NPB > 0);
   float* s_q = (float*)(mf_raw + Lo.q);            // [HB][D]
   float* s_qsum = (float*)(mf_raw + Lo.qsum);      // [HB][NG]
   float* s_qm = (float*)(mf_raw + Lo.qm);          // [HB][npat]
@@ -672,128 +672,155 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
   for (int s = 0; s < SPL; ++s)
     f[s] = (m_run[s] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run[s] - s_M[head0 + s]);
-  if (n16 == 0) {
-#pragma unroll
-    for (int s = 0; s < SPL; ++s) {
-      atomicAdd(&s_l[head0 + s], f[s] * l_run[s]);
-#pragma unroll
-      for (int g = 0; g < NG; ++g) atomicAdd(&s_z[(head0 + s) * NG + g], f[s] * zacc[s * NG + g]);
-    }
-  }
+  // Per-wave partials, relative to the block max, with plain LDS stores into
+  // the tile region (free now): o [WAVES][HB][D], then (l, z[NG]) per row.
+  float* s_ow = (float*)(mf_raw + Lo.tiles);
+  float* s_lz = s_ow + MF_WAVES * HB * D;
   {
     const float oscale = (float)(1 << (24 - EP));
     const int gcol = n16 / CPG;
 #pragma unroll
-    for (int bb = 0; bb < 8; ++bb) {
-      const int ch = 8 * n16 + bb;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (r % NG != gcol) continue;
-        const int s = r / NG, h = head0 + s;
-        if (h < a.gq) atomicAdd(&s_o[h * D + ch], oacc[bb][r] * oscale * f[s]);
-      }
+    for (int r = 0; r < 4; ++r) {
+      if (r % NG != gcol) continue;
+      const int s = r / NG;
+      const float sc = oscale * f[s];
+      float* dst = s_ow + (wave * HB + head0 + s) * D + 8 * n16;
+      *(float4*)dst = float4{oacc[0][r] * sc, oacc[1][r] * sc, oacc[2][r] * sc, oacc[3][r] * sc};
+      *(float4*)(dst + 4) = float4{oacc[4][r] * sc, oacc[5][r] * sc, oacc[6][r] * sc, oacc[7][r] * sc};
     }
+    if (n16 == 0)
+#pragma unroll
+      for (int s = 0; s < SPL; ++s) {
+        float* lz = s_lz + (wave * HB + head0 + s) * (1 + NG);
+        lz[0] = f[s] * l_run[s];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) lz[1 + g] = f[s] * zacc[s * NG + g];
+      }
   }
   if constexpr (NPB > 0) {
-    // w = (hi + lo rows) * 2^-15 / 2^-24
+    // w = (hi + lo rows) * 2^-15 / 2^-24, relative to the block max
 #pragma unroll
     for (int cb = 0; cb < NPB; ++cb) {
       const int pat = 16 * cb + n16;
 #pragma unroll
       for (int s = 0; s < SPL; ++s)
-        if (pat < npat) wrow[(head0 + s) * npat + pat] = (hacc[cb][s * NG] + hacc[cb][s * NG + 1]) * 512.0f;
+        if (pat < npat)
+          wrow[(head0 + s) * npat + pat] = (hacc[cb][s * NG] + hacc[cb][s * NG + 1]) * (512.0f * f[s]);
     }
-  }
-  if (!KVARN && n_pat > 0) {
+  } else if (!KVARN && n_pat > 0) {
     if (n16 == 0)
 #pragma unroll
       for (int s = 0; s < SPL; ++s) s_alpha[wave * HB + head0 + s] = f[s];
-    __syncthreads();
+  }
+  __syncthreads();
+  // block totals: pattern masses w[h][j], l[h], z[h][g]
+  if (!KVARN && n_pat > 0)
     for (int e = tid; e < a.gq * npat; e += MF_THREADS) {
       const int h = e / npat;
       float acc = 0.0f;
 #pragma unroll
-      for (int w = 0; w < MF_WAVES; ++w)
-        acc = __builtin_fmaf(s_alpha[w * HB + h], s_w[(w * HB) * npat + e], acc);
+      for (int w = 0; w < MF_WAVES; ++w) {
+        const float x = s_w[(w * HB) * npat + e];
+        acc = NPB > 0 ? acc + x : __builtin_fmaf(s_alpha[w * HB + h], x, acc);
+      }
       s_wsum[e] = acc;
     }
+  if (tid < HB * (1 + NG)) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < MF_WAVES; ++w) acc += s_lz[w * HB * (1 + NG) + tid];
+    const int h = tid / (1 + NG), k = tid % (1 + NG);
+    if (k == 0) s_l[h] = acc;
+    else s_z[h * NG + k - 1] = acc;
   }
   __syncthreads();
 
   // ---------------------------------------------------------------- partial out
-  // o (without the pattern term), running max M, sum l and the per-pattern
-  // mass w of this split, all relative to M.
+  // Row (b, head, split): o + z + sum_j w_j M^V_j and (M, l), all relative
+  // to this split's max M.  Stores are agent-scope atomics (coherent across
+  // the XCDs' L2s), so publishing them needs only their completion.
   const int S = a.splits;
-  const int64_t rows = (int64_t)a.B * a.Hq * S;
-  float* ml = a.r.ws + rows * D;
-  float* wp = ml + rows * 2;
+  float* ml = a.r.ws + (int64_t)a.B * a.Hq * S * D;
+  const float* mv = a.r.tab[1] + (int64_t)u * a.max_pat * D;
   for (int i = tid; i < a.gq * D; i += MF_THREADS) {
     const int h = i / D, d = i % D;
     const int64_t row = ((int64_t)b * a.Hq + hq0 + h) * S + split;
-    a.r.ws[row * D + d] = s_o[i] + s_z[h * NG + d / G];
+    float o = s_z[h * NG + d / G];
+#pragma unroll
+    for (int w = 0; w < MF_WAVES; ++w) o += s_ow[(w * HB + h) * D + d];
+    if (!KVARN)
+#pragma unroll 8
+      for (int jj = 0; jj < n_pat; ++jj) o = __builtin_fmaf(s_wsum[h * npat + jj], mv[(int64_t)jj * D + d], o);
+    __hip_atomic_store(&a.r.ws[row * D + d], o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (d == 0) {
-      ml[row * 2] = s_M[h];
-      ml[row * 2 + 1] = s_l[h];
+      __hip_atomic_store(&ml[row * 2], s_M[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&ml[row * 2 + 1], s_l[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  if (!KVARN)
-    for (int i = tid; i < a.gq * n_pat; i += MF_THREADS) {
-      const int h = i / n_pat, jj = i % n_pat;
-      const int64_t row = ((int64_t)b * a.Hq + hq0 + h) * S + split;
-      wp[row * a.max_pat + jj] = s_wsum[h * npat + jj];
-    }
   // ---------------------------------------------------------------- fused combine
-  // Every thread's partial stores complete before the barrier; thread 0's
-  // release-acquire increment (agent scope) publishes them, and the block
-  // that arrives last merges all splits of the unit.
+  // Each thread waits until its partial stores have completed at agent scope;
+  // after the barrier thread 0 counts this split in, and the block that
+  // arrives last (it observes S - 1 earlier increments, each made after that
+  // split's stores completed) merges all splits of the unit with agent-scope
+  // loads.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
   if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(&a.r.cnt[u], 1u, __ATOMIC_ACQ_REL,
+    const uint32_t prev = __hip_atomic_fetch_add(&a.r.cnt[u], 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     *s_last = prev == (uint32_t)(S - 1);
   }
   __syncthreads();
   if (!*s_last) return;
-  // split factors f_s = 2^(m_s - M) per head, kept in LDS (s_w is free now)
-  float* s_f = (float*)(mf_raw + Lo.f);     // [HB][S] split factors 2^(m_s - M)
-  if (tid < a.gq) {
-    const int64_t row0 = ((int64_t)b * a.Hq + hq0 + tid) * S;
-    float M = -INFINITY;
-    for (int sp = 0; sp < S; ++sp) M = fmaxf(M, ml[(row0 + sp) * 2]);
-    float L = 0.0f;
-    for (int sp = 0; sp < S; ++sp) {
-      const float fs = __builtin_amdgcn_exp2f(ml[(row0 + sp) * 2] - M);
-      s_f[tid * S + sp] = fs;
-      L = __builtin_fmaf(ml[(row0 + sp) * 2 + 1], fs, L);
-    }
-    s_l[tid] = L;
-  }
-  __syncthreads();
-  if (!KVARN && n_pat > 0) {
-    for (int i = tid; i < a.gq * n_pat; i += MF_THREADS) {
-      const int h = i / n_pat, jj = i % n_pat;
-      const int64_t row0 = ((int64_t)b * a.Hq + hq0 + h) * S;
-      float w = 0.0f;
-      for (int sp = 0; sp < S; ++sp) w = __builtin_fmaf(wp[(row0 + sp) * a.max_pat + jj], s_f[h * S + sp], w);
-      s_wsum[h * npat + jj] = w;
-    }
-    __syncthreads();
-  }
-  const float* mv = a.r.tab[1] + (int64_t)u * a.max_pat * D;
-  for (int i = tid; i < a.gq * D; i += MF_THREADS) {
-    const int h = i / D, d = i % D;
+  // out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, with a running max
+  // over chunks of 8 splits so that each chunk's loads are issued together
+  constexpr int OPT = HB * D / MF_THREADS;   // outputs per thread
+  float r_out[OPT];
+#pragma unroll
+  for (int k = 0; k < OPT; ++k) {
+    const int i = tid + k * MF_THREADS, h = i / D, d = i % D;
+    r_out[k] = 0.0f;
+    if (h >= a.gq) continue;
     const int64_t row0 = ((int64_t)b * a.Hq + hq0 + h) * S;
-    float o = 0.0f;
-#pragma unroll 4
-    for (int sp = 0; sp < S; ++sp) o = __builtin_fmaf(a.r.ws[(row0 + sp) * D + d], s_f[h * S + sp], o);
-    if (!KVARN)
-#pragma unroll 8
-      for (int jj = 0; jj < n_pat; ++jj) o = __builtin_fmaf(s_wsum[h * npat + jj], mv[(int64_t)jj * D + d], o);
-    const float r = o / s_l[h];
-    if (!KVARN) a.out[((int64_t)b * a.Hq + hq0 + h) * D + d] = r;
-    else s_o[i] = r * a.r.tab[1][(int64_t)u * D + d];
+    float M = -INFINITY, L = 0.0f, O = 0.0f;
+    for (int c0 = 0; c0 < S; c0 += 8) {
+      float mm[8], ll[8], oo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sp = c0 + e < S ? c0 + e : c0;
+        mm[e] = __hip_atomic_load(&ml[(row0 + sp) * 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ll[e] = __hip_atomic_load(&ml[(row0 + sp) * 2 + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        oo[e] = __hip_atomic_load(&a.r.ws[(row0 + sp) * D + d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      float cm = M;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cm = (c0 + e < S) ? fmaxf(cm, mm[e]) : cm;
+      const float rs = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - cm);
+      L *= rs;
+      O *= rs;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float fs = (c0 + e < S && mm[e] != -INFINITY) ? __builtin_amdgcn_exp2f(mm[e] - cm) : 0.0f;
+        L = __builtin_fmaf(ll[e], fs, L);
+        O = __builtin_fmaf(oo[e], fs, O);
+      }
+      M = cm;
+    }
+    r_out[k] = O / L;
   }
-  if (KVARN) {
+  if (!KVARN) {
+#pragma unroll
+    for (int k = 0; k < OPT; ++k) {
+      const int i = tid + k * MF_THREADS, h = i / D;
+      if (h < a.gq) a.out[((int64_t)b * a.Hq + hq0) * D + i] = r_out[k];
+    }
+  } else {
+    // undo the channel scale c_V, then the rotation: v = H (c_V * v^) / sqrt(D)
+#pragma unroll
+    for (int k = 0; k < OPT; ++k) {
+      const int i = tid + k * MF_THREADS;
+      s_o[i] = r_out[k] * a.r.tab[1][(int64_t)u * D + i % D];
+    }
     __syncthreads();
     for (int hs = 1; hs < D; hs <<= 1) {
       float v[HB * D / MF_THREADS];
@@ -812,14 +839,15 @@ attn_mfma_kernel(AttnArgs a) {
     for (int i = tid; i < a.gq * D; i += MF_THREADS)
       a.out[((int64_t)b * a.Hq + hq0) * D + i] = s_o[i] * isd;
   }
-  if (tid == 0) a.r.cnt[u] = 0;   // ready for the next call (stream-ordered)
+  // ready for the next call (stream-ordered)
+  if (tid == 0) __hip_atomic_store(&a.r.cnt[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int BITS, int NG, bool KVARN, int NPB>
 static hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
   constexpr int HB = 16 / NG;
   const int npat = pad_pat(KVARN ? 0 : a.n_pat);
-  const MfLds L = mf_lds(HB, NG, npat, TileShape<BITS, NG, KVARN>::BYTES, a.splits, NPB > 0);
+  const MfLds L = mf_lds(HB, NG, npat, TileShape<BITS, NG, KVARN>::BYTES, NPB > 0);
   static int attr = 0;
   if (L.total > attr) {
     hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel<BITS, NG, KVARN, NPB>,
