@@ -49,6 +49,14 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--attn-only", type=int, default=0,
                     help="profiling aid: run N attention calls on the layer caches and exit")
+    ap.add_argument("--calib-copy", type=int, default=0,
+                    help="with --attn-only: then run plain kernels of known traffic on this many "
+                         "MiB (4 reads: sum; 4 writes: fill; 4 copies: negation), whose HBM "
+                         "counters calibrate the attention's")
+    ap.add_argument("--traffic-from", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "RAW_DIR"),
+                    help="no GPU: summarise three rocprofv3 --pmc runs of --attn-only N "
+                         "--calib-copy M (FETCH_SIZE; WRITE_SIZE; TCC_EA0_RDREQ 32B/64B/128B) "
+                         "into profiles/traffic_attention.json")
     return ap.parse_args()
 
 
@@ -61,8 +69,69 @@ def attn_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def traffic_summary(args):
+    """Attention HBM bytes per launch from rocprofv3 counter CSVs, calibrated
+    against kernels of known traffic run in the same process."""
+    import csv
+    import glob
+
+    def rows(d):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        assert f, f"no counter_collection.csv under {d}"
+        return list(csv.DictReader(open(f[0])))
+
+    def per_dispatch(rs, counter, pred):
+        vals = {}
+        for r in rs:
+            if r["Counter_Name"] == counter and pred(r["Kernel_Name"]):
+                vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        return list(vals.values())
+
+    attn = lambda n: "attn_mfma_kernel" in n or "attn_split_kernel" in n
+    red = lambda n: "reduce_kernel" in n
+    fill = lambda n: "FillFunctor" in n
+    fr, wr, rr = rows(args.traffic_from[0]), rows(args.traffic_from[1]), rows(args.traffic_from[2])
+    f_attn = per_dispatch(fr, "FETCH_SIZE", attn)
+    w_attn = per_dispatch(wr, "WRITE_SIZE", attn)
+    f_red = per_dispatch(fr, "FETCH_SIZE", red)
+    w_fill = per_dispatch(wr, "WRITE_SIZE", fill)
+    n_calib = args.calib_copy * (1 << 20) if args.calib_copy else None
+    assert n_calib, "--traffic-from needs --calib-copy M (the MiB used in the runs)"
+    big = lambda xs: [x for x in xs if x * 1024 > 0.25 * n_calib]
+    f_red, w_fill = big(f_red), big(w_fill)
+    k_read = n_calib / (1024 * sum(f_red) / len(f_red))
+    k_write = n_calib / (1024 * sum(w_fill) / len(w_fill))
+    fetch_kib = sum(f_attn) / len(f_attn)
+    write_kib = sum(w_attn) / len(w_attn)
+    raw = {}
+    for c in ("TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum",
+              "TCC_EA0_RDREQ_sum"):
+        v = per_dispatch(rr, c, attn)
+        raw[c] = sum(v) / len(v) if v else None
+    raw_bytes = None
+    if all(raw[c] is not None for c in ("TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum",
+                                        "TCC_EA0_RDREQ_128B_sum")):
+        raw_bytes = (32 * raw["TCC_EA0_RDREQ_32B_sum"] + 64 * raw["TCC_EA0_RDREQ_64B_sum"] +
+                     128 * raw["TCC_EA0_RDREQ_128B_sum"])
+    out = {
+        "source_hash": attn_source_hash(),
+        "bytes_per_launch": round(fetch_kib * 1024 * k_read + write_kib * 1024 * k_write),
+        "fetch_size_kib": round(fetch_kib, 1), "write_size_kib": round(write_kib, 1),
+        "read_factor": round(k_read, 4), "write_factor": round(k_write, 4),
+        "calibration": f"{args.calib_copy} MiB torch sum (reads) and fill_ (writes)",
+        "dispatches": len(f_attn),
+        "raw_read_requests": raw, "raw_read_bytes_per_launch": raw_bytes,
+    }
+    dst = os.path.join(ROOT, "profiles", "traffic_attention.json")
+    json.dump(out, open(dst, "w"), indent=1)
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_summary(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the decode path shards by (batch, kv-head) with no communication; see "
@@ -121,6 +190,18 @@ def main():
             layers[i % L].attn_decode(qs[i % L], out=out)
         torch.cuda.synchronize()
         print(f"attn-only: {args.attn_only} calls done")
+        if args.calib_copy:
+            n = args.calib_copy * (1 << 20) // 4
+            src = torch.ones(n, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+            for _ in range(4):
+                src.sum()
+            for _ in range(4):
+                dst.fill_(2.0)
+            for _ in range(4):
+                torch.neg(src, out=dst)
+            torch.cuda.synchronize()
+            print(f"calib-copy: {args.calib_copy} MiB x 4 reads, 4 writes, 4 copies")
         return
 
     rec = base.layout.record_bytes
