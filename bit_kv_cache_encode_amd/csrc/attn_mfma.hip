@@ -171,13 +171,39 @@ __host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes
 }
 __host__ __device__ inline int pad_pat(int n) { return n < 4 ? 4 : (n + 3) & ~3; }
 
+// Reductions over the 16 lanes of a DPP row (lanes 16r .. 16r+15): swap
+// neighbours, swap pairs, mirror halves, mirror the row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
+  return fmaxf(v, dpp_f<0x140>(v)); // row_mirror
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  return v + dpp_f<0x140>(v);
+}
+
 // Two fp32 values -> packed binary16 hi parts and lo residuals (both rounded
 // toward zero; hi + lo keeps ~21 significant bits).
 __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
   auto h = __builtin_amdgcn_cvt_pkrtz(a, b);
   hi = __builtin_bit_cast(uint32_t, h);
-  auto l = __builtin_amdgcn_cvt_pkrtz(a - (float)h[0], b - (float)h[1]);
+  // a - hi is exact; written as an fma so that the binary16 operand is read in place
+  auto l = __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf((float)h[0], -1.0f, a),
+                                      __builtin_fmaf((float)h[1], -1.0f, b));
   lo = __builtin_bit_cast(uint32_t, l);
+}
+// p * s with s in binary16 (exact product rounded once; fma with -0 keeps a*b)
+__device__ __forceinline__ float mul_h(float p, uint16_t s) {
+  return __builtin_fmaf((float)__builtin_bit_cast(_Float16, s), p, -0.0f);
 }
 
 // Pattern-mass path: NPB > 0 -> one-hot MFMA over NPB blocks of 16 patterns;
@@ -195,7 +221,8 @@ attn_mfma_kernel(AttnArgs a) {
   constexpr int VTB = VT * D * BITS / 8;
   extern __shared__ __attribute__((aligned(16))) unsigned char mf_raw[];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = tid >> 6;
   const int j = lane >> 4, n16 = lane & 15;
   const int U = a.B * a.Hkv;
   const int u = blockIdx.x % U, split = blockIdx.x / U;
@@ -469,7 +496,7 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int s = 0; s < SPL; ++s) {
       float mt = fmaxf(fmaxf(sc[0][s], sc[1][s]), fmaxf(sc[2][s], sc[3][s]));
-      mt = wmax<16>(mt);
+      mt = row_max16(mt);
       mnew[s] = fmaxf(m_run[s], mt);
       grow |= mnew[s] > m_run[s];
     }
@@ -577,8 +604,8 @@ attn_mfma_kernel(AttnArgs a) {
     for (int kb = 0; kb < 2; ++kb) {
       u32x4 ahi, alo;
       {
+        // rows of heads >= gq hold finite values that are never stored
         const int h = n16 / NG, g = n16 % NG;
-        const bool live = h < a.gq;
         // element (p, e) of this lane reads token base + p + e*off: two runs of
         // four consecutive tokens
         const int base = 32 * kb + pv_token<BITS>(j, 0), off = pv_token<BITS>(j, 1) - pv_token<BITS>(j, 0);
@@ -590,10 +617,8 @@ attn_mfma_kernel(AttnArgs a) {
         const uint32_t va[2] = {v0.x, v0.y}, vb[2] = {v1.x, v1.y};
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const float s0 = bits2f((uint16_t)(va[p >> 1] >> (16 * (p & 1))));
-          const float s1 = bits2f((uint16_t)(vb[p >> 1] >> (16 * (p & 1))));
-          const float x0 = live ? pa[p] * s0 : 0.0f;
-          const float x1 = live ? pb[p] * s1 : 0.0f;
+          const float x0 = mul_h(pa[p], (uint16_t)(va[p >> 1] >> (16 * (p & 1))));
+          const float x1 = mul_h(pb[p], (uint16_t)(vb[p >> 1] >> (16 * (p & 1))));
           uint32_t hi, lo;
           split2(x0, x1, hi, lo);
           ahi[p] = hi;
@@ -651,13 +676,9 @@ attn_mfma_kernel(AttnArgs a) {
 
   // ---------------------------------------------------------------- merge waves
 #pragma unroll
-  for (int s = 0; s < SPL; ++s)
+  for (int s = 0; s < SPL; ++s) l_run[s] = row_sum16(l_run[s]);
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) l_run[s] += __shfl_xor(l_run[s], o, 64);
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) zacc[r] += __shfl_xor(zacc[r], o, 64);
+  for (int r = 0; r < 4; ++r) zacc[r] = row_sum16(zacc[r]);
   if (n16 == 0)
 #pragma unroll
     for (int s = 0; s < SPL; ++s) s_m[wave * HB + head0 + s] = m_run[s];
