@@ -126,19 +126,28 @@ struct TileShape {
   static constexpr int P_KS = KS / 16, P_IX = IX / 16;              // pieces (<= 64)
 };
 
-// Row offset (floats) of head h in a wave's p table.  Rows hold 64 tokens;
-// within each group of four rows the offsets are 0, 72, 168, 240 (banks
-// skewed by 0, 8, 40, 48 words) so that the four rows a lane group reads hit
-// different LDS banks; groups of four rows are 320 floats apart.
-__host__ __device__ inline int ps_row(int h) {
-  return (h >> 2) * 320 + (h & 3) * 72 + ((h & 2) ? 24 : 0);
+// LDS bank layout.  A wave's p tables hold one 64-token row per head; row h
+// starts at 64 h + o(h) words with o(h) = 16 h (4 heads) or
+// 16 (h / 2) + 4 (h % 2) (8 heads), so that the 16-word write runs of the
+// heads one instruction covers, and the 4-word reads of all heads of a lane
+// group, fall on distinct banks.
+template <int HB>
+__host__ __device__ inline int prow(int h) {
+  return 64 * h + (HB == 4 ? 16 * h : 16 * (h >> 1) + 4 * (h & 1));
 }
-constexpr int PS_FLOATS = 2 * 320;   // 8 rows
-
-// Row offset (words) of head h in a wave's packed (hi | lo << 16) p table;
-// 68-word rows put the 16-byte reads of different heads on different banks.
-__host__ __device__ inline int ph_row(int h) { return h * 68; }
-constexpr int PH_WORDS = 8 * 68;
+constexpr int PS_FLOATS = 640;   // >= prow<8>(7) + 64
+constexpr int PH_WORDS = 640;
+constexpr int VS_STRIDE = TILE + 16;   // binary16 per V-scale row: rows 40 words apart
+// 16-byte pieces of the staged code tiles are stored XOR-swizzled: K piece P
+// of a token record at P ^ ((P / 16) mod pieces-per-token), V piece P at
+// P ^ ((P / 16) mod 2), which makes the per-lane reads of 16 consecutive
+// tokens (K) or channel blocks (V) conflict-free.
+template <int BITS>
+__device__ __forceinline__ int kpiece(int P) {
+  constexpr int PPT = D * BITS / 8 / 16;
+  return P ^ ((P >> 4) & (PPT - 1));
+}
+__device__ __forceinline__ int vpiece(int P) { return P ^ ((P >> 4) & 1); }
 
 // Dynamic LDS layout of a block (bytes); npat = padded pattern count.
 struct MfLds {
@@ -153,7 +162,7 @@ __host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes
   L.qm = o; o = al16(o + HB * npat * 4);
   L.ps = o; o = al16(o + MF_WAVES * PS_FLOATS * 4);
   L.ph = o; o = al16(o + (hist_mfma ? MF_WAVES * PH_WORDS * 4 : 0));
-  L.vs = o; o = al16(o + MF_WAVES * NG * TILE * 2);
+  L.vs = o; o = al16(o + MF_WAVES * NG * VS_STRIDE * 2);
   L.w = o; o = al16(o + MF_WAVES * HB * npat * 4);
   L.alpha = o; o = al16(o + MF_WAVES * HB * 4);
   L.m = o; o = al16(o + MF_WAVES * HB * 4);
@@ -236,7 +245,7 @@ attn_mfma_kernel(AttnArgs a) {
   float* s_qm = (float*)(mf_raw + Lo.qm);          // [HB][npat]
   float* s_ps = (float*)(mf_raw + Lo.ps) + wave * PS_FLOATS;
   uint32_t* s_ph = (uint32_t*)(mf_raw + Lo.ph) + wave * PH_WORDS;
-  _Float16* s_vs = (_Float16*)(mf_raw + Lo.vs) + wave * NG * TILE;
+  _Float16* s_vs = (_Float16*)(mf_raw + Lo.vs) + wave * NG * VS_STRIDE;
   float* s_w = (float*)(mf_raw + Lo.w);            // [WAVES][HB][npat]
   float* s_alpha = (float*)(mf_raw + Lo.alpha);    // [WAVES][HB]
   float* s_m = (float*)(mf_raw + Lo.m);            // [WAVES][HB]
@@ -279,9 +288,9 @@ attn_mfma_kernel(AttnArgs a) {
   auto commit = [&]() {
     u32x4* t4 = (u32x4*)tb;
 #pragma unroll
-    for (int r = 0; r < TS::R_KC; ++r) t4[TS::O_KC / 16 + lane + 64 * r] = rkc[r];
+    for (int r = 0; r < TS::R_KC; ++r) t4[TS::O_KC / 16 + kpiece<BITS>(lane + 64 * r)] = rkc[r];
 #pragma unroll
-    for (int r = 0; r < TS::R_VC; ++r) t4[TS::O_VC / 16 + lane + 64 * r] = rvc[r];
+    for (int r = 0; r < TS::R_VC; ++r) t4[TS::O_VC / 16 + vpiece(lane + 64 * r)] = rvc[r];
     if (lane < TS::P_KS) {
       t4[TS::O_KS / 16 + lane] = rks;
       t4[TS::O_VS / 16 + lane] = rvs;
@@ -289,8 +298,20 @@ attn_mfma_kernel(AttnArgs a) {
     if (lane < 2 * TS::P_IX) t4[TS::O_KI / 16 + lane] = rix;
   };
 
-  // the first tile's loads are in flight while the prologue runs
+  // Prologue loads are all issued before anything waits on them: the first
+  // tile, q (below), and this thread's 32-channel slice of pattern row
+  // tid / 4 of M^K (for q' . M^K).
   if (t_begin + TILE * wave < t_end) issue(t_begin + TILE * wave);
+  const int qm_j = tid >> 2, qm_part = tid & 3;
+  const float* mk = a.r.tab[0] + (int64_t)u * a.max_pat * D;
+  float4 mkr[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) mkr[k] = float4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (!KVARN && qm_j < n_pat) {
+    const float4* m4 = (const float4*)(mk + (int64_t)qm_j * D + qm_part * 32);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mkr[k] = m4[k];
+  }
 
   // ---------------------------------------------------------------- prologue
   for (int i = tid; i < HB * D; i += MF_THREADS) {
@@ -338,25 +359,36 @@ attn_mfma_kernel(AttnArgs a) {
     for (int o = 1; o < G / 4; o <<= 1) s += __shfl_xor(s, o, 64);
     if (h < HB && ((tid & 31) % (G / 4)) == 0) s_qsum[h * NG + c0 / G] = s;
   }
-  // q' . M^K_j: four threads per (h, j), 32 channels each
+  // q' . M^K_j: four threads per pattern j (32 channels each), all heads;
+  // patterns beyond the first 64 take further passes
   if (!KVARN && n_pat > 0) {
-    const float* mk = a.r.tab[0] + (int64_t)u * a.max_pat * D;
-    for (int i = tid; i < 4 * a.gq * n_pat; i += MF_THREADS) {
-      const int part = i & 3, pj = i >> 2, h = pj / n_pat, jj = pj % n_pat;
-      const float4* m4 = (const float4*)(mk + (int64_t)jj * D + part * 32);
-      const float* qh = s_q + h * D + part * 32;
-      float s = 0.0f;
+    for (int j0 = 0; j0 < n_pat; j0 += 64) {
+      const int jj = j0 + qm_j;
+      if (j0 > 0) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float4 m = m4[k];
-        s = __builtin_fmaf(qh[4 * k], m.x, s);
-        s = __builtin_fmaf(qh[4 * k + 1], m.y, s);
-        s = __builtin_fmaf(qh[4 * k + 2], m.z, s);
-        s = __builtin_fmaf(qh[4 * k + 3], m.w, s);
+        for (int k = 0; k < 8; ++k) mkr[k] = float4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (jj < n_pat) {
+          const float4* m4 = (const float4*)(mk + (int64_t)jj * D + qm_part * 32);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) mkr[k] = m4[k];
+        }
       }
-      s += __shfl_xor(s, 1, 64);
-      s += __shfl_xor(s, 2, 64);
-      if (part == 0) s_qm[h * npat + jj] = s;
+#pragma unroll
+      for (int h = 0; h < HB; ++h) {
+        if (h >= a.gq) break;
+        const float* qh = s_q + h * D + qm_part * 32;
+        float sdot = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          sdot = __builtin_fmaf(qh[4 * k], mkr[k].x, sdot);
+          sdot = __builtin_fmaf(qh[4 * k + 1], mkr[k].y, sdot);
+          sdot = __builtin_fmaf(qh[4 * k + 2], mkr[k].z, sdot);
+          sdot = __builtin_fmaf(qh[4 * k + 3], mkr[k].w, sdot);
+        }
+        sdot += __shfl_xor(sdot, 1, 64);
+        sdot += __shfl_xor(sdot, 2, 64);
+        if (qm_part == 0 && jj < n_pat) s_qm[h * npat + jj] = sdot;
+      }
     }
   }
   __syncthreads();
@@ -426,10 +458,10 @@ attn_mfma_kernel(AttnArgs a) {
       for (int nb = 0; nb < 4; ++nb) {
         const int t64 = 16 * nb + n16;
         if (KW == 2) {
-          const uint2 w = *(const uint2*)(tb + TS::O_KC + t64 * TS::KREC + j * 8);
+          const uint2 w = *(const uint2*)(tb + TS::O_KC + kpiece<BITS>(2 * t64 + (j >> 1)) * 16 + (j & 1) * 8);
           kw[nb][0] = w.x; kw[nb][1 % KW] = w.y;
         } else {
-          const u32x4 w = *(const u32x4*)(tb + TS::O_KC + t64 * TS::KREC + j * 16);
+          const u32x4 w = *(const u32x4*)(tb + TS::O_KC + kpiece<BITS>(4 * t64 + j) * 16);
 #pragma unroll
           for (int q = 0; q < KW; ++q) kw[nb][q] = w[q];
         }
@@ -569,13 +601,13 @@ attn_mfma_kernel(AttnArgs a) {
         for (int g = 0; g < NG; ++g)
           zacc[s * NG + g] = __builtin_fmaf(pt, bits2f((uint16_t)(vszz[g] >> 16)), zacc[s * NG + g]);
         pk[nb][s] = p;
-        s_ps[ps_row(head0 + s) + t64] = ldexpf(pt, EP - pv_shift<BITS>(t64 & 31));
+        s_ps[prow<HB>(head0 + s) + t64] = ldexpf(pt, EP - pv_shift<BITS>(t64 & 31));
         if constexpr (NPB > 0) {
           // p * 2^15 <= 2^15 as binary16 hi + lo (round to nearest even)
           const float x = p * 32768.0f;
           const _Float16 hi = (_Float16)x;
           const _Float16 lo = (_Float16)(x - (float)hi);
-          s_ph[ph_row(head0 + s) + t64] = (uint32_t)h2bits(hi) | ((uint32_t)h2bits(lo) << 16);
+          s_ph[prow<HB>(head0 + s) + t64] = (uint32_t)h2bits(hi) | ((uint32_t)h2bits(lo) << 16);
         }
       }
       vk[nb] = vix;
@@ -583,7 +615,7 @@ attn_mfma_kernel(AttnArgs a) {
       uint32_t sw = vszz[0];
 #pragma unroll
       for (int g = 1; g < NG; ++g) sw = (j == g) ? vszz[g] : sw;
-      if (j < NG) s_vs[j * TILE + t64] = __builtin_bit_cast(_Float16, (uint16_t)(sw & 0xFFFFu));
+      if (j < NG) s_vs[j * VS_STRIDE + t64] = __builtin_bit_cast(_Float16, (uint16_t)(sw & 0xFFFFu));
     }
     // V pattern mass: the tile's LDS adds are issued back to back so their
     // latencies overlap (nothing reads LDS between them)
@@ -609,10 +641,10 @@ attn_mfma_kernel(AttnArgs a) {
         // element (p, e) of this lane reads token base + p + e*off: two runs of
         // four consecutive tokens
         const int base = 32 * kb + pv_token<BITS>(j, 0), off = pv_token<BITS>(j, 1) - pv_token<BITS>(j, 0);
-        const float4 p0 = *(const float4*)(s_ps + ps_row(h) + base);
-        const float4 p1 = *(const float4*)(s_ps + ps_row(h) + base + off);
-        const uint2 v0 = *(const uint2*)(s_vs + g * TILE + base);
-        const uint2 v1 = *(const uint2*)(s_vs + g * TILE + base + off);
+        const float4 p0 = *(const float4*)(s_ps + prow<HB>(h) + base);
+        const float4 p1 = *(const float4*)(s_ps + prow<HB>(h) + base + off);
+        const uint2 v0 = *(const uint2*)(s_vs + g * VS_STRIDE + base);
+        const uint2 v1 = *(const uint2*)(s_vs + g * VS_STRIDE + base + off);
         const float pa[4] = {p0.x, p0.y, p0.z, p0.w}, pb[4] = {p1.x, p1.y, p1.z, p1.w};
         const uint32_t va[2] = {v0.x, v0.y}, vb[2] = {v1.x, v1.y};
 #pragma unroll
@@ -627,8 +659,8 @@ attn_mfma_kernel(AttnArgs a) {
       }
       if constexpr (NPB > 0) {
         // element i = 2p + e of lane group j <-> token 32 kb + 8 j + i
-        const u32x4 h0 = *(const u32x4*)(s_ph + ph_row(n16 / NG) + 32 * kb + 8 * j);
-        const u32x4 h1 = *(const u32x4*)(s_ph + ph_row(n16 / NG) + 32 * kb + 8 * j + 4);
+        const u32x4 h0 = *(const u32x4*)(s_ph + prow<HB>(n16 / NG) + 32 * kb + 8 * j);
+        const u32x4 h1 = *(const u32x4*)(s_ph + prow<HB>(n16 / NG) + 32 * kb + 8 * j + 4);
         u32x4 ah;
         ah[0] = __builtin_amdgcn_perm(h0[1], h0[0], hsel);
         ah[1] = __builtin_amdgcn_perm(h0[3], h0[2], hsel);
@@ -657,8 +689,10 @@ attn_mfma_kernel(AttnArgs a) {
       }
       // this lane's word of channels 8*n16 .. 8*n16+7 (word-major V tile)
       const int word = BITS == 2 ? (j >> 1) : j;
-      const u32x4* vp = (const u32x4*)(tb + TS::O_VC + kb * VTB + (word * D + 8 * n16) * 4);
-      const u32x4 w0 = vp[0], w1 = vp[1];
+      // pieces 2 n16 and 2 n16 + 1 of this word's block, stored swapped for n16 >= 8
+      const u32x4* vp = (const u32x4*)(tb + TS::O_VC + kb * VTB) + word * (D / 4) + 2 * n16;
+      const int vk = (n16 >> 3) & 1;
+      const u32x4 w0 = vp[vk], w1 = vp[vk ^ 1];
 #pragma unroll
       for (int bb = 0; bb < 8; ++bb) {
         const u32x4 B = unpack_v<BITS>(bb < 4 ? w0[bb] : w1[bb - 4], j);
@@ -675,6 +709,14 @@ attn_mfma_kernel(AttnArgs a) {
   }
 
   // ---------------------------------------------------------------- merge waves
+  // The V pattern rows of this thread's output channel d = tid % D are
+  // loaded now, so that they arrive while the waves merge.
+  const float* mv = a.r.tab[1] + (int64_t)u * a.max_pat * D;
+  constexpr int MVR = NPB > 0 ? 16 * NPB : 1;
+  float mvr[MVR];
+#pragma unroll
+  for (int jj = 0; jj < MVR; ++jj)
+    mvr[jj] = (NPB > 0 && jj < n_pat) ? mv[(int64_t)jj * D + tid % D] : 0.0f;
 #pragma unroll
   for (int s = 0; s < SPL; ++s) l_run[s] = row_sum16(l_run[s]);
 #pragma unroll
@@ -762,16 +804,20 @@ attn_mfma_kernel(AttnArgs a) {
   // the XCDs' L2s), so publishing them needs only their completion.
   const int S = a.splits;
   float* ml = a.r.ws + (int64_t)a.B * a.Hq * S * D;
-  const float* mv = a.r.tab[1] + (int64_t)u * a.max_pat * D;
   for (int i = tid; i < a.gq * D; i += MF_THREADS) {
     const int h = i / D, d = i % D;
     const int64_t row = ((int64_t)b * a.Hq + hq0 + h) * S + split;
     float o = s_z[h * NG + d / G];
 #pragma unroll
     for (int w = 0; w < MF_WAVES; ++w) o += s_ow[(w * HB + h) * D + d];
-    if (!KVARN)
+    if constexpr (NPB > 0) {
+#pragma unroll
+      for (int jj = 0; jj < MVR; ++jj)
+        if (jj < n_pat) o = __builtin_fmaf(s_wsum[h * npat + jj], mvr[jj], o);
+    } else if (!KVARN) {
 #pragma unroll 8
       for (int jj = 0; jj < n_pat; ++jj) o = __builtin_fmaf(s_wsum[h * npat + jj], mv[(int64_t)jj * D + d], o);
+    }
     __hip_atomic_store(&a.r.ws[row * D + d], o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (d == 0) {
       __hip_atomic_store(&ml[row * 2], s_M[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
