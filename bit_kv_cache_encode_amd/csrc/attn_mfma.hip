@@ -135,8 +135,8 @@ template <int HB>
 __host__ __device__ inline int prow(int h) {
   return 64 * h + (HB == 4 ? 16 * h : 16 * (h >> 1) + 4 * (h & 1));
 }
-constexpr int PS_FLOATS = 640;   // >= prow<8>(7) + 64
-constexpr int PH_WORDS = 640;
+template <int HB>
+constexpr int ptab_words() { return HB == 4 ? 320 : 576; }   // >= prow<HB>(HB - 1) + 64
 constexpr int VS_STRIDE = TILE + 16;   // binary16 per V-scale row: rows 40 words apart
 // 16-byte pieces of the staged code tiles are stored XOR-swizzled: K piece P
 // of a token record at P ^ ((P / 16) mod pieces-per-token), V piece P at
@@ -159,9 +159,10 @@ __host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes
   int o = 0;
   L.q = o; o = al16(o + HB * D * 4);
   L.qsum = o; o = al16(o + HB * NG * 4);
-  L.qm = o; o = al16(o + HB * npat * 4);
-  L.ps = o; o = al16(o + MF_WAVES * PS_FLOATS * 4);
-  L.ph = o; o = al16(o + (hist_mfma ? MF_WAVES * PH_WORDS * 4 : 0));
+  L.qm = o; o = al16(o + HB * 256 * 4);
+  const int pw = HB == 4 ? ptab_words<4>() : ptab_words<8>();
+  L.ps = o; o = al16(o + MF_WAVES * pw * 4);
+  L.ph = o; o = al16(o + (hist_mfma ? MF_WAVES * pw * 4 : 0));
   L.vs = o; o = al16(o + MF_WAVES * NG * VS_STRIDE * 2);
   L.w = o; o = al16(o + MF_WAVES * HB * npat * 4);
   L.alpha = o; o = al16(o + MF_WAVES * HB * 4);
@@ -202,17 +203,20 @@ __device__ __forceinline__ float row_sum16(float v) {
 
 // Two fp32 values -> packed binary16 hi parts and lo residuals (both rounded
 // toward zero; hi + lo keeps ~21 significant bits).
-__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+// m1 is -1 and z is +0, passed in as values the compiler cannot fold, so that
+// fma(binary16, m1, a) and fma(binary16, p, z) stay single v_fma_mix
+// instructions that read the binary16 operand in place.
+__device__ __forceinline__ void split2(float a, float b, float m1, uint32_t& hi, uint32_t& lo) {
   auto h = __builtin_amdgcn_cvt_pkrtz(a, b);
   hi = __builtin_bit_cast(uint32_t, h);
-  // a - hi is exact; written as an fma so that the binary16 operand is read in place
-  auto l = __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf((float)h[0], -1.0f, a),
-                                      __builtin_fmaf((float)h[1], -1.0f, b));
+  // a - hi is exact
+  auto l = __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf((float)h[0], m1, a),
+                                      __builtin_fmaf((float)h[1], m1, b));
   lo = __builtin_bit_cast(uint32_t, l);
 }
-// p * s with s in binary16 (exact product rounded once; fma with -0 keeps a*b)
-__device__ __forceinline__ float mul_h(float p, uint16_t s) {
-  return __builtin_fmaf((float)__builtin_bit_cast(_Float16, s), p, -0.0f);
+// p * s with s in binary16 and p >= 0 (exact product rounded once)
+__device__ __forceinline__ float mul_h(float p, uint16_t s, float z) {
+  return __builtin_fmaf((float)__builtin_bit_cast(_Float16, s), p, z);
 }
 
 // Pattern-mass path: NPB > 0 -> one-hot MFMA over NPB blocks of 16 patterns;
@@ -242,9 +246,9 @@ attn_mfma_kernel(AttnArgs a) {
   const MfLds Lo = mf_lds(HB, NG, npat, TS::BYTES, NPB > 0);
   float* s_q = (float*)(mf_raw + Lo.q);            // [HB][D]
   float* s_qsum = (float*)(mf_raw + Lo.qsum);      // [HB][NG]
-  float* s_qm = (float*)(mf_raw + Lo.qm);          // [HB][npat]
-  float* s_ps = (float*)(mf_raw + Lo.ps) + wave * PS_FLOATS;
-  uint32_t* s_ph = (uint32_t*)(mf_raw + Lo.ph) + wave * PH_WORDS;
+  float* s_qm = (float*)(mf_raw + Lo.qm);          // [HB][256]; entry 0xFF (no pattern) is 0
+  float* s_ps = (float*)(mf_raw + Lo.ps) + wave * ptab_words<HB>();
+  uint32_t* s_ph = (uint32_t*)(mf_raw + Lo.ph) + wave * ptab_words<HB>();
   _Float16* s_vs = (_Float16*)(mf_raw + Lo.vs) + wave * NG * VS_STRIDE;
   float* s_w = (float*)(mf_raw + Lo.w);            // [WAVES][HB][npat]
   float* s_alpha = (float*)(mf_raw + Lo.alpha);    // [WAVES][HB]
@@ -320,7 +324,8 @@ attn_mfma_kernel(AttnArgs a) {
     s_o[i] = 0.0f;
   }
   for (int i = tid; i < MF_WAVES * HB * npat; i += MF_THREADS) s_w[i] = 0.0f;
-  for (int i = tid; i < HB * npat; i += MF_THREADS) { s_wsum[i] = 0.0f; s_qm[i] = 0.0f; }
+  for (int i = tid; i < HB * npat; i += MF_THREADS) s_wsum[i] = 0.0f;
+  for (int i = tid; i < HB * 256; i += MF_THREADS) s_qm[i] = 0.0f;
   if (tid < HB * NG) s_z[tid] = 0.0f;
   if (tid < HB) s_l[tid] = 0.0f;
   __syncthreads();
@@ -387,12 +392,15 @@ attn_mfma_kernel(AttnArgs a) {
         }
         sdot += __shfl_xor(sdot, 1, 64);
         sdot += __shfl_xor(sdot, 2, 64);
-        if (qm_part == 0 && jj < n_pat) s_qm[h * npat + jj] = sdot;
+        if (qm_part == 0 && jj < n_pat) s_qm[h * 256 + jj] = sdot;
       }
     }
   }
   __syncthreads();
 
+  // -1 and +0 the compiler cannot fold (qscale is finite)
+  const float k_m1 = __builtin_fmaf(a.qscale, 0.0f, -1.0f);
+  const float k_z = a.qscale * 0.0f;
   // QK A operands: row m = n16 -> (h, g); element i of chunk c -> channel.
   u32x4 aq_hi[4], aq_lo[4];
   {
@@ -408,7 +416,7 @@ attn_mfma_kernel(AttnArgs a) {
           v2[e] = (ch / G == g) ? ldexpf(s_q[h * D + ch], EQ - code_shift<BITS>(i)) : 0.0f;
         }
         uint32_t hi, lo;
-        split2(v2[0], v2[1], hi, lo);
+        split2(v2[0], v2[1], k_m1, hi, lo);
         aq_hi[c][p] = hi;
         aq_lo[c][p] = lo;
       }
@@ -498,8 +506,7 @@ attn_mfma_kernel(AttnArgs a) {
       if (KVARN) {
         tk = bits2f(((const uint16_t*)(tb + TS::O_KI))[t64]);
       } else {
-        const int ki = tb[TS::O_KI + t64];
-        kix = valid ? ki : KVQ_INDEX_NONE;
+        kix = tb[TS::O_KI + t64];   // 0xFF (no pattern) reads a 0 entry
       }
 #pragma unroll
       for (int s = 0; s < SPL; ++s) {
@@ -512,9 +519,7 @@ attn_mfma_kernel(AttnArgs a) {
         }
         float v = __builtin_fmaf(dot, (float)(1 << (24 - EQ)), zt);
         if (!KVARN) {
-          const bool has = kix != KVQ_INDEX_NONE;
-          const float qm = s_qm[(head0 + s) * npat + (has ? kix : 0)];
-          v += has ? qm : 0.0f;
+          v += s_qm[(head0 + s) * 256 + kix];
         } else {
           v *= tk;
         }
@@ -606,7 +611,7 @@ attn_mfma_kernel(AttnArgs a) {
           // p * 2^15 <= 2^15 as binary16 hi + lo (round to nearest even)
           const float x = p * 32768.0f;
           const _Float16 hi = (_Float16)x;
-          const _Float16 lo = (_Float16)(x - (float)hi);
+          const _Float16 lo = (_Float16)__builtin_fmaf((float)hi, k_m1, x);
           s_ph[prow<HB>(head0 + s) + t64] = (uint32_t)h2bits(hi) | ((uint32_t)h2bits(lo) << 16);
         }
       }
@@ -649,10 +654,10 @@ attn_mfma_kernel(AttnArgs a) {
         const uint32_t va[2] = {v0.x, v0.y}, vb[2] = {v1.x, v1.y};
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const float x0 = mul_h(pa[p], (uint16_t)(va[p >> 1] >> (16 * (p & 1))));
-          const float x1 = mul_h(pb[p], (uint16_t)(vb[p >> 1] >> (16 * (p & 1))));
+          const float x0 = mul_h(pa[p], (uint16_t)(va[p >> 1] >> (16 * (p & 1))), k_z);
+          const float x1 = mul_h(pb[p], (uint16_t)(vb[p >> 1] >> (16 * (p & 1))), k_z);
           uint32_t hi, lo;
-          split2(x0, x1, hi, lo);
+          split2(x0, x1, k_m1, hi, lo);
           ahi[p] = hi;
           alo[p] = lo;
         }
