@@ -50,9 +50,11 @@ def gpu_t16(cache, which: int) -> np.ndarray:
     return cache.region("kv"[which] + "_t16").cpu().numpy().view(np.uint16).reshape(-1, L.token_cap)
 
 
-def gpu_codes(cache, which: int, T: int) -> np.ndarray:
+def gpu_codes(cache, which: int, T: int, units=None) -> np.ndarray:
     c = cache.cfg
     packed = cache.region("kv"[which] + "_codes").cpu().numpy().reshape(c.batch * c.n_kv_heads, -1)
+    if units is not None:
+        packed = packed[list(units)]
     return O.unpack_codes(packed, which, T, c.head_dim, c.bits)
 
 
@@ -72,8 +74,8 @@ def assert_same_encode(ref: "O.RefCache", cache, T: int, units=None, ref_units=N
     units = list(range(U)) if units is None else list(units)
     ref_units = units if ref_units is None else list(ref_units)
     for which in (0, 1):
-        gc = gpu_codes(cache, which, T)[units]
-        rc = O.unpack_codes(ref.codes(which), which, T, c.head_dim, c.bits)[ref_units]
+        gc = gpu_codes(cache, which, T, units)
+        rc = O.unpack_codes(ref.codes(which)[ref_units], which, T, c.head_dim, c.bits)
         bad = gc != rc
         assert not bad.any(), (f"{'KV'[which]} codes differ at {np.argwhere(bad)[:5]} "
                                f"(ties there: {ref.ties(which)[ref_units][:, :T][bad][:5]})")
