@@ -214,6 +214,8 @@ def main():
 
     def step(s, ev=None):
         for li, c in enumerate(layers):
+            if ev is not None:
+                ev[li][2].record()
             c.encode_append(kn[s, li][:, :, None, :], vn[s, li][:, :, None, :],
                             update_patterns=True)
             if ev is not None:
@@ -226,7 +228,7 @@ def main():
         step(s)
     torch.cuda.synchronize()
     T_start = layers[0].n_tokens
-    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)]
             for _ in range(L)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -237,6 +239,19 @@ def main():
     ms_step = wall * 1e3 / args.steps
     attn_ms = [e[0].elapsed_time(e[1]) for st in evs for e in st]
     attn_avg_us = 1e3 * sum(attn_ms) / len(attn_ms)
+    enc_ms = [e[2].elapsed_time(e[0]) for st in evs for e in st]
+    enc_avg_us = 1e3 * sum(enc_ms) / len(enc_ms)
+    # the box's own streaming-read rate (a 1 GiB sum), a second reference
+    big = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    for _ in range(2):
+        big.sum()
+    e0.record()
+    for _ in range(10):
+        big.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    stream_gbs = 10 * big.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del big
     T_mid = T_start + args.steps // 2 + 1
     step_bytes = L * (attn_bytes(T_mid) + enc_bytes)
     value = step_bytes / (ms_step * 1e-3) / 1e9
@@ -264,9 +279,13 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "attention (split + combine)",
                      "avg_launch_us": round(attn_avg_us, 3),
-                     "algorithmic_bytes_per_launch": attn_bytes(T_mid)},
+                     "algorithmic_bytes_per_launch": attn_bytes(T_mid),
+                     "stream_read_gbs": round(stream_gbs, 1),
+                     "frac_of_stream_read": round(achieved / stream_gbs, 4)},
         "encode": {"bulk_tok_s": round(B * T0 / (bulk_ms * 1e-3), 1),
                    "bulk_tokens": B * T0, "bulk_ms": round(bulk_ms, 3),
+                   "decode_step_tok_s": round(B / (enc_avg_us * 1e-6), 1),
+                   "decode_step_avg_us": round(enc_avg_us, 3),
                    "token": "one position's K and V for all 8 kv-heads of one layer"},
     }
     if not args.no_cpu_baseline:
