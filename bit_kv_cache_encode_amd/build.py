@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libkvq.so")
 OBJ = os.path.join(HERE, "_build")
-SOURCES = ["kvq_api.hip", "encode.hip", "attn.hip", "attn_mfma.hip", "misc.hip"]
+SOURCES = ["kvq_api.hip", "encode.hip", "attn.hip", "attn_mfma.hip", "attn_pp.hip", "misc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

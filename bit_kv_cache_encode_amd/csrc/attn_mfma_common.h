@@ -1,0 +1,157 @@
+// attn_mfma_common.h -- device helpers shared by the MFMA decode-attention
+// kernels: operand layouts of v_mfma_f32_16x16x32_f16 for the QK and PV
+// products over packed codes, the staged-tile shapes and LDS swizzles, DPP row
+// reductions and the binary16 hi/lo operand split.
+#pragma once
+
+#include "kvq_internal.h"
+
+namespace kvq {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int TILE = 64;         // tokens per wave iteration (4 QK column blocks, 2 V tiles)
+constexpr int EQ = 10;           // q operand carries 2^EQ
+constexpr int EP = 4;            // p*s operand carries 2^EP
+
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a),
+                                                __builtin_bit_cast(half8, b), c, 0, 0, 0);
+}
+
+// ---- K side: lane group j owns channels 32j..32j+31 of a token (8 or 16 B).
+// MFMA element i = 2p + e of reduction chunk c maps to this channel:
+template <int BITS>
+__device__ __forceinline__ int qk_channel(int j, int c, int i) {
+  const int p = i >> 1, e = i & 1;
+  return BITS == 2 ? 32 * j + 16 * (c >> 1) + 4 * (c & 1) + 8 * e + p : 32 * j + 8 * c + p + 4 * e;
+}
+// log2 of the power the unpacked code carries in element i
+template <int BITS>
+__device__ __forceinline__ int code_shift(int i) {
+  const int p = i >> 1;
+  return BITS == 2 ? 2 * p : 4 * (p & 1);
+}
+template <int BITS>
+__device__ __forceinline__ u32x4 unpack_k(const uint32_t* w, int c) {
+  u32x4 r;
+  if (BITS == 2) {
+    const uint32_t x = w[c >> 1] >> (8 * (c & 1));
+    r[0] = x & 0x00030003u; r[1] = x & 0x000C000Cu; r[2] = x & 0x00300030u; r[3] = x & 0x00C000C0u;
+  } else {
+    const uint32_t x = w[c], y = x >> 8;
+    r[0] = x & 0x000F000Fu; r[1] = x & 0x00F000F0u; r[2] = y & 0x000F000Fu; r[3] = y & 0x00F000F0u;
+  }
+  return r;
+}
+
+// ---- V side: lane group j, element i = 2p + e -> token slot of a 32-token tile
+template <int BITS>
+__device__ __forceinline__ int pv_token(int j, int i) {
+  const int p = i >> 1, e = i & 1;
+  return BITS == 2 ? 16 * (j >> 1) + 4 * (j & 1) + p + 8 * e : 8 * j + p + 4 * e;
+}
+// power of two the code of token slot tau carries (slot tau & 3 = p)
+template <int BITS>
+__device__ __forceinline__ int pv_shift(int tau) {
+  return BITS == 2 ? 2 * (tau & 3) : 4 * (tau & 1);
+}
+template <int BITS>
+__device__ __forceinline__ u32x4 unpack_v(uint32_t w, int j) {
+  u32x4 r;
+  if (BITS == 2) {
+    const uint32_t x = w >> (8 * (j & 1));
+    r[0] = x & 0x00030003u; r[1] = x & 0x000C000Cu; r[2] = x & 0x00300030u; r[3] = x & 0x00C000C0u;
+  } else {
+    const uint32_t y = w >> 8;
+    r[0] = w & 0x000F000Fu; r[1] = w & 0x00F000F0u; r[2] = y & 0x000F000Fu; r[3] = y & 0x00F000F0u;
+  }
+  return r;
+}
+
+// Per-wave LDS copy of one 64-token tile, byte offsets.  Every segment is
+// contiguous in the cache and 16-byte aligned, so the copy is plain 16-byte
+// loads per lane.
+template <int BITS, int NG, bool KVARN>
+struct TileShape {
+  static constexpr int KREC = D * BITS / 8;
+  static constexpr int KC = TILE * KREC;            // K codes
+  static constexpr int KS = TILE * NG * 4;          // K (s, z) words
+  static constexpr int VC = 2 * VT * D * BITS / 8;  // two V code tiles
+  static constexpr int VS = TILE * NG * 4;          // V (s, z) words
+  static constexpr int IX = KVARN ? 2 * TILE : TILE;// K idx or t16; V likewise
+  static constexpr int O_KC = 0, O_KS = KC, O_VC = O_KS + KS, O_VS = O_VC + VC;
+  static constexpr int O_KI = O_VS + VS, O_VI = O_KI + IX;
+  static constexpr int BYTES = O_VI + IX;
+  static constexpr int R_KC = KC / 16 / 64, R_VC = VC / 16 / 64;   // pieces per lane
+  static constexpr int P_KS = KS / 16, P_IX = IX / 16;              // pieces (<= 64)
+};
+
+// LDS bank layout.  A wave's p tables hold one 64-token row per head; row h
+// starts at 64 h + o(h) words with o(h) = 16 h (4 heads) or
+// 16 (h / 2) + 4 (h % 2) (8 heads), so that the 16-word write runs of the
+// heads one instruction covers, and the 4-word reads of all heads of a lane
+// group, fall on distinct banks.
+template <int HB>
+__host__ __device__ inline int prow(int h) {
+  return 64 * h + (HB == 4 ? 16 * h : 16 * (h >> 1) + 4 * (h & 1));
+}
+template <int HB>
+constexpr int ptab_words() { return HB == 4 ? 320 : 576; }   // >= prow<HB>(HB - 1) + 64
+constexpr int VS_STRIDE = TILE + 16;   // binary16 per V-scale row: rows 40 words apart
+// 16-byte pieces of the staged code tiles are stored XOR-swizzled: K piece P
+// of a token record at P ^ ((P / 16) mod pieces-per-token), V piece P at
+// P ^ ((P / 16) mod 2), which makes the per-lane reads of 16 consecutive
+// tokens (K) or channel blocks (V) conflict-free.
+template <int BITS>
+__device__ __forceinline__ int kpiece(int P) {
+  constexpr int PPT = D * BITS / 8 / 16;
+  return P ^ ((P >> 4) & (PPT - 1));
+}
+__device__ __forceinline__ int vpiece(int P) { return P ^ ((P >> 4) & 1); }
+
+__host__ __device__ inline int al16(int x) { return (x + 15) & ~15; }
+__host__ __device__ inline int pad_pat(int n) { return n < 4 ? 4 : (n + 3) & ~3; }
+
+// Reductions over the 16 lanes of a DPP row (lanes 16r .. 16r+15): swap
+// neighbours, swap pairs, mirror halves, mirror the row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
+  return fmaxf(v, dpp_f<0x140>(v)); // row_mirror
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  return v + dpp_f<0x140>(v);
+}
+
+// Two fp32 values -> packed binary16 hi parts and lo residuals (both rounded
+// toward zero; hi + lo keeps ~21 significant bits).
+// m1 is -1 and z is +0, passed in as values the compiler cannot fold, so that
+// fma(binary16, m1, a) and fma(binary16, p, z) stay single v_fma_mix
+// instructions that read the binary16 operand in place.
+__device__ __forceinline__ void split2(float a, float b, float m1, uint32_t& hi, uint32_t& lo) {
+  auto h = __builtin_amdgcn_cvt_pkrtz(a, b);
+  hi = __builtin_bit_cast(uint32_t, h);
+  // a - hi is exact
+  auto l = __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf((float)h[0], m1, a),
+                                      __builtin_fmaf((float)h[1], m1, b));
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+// p * s with s in binary16 and p >= 0 (exact product rounded once)
+__device__ __forceinline__ float mul_h(float p, uint16_t s, float z) {
+  return __builtin_fmaf((float)__builtin_bit_cast(_Float16, s), p, z);
+}
+
+}  // namespace kvq

@@ -354,14 +354,16 @@ int kvq_attn_decode(kvq_cache* cache, const void* q, float* out, float sm_scale,
   const float sm = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)D);
   a.qscale = sm * 1.4426950408889634f;
   const int units = c.batch * c.n_kv_heads;
-  // Kernel choice: the MFMA kernel covers groups of 32 / 64 channels with up
-  // to 16/(128/group) q-heads per kv-head; KVQ_ATTN_KERNEL=valu forces the
-  // VALU kernel (used to cross-check both).  KVQ_ATTN_BLOCKS sets the target
-  // grid size of the MFMA kernel.
+  // Kernel choice: the MFMA kernels cover groups of 32 / 64 channels with up
+  // to 16/(128/group) q-heads per kv-head.  The single-role MFMA kernel is the
+  // default; KVQ_ATTN_KERNEL=pp selects the paired score/value-wave kernel and
+  // KVQ_ATTN_KERNEL=valu the VALU kernel (used to cross-check them).
+  // KVQ_ATTN_BLOCKS sets the target grid size.
   const char* kenv = getenv("KVQ_ATTN_KERNEL");
-  const bool use_mfma = mfma_attention_supported(c.bits, c.group, a.gq) &&
-                        !(kenv && strcmp(kenv, "valu") == 0);
-  int target = use_mfma ? 512 : ATTN_TARGET_BLOCKS;
+  const bool mfma_ok = mfma_attention_supported(c.bits, c.group, a.gq);
+  const bool use_valu = !mfma_ok || (kenv && strcmp(kenv, "valu") == 0);
+  const bool use_pp = !use_valu && kenv && strcmp(kenv, "pp") == 0;
+  int target = use_valu ? ATTN_TARGET_BLOCKS : (use_pp ? 768 : 512);
   const char* benv = getenv("KVQ_ATTN_BLOCKS");
   if (benv && atoi(benv) > 0) target = atoi(benv);
   int want = (target + units - 1) / units;
@@ -371,8 +373,9 @@ int kvq_attn_decode(kvq_cache* cache, const void* q, float* out, float sm_scale,
   chunk = (chunk + ATTN_MIN_CHUNK - 1) / ATTN_MIN_CHUNK * ATTN_MIN_CHUNK;
   a.chunk = chunk;
   a.splits = (a.T + chunk - 1) / chunk;
-  if (use_mfma) {
-    hipError_t e = launch_attention_mfma(a, (hipStream_t)stream);
+  if (!use_valu) {
+    hipError_t e = use_pp ? launch_attention_pp(a, (hipStream_t)stream)
+                          : launch_attention_mfma(a, (hipStream_t)stream);
     if (e != hipSuccess) return dev_fail(e);
     return KVQ_OK;
   }

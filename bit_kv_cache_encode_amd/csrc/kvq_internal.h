@@ -120,6 +120,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_combine(const AttnArgs& a, hipStream_t s);
 bool mfma_attention_supported(int bits, int group, int gq);
 hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attention_pp(const AttnArgs& a, hipStream_t s);
 hipError_t launch_kmeans_pair(const void* xk, const void* xv, int bf16, int n_tok, int k,
                               float* tab_k, float* tab_v, int max_pat, int units, uint8_t* assign,
                               hipStream_t s);

@@ -203,8 +203,9 @@ def test_determinism_and_checkpoint():
     (2, 64, 2, "pattern"), (4, 32, 3, "pattern"), (2, 32, 4, "kvarn"), (4, 64, 8, "kvarn")])
 @pytest.mark.parametrize("blocks", [1, 40, 4096])
 def test_attention_kernels_agree(monkeypatch, bits, group, gq, mode, blocks):
-    """The MFMA kernel (fused split-K combine) and the VALU kernel both match
-    the oracle, for one block per unit up to many splits, ragged lengths."""
+    """The single-role MFMA kernel (default), the paired score/value-wave MFMA
+    kernel and the VALU kernel all match the oracle, for one block per unit up
+    to many splits, ragged lengths."""
     B, H, T = 2, 2, 1000
     gpu, ref, dt = make_pair(B, gq * H, H, 1024, bits=bits, group=group, mode=mode,
                              max_patterns=24)
@@ -222,12 +223,15 @@ def test_attention_kernels_agree(monkeypatch, bits, group, gq, mode, blocks):
     for step, qmul in ((0, 1.0), (1, 6.0)):          # flat and peaked softmax
         q = synth.queries(B, gq * H, 128, step=step) * np.float32(qmul)
         want = ref.attn_decode(to_oracle(q, True))
-        monkeypatch.delenv("KVQ_ATTN_KERNEL", raising=False)
-        got_m = gpu.attn_decode(to_dev(q, dt)).cpu().numpy()
-        monkeypatch.setenv("KVQ_ATTN_KERNEL", "valu")
-        got_v = gpu.attn_decode(to_dev(q, dt)).cpu().numpy()
-        em, ev = np.abs(got_m - want).max(), np.abs(got_v - want).max()
-        assert em <= ATTN_TOL and ev <= ATTN_TOL, (em, ev)
+        errs = {}
+        for kern in ("", "pp", "valu"):
+            if kern:
+                monkeypatch.setenv("KVQ_ATTN_KERNEL", kern)
+            else:
+                monkeypatch.delenv("KVQ_ATTN_KERNEL", raising=False)
+            got = gpu.attn_decode(to_dev(q, dt)).cpu().numpy()
+            errs[kern or "default"] = float(np.abs(got - want).max())
+        assert max(errs.values()) <= ATTN_TOL, errs
 
 
 def test_attention_repeated_calls_reset_counters(monkeypatch):
