@@ -6,40 +6,94 @@
 // window (section 3.1, Eq 5).  KVarN-style mode (arXiv 2606.03458, abstract):
 // Hadamard rotation, channel scale, token RMS scale, then the same quantizer.
 //
-// Work split: one block per (V code tile of 32 tokens, unit, K|V).  Its four
-// waves encode the tile's new tokens one vector per wave; lane l holds
-// channels l and l+64.  Pattern distances use a lane-per-pattern mapping over
-// an LDS copy of the table.  K records (token-major) are written directly;
-// V codes are staged in LDS and written word by word once per tile, merging
-// with the bits of tokens outside this call at the tile's edges.
+// One wave encodes one vector; lane l holds channels l and l + 64.  All
+// reductions across lanes (group min / max, the distance argmin, the range
+// used by the V threshold, the OR that packs K records) are DPP row
+// operations plus readlane across rows, so a vector's chain has no LDS round
+// trips except for staging the vector for the distance loop.  The distance
+// to the patterns uses every lane: lane = (pattern p, channel chunk s) with S
+// chunks per pattern, S = 4, 2 or 1 for up to 16, 32 or 64 patterns.
+//
+// Two kernels share that per-vector code:
+//  * encode_kernel: one block per (V code tile of 32 tokens, unit, K|V), four
+//    waves taking the tile's tokens in turn, the pattern table staged in LDS;
+//    V codes are staged and written as whole 32-bit words once per tile;
+//  * encode_token_kernel: one wave per (unit, K|V) for a single appended
+//    token (the decode step), every load issued up front, V codes OR-ed into
+//    their words (a tile's words are written whole, later positions zero,
+//    when its first token is appended).
 #include "kvq_internal.h"
 
 namespace kvq {
 
 constexpr int ENC_WAVES = 4;
 constexpr int ENC_THREADS = ENC_WAVES * 64;
-constexpr int PAT_LDS = 64;   // patterns staged in LDS per pass
+constexpr int PAT_PASS = 64;       // patterns per distance pass (one per lane at S = 1)
+constexpr int XS = D + 16;         // staged vector: S chunks of D/S (+4 pad) floats
 
-struct EncodeShared {
-  float pat[D / 4][PAT_LDS][4];    // pattern block, [channel/4][pattern][4]
-  float x[ENC_WAVES][D];           // the vector each wave encodes
-  uint8_t vcode[VT][D];            // V codes of the tile, [token][channel]
-  float wlo[ENC_WAVES][D];         // per-wave window partials
-  float whi[ENC_WAVES][D];
-};
+// ---------------------------------------------------------------- DPP reductions
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_fl(float v) {
+  return __builtin_bit_cast(float, dpp_u<CTRL>(__builtin_bit_cast(uint32_t, v)));
+}
+__device__ __forceinline__ float rlane(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ uint32_t rlane_u(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
 
-// Quantize the two channels a lane holds (group of channel l and of l+64)
-// with Eq 1 per group; returns codes and writes the packed (s, z) words.
+// Every lane receives the min (MAX = false) or max over its aligned group of
+// W lanes, W in {1, 2, 4, ..., 64}.  Exact: min / max do not round.
+template <bool MAX>
+__device__ __forceinline__ float fmm(float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); }
+template <bool MAX>
+__device__ __forceinline__ float group_mm(float v, int W, int lane) {
+  if (W >= 2) v = fmm<MAX>(v, dpp_fl<0xB1>(v));    // quad_perm [1,0,3,2]
+  if (W >= 4) v = fmm<MAX>(v, dpp_fl<0x4E>(v));    // quad_perm [2,3,0,1]
+  if (W >= 8) v = fmm<MAX>(v, dpp_fl<0x141>(v));   // row_half_mirror
+  if (W >= 16) v = fmm<MAX>(v, dpp_fl<0x140>(v));  // row_mirror
+  if (W >= 32) {
+    const float lo = fmm<MAX>(rlane(v, 0), rlane(v, 16));
+    const float hi = fmm<MAX>(rlane(v, 32), rlane(v, 48));
+    v = W >= 64 ? fmm<MAX>(lo, hi) : ((lane & 32) ? hi : lo);
+  }
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_min_u(uint32_t v) {
+  v = min(v, dpp_u<0xB1>(v));
+  v = min(v, dpp_u<0x4E>(v));
+  v = min(v, dpp_u<0x141>(v));
+  v = min(v, dpp_u<0x140>(v));
+  return min(min(rlane_u(v, 0), rlane_u(v, 16)), min(rlane_u(v, 32), rlane_u(v, 48)));
+}
+// OR over aligned groups of W <= 16 lanes
+__device__ __forceinline__ uint32_t group_or(uint32_t v, int W) {
+  if (W >= 2) v |= dpp_u<0xB1>(v);
+  if (W >= 4) v |= dpp_u<0x4E>(v);
+  if (W >= 8) v |= dpp_u<0x141>(v);
+  if (W >= 16) v |= dpp_u<0x140>(v);
+  return v;
+}
+
+// ---------------------------------------------------------------- Eq 1 quantizer
+// Quantize the two channels a lane holds (group of channel l and of l + 64);
+// returns the codes and the packed (s | z << 16) words of the lane's groups.
 __device__ __forceinline__ void quantize_pair(float r0, float r1, int lane, int group, int bits,
-                                              uint32_t* sz_tok, uint32_t& c0, uint32_t& c1) {
+                                              uint32_t& c0, uint32_t& c1, uint32_t& w0,
+                                              uint32_t& w1) {
   const float qmax = (float)((1 << bits) - 1);
   float lo0, hi0, lo1, hi1;
   if (group <= 64) {
-    lo0 = wmin_n(r0, group); hi0 = wmax_n(r0, group);
-    lo1 = wmin_n(r1, group); hi1 = wmax_n(r1, group);
+    lo0 = group_mm<false>(r0, group, lane); hi0 = group_mm<true>(r0, group, lane);
+    lo1 = group_mm<false>(r1, group, lane); hi1 = group_mm<true>(r1, group, lane);
   } else {  // group of 128: both halves together
-    lo0 = lo1 = wmin<64>(fminf(r0, r1));
-    hi0 = hi1 = wmax<64>(fmaxf(r0, r1));
+    lo0 = lo1 = group_mm<false>(fminf(r0, r1), 64, lane);
+    hi0 = hi1 = group_mm<true>(fmaxf(r0, r1), 64, lane);
   }
   uint16_t zb0 = f16_down(lo0), zb1 = f16_down(lo1);
   float z0 = bits2f(zb0), z1 = bits2f(zb1);
@@ -58,26 +112,209 @@ __device__ __forceinline__ void quantize_pair(float r0, float r1, int lane, int 
     float v = rintf((r1 - z1) * inv);
     c1 = (uint32_t)fminf(fmaxf(v, 0.0f), qmax);
   }
-  int ch0 = lane, ch1 = lane + 64;
-  if (ch0 % group == 0) sz_tok[ch0 / group] = (uint32_t)sb0 | ((uint32_t)zb0 << 16);
-  if (ch1 % group == 0) sz_tok[ch1 / group] = (uint32_t)sb1 | ((uint32_t)zb1 << 16);
+  w0 = (uint32_t)sb0 | ((uint32_t)zb0 << 16);
+  w1 = (uint32_t)sb1 | ((uint32_t)zb1 << 16);
 }
 
-// Write one token's K codes (token-major record): code of channel d at bit
-// bits*d.  Lanes OR their shifted codes into 32-bit words.
-__device__ __forceinline__ void store_k_record(uint8_t* rec, int lane, int bits, uint32_t c0,
-                                               uint32_t c1) {
-  const int per = 32 / bits;                 // channels per 32-bit word
-  uint32_t w0 = c0 << (bits * (lane % per));
-  uint32_t w1 = c1 << (bits * (lane % per));
-  w0 = wor_n(w0, per);
-  w1 = wor_n(w1, per);
-  if (lane % per == 0) {
-    uint32_t* out = (uint32_t*)rec;
-    out[lane / per] = w0;
-    out[(lane + 64) / per] = w1;
+// ---------------------------------------------------------------- Eq 6 distance
+// Chunks per pattern for n patterns in one pass.
+__host__ __device__ inline int dist_chunks(int n) { return n <= 16 ? 4 : (n <= 32 ? 2 : 1); }
+
+// Staged vector (per wave): chunk s of D/S channels at s * (D/S + 4).
+__device__ __forceinline__ void stage_x(float* sx, float x0, float x1, int lane, int S) {
+  const int ch = D / S;
+  sx[(lane / ch) * (ch + 4) + lane % ch] = x0;
+  sx[((lane + 64) / ch) * (ch + 4) + (lane + 64) % ch] = x1;
+}
+
+// d_mm(x, M_j) for the pattern j = j0 + lane / S of this lane's pass, reading
+// chunk s = lane % S; `row` is the start of that pattern chunk (LDS or global).
+// FULL unrolls the chunk loop so that every load is in flight at once (the
+// global table of the one-token kernel); the LDS table of the bulk kernel
+// takes four chunks per step to keep registers for more waves.
+template <int S, bool FULL>
+__device__ __forceinline__ float dist_chunk(const float* sx, const float* row, int lane) {
+  constexpr int ch = D / S;
+  const int s = lane % S;
+  const float* xs = sx + s * (ch + 4);
+  float mx = -INFINITY, mn = INFINITY;
+  constexpr int UNR = FULL ? ch / 4 : 4;
+#pragma unroll UNR
+  for (int i = 0; i < ch; i += 4) {
+    const float4 xv = *(const float4*)(xs + i);
+    const float4 mv = *(const float4*)(row + i);
+    const float e0 = xv.x - mv.x, e1 = xv.y - mv.y, e2 = xv.z - mv.z, e3 = xv.w - mv.w;
+    mx = fmaxf(mx, fmaxf(e0, e1)); mx = fmaxf(mx, fmaxf(e2, e3));
+    mn = fminf(mn, fminf(e0, e1)); mn = fminf(mn, fminf(e2, e3));
+  }
+  // combine the S chunks of the pattern (adjacent lanes)
+  if (S >= 2) { mx = fmaxf(mx, dpp_fl<0xB1>(mx)); mn = fminf(mn, dpp_fl<0xB1>(mn)); }
+  if (S >= 4) { mx = fmaxf(mx, dpp_fl<0x4E>(mx)); mn = fminf(mn, dpp_fl<0x4E>(mn)); }
+  return mx - mn;
+}
+
+// Nearest pattern (lowest index on ties) of the staged vector; `best` = its
+// distance.  tab_lds: the unit's table in pass-0 row layout (row = lane, D/S
+// + 4 floats), used when n_pat <= PAT_PASS; otherwise the global table.
+template <int S, bool FULL>
+__device__ __forceinline__ int nearest_pattern_s(const float* sx, const float* tab_lds,
+                                                 const float* tab, int n_pat, int lane, float& best) {
+  int kbest = KVQ_INDEX_NONE;
+  best = INFINITY;
+  constexpr int ch = D / S;
+  for (int j0 = 0; j0 < n_pat; j0 += PAT_PASS / S) {
+    // every lane runs the chunk loop (the DPP combines read neighbours);
+    // lanes past the last pattern read pattern 0 (or a zero LDS row) and are
+    // masked afterwards
+    const int j = j0 + lane / S;
+    const int jr = j < n_pat ? j : 0;
+    const float* row = tab_lds ? tab_lds + lane * (ch + 4) : tab + (int64_t)jr * D + (lane % S) * ch;
+    float e = dist_chunk<S, FULL>(sx, row, lane);
+    if (j >= n_pat) e = INFINITY;
+    const float emin = group_mm<false>(e, 64, lane);
+    const uint32_t jmin = wave_min_u(e == emin && j < n_pat ? (uint32_t)j : 0xFFFFFFFFu);
+    if (jmin != 0xFFFFFFFFu && (emin < best || kbest == KVQ_INDEX_NONE)) {
+      best = emin;
+      kbest = (int)jmin;
+    }
+  }
+  return kbest;
+}
+template <bool FULL>
+__device__ __forceinline__ int nearest_pattern(const float* sx, const float* tab_lds,
+                                               const float* tab, int n_pat, int lane, float& best) {
+  const int S = dist_chunks(n_pat);
+  if (S == 4) return nearest_pattern_s<4, FULL>(sx, tab_lds, tab, n_pat, lane, best);
+  if (S == 2) return nearest_pattern_s<2, FULL>(sx, tab_lds, tab, n_pat, lane, best);
+  return nearest_pattern_s<1, FULL>(sx, tab_lds, tab, n_pat, lane, best);
+}
+
+// Encode one vector (PATTERN or KVARN) held as x0 = x[lane], x1 = x[lane + 64];
+// returns the codes and the lane's (s, z) words; `kidx` = pattern index and
+// `t16` = token scale.  `sx` is this wave's staging area; `sres` (PATTERN)
+// receives the chosen pattern row for the residual when tab_lds is null.
+template <bool FULL>
+__device__ __forceinline__ void encode_vector(const EncodeArgs& a, int kind, int64_t u, float x0,
+                                              float x1, int lane, float* sx, const float* tab_lds,
+                                              uint32_t& c0, uint32_t& c1, uint32_t& w0,
+                                              uint32_t& w1, int& kidx, uint16_t& t16) {
+  const float* tab = a.r.tab[kind] + (a.mode == KVQ_MODE_PATTERN ? u * a.max_pat * D : u * D);
+  kidx = KVQ_INDEX_NONE;
+  t16 = 0;
+  if (a.mode == KVQ_MODE_PATTERN) {
+    float r0 = x0, r1 = x1;
+    if (a.n_pat > 0) {
+      const int S = dist_chunks(a.n_pat);
+      stage_x(sx, x0, x1, lane, S);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      float best;
+      int kbest = nearest_pattern<FULL>(sx, tab_lds, tab, a.n_pat, lane, best);
+      // section 3.3: V keeps its pattern iff R_flat <= rho* R_raw
+      if (kind == 1 && a.rho >= 0.0f && kbest != KVQ_INDEX_NONE) {
+        const float mx = group_mm<true>(fmaxf(x0, x1), 64, lane);
+        const float mn = group_mm<false>(fminf(x0, x1), 64, lane);
+        const float r_raw = mx - mn;
+        const float lim = a.rho * r_raw;
+        if (!(best <= lim)) kbest = KVQ_INDEX_NONE;
+      }
+      if (kbest != KVQ_INDEX_NONE) {
+        float m0, m1;
+        if (tab_lds) {
+          const int ch = D / S;
+          const float* base = tab_lds + (kbest * S) * (ch + 4);
+          m0 = base[(lane / ch) * (ch + 4) + lane % ch];
+          m1 = base[((lane + 64) / ch) * (ch + 4) + (lane + 64) % ch];
+        } else {
+          m0 = tab[(int64_t)kbest * D + lane];
+          m1 = tab[(int64_t)kbest * D + lane + 64];
+        }
+        r0 = x0 - m0;
+        r1 = x1 - m1;
+      }
+      kidx = kbest;
+      // the staged vector is rewritten by the wave's next token
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    quantize_pair(r0, r1, lane, a.group, a.bits, c0, c1, w0, w1);
+  } else {
+    // KVarN reading: FWHT (stages h = 1..64), 1/sqrt(D), channel scale,
+    // token RMS (halving-fold sum), then Eq 1 on u = y~ / t.
+#pragma unroll
+    for (int h = 1; h < 64; h <<= 1) {
+      float p0 = __shfl_xor(x0, h, 64), p1 = __shfl_xor(x1, h, 64);
+      if (lane & h) { x0 = p0 - x0; x1 = p1 - x1; }
+      else { x0 = x0 + p0; x1 = x1 + p1; }
+    }
+    {
+      float a0 = x0 + x1, a1 = x0 - x1;   // stage h = 64 (in-lane)
+      x0 = a0; x1 = a1;
+    }
+    const float isd = (float)(1.0 / __builtin_sqrt(128.0));   // fp32(1/sqrt(128))
+    x0 = x0 * isd;
+    x1 = x1 * isd;
+    const float ic0 = 1.0f / tab[lane], ic1 = 1.0f / tab[lane + 64];
+    x0 = x0 * ic0;
+    x1 = x1 * ic1;
+    float v = x0 * x0;
+    float v1 = x1 * x1;
+    v = v + v1;                                         // fold h = 64
+#pragma unroll
+    for (int h = 32; h >= 1; h >>= 1) {
+      float o = __shfl_down(v, h, 64);
+      if (lane < h) v = v + o;
+    }
+    float ss = __shfl(v, 0, 64);
+    float tt = sqrtf(ss * (1.0f / 128.0f));
+    uint16_t tb = h2bits((_Float16)tt);
+    float tf = bits2f(tb);
+    t16 = tb;
+    float u0 = 0.0f, u1 = 0.0f;
+    if (tf != 0.0f) {
+      float it = 1.0f / tf;
+      u0 = x0 * it;
+      u1 = x1 * it;
+    }
+    quantize_pair(u0, u1, lane, a.group, a.bits, c0, c1, w0, w1);
   }
 }
+
+// Store a token's (s, z) words, index / token scale and (K) packed record.
+__device__ __forceinline__ void store_token(const EncodeArgs& a, int kind, int64_t u, int t,
+                                            int lane, uint32_t c0, uint32_t c1, uint32_t w0,
+                                            uint32_t w1, int kidx, uint16_t t16) {
+  uint32_t* sz_tok = a.r.sz[kind] + ((u * a.tcap) + t) * a.ngroups;
+  if (lane % a.group == 0) sz_tok[lane / a.group] = w0;
+  if ((lane + 64) % a.group == 0 && a.group <= 64) sz_tok[(lane + 64) / a.group] = w1;
+  if (lane == 0) {
+    if (a.mode == KVQ_MODE_PATTERN) a.r.idx[kind][u * a.tcap + t] = (uint8_t)kidx;
+    else a.r.t16[kind][u * a.tcap + t] = t16;
+  }
+  if (kind == 0) {
+    // token-major record: channel d's code at bit bits*d; lanes OR their
+    // shifted codes into 32-bit words
+    const int per = 32 / a.bits;
+    const uint32_t s0 = group_or(c0 << (a.bits * (lane % per)), per);
+    const uint32_t s1 = group_or(c1 << (a.bits * (lane % per)), per);
+    if (lane % per == 0) {
+      uint32_t* out = (uint32_t*)(a.r.codes[0] + (u * a.tcap + t) * (D * a.bits / 8));
+      out[lane / per] = s0;
+      out[(lane + 64) / per] = s1;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- bulk kernel
+struct EncodeShared {
+  float tab[PAT_PASS * (D + 4)];   // pass-0 table rows, row = lane (pattern, chunk)
+  float x[ENC_WAVES][XS];          // the vector each wave encodes, in chunks
+  uint8_t vcode[VT][D];            // V codes of the tile, [token][channel]
+  float wlo[ENC_WAVES][D];         // per-wave window partials
+  float whi[ENC_WAVES][D];
+};
 
 __global__ void __launch_bounds__(ENC_THREADS) encode_kernel(EncodeArgs a) {
   __shared__ EncodeShared sh;
@@ -87,16 +324,16 @@ __global__ void __launch_bounds__(ENC_THREADS) encode_kernel(EncodeArgs a) {
   const int t_end = a.t0 + a.n_new;
   const int tile_first = a.t0 / VT + blockIdx.x * a.tiles_per_block;
   const int tile_last = min((t_end - 1) / VT, tile_first + a.tiles_per_block - 1);
-  const float* tab = a.r.tab[kind] + (a.mode == KVQ_MODE_PATTERN ? u * a.max_pat * D : u * D);
-  const int use_thr = (kind == 1) && (a.rho >= 0.0f);
 
   float wlo0 = INFINITY, wlo1 = INFINITY, whi0 = -INFINITY, whi1 = -INFINITY;
-  // Pattern table resident in LDS when it fits in one pass.
-  const bool one_pass = a.mode == KVQ_MODE_PATTERN && a.n_pat <= PAT_LDS;
-  if (one_pass) {
-    for (int i = threadIdx.x; i < a.n_pat * D; i += ENC_THREADS) {
-      int j = i / D, d = i % D;
-      sh.pat[d / 4][j][d % 4] = tab[(int64_t)j * D + d];
+  // The pattern table in the pass-0 row layout, when one pass covers it.
+  const bool staged = a.mode == KVQ_MODE_PATTERN && a.n_pat > 0 && a.n_pat <= PAT_PASS;
+  if (staged) {
+    const float* tab = a.r.tab[kind] + u * a.max_pat * D;
+    const int S = dist_chunks(a.n_pat), ch = D / S;
+    for (int i = threadIdx.x; i < PAT_PASS * ch; i += ENC_THREADS) {
+      const int row = i / ch, c = i % ch, j = row / S, s = row % S;
+      sh.tab[row * (ch + 4) + c] = j < a.n_pat ? tab[(int64_t)j * D + s * ch + c] : 0.0f;
     }
     __syncthreads();
   }
@@ -105,122 +342,27 @@ __global__ void __launch_bounds__(ENC_THREADS) encode_kernel(EncodeArgs a) {
     const int tt0 = max(tile * VT, a.t0), tt1 = min(tile * VT + VT, t_end);
     for (int t = tt0 + wave; t < tt1; t += ENC_WAVES) {
       const int64_t row = u * a.src_rows + (t - a.t0);
-      float x0 = load_in(a.src[kind], row * D + lane, a.bf16);
-      float x1 = load_in(a.src[kind], row * D + lane + 64, a.bf16);
+      const float x0 = load_in(a.src[kind], row * D + lane, a.bf16);
+      const float x1 = load_in(a.src[kind], row * D + lane + 64, a.bf16);
       if (a.win_update) {
         wlo0 = fminf(wlo0, x0); wlo1 = fminf(wlo1, x1);
         whi0 = fmaxf(whi0, x0); whi1 = fmaxf(whi1, x1);
       }
-      uint32_t* sz_tok = a.r.sz[kind] + ((u * a.tcap) + t) * a.ngroups;
-      uint32_t c0, c1;
-      if (a.mode == KVQ_MODE_PATTERN) {
-        // ---- Eq 6: nearest pattern under d_mm, lane-per-pattern.
-        sh.x[wave][lane] = x0;
-        sh.x[wave][lane + 64] = x1;
-        __builtin_amdgcn_wave_barrier();
-        float best = INFINITY;
-        int kbest = KVQ_INDEX_NONE;
-        for (int j0 = 0; j0 < a.n_pat; j0 += 64) {
-          const int j = j0 + lane;
-          float e = INFINITY;
-          if (j < a.n_pat) {
-            float mx = -INFINITY, mn = INFINITY;
-            if (one_pass) {
-              for (int d4 = 0; d4 < D / 4; ++d4) {
-                const float4 xv = *(const float4*)&sh.x[wave][d4 * 4];
-                const float4 mv = *(const float4*)&sh.pat[d4][j][0];
-                float e0 = xv.x - mv.x, e1 = xv.y - mv.y, e2 = xv.z - mv.z, e3 = xv.w - mv.w;
-                mx = fmaxf(mx, fmaxf(e0, e1)); mx = fmaxf(mx, fmaxf(e2, e3));
-                mn = fminf(mn, fminf(e0, e1)); mn = fminf(mn, fminf(e2, e3));
-              }
-            } else {
-              const float* m = tab + (int64_t)j * D;
-              for (int d4 = 0; d4 < D / 4; ++d4) {
-                const float4 xv = *(const float4*)&sh.x[wave][d4 * 4];
-                const float4 mv = *(const float4*)&m[d4 * 4];
-                float e0 = xv.x - mv.x, e1 = xv.y - mv.y, e2 = xv.z - mv.z, e3 = xv.w - mv.w;
-                mx = fmaxf(mx, fmaxf(e0, e1)); mx = fmaxf(mx, fmaxf(e2, e3));
-                mn = fminf(mn, fminf(e0, e1)); mn = fminf(mn, fminf(e2, e3));
-              }
-            }
-            e = mx - mn;
-          }
-          // argmin over lanes, lowest index on ties
-          int jj = (j < a.n_pat) ? j : 0x7FFFFFFF;
-#pragma unroll
-          for (int o = 1; o < 64; o <<= 1) {
-            float eo = __shfl_xor(e, o, 64);
-            int jo = __shfl_xor(jj, o, 64);
-            if (eo < e || (eo == e && jo < jj)) { e = eo; jj = jo; }
-          }
-          if (jj != 0x7FFFFFFF && (e < best || kbest == KVQ_INDEX_NONE)) { best = e; kbest = jj; }
-        }
-        __builtin_amdgcn_wave_barrier();
-        // ---- section 3.3: V keeps its pattern iff R_flat <= rho* R_raw.
-        if (use_thr && kbest != KVQ_INDEX_NONE) {
-          float mx = wmax<64>(fmaxf(x0, x1)), mn = wmin<64>(fminf(x0, x1));
-          float r_raw = mx - mn;
-          float lim = a.rho * r_raw;
-          if (!(best <= lim)) kbest = KVQ_INDEX_NONE;
-        }
-        float r0 = x0, r1 = x1;
-        if (kbest != KVQ_INDEX_NONE) {
-          const float* m = tab + (int64_t)kbest * D;
-          r0 = x0 - m[lane];
-          r1 = x1 - m[lane + 64];
-        }
-        if (lane == 0) a.r.idx[kind][u * a.tcap + t] = (uint8_t)kbest;
-        quantize_pair(r0, r1, lane, a.group, a.bits, sz_tok, c0, c1);
-      } else {
-        // ---- KVarN reading: FWHT (stages h = 1..64), 1/sqrt(D), channel
-        // scale, token RMS (halving-fold sum), then Eq 1 on u = y~ / t.
-#pragma unroll
-        for (int h = 1; h < 64; h <<= 1) {
-          float p0 = __shfl_xor(x0, h, 64), p1 = __shfl_xor(x1, h, 64);
-          if (lane & h) { x0 = p0 - x0; x1 = p1 - x1; }
-          else { x0 = x0 + p0; x1 = x1 + p1; }
-        }
-        {
-          float a0 = x0 + x1, a1 = x0 - x1;   // stage h = 64 (in-lane)
-          x0 = a0; x1 = a1;
-        }
-        const float isd = (float)(1.0 / __builtin_sqrt(128.0));   // fp32(1/sqrt(128))
-        x0 = x0 * isd;
-        x1 = x1 * isd;
-        const float ic0 = 1.0f / tab[lane], ic1 = 1.0f / tab[lane + 64];
-        x0 = x0 * ic0;
-        x1 = x1 * ic1;
-        float v = x0 * x0;
-        float v1 = x1 * x1;
-        v = v + v1;                                         // fold h = 64
-#pragma unroll
-        for (int h = 32; h >= 1; h >>= 1) {
-          float o = __shfl_down(v, h, 64);
-          if (lane < h) v = v + o;
-        }
-        float ss = __shfl(v, 0, 64);
-        float tt = sqrtf(ss * (1.0f / 128.0f));
-        uint16_t tb = h2bits((_Float16)tt);
-        float tf = bits2f(tb);
-        if (lane == 0) a.r.t16[kind][u * a.tcap + t] = tb;
-        float u0 = 0.0f, u1 = 0.0f;
-        if (tf != 0.0f) {
-          float it = 1.0f / tf;
-          u0 = x0 * it;
-          u1 = x1 * it;
-        }
-        quantize_pair(u0, u1, lane, a.group, a.bits, sz_tok, c0, c1);
-      }
-      if (kind == 0) {
-        store_k_record(a.r.codes[0] + (u * a.tcap + t) * (D * a.bits / 8), lane, a.bits, c0, c1);
-      } else {
+      uint32_t c0, c1, w0, w1;
+      int kidx;
+      uint16_t t16;
+      encode_vector<false>(a, kind, u, x0, x1, lane, sh.x[wave], staged ? sh.tab : nullptr, c0,
+                           c1, w0, w1, kidx, t16);
+      store_token(a, kind, u, t, lane, c0, c1, w0, w1, kidx, t16);
+      if (kind == 1) {
         sh.vcode[t - tile * VT][lane] = (uint8_t)c0;
         sh.vcode[t - tile * VT][lane + 64] = (uint8_t)c1;
       }
     }
     if (kind == 1) {
       // Pack the V tile: 32-bit word (wi, d) holds tokens wi*per .. +per-1
-      // of channel d and sits at word index wi*D + d of the tile.
+      // of channel d and sits at word index wi*D + d of the tile.  Tokens
+      // before this call keep their bits; positions after it are zero.
       __syncthreads();
       const int per = 32 / a.bits;                    // tokens per word
       const int words = D * a.bits;                   // words per tile (VT*D*bits/32)
@@ -232,7 +374,7 @@ __global__ void __launch_bounds__(ENC_THREADS) encode_kernel(EncodeArgs a) {
           const int t = tile * VT + tok0 + i;
           const uint32_t m = ((1u << a.bits) - 1u) << (i * a.bits);
           if (t >= tt0 && t < tt1) word |= ((uint32_t)sh.vcode[tok0 + i][d] << (i * a.bits));
-          else keep |= m;
+          else if (t < tt0) keep |= m;
         }
         if (keep) word |= tile_out[w] & keep;
         tile_out[w] = word;
@@ -269,7 +411,68 @@ __global__ void __launch_bounds__(ENC_THREADS) encode_kernel(EncodeArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- one token
+// One wave per (unit, K|V): the token at position t0 (row 0 of the input).
+__global__ void __launch_bounds__(64) encode_token_kernel(EncodeArgs a) {
+  __shared__ float sx[XS];
+  const int lane = threadIdx.x;
+  const int64_t u = blockIdx.x;
+  const int kind = blockIdx.y;
+  const int t = a.t0;
+  const int64_t row = u * a.src_rows;
+  const float x0 = load_in(a.src[kind], row * D + lane, a.bf16);
+  const float x1 = load_in(a.src[kind], row * D + lane + 64, a.bf16);
+  float* win = a.r.win[kind] + u * 2 * D;
+  float wl0 = 0.0f, wl1 = 0.0f, wh0 = 0.0f, wh1 = 0.0f;
+  if (a.win_update) {
+    wl0 = win[lane]; wl1 = win[lane + 64];
+    wh0 = win[D + lane]; wh1 = win[D + lane + 64];
+  }
+  uint32_t c0, c1, w0, w1;
+  int kidx;
+  uint16_t t16;
+  encode_vector<true>(a, kind, u, x0, x1, lane, sx, nullptr, c0, c1, w0, w1, kidx, t16);
+  store_token(a, kind, u, t, lane, c0, c1, w0, w1, kidx, t16);
+  if (kind == 1) {
+    // V word of channel d holding token t: whole tile written on its first
+    // token (other positions zero), OR-ed in afterwards
+    const int per = 32 / a.bits, tt = t % VT, wi = tt / per, bit = (tt % per) * a.bits;
+    uint32_t* tile_out = (uint32_t*)(a.r.codes[1] + ((u * (a.tcap / VT)) + t / VT) * (VT * D * a.bits / 8));
+    if (tt == 0) {
+      for (int w = 0; w < a.bits; ++w) {
+        tile_out[w * D + lane] = w == wi ? c0 << bit : 0u;
+        tile_out[w * D + lane + 64] = w == wi ? c1 << bit : 0u;
+      }
+    } else {
+      if (c0) atomicOr(&tile_out[wi * D + lane], c0 << bit);
+      if (c1) atomicOr(&tile_out[wi * D + lane + 64], c1 << bit);
+    }
+  }
+  if (a.win_update) {
+    // Chebyshev window (Eq 5) over this token
+    const float lo0 = fminf(wl0, x0), lo1 = fminf(wl1, x1);
+    const float hi0 = fmaxf(wh0, x0), hi1 = fmaxf(wh1, x1);
+    if (a.win_close) {
+      if (a.close_slot >= 0) {
+        float* dst = a.r.tab[kind] + (u * a.max_pat + a.close_slot) * D;
+        const float s0 = lo0 + hi0, s1 = lo1 + hi1;
+        dst[lane] = s0 * 0.5f;
+        dst[lane + 64] = s1 * 0.5f;
+      }
+      win[lane] = INFINITY; win[lane + 64] = INFINITY;
+      win[D + lane] = -INFINITY; win[D + lane + 64] = -INFINITY;
+    } else {
+      win[lane] = lo0; win[lane + 64] = lo1;
+      win[D + lane] = hi0; win[D + lane + 64] = hi1;
+    }
+  }
+}
+
 hipError_t launch_encode(const EncodeArgs& a, int units, int n_blocks_x, hipStream_t s) {
+  if (a.n_new == 1) {
+    hipLaunchKernelGGL(encode_token_kernel, dim3(units, 2), dim3(64), 0, s, a);
+    return hipGetLastError();
+  }
   dim3 grid(n_blocks_x, units, 2);
   hipLaunchKernelGGL(encode_kernel, grid, dim3(ENC_THREADS), 0, s, a);
   return hipGetLastError();
