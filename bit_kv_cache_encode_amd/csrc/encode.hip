@@ -189,15 +189,27 @@ __device__ __forceinline__ int nearest_pattern(const float* sx, const float* tab
   return nearest_pattern_s<1, FULL>(sx, tab_lds, tab, n_pat, lane, best);
 }
 
+// Four consecutive channels of an input row as fp32.
+__device__ __forceinline__ float4 load4_in(const void* p, int64_t idx, int bf16) {
+  if (bf16) {
+    const uint2 w = *(const uint2*)((const uint16_t*)p + idx);
+    return float4{bf16_to_f32((uint16_t)(w.x & 0xFFFFu)), bf16_to_f32((uint16_t)(w.x >> 16)),
+                  bf16_to_f32((uint16_t)(w.y & 0xFFFFu)), bf16_to_f32((uint16_t)(w.y >> 16))};
+  }
+  return *(const float4*)((const float*)p + idx);
+}
+
 // Encode one vector (PATTERN or KVARN) held as x0 = x[lane], x1 = x[lane + 64];
 // returns the codes and the lane's (s, z) words; `kidx` = pattern index and
 // `t16` = token scale.  `sx` is this wave's staging area; `sres` (PATTERN)
 // receives the chosen pattern row for the residual when tab_lds is null.
+// FULL: fully unrolled distance loop (the one-token kernel).
 template <bool FULL>
 __device__ __forceinline__ void encode_vector(const EncodeArgs& a, int kind, int64_t u, float x0,
                                               float x1, int lane, float* sx, const float* tab_lds,
-                                              uint32_t& c0, uint32_t& c1, uint32_t& w0,
-                                              uint32_t& w1, int& kidx, uint16_t& t16) {
+                                              int64_t row, uint32_t& c0, uint32_t& c1,
+                                              uint32_t& w0, uint32_t& w1, int& kidx,
+                                              uint16_t& t16) {
   const float* tab = a.r.tab[kind] + (a.mode == KVQ_MODE_PATTERN ? u * a.max_pat * D : u * D);
   kidx = KVQ_INDEX_NONE;
   t16 = 0;
@@ -205,12 +217,13 @@ __device__ __forceinline__ void encode_vector(const EncodeArgs& a, int kind, int
     float r0 = x0, r1 = x1;
     if (a.n_pat > 0) {
       const int S = dist_chunks(a.n_pat);
+      float best;
+      int kbest;
       stage_x(sx, x0, x1, lane, S);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      float best;
-      int kbest = nearest_pattern<FULL>(sx, tab_lds, tab, a.n_pat, lane, best);
+      kbest = nearest_pattern<FULL>(sx, tab_lds, tab, a.n_pat, lane, best);
       // section 3.3: V keeps its pattern iff R_flat <= rho* R_raw
       if (kind == 1 && a.rho >= 0.0f && kbest != KVQ_INDEX_NONE) {
         const float mx = group_mm<true>(fmaxf(x0, x1), 64, lane);
@@ -309,15 +322,22 @@ __device__ __forceinline__ void store_token(const EncodeArgs& a, int kind, int64
 
 // ---------------------------------------------------------------- bulk kernel
 struct EncodeShared {
-  float tab[PAT_PASS * (D + 4)];   // pass-0 table rows, row = lane (pattern, chunk)
   float x[ENC_WAVES][XS];          // the vector each wave encodes, in chunks
   uint8_t vcode[VT][D];            // V codes of the tile, [token][channel]
   float wlo[ENC_WAVES][D];         // per-wave window partials
   float whi[ENC_WAVES][D];
 };
 
+// Dynamic LDS: the pass-0 pattern table, row = lane (pattern, chunk) of
+// D/S + 4 floats, when one pass covers the table (sized by the host).
+__host__ __device__ inline int enc_tab_floats(int mode, int n_pat) {
+  if (mode != KVQ_MODE_PATTERN || n_pat <= 0 || n_pat > PAT_PASS) return 0;
+  return PAT_PASS * (D / dist_chunks(n_pat) + 4);
+}
+
 __global__ void __launch_bounds__(ENC_THREADS) encode_kernel(EncodeArgs a) {
   __shared__ EncodeShared sh;
+  extern __shared__ __attribute__((aligned(16))) float s_tab[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kind = blockIdx.z;
   const int64_t u = blockIdx.y;
@@ -333,17 +353,27 @@ __global__ void __launch_bounds__(ENC_THREADS) encode_kernel(EncodeArgs a) {
     const int S = dist_chunks(a.n_pat), ch = D / S;
     for (int i = threadIdx.x; i < PAT_PASS * ch; i += ENC_THREADS) {
       const int row = i / ch, c = i % ch, j = row / S, s = row % S;
-      sh.tab[row * (ch + 4) + c] = j < a.n_pat ? tab[(int64_t)j * D + s * ch + c] : 0.0f;
+      s_tab[row * (ch + 4) + c] = j < a.n_pat ? tab[(int64_t)j * D + s * ch + c] : 0.0f;
     }
     __syncthreads();
   }
 
   for (int tile = tile_first; tile <= tile_last; ++tile) {
     const int tt0 = max(tile * VT, a.t0), tt1 = min(tile * VT + VT, t_end);
+    // the next token's vector is loaded while this one is encoded
+    float nx0 = 0.0f, nx1 = 0.0f;
+    if (tt0 + wave < tt1) {
+      const int64_t row = u * a.src_rows + (tt0 + wave - a.t0);
+      nx0 = load_in(a.src[kind], row * D + lane, a.bf16);
+      nx1 = load_in(a.src[kind], row * D + lane + 64, a.bf16);
+    }
     for (int t = tt0 + wave; t < tt1; t += ENC_WAVES) {
       const int64_t row = u * a.src_rows + (t - a.t0);
-      const float x0 = load_in(a.src[kind], row * D + lane, a.bf16);
-      const float x1 = load_in(a.src[kind], row * D + lane + 64, a.bf16);
+      const float x0 = nx0, x1 = nx1;
+      if (t + ENC_WAVES < tt1) {
+        nx0 = load_in(a.src[kind], (row + ENC_WAVES) * D + lane, a.bf16);
+        nx1 = load_in(a.src[kind], (row + ENC_WAVES) * D + lane + 64, a.bf16);
+      }
       if (a.win_update) {
         wlo0 = fminf(wlo0, x0); wlo1 = fminf(wlo1, x1);
         whi0 = fmaxf(whi0, x0); whi1 = fmaxf(whi1, x1);
@@ -351,8 +381,8 @@ __global__ void __launch_bounds__(ENC_THREADS) encode_kernel(EncodeArgs a) {
       uint32_t c0, c1, w0, w1;
       int kidx;
       uint16_t t16;
-      encode_vector<false>(a, kind, u, x0, x1, lane, sh.x[wave], staged ? sh.tab : nullptr, c0,
-                           c1, w0, w1, kidx, t16);
+      encode_vector<false>(a, kind, u, x0, x1, lane, sh.x[wave], staged ? s_tab : nullptr, row,
+                           c0, c1, w0, w1, kidx, t16);
       store_token(a, kind, u, t, lane, c0, c1, w0, w1, kidx, t16);
       if (kind == 1) {
         sh.vcode[t - tile * VT][lane] = (uint8_t)c0;
@@ -413,8 +443,13 @@ __global__ void __launch_bounds__(ENC_THREADS) encode_kernel(EncodeArgs a) {
 
 // ---------------------------------------------------------------- one token
 // One wave per (unit, K|V): the token at position t0 (row 0 of the input).
+// The vector, the window state and the pattern table (coalesced, up to
+// PAT_PASS patterns) are loaded before anything waits; the table is then
+// written to LDS in the distance loop's row layout.
+constexpr int TOK_TAB4 = PAT_PASS * D / 4 / 64;   // float4 per lane for a full pass
 __global__ void __launch_bounds__(64) encode_token_kernel(EncodeArgs a) {
   __shared__ float sx[XS];
+  __shared__ __attribute__((aligned(16))) float stab[PAT_PASS * (D + 4)];
   const int lane = threadIdx.x;
   const int64_t u = blockIdx.x;
   const int kind = blockIdx.y;
@@ -428,10 +463,32 @@ __global__ void __launch_bounds__(64) encode_token_kernel(EncodeArgs a) {
     wl0 = win[lane]; wl1 = win[lane + 64];
     wh0 = win[D + lane]; wh1 = win[D + lane + 64];
   }
+  const bool staged = a.mode == KVQ_MODE_PATTERN && a.n_pat > 0 && a.n_pat <= PAT_PASS;
+  if (staged) {
+    const float4* tab4 = (const float4*)(a.r.tab[kind] + u * a.max_pat * D);
+    const int n4 = a.n_pat * D / 4;
+    float4 tr[TOK_TAB4];
+#pragma unroll
+    for (int r = 0; r < TOK_TAB4; ++r) {
+      const int f = lane + 64 * r;
+      tr[r] = f < n4 ? tab4[f] : float4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    const int S = dist_chunks(a.n_pat), ch = D / S;
+#pragma unroll
+    for (int r = 0; r < TOK_TAB4; ++r) {
+      const int f = lane + 64 * r, j = f / (D / 4), c = 4 * (f % (D / 4));
+      if (j < PAT_PASS / S) *(float4*)(stab + (j * S + c / ch) * (ch + 4) + c % ch) = tr[r];
+    }
+    // (rows of the pass past the last pattern receive the zero pieces above)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
   uint32_t c0, c1, w0, w1;
   int kidx;
   uint16_t t16;
-  encode_vector<true>(a, kind, u, x0, x1, lane, sx, nullptr, c0, c1, w0, w1, kidx, t16);
+  encode_vector<true>(a, kind, u, x0, x1, lane, sx, staged ? stab : nullptr, row, c0, c1, w0, w1,
+                      kidx, t16);
   store_token(a, kind, u, t, lane, c0, c1, w0, w1, kidx, t16);
   if (kind == 1) {
     // V word of channel d holding token t: whole tile written on its first
@@ -474,7 +531,8 @@ hipError_t launch_encode(const EncodeArgs& a, int units, int n_blocks_x, hipStre
     return hipGetLastError();
   }
   dim3 grid(n_blocks_x, units, 2);
-  hipLaunchKernelGGL(encode_kernel, grid, dim3(ENC_THREADS), 0, s, a);
+  const size_t lds = (size_t)enc_tab_floats(a.mode, a.n_pat) * 4;
+  hipLaunchKernelGGL(encode_kernel, grid, dim3(ENC_THREADS), lds, s, a);
   return hipGetLastError();
 }
 

@@ -289,7 +289,10 @@ int kvq_encode_append(kvq_cache* cache, const void* k_new, const void* v_new, in
     a.t0 = cache->n_tokens;
     a.n_pat = cache->n_patterns;
     const int tiles = (a.t0 + n_new - 1) / VT - a.t0 / VT + 1;
-    a.tiles_per_block = tiles > 4096 ? 4 : 1;
+    // about 2048 blocks in all, so that each block's pattern-table copy
+    // serves many tokens
+    int tpb = (int)(((int64_t)tiles * units * 2 + 2047) / 2048);
+    a.tiles_per_block = tpb < 1 ? 1 : tpb;
     hipError_t e = launch_encode(a, units, (tiles + a.tiles_per_block - 1) / a.tiles_per_block, s);
     if (e != hipSuccess) return dev_fail(e);
     cache->n_tokens += n_new;
