@@ -23,27 +23,30 @@
 // Codes enter the MFMA as binary16 subnormals: a 2-bit (4-bit) field masked
 // in place inside a 32-bit word is the integer code times 2^-24 times a power
 // of 4 (16) that depends only on the field's position; the other operand
-// carries the inverse power, so unpacking a pair of codes is one AND.  q and
-// p*s are split into binary16 hi + lo parts (two MFMAs), so products keep
-// about 22 bits; accumulation is fp32.
+// carries the inverse power, so unpacking a pair of codes is one AND.  p*s
+// is split into binary16 hi + lo parts (two MFMAs), so products keep about 22
+// bits; q is one binary16 operand when it comes in bfloat16 (exact, see the
+// exponent choice) and hi + lo otherwise; accumulation is fp32.
 #include <type_traits>
 
 #include "attn_mfma_common.h"
 
 namespace kvq {
 
-constexpr int MF_WAVES = 4;
+constexpr int MF_WAVES = 8;
 constexpr int MF_THREADS = MF_WAVES * 64;
 
 // Dynamic LDS layout of a block (bytes); npat = padded pattern count.
 struct MfLds {
-  int q, qsum, qm, ps, ph, vs, w, alpha, m, o, z, l, wsum, M, last, tiles, total;
+  int q, qsum, qe, next, qm, ps, ph, vs, w, alpha, m, o, z, l, wsum, M, last, tiles, total;
 };
 __host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes, bool hist_mfma) {
   MfLds L;
   int o = 0;
   L.q = o; o = al16(o + HB * D * 4);
   L.qsum = o; o = al16(o + HB * NG * 4);
+  L.qe = o; o = al16(o + HB * 4);
+  L.next = o; o = al16(o + 4);
   L.qm = o; o = al16(o + HB * 256 * 4);
   const int pw = HB == 4 ? ptab_words<4>() : ptab_words<8>();
   L.ps = o; o = al16(o + MF_WAVES * pw * 4);
@@ -67,7 +70,9 @@ __host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes
 
 // Pattern-mass path: NPB > 0 -> one-hot MFMA over NPB blocks of 16 patterns;
 // NPB == 0 -> LDS atomics (or no pattern term at all for KVarN).
-template <int BITS, int NG, bool KVARN, int NPB>
+// QLO: q needs a binary16 lo part (binary32 queries, or the KVarN rotation);
+// a bfloat16 query is a single binary16 operand (see the exponent choice).
+template <int BITS, int NG, bool KVARN, int NPB, bool QLO>
 __global__ void __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_mfma_kernel(AttnArgs a) {
   static_assert(!(KVARN && NPB), "KVarN has no pattern term");
@@ -92,6 +97,8 @@ attn_mfma_kernel(AttnArgs a) {
   const MfLds Lo = mf_lds(HB, NG, npat, TS::BYTES, NPB > 0);
   float* s_q = (float*)(mf_raw + Lo.q);            // [HB][D]
   float* s_qsum = (float*)(mf_raw + Lo.qsum);      // [HB][NG]
+  int* s_qe = (int*)(mf_raw + Lo.qe);              // [HB]: max |q| bits, then the exponent
+  int* s_next = (int*)(mf_raw + Lo.next);          // next unclaimed tile of the block
   float* s_qm = (float*)(mf_raw + Lo.qm);          // [HB][256]; entry 0xFF (no pattern) is 0
   float* s_ps = (float*)(mf_raw + Lo.ps) + wave * ptab_words<HB>();
   uint32_t* s_ph = (uint32_t*)(mf_raw + Lo.ph) + wave * ptab_words<HB>();
@@ -151,7 +158,8 @@ attn_mfma_kernel(AttnArgs a) {
   // Prologue loads are all issued before anything waits on them: the first
   // tile, q (below), and this thread's 32-channel slice of pattern row
   // tid / 4 of M^K (for q' . M^K).
-  if (t_begin + TILE * wave < t_end) issue(t_begin + TILE * wave);
+  const int n_tiles = (t_end - t_begin + TILE - 1) / TILE;
+  if (wave < n_tiles) issue(t_begin + TILE * wave);
   const int qm_j = tid >> 2, qm_part = tid & 3;
   const float* mk = a.r.tab[0] + (int64_t)u * a.max_pat * D;
   float4 mkr[8];
@@ -173,7 +181,8 @@ attn_mfma_kernel(AttnArgs a) {
   for (int i = tid; i < HB * npat; i += MF_THREADS) s_wsum[i] = 0.0f;
   for (int i = tid; i < HB * 256; i += MF_THREADS) s_qm[i] = 0.0f;
   if (tid < HB * NG) s_z[tid] = 0.0f;
-  if (tid < HB) s_l[tid] = 0.0f;
+  if (tid < HB) { s_l[tid] = 0.0f; s_qe[tid] = 0; }
+  if (tid == 0) *s_next = MF_WAVES;
   __syncthreads();
   if (KVARN) {
     for (int hs = 1; hs < D; hs <<= 1) {
@@ -196,10 +205,34 @@ attn_mfma_kernel(AttnArgs a) {
     for (int i = tid; i < HB * D; i += MF_THREADS) {
       float v = s_q[i];
       if (KVARN) v = v * isd * ck[i % D];
-      s_q[i] = v * a.qscale;
+      s_q[i] = v;
     }
   }
   __syncthreads();
+  // Per-head binary exponent e_h that puts max_d |q_hd| 2^e_h in [2^14, 2^15).
+  // The QK A operand is q 2^(e_h - shift) in binary16 (shift <= 6): a
+  // bfloat16 q (8 significant bits) is exact there except for elements below
+  // the binary16 subnormal step 2^-24, whose error is then under 2^-24, i.e.
+  // under 2^-38 of the largest operand.  Other queries add a lo part.  The
+  // softmax scale is applied after the products.
+  {
+    // max |q_h| as binary32 bits (ordered like the values for x >= 0):
+    // lanes of one head reduce, then one LDS max per wave and head
+    constexpr int VPT = HB * D / MF_THREADS, TPH = D / VPT, RED = TPH < 64 ? TPH : 64;
+    const int h = tid / TPH;
+    float mx = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) mx = fmaxf(mx, fabsf(s_q[tid * VPT + k]));
+#pragma unroll
+    for (int o = 1; o < RED; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if (tid % RED == 0) atomicMax(&s_qe[h], __builtin_bit_cast(int, mx));
+  }
+  __syncthreads();
+  if (tid < HB) {
+    const int bits = s_qe[tid];
+    const int ex = ((bits >> 23) & 0xFF) - 127;
+    s_qe[tid] = bits > 0 ? min(14 - ex, 120) : 0;
+  }
   // per-group sums of q': thread (h = tid/32) adds 4 channels, then lanes of a
   // group reduce (G/4 lanes per group)
   {
@@ -208,12 +241,12 @@ attn_mfma_kernel(AttnArgs a) {
     if (h < HB) s = (s_q[h * D + c0] + s_q[h * D + c0 + 1]) + (s_q[h * D + c0 + 2] + s_q[h * D + c0 + 3]);
 #pragma unroll
     for (int o = 1; o < G / 4; o <<= 1) s += __shfl_xor(s, o, 64);
-    if (h < HB && ((tid & 31) % (G / 4)) == 0) s_qsum[h * NG + c0 / G] = s;
+    if (h < HB && ((tid & 31) % (G / 4)) == 0) s_qsum[h * NG + c0 / G] = s * a.qscale;
   }
   // q' . M^K_j: four threads per pattern j (32 channels each), all heads;
-  // patterns beyond the first 64 take further passes
+  // patterns beyond the first MF_THREADS / 4 take further passes
   if (!KVARN && n_pat > 0) {
-    for (int j0 = 0; j0 < n_pat; j0 += 64) {
+    for (int j0 = 0; j0 < n_pat; j0 += MF_THREADS / 4) {
       const int jj = j0 + qm_j;
       if (j0 > 0) {
 #pragma unroll
@@ -238,7 +271,7 @@ attn_mfma_kernel(AttnArgs a) {
         }
         sdot += __shfl_xor(sdot, 1, 64);
         sdot += __shfl_xor(sdot, 2, 64);
-        if (qm_part == 0 && jj < n_pat) s_qm[h * 256 + jj] = sdot;
+        if (qm_part == 0 && jj < n_pat) s_qm[h * 256 + jj] = sdot * a.qscale;
       }
     }
   }
@@ -248,9 +281,10 @@ attn_mfma_kernel(AttnArgs a) {
   const float k_m1 = __builtin_fmaf(a.qscale, 0.0f, -1.0f);
   const float k_z = a.qscale * 0.0f;
   // QK A operands: row m = n16 -> (h, g); element i of chunk c -> channel.
-  u32x4 aq_hi[4], aq_lo[4];
+  u32x4 aq_hi[4], aq_lo[QLO ? 4 : 1];
   {
     const int h = n16 / NG, g = n16 % NG;
+    const int eh = s_qe[h];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
@@ -259,12 +293,12 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int i = 2 * p + e, ch = qk_channel<BITS>(j, c, i);
-          v2[e] = (ch / G == g) ? ldexpf(s_q[h * D + ch], EQ - code_shift<BITS>(i)) : 0.0f;
+          v2[e] = (ch / G == g) ? ldexpf(s_q[h * D + ch], eh - code_shift<BITS>(i)) : 0.0f;
         }
         uint32_t hi, lo;
         split2(v2[0], v2[1], k_m1, hi, lo);
         aq_hi[c][p] = hi;
-        aq_lo[c][p] = lo;
+        if (QLO) aq_lo[QLO ? c : 0][p] = lo;
       }
     }
   }
@@ -273,6 +307,11 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) qsum[r] = s_qsum[((4 * j + r) / NG) * NG + r % NG];
   const int head0 = (4 * j) / NG;   // head of register slot s is head0 + s
+  // scale of the binary16 partial dots: 2^(24 - e_h) (code and q operand
+  // powers) times the softmax scale
+  float dsc[SPL];
+#pragma unroll
+  for (int s = 0; s < SPL; ++s) dsc[s] = a.qscale * ldexpf(1.0f, 24 - s_qe[head0 + s]);
 
   float m_run[SPL], l_run[SPL], zacc[4];
 #pragma unroll
@@ -291,14 +330,22 @@ attn_mfma_kernel(AttnArgs a) {
   const uint32_t hsel = (n16 / NG >= a.gq || n16 % NG > 1) ? 0x0C0C0C0Cu
                         : (n16 % NG == 0 ? 0x05040100u : 0x07060302u);
 
-  int tile = t_begin + TILE * wave;
-  for (; tile < t_end; tile += TILE * MF_WAVES) {
+  // Tiles are handed out dynamically: each wave starts with tile `wave` and
+  // claims its next one from the block counter while the current one is
+  // computed, so the waves of the block finish together whatever their
+  // issue priority.
+  for (int cur = wave; cur < n_tiles;) {
+    const int tile = t_begin + TILE * cur;
     __builtin_amdgcn_wave_barrier();
     commit();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (tile + TILE * MF_WAVES < t_end) issue(tile + TILE * MF_WAVES);
+    int nxt = 0;
+    if (lane == 0) nxt = atomicAdd(s_next, 1);
+    nxt = __builtin_amdgcn_readfirstlane(nxt);
+    if (nxt < n_tiles) issue(t_begin + TILE * nxt);
+    cur = nxt;
     const int nvalid = t_end - tile;
     auto tile_body = [&](auto full_tag) {
       constexpr bool FULL = decltype(full_tag)::value;
@@ -307,18 +354,22 @@ attn_mfma_kernel(AttnArgs a) {
     // so consecutive MFMAs never wait on each other.
     f32x4 C[4];
     {
-      uint32_t kw[4][KW];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
+      // this lane's K words of column block nb: 32 channels of token 16 nb + n16
+      auto load_kw = [&](int nb, uint32_t* kw) {
         const int t64 = 16 * nb + n16;
         if (KW == 2) {
           const uint2 w = *(const uint2*)(tb + TS::O_KC + kpiece<BITS>(2 * t64 + (j >> 1)) * 16 + (j & 1) * 8);
-          kw[nb][0] = w.x; kw[nb][1 % KW] = w.y;
+          kw[0] = w.x; kw[1 % KW] = w.y;
         } else {
           const u32x4 w = *(const u32x4*)(tb + TS::O_KC + kpiece<BITS>(4 * t64 + j) * 16);
 #pragma unroll
-          for (int q = 0; q < KW; ++q) kw[nb][q] = w[q];
+          for (int q = 0; q < KW; ++q) kw[q] = w[q];
         }
+      };
+      uint32_t kw[4][KW];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        load_kw(nb, kw[nb]);
         C[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       }
 #pragma unroll
@@ -327,7 +378,7 @@ attn_mfma_kernel(AttnArgs a) {
         for (int nb = 0; nb < 4; ++nb) {
           const u32x4 B = unpack_k<BITS>(kw[nb], c);
           C[nb] = mfma16(aq_hi[c], B, C[nb]);
-          C[nb] = mfma16(aq_lo[c], B, C[nb]);
+          if constexpr (QLO) C[nb] = mfma16(aq_lo[QLO ? c : 0], B, C[nb]);
         }
     }
     float sc[4][SPL];
@@ -356,19 +407,16 @@ attn_mfma_kernel(AttnArgs a) {
       }
 #pragma unroll
       for (int s = 0; s < SPL; ++s) {
-        float dot = 0.0f, zt = 0.0f;
+        // the pattern term (q . M^K)[k*] starts the zero-point sum
+        float dot = 0.0f, zt = KVARN ? 0.0f : s_qm[(head0 + s) * 256 + kix];
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
           const int r = s * NG + g;
           dot = __builtin_fmaf(bits2f((uint16_t)(kszw[g] & 0xFFFFu)), C[nb][r], dot);
           zt = __builtin_fmaf(bits2f((uint16_t)(kszw[g] >> 16)), qsum[r], zt);
         }
-        float v = __builtin_fmaf(dot, (float)(1 << (24 - EQ)), zt);
-        if (!KVARN) {
-          v += s_qm[(head0 + s) * 256 + kix];
-        } else {
-          v *= tk;
-        }
+        float v = __builtin_fmaf(dot, dsc[s], zt);
+        if (KVARN) v *= tk;
         sc[nb][s] = valid ? v : -INFINITY;
       }
     }
@@ -761,31 +809,36 @@ attn_mfma_kernel(AttnArgs a) {
   if (tid == 0) __hip_atomic_store(&a.r.cnt[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int BITS, int NG, bool KVARN, int NPB>
+template <int BITS, int NG, bool KVARN, int NPB, bool QLO>
 static hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
   constexpr int HB = 16 / NG;
   const int npat = pad_pat(KVARN ? 0 : a.n_pat);
   const MfLds L = mf_lds(HB, NG, npat, TileShape<BITS, NG, KVARN>::BYTES, NPB > 0);
   static int attr = 0;
   if (L.total > attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel<BITS, NG, KVARN, NPB>,
+    hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel<BITS, NG, KVARN, NPB, QLO>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, L.total);
     if (e != hipSuccess) return e;
     attr = L.total;
   }
-  hipLaunchKernelGGL((attn_mfma_kernel<BITS, NG, KVARN, NPB>), dim3(a.B * a.Hkv * a.splits),
+  hipLaunchKernelGGL((attn_mfma_kernel<BITS, NG, KVARN, NPB, QLO>), dim3(a.B * a.Hkv * a.splits),
                      dim3(MF_THREADS), L.total, s, a);
   return hipGetLastError();
 }
 
+template <int BITS, int NG, bool QLO>
+static hipError_t launch_pattern(const AttnArgs& a, hipStream_t s) {
+  if (a.n_pat <= 0) return launch_one<BITS, NG, false, 0, QLO>(a, s);
+  if (a.n_pat <= 16) return launch_one<BITS, NG, false, 1, QLO>(a, s);
+  if (a.n_pat <= 32) return launch_one<BITS, NG, false, 2, QLO>(a, s);
+  if (a.n_pat <= 64) return launch_one<BITS, NG, false, 4, QLO>(a, s);
+  return launch_one<BITS, NG, false, 0, QLO>(a, s);
+}
+
 template <int BITS, int NG>
 static hipError_t launch_bits_group(const AttnArgs& a, hipStream_t s) {
-  if (a.mode == KVQ_MODE_KVARN) return launch_one<BITS, NG, true, 0>(a, s);
-  if (a.n_pat <= 0) return launch_one<BITS, NG, false, 0>(a, s);
-  if (a.n_pat <= 16) return launch_one<BITS, NG, false, 1>(a, s);
-  if (a.n_pat <= 32) return launch_one<BITS, NG, false, 2>(a, s);
-  if (a.n_pat <= 64) return launch_one<BITS, NG, false, 4>(a, s);
-  return launch_one<BITS, NG, false, 0>(a, s);
+  if (a.mode == KVQ_MODE_KVARN) return launch_one<BITS, NG, true, 0, true>(a, s);
+  return a.bf16 ? launch_pattern<BITS, NG, false>(a, s) : launch_pattern<BITS, NG, true>(a, s);
 }
 
 bool mfma_attention_supported(int bits, int group, int gq) {

@@ -366,7 +366,8 @@ int kvq_attn_decode(kvq_cache* cache, const void* q, float* out, float sm_scale,
   const bool mfma_ok = mfma_attention_supported(c.bits, c.group, a.gq);
   const bool use_valu = !mfma_ok || (kenv && strcmp(kenv, "valu") == 0);
   const bool use_pp = !use_valu && kenv && strcmp(kenv, "pp") == 0;
-  int target = use_valu ? ATTN_TARGET_BLOCKS : (use_pp ? 768 : 512);
+  // one 8-wave MFMA block per compute unit
+  int target = use_valu ? ATTN_TARGET_BLOCKS : (use_pp ? 768 : 256);
   const char* benv = getenv("KVQ_ATTN_BLOCKS");
   if (benv && atoi(benv) > 0) target = atoi(benv);
   int want = (target + units - 1) / units;

@@ -202,27 +202,29 @@ def test_determinism_and_checkpoint():
     (2, 32, 4, "pattern"), (2, 32, 1, "pattern"), (4, 64, 4, "pattern"), (4, 64, 8, "pattern"),
     (2, 64, 2, "pattern"), (4, 32, 3, "pattern"), (2, 32, 4, "kvarn"), (4, 64, 8, "kvarn")])
 @pytest.mark.parametrize("blocks", [1, 40, 4096])
-def test_attention_kernels_agree(monkeypatch, bits, group, gq, mode, blocks):
+@pytest.mark.parametrize("bf16", [True, False])
+def test_attention_kernels_agree(monkeypatch, bits, group, gq, mode, blocks, bf16):
     """The single-role MFMA kernel (default), the paired score/value-wave MFMA
     kernel and the VALU kernel all match the oracle, for one block per unit up
-    to many splits, ragged lengths."""
+    to many splits, ragged lengths, bfloat16 and binary32 inputs (a binary32
+    query takes the binary16 hi + lo operand path)."""
     B, H, T = 2, 2, 1000
     gpu, ref, dt = make_pair(B, gq * H, H, 1024, bits=bits, group=group, mode=mode,
-                             max_patterns=24)
+                             max_patterns=24, bf16=bf16)
     k, v = _inputs(B, H, T, seed_off=bits + gq)
     if mode == "pattern":
-        ref.init_patterns(to_oracle(k[:, :, :256], True), to_oracle(v[:, :, :256], True), 24)
+        ref.init_patterns(to_oracle(k[:, :, :256], bf16), to_oracle(v[:, :, :256], bf16), 24)
         gpu.init_patterns(to_dev(k[:, :, :256], dt), to_dev(v[:, :, :256], dt), 24)
     else:
-        ref.init_patterns(to_oracle(k[:, :, :256], True), to_oracle(v[:, :, :256], True), 0)
+        ref.init_patterns(to_oracle(k[:, :, :256], bf16), to_oracle(v[:, :, :256], bf16), 0)
         gpu.set_patterns(torch.from_numpy(ref.scales(0).reshape(B, H, 128).copy()).cuda(),
                          torch.from_numpy(ref.scales(1).reshape(B, H, 128).copy()).cuda())
-    ref.encode_append(to_oracle(k, True), to_oracle(v, True))
+    ref.encode_append(to_oracle(k, bf16), to_oracle(v, bf16))
     gpu.encode_append(to_dev(k, dt), to_dev(v, dt))
     monkeypatch.setenv("KVQ_ATTN_BLOCKS", str(blocks))
     for step, qmul in ((0, 1.0), (1, 6.0)):          # flat and peaked softmax
         q = synth.queries(B, gq * H, 128, step=step) * np.float32(qmul)
-        want = ref.attn_decode(to_oracle(q, True))
+        want = ref.attn_decode(to_oracle(q, bf16))
         errs = {}
         for kern in ("", "pp", "valu"):
             if kern:
@@ -232,6 +234,27 @@ def test_attention_kernels_agree(monkeypatch, bits, group, gq, mode, blocks):
             got = gpu.attn_decode(to_dev(q, dt)).cpu().numpy()
             errs[kern or "default"] = float(np.abs(got - want).max())
         assert max(errs.values()) <= ATTN_TOL, errs
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+def test_attention_query_dynamic_range(bf16):
+    """Query heads far from unit scale: one head with |q| in the thousands,
+    one around 1e-3, one with elements near 1e-9 among normal ones.  The QK
+    operand's per-head exponent keeps every head in binary16 range."""
+    B, H, gq, T = 2, 2, 4, 700
+    gpu, ref, dt = make_pair(B, gq * H, H, 1024, max_patterns=16, bf16=bf16)
+    k, v = _inputs(B, H, T, seed_off=11)
+    ref.init_patterns(to_oracle(k[:, :, :256], bf16), to_oracle(v[:, :, :256], bf16), 16)
+    gpu.init_patterns(to_dev(k[:, :, :256], dt), to_dev(v[:, :, :256], dt), 16)
+    ref.encode_append(to_oracle(k, bf16), to_oracle(v, bf16))
+    gpu.encode_append(to_dev(k, dt), to_dev(v, dt))
+    q = synth.queries(B, gq * H, 128, step=5).copy()
+    q[:, 0::gq] *= np.float32(300.0)
+    q[:, 1::gq] *= np.float32(1e-3)
+    q[:, 2::gq, ::3] *= np.float32(1e-9)
+    want = ref.attn_decode(to_oracle(q, bf16))
+    got = gpu.attn_decode(to_dev(q, dt)).cpu().numpy()
+    assert np.abs(got - want).max() <= ATTN_TOL
 
 
 def test_attention_repeated_calls_reset_counters(monkeypatch):
