@@ -38,9 +38,11 @@ constexpr int MF_THREADS = MF_WAVES * 64;
 
 // Dynamic LDS layout of a block (bytes); npat = padded pattern count.
 struct MfLds {
-  int q, qsum, qe, next, qm, ps, ph, vs, w, alpha, m, o, z, l, wsum, M, last, tiles, total;
+  int q, qsum, qe, next, qm, mv, mv_rows, ps, ph, vs, w, alpha, m, o, z, l, wsum, M, last, tiles, total;
 };
-__host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes, bool hist_mfma) {
+// mv_rows: rows of M^V staged for the pattern term (0 without the one-hot path)
+__host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes, int mv_rows) {
+  const bool hist_mfma = mv_rows > 0;
   MfLds L;
   int o = 0;
   L.q = o; o = al16(o + HB * D * 4);
@@ -64,6 +66,10 @@ __host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes
   // the tile buffers, reused after the loop for per-wave o[HB][D] and (l, z[NG])
   const int part_bytes = MF_WAVES * HB * (D + 1 + NG) * 4;
   L.tiles = o; o = al16(o + (MF_WAVES * tile_bytes > part_bytes ? MF_WAVES * tile_bytes : part_bytes));
+  // M^V rows are staged only where they fit the 160 KiB of a compute unit
+  L.mv = o;
+  L.mv_rows = (mv_rows > 0 && o + mv_rows * D * 4 <= 160 * 1024) ? mv_rows : 0;
+  o = al16(o + L.mv_rows * D * 4);
   L.total = o;
   return L;
 }
@@ -94,11 +100,12 @@ attn_mfma_kernel(AttnArgs a) {
   const int t_begin = split * a.chunk, t_end = min(a.T, t_begin + a.chunk);
   const int n_pat = KVARN ? 0 : a.n_pat;
   const int npat = pad_pat(n_pat);
-  const MfLds Lo = mf_lds(HB, NG, npat, TS::BYTES, NPB > 0);
+  const MfLds Lo = mf_lds(HB, NG, npat, TS::BYTES, 16 * NPB);
   float* s_q = (float*)(mf_raw + Lo.q);            // [HB][D]
   float* s_qsum = (float*)(mf_raw + Lo.qsum);      // [HB][NG]
   int* s_qe = (int*)(mf_raw + Lo.qe);              // [HB]: max |q| bits, then the exponent
   int* s_next = (int*)(mf_raw + Lo.next);          // next unclaimed tile of the block
+  float* s_mv = (float*)(mf_raw + Lo.mv);          // [16 NPB][D] rows of M^V
   float* s_qm = (float*)(mf_raw + Lo.qm);          // [HB][256]; entry 0xFF (no pattern) is 0
   float* s_ps = (float*)(mf_raw + Lo.ps) + wave * ptab_words<HB>();
   uint32_t* s_ph = (uint32_t*)(mf_raw + Lo.ph) + wave * ptab_words<HB>();
@@ -160,6 +167,20 @@ attn_mfma_kernel(AttnArgs a) {
   // tid / 4 of M^K (for q' . M^K).
   const int n_tiles = (t_end - t_begin + TILE - 1) / TILE;
   if (wave < n_tiles) issue(t_begin + TILE * wave);
+  // M^V rows for the pattern term go straight to LDS (no registers held
+  // through the loop); 16 bytes per lane, one kilobyte per wave instruction.
+  // Completion is awaited before the merge reads them.
+  const bool stage_mv = NPB > 0 && Lo.mv_rows > 0;
+  if (stage_mv) {
+    const float* mv = a.r.tab[1] + (int64_t)u * a.max_pat * D;
+    const int n16b = min(n_pat, 16 * NPB) * (D / 4);
+    for (int g = wave; g * 64 < n16b; g += MF_WAVES) {
+      const int c = g * 64 + lane;
+      if (c < n16b)
+        __builtin_amdgcn_global_load_lds((const void*)(mv + 4 * c),
+                                         (__attribute__((address_space(3))) void*)(s_mv + 256 * g), 16, 0, 0);
+    }
+  }
   const int qm_j = tid >> 2, qm_part = tid & 3;
   const float* mk = a.r.tab[0] + (int64_t)u * a.max_pat * D;
   float4 mkr[8];
@@ -511,10 +532,10 @@ attn_mfma_kernel(AttnArgs a) {
       }
       vk[nb] = vix;
       // V group scale of this token for group j (lanes j < NG)
-      uint32_t sw = vszz[0];
-#pragma unroll
-      for (int g = 1; g < NG; ++g) sw = (j == g) ? vszz[g] : sw;
-      if (j < NG) s_vs[j * VS_STRIDE + t64] = __builtin_bit_cast(_Float16, (uint16_t)(sw & 0xFFFFu));
+      if (j < NG) {
+        const uint32_t sw = ((const uint32_t*)(tb + TS::O_VS))[t64 * NG + j];
+        s_vs[j * VS_STRIDE + t64] = __builtin_bit_cast(_Float16, (uint16_t)(valid ? sw & 0xFFFFu : 0u));
+      }
     }
     // V pattern mass: the tile's LDS adds are issued back to back so their
     // latencies overlap (nothing reads LDS between them)
@@ -608,14 +629,11 @@ attn_mfma_kernel(AttnArgs a) {
   }
 
   // ---------------------------------------------------------------- merge waves
-  // The V pattern rows of this thread's output channel d = tid % D are
-  // loaded now, so that they arrive while the waves merge.
+  // the M^V rows staged in the prologue have landed once this wave's vector
+  // memory operations are done (the barriers below publish them)
+  if (stage_mv) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   const float* mv = a.r.tab[1] + (int64_t)u * a.max_pat * D;
   constexpr int MVR = NPB > 0 ? 16 * NPB : 1;
-  float mvr[MVR];
-#pragma unroll
-  for (int jj = 0; jj < MVR; ++jj)
-    mvr[jj] = (NPB > 0 && jj < n_pat) ? mv[(int64_t)jj * D + tid % D] : 0.0f;
 #pragma unroll
   for (int s = 0; s < SPL; ++s) l_run[s] = row_sum16(l_run[s]);
 #pragma unroll
@@ -712,7 +730,8 @@ attn_mfma_kernel(AttnArgs a) {
     if constexpr (NPB > 0) {
 #pragma unroll
       for (int jj = 0; jj < MVR; ++jj)
-        if (jj < n_pat) o = __builtin_fmaf(s_wsum[h * npat + jj], mvr[jj], o);
+        if (jj < n_pat)
+          o = __builtin_fmaf(s_wsum[h * npat + jj], stage_mv ? s_mv[jj * D + d] : mv[(int64_t)jj * D + d], o);
     } else if (!KVARN) {
 #pragma unroll 8
       for (int jj = 0; jj < n_pat; ++jj) o = __builtin_fmaf(s_wsum[h * npat + jj], mv[(int64_t)jj * D + d], o);
@@ -813,7 +832,7 @@ template <int BITS, int NG, bool KVARN, int NPB, bool QLO>
 static hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
   constexpr int HB = 16 / NG;
   const int npat = pad_pat(KVARN ? 0 : a.n_pat);
-  const MfLds L = mf_lds(HB, NG, npat, TileShape<BITS, NG, KVARN>::BYTES, NPB > 0);
+  const MfLds L = mf_lds(HB, NG, npat, TileShape<BITS, NG, KVARN>::BYTES, 16 * NPB);
   static int attr = 0;
   if (L.total > attr) {
     hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel<BITS, NG, KVARN, NPB, QLO>,

@@ -123,11 +123,24 @@ __device__ __forceinline__ float dpp_f(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
                                                                 0xF, 0xF, false));
 }
+// Max over the 16 lanes of a DPP row on an integer key that orders like the
+// binary32 values (non-NaN): integer max folds into the DPP move, a float max
+// would not (its operands need canonicalising).
+__device__ __forceinline__ int f32_key(float f) {
+  const int b = __builtin_bit_cast(int, f);
+  return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, true);
+}
 __device__ __forceinline__ float row_max16(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));    // quad_perm [1,0,3,2]
-  v = fmaxf(v, dpp_f<0x4E>(v));    // quad_perm [2,3,0,1]
-  v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
-  return fmaxf(v, dpp_f<0x140>(v)); // row_mirror
+  int k = f32_key(v);
+  k = max(k, dpp_i<0xB1>(k));    // quad_perm [1,0,3,2]
+  k = max(k, dpp_i<0x4E>(k));    // quad_perm [2,3,0,1]
+  k = max(k, dpp_i<0x141>(k));   // row_half_mirror
+  k = max(k, dpp_i<0x140>(k));   // row_mirror
+  return __builtin_bit_cast(float, k ^ ((k >> 31) & 0x7FFFFFFF));
 }
 __device__ __forceinline__ float row_sum16(float v) {
   v += dpp_f<0xB1>(v);
