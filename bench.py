@@ -62,7 +62,7 @@ def parse():
 
 def attn_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("attn.hip", "attn_mfma.hip", "kvq_internal.h"):
+    for f in ("attn.hip", "attn_mfma.hip", "attn_mfma_common.h", "kvq_internal.h"):
         p = os.path.join(ROOT, "bit_kv_cache_encode_amd", "csrc", f)
         if os.path.exists(p):
             h.update(open(p, "rb").read())
