@@ -47,8 +47,12 @@ def parse():
     ap.add_argument("--kmeans-tokens", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--split-step", action="store_true",
+                    help="run each layer's step as two calls (encode-append, then attention) "
+                         "instead of the one-launch kvq_decode_step")
     ap.add_argument("--attn-only", type=int, default=0,
-                    help="profiling aid: run N attention calls on the layer caches and exit")
+                    help="profiling aid: run N launches of the step's dominant kernel (the "
+                         "one-launch step, or with --split-step the attention) and exit")
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="with --attn-only: then run plain kernels of known traffic on this many "
                          "MiB (4 reads: sum; 4 writes: fill; 4 copies: negation), whose HBM "
@@ -62,7 +66,7 @@ def parse():
 
 def attn_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("attn.hip", "attn_mfma.hip", "attn_mfma_common.h", "kvq_internal.h"):
+    for f in ("attn.hip", "attn_mfma.hip", "attn_mfma_common.h", "encode_vec.h", "kvq_internal.h"):
         p = os.path.join(ROOT, "bit_kv_cache_encode_amd", "csrc", f)
         if os.path.exists(p):
             h.update(open(p, "rb").read())
@@ -137,6 +141,18 @@ def traffic_summary(args):
         "dispatches": len(f_attn),
         "raw_read_requests": raw, "raw_read_bytes_per_launch": raw_bytes,
     }
+    if not args.split_step:
+        # one-launch step over context + 1 tokens: attention bytes plus the
+        # new token's encode (K/V in, records out, the two pattern tables)
+        out["kernel"] = "decode step in one launch: encode 1 token + attention (split + combine)"
+        out["algorithmic_bytes_per_launch"] = (2 * 64 * (args.context + 1) * 49 + 2 * 64 * 32 * 128 * 4
+                                               + 8 * 32 * 128 * 6
+                                               + 2 * 64 * 128 * 2 + 2 * 64 * 49 + 2 * 64 * 32 * 128 * 4)
+    else:
+        out["kernel"] = "attention (split + combine)"
+    flag = "" if not args.split_step else " --split-step"
+    out["commands"] = [c.replace("--calib-copy", flag.strip() + " --calib-copy").replace("  ", " ")
+                       if flag else c for c in out["commands"]]
     dst = os.path.join(ROOT, "profiles", "traffic_attention.json")
     json.dump(out, open(dst, "w"), indent=1)
     print(json.dumps(out))
@@ -201,8 +217,16 @@ def main():
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
 
     if args.attn_only:
+        # the step's dominant kernel: the one-launch step (default) or the
+        # attention launch of the two-call form
         for i in range(args.attn_only):
-            layers[i % L].attn_decode(qs[i % L], out=out)
+            c = layers[i % L]
+            if args.split_step:
+                c.attn_decode(qs[i % L], out=out)
+            else:
+                s_ = i // L
+                c.decode_step(kn[s_, i % L][:, :, None, :], vn[s_, i % L][:, :, None, :], qs[i % L],
+                              out=out)
         torch.cuda.synchronize()
         print(f"attn-only: {args.attn_only} calls done")
         if args.calib_copy:
@@ -227,15 +251,20 @@ def main():
 
     enc_bytes = 2 * U * D * in_b + 2 * U * rec + 2 * U * P * D * 4
 
+    # events per layer: [0] before the layer's calls, [1] after them; in the
+    # two-call form [2] sits between the encode and the attention
     def step(s, ev=None):
         for li, c in enumerate(layers):
             if ev is not None:
-                ev[li][2].record()
-            c.encode_append(kn[s, li][:, :, None, :], vn[s, li][:, :, None, :],
-                            update_patterns=True)
-            if ev is not None:
                 ev[li][0].record()
-            c.attn_decode(qs[li], out=out)
+            if args.split_step:
+                c.encode_append(kn[s, li][:, :, None, :], vn[s, li][:, :, None, :],
+                                update_patterns=True)
+                if ev is not None:
+                    ev[li][2].record()
+                c.attn_decode(qs[li], out=out)
+            else:
+                c.decode_step(kn[s, li][:, :, None, :], vn[s, li][:, :, None, :], qs[li], out=out)
             if ev is not None:
                 ev[li][1].record()
 
@@ -252,14 +281,37 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    attn_ms = [e[0].elapsed_time(e[1]) for st in evs for e in st]
-    attn_avg_us = 1e3 * sum(attn_ms) / len(attn_ms)
-    enc_ms = [e[2].elapsed_time(e[0]) for st in evs for e in st]
-    enc_avg_us = 1e3 * sum(enc_ms) / len(enc_ms)
+    layer_ms = [e[0].elapsed_time(e[1]) for st in evs for e in st]
+    layer_avg_us = 1e3 * sum(layer_ms) / len(layer_ms)
     T_mid = T_start + args.steps // 2 + 1
     step_bytes = L * (attn_bytes(T_mid) + enc_bytes)
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    achieved = attn_bytes(T_mid) / (attn_avg_us * 1e-6) / 1e9
+    if args.split_step:
+        # dominant kernel: the attention launch; the encode launch on its own
+        attn_avg_us = 1e3 * sum(e[2].elapsed_time(e[1]) for st in evs for e in st) / (L * args.steps)
+        enc_avg_us = 1e3 * sum(e[0].elapsed_time(e[2]) for st in evs for e in st) / (L * args.steps)
+        kern, kern_us, kern_bytes = "attention (split + combine)", attn_avg_us, attn_bytes(T_mid)
+    else:
+        # dominant kernel: the one-launch step (encode 1 token + attention)
+        kern = "decode step in one launch: encode 1 token + attention (split + combine)"
+        kern_us, kern_bytes = layer_avg_us, attn_bytes(T_mid) + enc_bytes
+        # the single-token encode as its own launch, on a copy of one layer,
+        # with the device kept busy while the host queues the launches
+        enc_copy = layers[0].clone()
+        eev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(L)]
+        try:
+            torch.cuda._sleep(50_000_000)
+        except Exception:
+            pass
+        for i in range(L):
+            eev[i][0].record()
+            enc_copy.encode_append(kn[i % n_steps, 0][:, :, None, :], vn[i % n_steps, 0][:, :, None, :],
+                                   update_patterns=True)
+            eev[i][1].record()
+        torch.cuda.synchronize()
+        enc_avg_us = 1e3 * sum(e[0].elapsed_time(e[1]) for e in eev[1:]) / (L - 1)
+        del enc_copy
+    achieved = kern_bytes / (kern_us * 1e-6) / 1e9
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -275,15 +327,17 @@ def main():
         "config": {"workload": (f"decode step of a {L}-layer Llama-3-8B-shaped stack: batch {B}, "
                                 f"{Hq} q / {H} kv heads, head_dim {D}, context {T0}, bf16 in, "
                                 f"2-bit PatternKV codes (group 32, {P} patterns, alpha 0.05, "
-                                f"window {W}); per layer encode-append 1 token + decode attention"),
+                                f"window {W}); per layer encode-append 1 token + decode attention"
+                                + (" (two calls)" if args.split_step else " in one launch")),
                    "batch": B, "context": T0, "layers": L, "n_q_heads": Hq, "n_kv_heads": H,
                    "head_dim": D, "bits": 2, "group": 32, "patterns": P},
         "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "attention (split + combine)",
-                     "avg_launch_us": round(attn_avg_us, 3),
-                     "algorithmic_bytes_per_launch": attn_bytes(T_mid)},
+                     "traffic": traffic, "kernel": kern,
+                     "avg_launch_us": round(kern_us, 3),
+                     "algorithmic_bytes_per_launch": kern_bytes},
+        "layer_step_avg_us": round(layer_avg_us, 3),
         "encode": {"bulk_tok_s": round(B * T0 / (bulk_ms * 1e-3), 1),
                    "bulk_tokens": B * T0, "bulk_ms": round(bulk_ms, 3),
                    "decode_step_tok_s": round(B / (enc_avg_us * 1e-6), 1),

@@ -19,7 +19,7 @@ INDEX_NONE = 0xFF
 VTILE = 32
 
 EXPORTS = ("kvq_layout_of", "kvq_cache_init", "kvq_init_patterns", "kvq_set_patterns",
-           "kvq_encode_append", "kvq_attn_decode", "kvq_dequant", "kvq_strerror",
+           "kvq_encode_append", "kvq_attn_decode", "kvq_decode_step", "kvq_dequant", "kvq_strerror",
            "kvq_last_device_error")
 
 
@@ -75,6 +75,7 @@ def lib():
             "kvq_set_patterns": (I, [C.POINTER(kvq_cache), P, P, I, P]),
             "kvq_encode_append": (I, [C.POINTER(kvq_cache), P, P, I, I, P]),
             "kvq_attn_decode": (I, [C.POINTER(kvq_cache), P, P, C.c_float, P]),
+            "kvq_decode_step": (I, [C.POINTER(kvq_cache), P, P, P, P, C.c_float, C.c_int32, P]),
             "kvq_dequant": (I, [C.POINTER(kvq_cache), I, I, I, P, P]),
             "kvq_strerror": (C.c_char_p, [I]),
             "kvq_last_device_error": (I, []),
@@ -116,6 +117,11 @@ def kvq_encode_append(cache, k_ptr, v_ptr, n_new, update_patterns, stream) -> in
 
 def kvq_attn_decode(cache, q_ptr, out_ptr, sm_scale, stream) -> int:
     return lib().kvq_attn_decode(C.byref(cache), q_ptr, out_ptr, sm_scale, stream)
+
+
+def kvq_decode_step(cache, k_ptr, v_ptr, q_ptr, out_ptr, sm_scale, update_patterns, stream) -> int:
+    return lib().kvq_decode_step(C.byref(cache), k_ptr, v_ptr, q_ptr, out_ptr, sm_scale,
+                                 update_patterns, stream)
 
 
 def kvq_dequant(cache, which, tok0, n, out_ptr, stream) -> int:

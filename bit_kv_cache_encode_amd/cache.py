@@ -103,6 +103,25 @@ class KVCache:
                                                      _stream(self.device)))
         return out
 
+    def decode_step(self, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor,
+                    out: torch.Tensor | None = None, sm_scale: float = 0.0,
+                    update_patterns: bool = True) -> torch.Tensor:
+        """Append one token (k, v: [B][Hkv][1][D]) and attend with q over the
+        cache including it, in one launch (kvq_decode_step)."""
+        c = self.cfg
+        self._in(k, "k", 1)
+        self._in(v, "v", 1)
+        if q.device != self.device or q.dtype != self.in_dtype or not q.is_contiguous() or \
+                tuple(q.shape) != (c.batch, c.n_q_heads, c.head_dim):
+            raise ValueError("q must be contiguous [B][Hq][D] in the cache's input dtype")
+        if out is None:
+            out = torch.empty((c.batch, c.n_q_heads, c.head_dim), dtype=torch.float32,
+                              device=self.device)
+        B.check("kvq_decode_step", B.kvq_decode_step(self.c, _ptr(k), _ptr(v), _ptr(q), _ptr(out),
+                                                     sm_scale, int(update_patterns),
+                                                     _stream(self.device)))
+        return out
+
     def dequant(self, which: int, tok0: int = 0, n: int | None = None,
                 out: torch.Tensor | None = None) -> torch.Tensor:
         c = self.cfg

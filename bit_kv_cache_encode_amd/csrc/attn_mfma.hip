@@ -30,6 +30,7 @@
 #include <type_traits>
 
 #include "attn_mfma_common.h"
+#include "encode_vec.h"
 
 namespace kvq {
 
@@ -98,6 +99,10 @@ attn_mfma_kernel(AttnArgs a) {
   const int u = blockIdx.x % U, split = blockIdx.x / U;
   const int b = u / a.Hkv, hk = u % a.Hkv, hq0 = hk * a.gq;
   const int t_begin = split * a.chunk, t_end = min(a.T, t_begin + a.chunk);
+  // fused decode step: split 0 also appends the new token and writes its
+  // one-token partial into slot a.splits
+  const bool fuse_here = !KVARN && a.fuse && split == 0;
+  const int S_tot = a.splits + a.fuse;
   const int n_pat = KVARN ? 0 : a.n_pat;
   const int npat = pad_pat(n_pat);
   const MfLds Lo = mf_lds(HB, NG, npat, TS::BYTES, 16 * NPB);
@@ -166,7 +171,10 @@ attn_mfma_kernel(AttnArgs a) {
   // tile, q (below), and this thread's 32-channel slice of pattern row
   // tid / 4 of M^K (for q' . M^K).
   const int n_tiles = (t_end - t_begin + TILE - 1) / TILE;
-  if (wave < n_tiles) issue(t_begin + TILE * wave);
+  // in the fused step waves 0 and 1 of split 0 encode the new token first and
+  // take their tiles from the counter afterwards
+  const int first = !fuse_here ? wave : (wave < 2 ? n_tiles : wave - 2);
+  if (first < n_tiles) issue(t_begin + TILE * first);
   // M^V rows for the pattern term go straight to LDS (no registers held
   // through the loop); 16 bytes per lane, one kilobyte per wave instruction.
   // Completion is awaited before the merge reads them.
@@ -203,7 +211,7 @@ attn_mfma_kernel(AttnArgs a) {
   for (int i = tid; i < HB * 256; i += MF_THREADS) s_qm[i] = 0.0f;
   if (tid < HB * NG) s_z[tid] = 0.0f;
   if (tid < HB) { s_l[tid] = 0.0f; s_qe[tid] = 0; }
-  if (tid == 0) *s_next = MF_WAVES;
+  if (tid == 0) *s_next = fuse_here ? MF_WAVES - 2 : MF_WAVES;
   __syncthreads();
   if (KVARN) {
     for (int hs = 1; hs < D; hs <<= 1) {
@@ -355,7 +363,59 @@ attn_mfma_kernel(AttnArgs a) {
   // claims its next one from the block counter while the current one is
   // computed, so the waves of the block finish together whatever their
   // issue priority.
-  for (int cur = wave; cur < n_tiles;) {
+  int cur = first;
+  if constexpr (!KVARN) if (fuse_here && wave < 2) {
+    // ---- the new token (position a.enc.t0): wave 0 encodes K, wave 1 V,
+    // with the one-token encode of the append path; then its dequantised
+    // vector gives this token's own partial (m = its score, l = 1, o = v^)
+    const EncodeArgs& e = a.enc;
+    const int kind = wave;
+    const int64_t uu = u;
+    const float x0 = load_in(e.src[kind], uu * D + lane, e.bf16);
+    const float x1 = load_in(e.src[kind], uu * D + lane + 64, e.bf16);
+    float wl0 = 0.0f, wl1 = 0.0f, wh0 = 0.0f, wh1 = 0.0f;
+    if (e.win_update) {
+      const float* win = e.r.win[kind] + uu * 2 * D;
+      wl0 = win[lane]; wl1 = win[lane + 64];
+      wh0 = win[D + lane]; wh1 = win[D + lane + 64];
+    }
+    uint32_t c0, c1, w0, w1;
+    int kidx;
+    uint16_t t16;
+    float* sx = (float*)tb;   // this wave's tile buffer is idle until its first tile
+    encode_vector<true>(e, kind, uu, x0, x1, lane, sx, nullptr, uu, c0, c1, w0, w1, kidx, t16);
+    token_append(e, kind, uu, e.t0, lane, x0, x1, wl0, wl1, wh0, wh1, c0, c1, w0, w1, kidx, t16);
+    float m0 = 0.0f, m1 = 0.0f;
+    if (kidx != KVQ_INDEX_NONE) {
+      const float* mrow = e.r.tab[kind] + (uu * e.max_pat + kidx) * D;
+      m0 = mrow[lane];
+      m1 = mrow[lane + 64];
+    }
+    const float xh0 = __builtin_fmaf((float)c0, bits2f((uint16_t)(w0 & 0xFFFFu)), bits2f((uint16_t)(w0 >> 16))) + m0;
+    const float xh1 = __builtin_fmaf((float)c1, bits2f((uint16_t)(w1 & 0xFFFFu)), bits2f((uint16_t)(w1 >> 16))) + m1;
+    float* mlp = a.r.ws + (int64_t)a.B * a.Hq * S_tot * D;
+    for (int h = 0; h < a.gq; ++h) {
+      const int64_t qrow = (int64_t)b * a.Hq + hq0 + h, row = qrow * S_tot + a.splits;
+      if (kind == 0) {
+        float dot = __builtin_fmaf(load_in(a.q, qrow * D + lane, a.bf16), xh0,
+                                   load_in(a.q, qrow * D + lane + 64, a.bf16) * xh1);
+        dot = row_sum16(dot);
+        dot = (rlane(dot, 0) + rlane(dot, 16)) + (rlane(dot, 32) + rlane(dot, 48));
+        if (lane == 0) {
+          __hip_atomic_store(&mlp[row * 2], dot * a.qscale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(&mlp[row * 2 + 1], 1.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      } else {
+        __hip_atomic_store(&a.r.ws[row * D + lane], xh0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.r.ws[row * D + lane + 64], xh1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    int nx = 0;
+    if (lane == 0) nx = atomicAdd(s_next, 1);
+    cur = __builtin_amdgcn_readfirstlane(nx);
+    if (cur < n_tiles) issue(t_begin + TILE * cur);
+  }
+  for (; cur < n_tiles;) {
     const int tile = t_begin + TILE * cur;
     __builtin_amdgcn_wave_barrier();
     commit();
@@ -719,7 +779,7 @@ attn_mfma_kernel(AttnArgs a) {
   // Row (b, head, split): o + z + sum_j w_j M^V_j and (M, l), all relative
   // to this split's max M.  Stores are agent-scope atomics (coherent across
   // the XCDs' L2s), so publishing them needs only their completion.
-  const int S = a.splits;
+  const int S = S_tot;
   float* ml = a.r.ws + (int64_t)a.B * a.Hq * S * D;
   for (int i = tid; i < a.gq * D; i += MF_THREADS) {
     const int h = i / D, d = i % D;
@@ -745,15 +805,16 @@ attn_mfma_kernel(AttnArgs a) {
   // ---------------------------------------------------------------- fused combine
   // Each thread waits until its partial stores have completed at agent scope;
   // after the barrier thread 0 counts this split in, and the block that
-  // arrives last (it observes S - 1 earlier increments, each made after that
-  // split's stores completed) merges all splits of the unit with agent-scope
-  // loads.
+  // arrives last (it observes splits - 1 earlier increments, each made after
+  // that split's stores completed) merges all partials of the unit (the
+  // splits', and in the fused step the new token's, written by split 0
+  // before it counted itself in) with agent-scope loads.
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
   if (tid == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(&a.r.cnt[u], 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
-    *s_last = prev == (uint32_t)(S - 1);
+    *s_last = prev == (uint32_t)(a.splits - 1);
   }
   __syncthreads();
   if (!*s_last) return;

@@ -330,13 +330,17 @@ int kvq_encode_append(kvq_cache* cache, const void* k_new, const void* v_new, in
   return KVQ_OK;
 }
 
-int kvq_attn_decode(kvq_cache* cache, const void* q, float* out, float sm_scale, void* stream) {
-  kvq_layout L;
-  if (!cache || !cache->base || kvq_layout_of(&cache->cfg, &L) != KVQ_OK) return KVQ_EINVAL;
-  if (!q || !out || !aligned16(q) || !aligned16(out)) return KVQ_EINVAL;
-  if (cache->n_tokens <= 0) return KVQ_ESTATE;
+// Attention arguments over the cache's first T tokens and the kernel choice.
+// `reserve` partial slots per (b, q-head) are kept free for a fused step.
+// Kernel choice: the MFMA kernels cover groups of 32 / 64 channels with up
+// to 16/(128/group) q-heads per kv-head.  The single-role MFMA kernel is the
+// default; KVQ_ATTN_KERNEL=pp selects the paired score/value-wave kernel and
+// KVQ_ATTN_KERNEL=valu the VALU kernel (used to cross-check them).
+// KVQ_ATTN_BLOCKS sets the target grid size.
+enum AttnKernel { ATTN_MFMA, ATTN_PP, ATTN_VALU };
+static AttnKernel attn_setup(const kvq_cache* cache, const kvq_layout& L, const void* q, float* out,
+                             float sm_scale, int T, int reserve, AttnArgs& a) {
   const kvq_config& c = cache->cfg;
-  AttnArgs a;
   memset(&a, 0, sizeof(a));
   a.r = regions_of(cache, L);
   a.q = q;
@@ -345,7 +349,7 @@ int kvq_attn_decode(kvq_cache* cache, const void* q, float* out, float sm_scale,
   a.Hq = c.n_q_heads;
   a.Hkv = c.n_kv_heads;
   a.gq = c.n_q_heads / c.n_kv_heads;
-  a.T = cache->n_tokens;
+  a.T = T;
   a.tcap = L.token_cap;
   a.ngroups = L.n_groups;
   a.group = c.group;
@@ -357,34 +361,96 @@ int kvq_attn_decode(kvq_cache* cache, const void* q, float* out, float sm_scale,
   const float sm = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)D);
   a.qscale = sm * 1.4426950408889634f;
   const int units = c.batch * c.n_kv_heads;
-  // Kernel choice: the MFMA kernels cover groups of 32 / 64 channels with up
-  // to 16/(128/group) q-heads per kv-head.  The single-role MFMA kernel is the
-  // default; KVQ_ATTN_KERNEL=pp selects the paired score/value-wave kernel and
-  // KVQ_ATTN_KERNEL=valu the VALU kernel (used to cross-check them).
-  // KVQ_ATTN_BLOCKS sets the target grid size.
   const char* kenv = getenv("KVQ_ATTN_KERNEL");
   const bool mfma_ok = mfma_attention_supported(c.bits, c.group, a.gq);
-  const bool use_valu = !mfma_ok || (kenv && strcmp(kenv, "valu") == 0);
-  const bool use_pp = !use_valu && kenv && strcmp(kenv, "pp") == 0;
+  const AttnKernel k = (!mfma_ok || (kenv && strcmp(kenv, "valu") == 0)) ? ATTN_VALU
+                       : (kenv && strcmp(kenv, "pp") == 0) ? ATTN_PP : ATTN_MFMA;
   // one 8-wave MFMA block per compute unit
-  int target = use_valu ? ATTN_TARGET_BLOCKS : (use_pp ? 768 : 256);
+  int target = k == ATTN_VALU ? ATTN_TARGET_BLOCKS : (k == ATTN_PP ? 768 : 256);
   const char* benv = getenv("KVQ_ATTN_BLOCKS");
   if (benv && atoi(benv) > 0) target = atoi(benv);
   int want = (target + units - 1) / units;
-  if (want > L.max_splits) want = L.max_splits;
+  if (want > L.max_splits - reserve) want = L.max_splits - reserve;
   if (want < 1) want = 1;
   int chunk = (a.T + want - 1) / want;
   chunk = (chunk + ATTN_MIN_CHUNK - 1) / ATTN_MIN_CHUNK * ATTN_MIN_CHUNK;
   a.chunk = chunk;
   a.splits = (a.T + chunk - 1) / chunk;
-  if (!use_valu) {
-    hipError_t e = use_pp ? launch_attention_pp(a, (hipStream_t)stream)
-                          : launch_attention_mfma(a, (hipStream_t)stream);
-    if (e != hipSuccess) return dev_fail(e);
-    return KVQ_OK;
+  return k;
+}
+
+static int attn_launch(AttnKernel k, const AttnArgs& a, void* stream) {
+  hipError_t e = k == ATTN_MFMA ? launch_attention_mfma(a, (hipStream_t)stream)
+               : k == ATTN_PP   ? launch_attention_pp(a, (hipStream_t)stream)
+                                : launch_attention(a, (hipStream_t)stream);
+  return e == hipSuccess ? KVQ_OK : dev_fail(e);
+}
+
+int kvq_attn_decode(kvq_cache* cache, const void* q, float* out, float sm_scale, void* stream) {
+  kvq_layout L;
+  if (!cache || !cache->base || kvq_layout_of(&cache->cfg, &L) != KVQ_OK) return KVQ_EINVAL;
+  if (!q || !out || !aligned16(q) || !aligned16(out)) return KVQ_EINVAL;
+  if (cache->n_tokens <= 0) return KVQ_ESTATE;
+  AttnArgs a;
+  const AttnKernel k = attn_setup(cache, L, q, out, sm_scale, cache->n_tokens, 0, a);
+  return attn_launch(k, a, stream);
+}
+
+int kvq_decode_step(kvq_cache* cache, const void* k_new, const void* v_new, const void* q,
+                    float* out, float sm_scale, int32_t update_patterns, void* stream) {
+  kvq_layout L;
+  if (!cache || !cache->base || kvq_layout_of(&cache->cfg, &L) != KVQ_OK) return KVQ_EINVAL;
+  if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return KVQ_EINVAL;
+  if (!q || !out || !aligned16(q) || !aligned16(out)) return KVQ_EINVAL;
+  const kvq_config& c = cache->cfg;
+  if ((int64_t)cache->n_tokens + 1 > c.max_tokens) return KVQ_ECAPACITY;
+  AttnArgs a;
+  const AttnKernel k = cache->n_tokens > 0 && L.max_splits >= 2
+                           ? attn_setup(cache, L, q, out, sm_scale, cache->n_tokens, 1, a)
+                           : ATTN_VALU;
+  // The fused launch covers the MFMA kernel in PatternKV mode with a
+  // non-empty cache; anything else is the two calls in sequence.
+  if (k != ATTN_MFMA || c.mode != KVQ_MODE_PATTERN) {
+    int st = kvq_encode_append(cache, k_new, v_new, 1, update_patterns, stream);
+    if (st != KVQ_OK) return st;
+    return kvq_attn_decode(cache, q, out, sm_scale, stream);
   }
-  hipError_t e = launch_attention(a, (hipStream_t)stream);
-  if (e != hipSuccess) return dev_fail(e);
+  EncodeArgs& e = a.enc;
+  memset(&e, 0, sizeof(e));
+  e.r = a.r;
+  e.src[0] = k_new;
+  e.src[1] = v_new;
+  e.src_rows = 1;
+  e.n_new = 1;
+  e.t0 = cache->n_tokens;
+  e.tcap = L.token_cap;
+  e.ngroups = L.n_groups;
+  e.group = c.group;
+  e.bits = c.bits;
+  e.bf16 = c.in_dtype == KVQ_BF16;
+  e.mode = c.mode;
+  e.n_pat = cache->n_patterns;
+  e.max_pat = c.max_patterns;
+  e.rho = cache->rho;
+  e.tiles_per_block = 1;
+  const bool window = update_patterns && c.pattern_window > 0;
+  if (window) {
+    e.win_update = 1;
+    e.win_close = cache->win_count + 1 == c.pattern_window;
+    e.close_slot = cache->n_patterns < c.max_patterns ? cache->n_patterns : -1;
+  }
+  a.fuse = 1;
+  const int st = attn_launch(k, a, stream);
+  if (st != KVQ_OK) return st;
+  cache->n_tokens += 1;
+  if (window) {
+    cache->win_count += 1;
+    if (e.win_close) {
+      if (e.close_slot >= 0) cache->n_patterns += 1;
+      else cache->dropped += 1;
+      cache->win_count = 0;
+    }
+  }
   return KVQ_OK;
 }
 

@@ -103,6 +103,12 @@ struct AttnArgs {
   int n_pat, max_pat;
   int splits, chunk;    // tokens per split (multiple of 64)
   float qscale;         // sm_scale * log2(e)
+  // Fused one-token decode step: the block of split 0 of each unit also
+  // encodes and appends the new token (position T, described by `enc`) and
+  // writes its one-token softmax partial into slot `splits` (so the combine
+  // merges splits + 1 partials).  The splits cover tokens [0, T).
+  int fuse;
+  EncodeArgs enc;
 };
 
 struct DequantArgs {

@@ -165,6 +165,22 @@ int kvq_encode_append(kvq_cache* cache, const void* k_new, const void* v_new, in
  * KVQ_ESTATE if the cache is empty; KVQ_EINVAL on null pointers. */
 int kvq_attn_decode(kvq_cache* cache, const void* q, float* out, float sm_scale, void* stream);
 
+/* One decode step in one launch: append one token per unit (k_new, v_new:
+ * [B][Hkv][1][D], encoded exactly as kvq_encode_append with n_new = 1) and
+ * attend with q over all n_tokens + 1 tokens (as kvq_attn_decode after the
+ * append).  The new token's own attention term is computed from its freshly
+ * dequantized K and V by the block that encodes it, while the other blocks
+ * attend over the earlier tokens; the split-K combine merges both (the
+ * decode-stage fusion of PatternKV section 3.4 extended to the append).
+ * Cache contents afterwards are identical to the two separate calls; `out`
+ * agrees with them to floating-point rounding.  Falls back to the two calls
+ * in sequence where the fused launch does not apply (KVARN mode, an empty
+ * cache, shapes served by the VALU kernel).
+ * Errors as kvq_encode_append (n_new = 1) and kvq_attn_decode; nothing is
+ * written when a check fails. */
+int kvq_decode_step(kvq_cache* cache, const void* k_new, const void* v_new, const void* q,
+                    float* out, float sm_scale, int32_t update_patterns, void* stream);
+
 /* Dequantize tokens tok0 .. tok0+n-1 of K (which = 0) or V (which = 1) into
  * fp32 out [B][Hkv][n][D]: PATTERN x^ = fl(fmaf(q, s, z) + M_k*) (the index
  * restore of section 3.2), or fmaf(q, s, z) alone for index 0xFF; KVARN
