@@ -98,7 +98,8 @@ attn_mfma_kernel(AttnArgs a) {
   const int U = a.B * a.Hkv;
   const int u = blockIdx.x % U, split = blockIdx.x / U;
   const int b = u / a.Hkv, hk = u % a.Hkv, hq0 = hk * a.gq;
-  const int t_begin = split * a.chunk, t_end = min(a.T, t_begin + a.chunk);
+  const int t_begin = split == 0 ? 0 : a.chunk0 + (split - 1) * a.chunk;
+  const int t_end = min(a.T, split == 0 ? a.chunk0 : t_begin + a.chunk);
   // fused decode step: split 0 also appends the new token and writes its
   // one-token partial into slot a.splits
   const bool fuse_here = !KVARN && a.fuse && split == 0;
@@ -788,10 +789,16 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int w = 0; w < MF_WAVES; ++w) o += s_ow[(w * HB + h) * D + d];
     if constexpr (NPB > 0) {
+      // separate loops keep each one's loads in a single address space
+      if (stage_mv) {
 #pragma unroll
-      for (int jj = 0; jj < MVR; ++jj)
-        if (jj < n_pat)
-          o = __builtin_fmaf(s_wsum[h * npat + jj], stage_mv ? s_mv[jj * D + d] : mv[(int64_t)jj * D + d], o);
+        for (int jj = 0; jj < MVR; ++jj)
+          if (jj < n_pat) o = __builtin_fmaf(s_wsum[h * npat + jj], s_mv[jj * D + d], o);
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < MVR; ++jj)
+          if (jj < n_pat) o = __builtin_fmaf(s_wsum[h * npat + jj], mv[(int64_t)jj * D + d], o);
+      }
     } else if (!KVARN) {
 #pragma unroll 8
       for (int jj = 0; jj < n_pat; ++jj) o = __builtin_fmaf(s_wsum[h * npat + jj], mv[(int64_t)jj * D + d], o);

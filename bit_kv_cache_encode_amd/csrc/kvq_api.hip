@@ -15,6 +15,10 @@ thread_local int g_last_hip = 0;
 
 constexpr int KM_GPU_MAX_PATTERNS = 64;
 constexpr int ATTN_MIN_CHUNK = 64;
+// In the one-launch step, split 0's block also encodes the new token in two
+// of its eight waves (about 4 tiles' worth of wave time), so its token range
+// is this much shorter.
+constexpr int FUSED_LEAD_TOKENS = 256;
 constexpr int ATTN_TARGET_BLOCKS = 2048;
 
 int dev_fail(hipError_t e) {
@@ -372,10 +376,14 @@ static AttnKernel attn_setup(const kvq_cache* cache, const kvq_layout& L, const 
   int want = (target + units - 1) / units;
   if (want > L.max_splits - reserve) want = L.max_splits - reserve;
   if (want < 1) want = 1;
-  int chunk = (a.T + want - 1) / want;
+  // split 0 is `lead` tokens shorter (at least one chunk unit long)
+  const int lead = reserve ? FUSED_LEAD_TOKENS : 0;
+  int chunk = (a.T + lead + want - 1) / want;
   chunk = (chunk + ATTN_MIN_CHUNK - 1) / ATTN_MIN_CHUNK * ATTN_MIN_CHUNK;
+  int chunk0 = chunk - lead < ATTN_MIN_CHUNK ? ATTN_MIN_CHUNK : chunk - lead;
   a.chunk = chunk;
-  a.splits = (a.T + chunk - 1) / chunk;
+  a.chunk0 = chunk0;
+  a.splits = a.T <= chunk0 ? 1 : 1 + (a.T - chunk0 + chunk - 1) / chunk;
   return k;
 }
 

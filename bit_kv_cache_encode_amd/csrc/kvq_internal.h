@@ -102,6 +102,8 @@ struct AttnArgs {
   int B, Hq, Hkv, gq, T, tcap, ngroups, group, bits, bf16, mode;
   int n_pat, max_pat;
   int splits, chunk;    // tokens per split (multiple of 64)
+  int chunk0;           // tokens of split 0 (multiple of 64; = chunk unless the
+                        // fused step shortens it to offset its encode)
   float qscale;         // sm_scale * log2(e)
   // Fused one-token decode step: the block of split 0 of each unit also
   // encodes and appends the new token (position T, described by `enc`) and
