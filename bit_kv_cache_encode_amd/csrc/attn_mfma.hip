@@ -96,8 +96,13 @@ attn_mfma_kernel(AttnArgs a) {
   const int wave = tid >> 6;
   const int j = lane >> 4, n16 = lane & 15;
   const int U = a.B * a.Hkv;
-  const int u = blockIdx.x % U, split = blockIdx.x / U;
-  const int b = u / a.Hkv, hk = u % a.Hkv, hq0 = hk * a.gq;
+  // blocks: (unit, q-head block of HB heads, split); unit fastest so that all
+  // blocks of a unit share an XCD
+  const int n_hb = (a.gq + HB - 1) / HB;
+  const int u = blockIdx.x % U, hb = (blockIdx.x / U) % n_hb, split = blockIdx.x / U / n_hb;
+  const int b = u / a.Hkv, hk = u % a.Hkv, hq0 = hk * a.gq + hb * HB;
+  const int gq = min(HB, a.gq - hb * HB);   // q-heads of this block
+  const int cu = u * n_hb + hb;              // arrival counter of (unit, head block)
   const int t_begin = split == 0 ? 0 : a.chunk0 + (split - 1) * a.chunk;
   const int t_end = min(a.T, split == 0 ? a.chunk0 : t_begin + a.chunk);
   // fused decode step: split 0 also appends the new token and writes its
@@ -204,7 +209,7 @@ attn_mfma_kernel(AttnArgs a) {
   // ---------------------------------------------------------------- prologue
   for (int i = tid; i < HB * D; i += MF_THREADS) {
     const int h = i / D, d = i % D;
-    s_q[i] = h < a.gq ? load_in(a.q, ((int64_t)b * a.Hq + hq0 + h) * D + d, a.bf16) : 0.0f;
+    s_q[i] = h < gq ? load_in(a.q, ((int64_t)b * a.Hq + hq0 + h) * D + d, a.bf16) : 0.0f;
     s_o[i] = 0.0f;
   }
   for (int i = tid; i < MF_WAVES * HB * npat; i += MF_THREADS) s_w[i] = 0.0f;
@@ -289,7 +294,7 @@ attn_mfma_kernel(AttnArgs a) {
       }
 #pragma unroll
       for (int h = 0; h < HB; ++h) {
-        if (h >= a.gq) break;
+        if (h >= gq) break;
         const float* qh = s_q + h * D + qm_part * 32;
         float sdot = 0.0f;
 #pragma unroll
@@ -357,7 +362,7 @@ attn_mfma_kernel(AttnArgs a) {
   for (int cb = 0; cb < (NPB > 0 ? NPB : 1); ++cb) hacc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   // hist A: this lane's row (head n16 / NG, part n16 % NG) takes the low
   // (part 0) or high (part 1) binary16 of each packed word; other rows are 0
-  const uint32_t hsel = (n16 / NG >= a.gq || n16 % NG > 1) ? 0x0C0C0C0Cu
+  const uint32_t hsel = (n16 / NG >= gq || n16 % NG > 1) ? 0x0C0C0C0Cu
                         : (n16 % NG == 0 ? 0x05040100u : 0x07060302u);
 
   // Tiles are handed out dynamically: each wave starts with tile `wave` and
@@ -395,7 +400,7 @@ attn_mfma_kernel(AttnArgs a) {
     const float xh0 = __builtin_fmaf((float)c0, bits2f((uint16_t)(w0 & 0xFFFFu)), bits2f((uint16_t)(w0 >> 16))) + m0;
     const float xh1 = __builtin_fmaf((float)c1, bits2f((uint16_t)(w1 & 0xFFFFu)), bits2f((uint16_t)(w1 >> 16))) + m1;
     float* mlp = a.r.ws + (int64_t)a.B * a.Hq * S_tot * D;
-    for (int h = 0; h < a.gq; ++h) {
+    for (int h = 0; h < gq; ++h) {
       const int64_t qrow = (int64_t)b * a.Hq + hq0 + h, row = qrow * S_tot + a.splits;
       if (kind == 0) {
         float dot = __builtin_fmaf(load_in(a.q, qrow * D + lane, a.bf16), xh0,
@@ -539,7 +544,7 @@ attn_mfma_kernel(AttnArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        for (int e = lane; e < a.gq * npat; e += 64) wrow[e] *= s_alpha[wave * HB + e / npat];
+        for (int e = lane; e < gq * npat; e += 64) wrow[e] *= s_alpha[wave * HB + e / npat];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -605,7 +610,7 @@ attn_mfma_kernel(AttnArgs a) {
       for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
         for (int s = 0; s < SPL; ++s)
-          if (vk[nb] != KVQ_INDEX_NONE && head0 + s < a.gq)
+          if (vk[nb] != KVQ_INDEX_NONE && head0 + s < gq)
             atomicAdd(&wrow[(head0 + s) * npat + vk[nb]], pk[nb][s]);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -756,7 +761,7 @@ attn_mfma_kernel(AttnArgs a) {
   __syncthreads();
   // block totals: pattern masses w[h][j], l[h], z[h][g]
   if (!KVARN && n_pat > 0)
-    for (int e = tid; e < a.gq * npat; e += MF_THREADS) {
+    for (int e = tid; e < gq * npat; e += MF_THREADS) {
       const int h = e / npat;
       float acc = 0.0f;
 #pragma unroll
@@ -782,7 +787,7 @@ attn_mfma_kernel(AttnArgs a) {
   // the XCDs' L2s), so publishing them needs only their completion.
   const int S = S_tot;
   float* ml = a.r.ws + (int64_t)a.B * a.Hq * S * D;
-  for (int i = tid; i < a.gq * D; i += MF_THREADS) {
+  for (int i = tid; i < gq * D; i += MF_THREADS) {
     const int h = i / D, d = i % D;
     const int64_t row = ((int64_t)b * a.Hq + hq0 + h) * S + split;
     float o = s_z[h * NG + d / G];
@@ -819,7 +824,7 @@ attn_mfma_kernel(AttnArgs a) {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
   if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(&a.r.cnt[u], 1u, __ATOMIC_RELAXED,
+    const uint32_t prev = __hip_atomic_fetch_add(&a.r.cnt[cu], 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     *s_last = prev == (uint32_t)(a.splits - 1);
   }
@@ -833,7 +838,7 @@ attn_mfma_kernel(AttnArgs a) {
   for (int k = 0; k < OPT; ++k) {
     const int i = tid + k * MF_THREADS, h = i / D, d = i % D;
     r_out[k] = 0.0f;
-    if (h >= a.gq) continue;
+    if (h >= gq) continue;
     const int64_t row0 = ((int64_t)b * a.Hq + hq0 + h) * S;
     float M = -INFINITY, L = 0.0f, O = 0.0f;
     for (int c0 = 0; c0 < S; c0 += 8) {
@@ -865,7 +870,7 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < OPT; ++k) {
       const int i = tid + k * MF_THREADS, h = i / D;
-      if (h < a.gq) a.out[((int64_t)b * a.Hq + hq0) * D + i] = r_out[k];
+      if (h < gq) a.out[((int64_t)b * a.Hq + hq0) * D + i] = r_out[k];
     }
   } else {
     // undo the channel scale c_V, then the rotation: v = H (c_V * v^) / sqrt(D)
@@ -889,11 +894,11 @@ attn_mfma_kernel(AttnArgs a) {
       __syncthreads();
     }
     const float isd = (float)(1.0 / __builtin_sqrt(128.0));
-    for (int i = tid; i < a.gq * D; i += MF_THREADS)
+    for (int i = tid; i < gq * D; i += MF_THREADS)
       a.out[((int64_t)b * a.Hq + hq0) * D + i] = s_o[i] * isd;
   }
   // ready for the next call (stream-ordered)
-  if (tid == 0) __hip_atomic_store(&a.r.cnt[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(&a.r.cnt[cu], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int BITS, int NG, bool KVARN, int NPB, bool QLO>
@@ -908,7 +913,8 @@ static hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr = L.total;
   }
-  hipLaunchKernelGGL((attn_mfma_kernel<BITS, NG, KVARN, NPB, QLO>), dim3(a.B * a.Hkv * a.splits),
+  const int n_hb = (a.gq + 16 / NG - 1) / (16 / NG);
+  hipLaunchKernelGGL((attn_mfma_kernel<BITS, NG, KVARN, NPB, QLO>), dim3(a.B * a.Hkv * a.splits * n_hb),
                      dim3(MF_THREADS), L.total, s, a);
   return hipGetLastError();
 }
@@ -930,8 +936,9 @@ static hipError_t launch_bits_group(const AttnArgs& a, hipStream_t s) {
 
 bool mfma_attention_supported(int bits, int group, int gq) {
   if (bits != 2 && bits != 4) return false;
-  if (group == 32) return gq <= 4;
-  if (group == 64) return gq <= 8;
+  // q-heads beyond one row block (4 at G = 32, 8 at G = 64) take further
+  // blocks that re-read the unit's cache
+  if (group == 32 || group == 64) return gq >= 1 && gq <= 16;
   return false;
 }
 

@@ -32,7 +32,10 @@ bool cfg_ok(const kvq_config* c) {
   if (!c) return false;
   if (c->batch <= 0 || c->n_kv_heads <= 0 || c->n_q_heads <= 0) return false;
   if (c->n_q_heads % c->n_kv_heads) return false;
-  if (c->n_q_heads / c->n_kv_heads > MAX_GQ) return false;
+  // up to MAX_GQ q-heads per kv-head on every path; up to 16 where the MFMA
+  // attention serves the shape (q-head blocks)
+  const int gq = c->n_q_heads / c->n_kv_heads;
+  if (gq > MAX_GQ && !(gq <= 16 && mfma_attention_supported(c->bits, c->group, gq))) return false;
   if (c->head_dim != D) return false;
   if (c->max_tokens <= 0 || c->max_tokens > (1 << 28)) return false;
   if (c->bits != 2 && c->bits != 4) return false;
@@ -166,7 +169,7 @@ int kvq_layout_of(const kvq_config* cfg, kvq_layout* out) {
   L.k_win = place(L.win_bytes);
   L.v_win = place(L.win_bytes);
   L.ws = place(L.ws_bytes);
-  L.cnt_bytes = U * 4;
+  L.cnt_bytes = (uint64_t)cfg->batch * cfg->n_q_heads * 4;   // one per (unit, q-head block) at most
   L.cnt = place(L.cnt_bytes);
   L.total = off;
   *out = L;
@@ -367,8 +370,12 @@ static AttnKernel attn_setup(const kvq_cache* cache, const kvq_layout& L, const 
   const int units = c.batch * c.n_kv_heads;
   const char* kenv = getenv("KVQ_ATTN_KERNEL");
   const bool mfma_ok = mfma_attention_supported(c.bits, c.group, a.gq);
-  const AttnKernel k = (!mfma_ok || (kenv && strcmp(kenv, "valu") == 0)) ? ATTN_VALU
-                       : (kenv && strcmp(kenv, "pp") == 0) ? ATTN_PP : ATTN_MFMA;
+  // the paired kernel serves one q-head block per unit
+  const bool pp_ok = mfma_ok && a.gq <= 16 / (D / c.group);
+  // (the VALU kernel holds at most MAX_GQ q-heads per kv-head)
+  const bool valu_ok = a.gq <= MAX_GQ;
+  const AttnKernel k = (!mfma_ok || (valu_ok && kenv && strcmp(kenv, "valu") == 0)) ? ATTN_VALU
+                       : (pp_ok && kenv && strcmp(kenv, "pp") == 0) ? ATTN_PP : ATTN_MFMA;
   // one 8-wave MFMA block per compute unit
   int target = k == ATTN_VALU ? ATTN_TARGET_BLOCKS : (k == ATTN_PP ? 768 : 256);
   const char* benv = getenv("KVQ_ATTN_BLOCKS");
@@ -417,8 +424,9 @@ int kvq_decode_step(kvq_cache* cache, const void* k_new, const void* v_new, cons
                            ? attn_setup(cache, L, q, out, sm_scale, cache->n_tokens, 1, a)
                            : ATTN_VALU;
   // The fused launch covers the MFMA kernel in PatternKV mode with a
-  // non-empty cache; anything else is the two calls in sequence.
-  if (k != ATTN_MFMA || c.mode != KVQ_MODE_PATTERN) {
+  // non-empty cache and one q-head block per unit; anything else is the two
+  // calls in sequence.
+  if (k != ATTN_MFMA || c.mode != KVQ_MODE_PATTERN || a.gq > 16 / (D / c.group)) {
     int st = kvq_encode_append(cache, k_new, v_new, 1, update_patterns, stream);
     if (st != KVQ_OK) return st;
     return kvq_attn_decode(cache, q, out, sm_scale, stream);

@@ -112,6 +112,12 @@ def test_decode_step_4bit_gqa8_binary32():
     _run(1, 16, 2, 500, 10, bits=4, group=64, P=40, W=6, bf16=False, seed_off=5)
 
 
+def test_decode_step_gqa7_two_calls():
+    """7 q-heads per kv-head at group 32 (two q-head blocks) takes the
+    two-call path; results as the separate calls."""
+    _run(2, 14, 2, 400, 6, P=20, W=4, seed_off=9)
+
+
 def test_decode_step_kvarn_two_calls():
     """KVarN mode takes the two-call path; results as the separate calls."""
     _run(2, 8, 2, 300, 6, mode="kvarn", P=0, W=0, seed_off=7)

@@ -75,9 +75,11 @@ def test_layout_regions():
 
 @pytest.mark.parametrize("bad", [
     dict(head_dim=64), dict(bits=3), dict(group=48), dict(group=4), dict(n_q_heads=12),
-    dict(n_q_heads=72), dict(max_patterns=256), dict(mode=5), dict(in_dtype=7),
+    dict(n_q_heads=136), dict(n_q_heads=72, group=16), dict(max_patterns=256), dict(mode=5), dict(in_dtype=7),
     dict(v_alpha=0.5), dict(max_tokens=0), dict(batch=0), dict(pattern_window=-1)])
 def test_layout_rejects_bad_configs(bad):
+    """(n_q_heads 136 = 17 q-heads per kv-head; 72 at group 16 = 9 q-heads on
+    a shape only the VALU attention serves, which holds at most 8.)"""
     with pytest.raises(B.KvqError) as e:
         B.kvq_layout_of(_cfg(**bad))
     assert e.value.status == B.KVQ_EINVAL
