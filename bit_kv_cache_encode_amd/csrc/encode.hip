@@ -151,6 +151,175 @@ __global__ void __launch_bounds__(ENC_THREADS) encode_kernel(EncodeArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- bulk, lane per token
+// PATTERN-mode bulk appends (no window): one lane encodes one token's vector
+// (all 128 channels in registers), so the distance, argmin, group min/max and
+// packing are in-lane sequences with no cross-lane reduction, and each
+// instruction serves 64 tokens.  The pattern table sits in LDS with rows of
+// D + 4 floats: the distance loop reads one element for all lanes
+// (broadcast), the residual gathers the chosen row per lane.
+// Work: a block of LANE_WAVES waves owns LANE_SPAN consecutive tokens
+// (aligned, so that no V tile is shared with another block); each wave
+// takes one 64-token chunk.  Short spans give 32k tokens of one kv-head
+// 128 blocks per K/V, so a batch-1 prefill fills the chip; the register
+// budget is capped for three waves per SIMD (latency of the LDS reads in the
+// distance loop is what the extra wave hides).
+constexpr int LANE_WAVES = 4;
+constexpr int LANE_SPAN = 256;
+constexpr int LROW = D + 4;          // LDS table row (floats)
+constexpr int LANE_MAX_PAT = 64;
+
+__host__ __device__ inline bool lane_encode_ok(const EncodeArgs& a) {
+  return a.mode == KVQ_MODE_PATTERN && !a.win_update && a.n_pat <= LANE_MAX_PAT && a.n_new > 1 &&
+         (a.group == 32 || a.group == 64);
+}
+
+template <int BITS, int G>
+__global__ void __launch_bounds__(LANE_WAVES * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
+encode_lane_kernel(EncodeArgs a) {
+  constexpr int NGL = D / G;
+  constexpr int RW = D * BITS / 32;           // words of a packed record
+  extern __shared__ __attribute__((aligned(16))) float s_tab[];   // [n_pat][LROW]
+  // V records of a chunk's 64 tokens (row padded by one word: the lanes'
+  // stores fall on distinct banks)
+  __shared__ uint32_t s_vr[LANE_WAVES][64][RW + 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kind = blockIdx.z;
+  const int64_t u = blockIdx.y;
+  const int t_end = a.t0 + a.n_new;
+  const int span0 = (a.t0 / LANE_SPAN + blockIdx.x) * LANE_SPAN;
+  const int s_begin = max(span0, a.t0), s_end = min(span0 + LANE_SPAN, t_end);
+  const int n_pat = a.n_pat;
+  {
+    const float* tab = a.r.tab[kind] + u * a.max_pat * D;
+    for (int i = threadIdx.x; i < n_pat * D; i += LANE_WAVES * 64)
+      s_tab[(i / D) * LROW + i % D] = tab[i];
+  }
+  __syncthreads();
+  constexpr float qmax = (float)((1 << BITS) - 1);
+  constexpr int per = 32 / BITS;                     // codes per 32-bit word
+  for (int c0 = (s_begin / 64) * 64 + 64 * wave; c0 < s_end; c0 += 64 * LANE_WAVES) {
+    const int t = c0 + lane;
+    const bool valid = t >= s_begin && t < s_end;
+    float x[D];
+    {
+      const int64_t row = u * a.src_rows + (valid ? t - a.t0 : s_begin - a.t0);
+#pragma unroll
+      for (int i = 0; i < D; i += 4) {
+        const float4 v = load4_in(a.src[kind], row * D + i, a.bf16);
+        x[i] = v.x; x[i + 1] = v.y; x[i + 2] = v.z; x[i + 3] = v.w;
+      }
+    }
+    // nearest pattern under d_mm, lowest index on ties (Eq 6)
+    int kbest = KVQ_INDEX_NONE;
+    float best = INFINITY;
+#pragma unroll 2
+    for (int jp = 0; jp < n_pat; ++jp) {
+      const float* m = s_tab + jp * LROW;
+      // two max and two min chains, each step a three-operand max / min
+      float mxa = -INFINITY, mxb = -INFINITY, mna = INFINITY, mnb = INFINITY;
+#pragma unroll
+      for (int i = 0; i < D; i += 4) {
+        const float4 mv = *(const float4*)(m + i);
+        const float e0 = x[i] - mv.x, e1 = x[i + 1] - mv.y, e2 = x[i + 2] - mv.z, e3 = x[i + 3] - mv.w;
+        mxa = fmaxf(fmaxf(mxa, e0), e1); mxb = fmaxf(fmaxf(mxb, e2), e3);
+        mna = fminf(fminf(mna, e0), e1); mnb = fminf(fminf(mnb, e2), e3);
+      }
+      const float e = fmaxf(mxa, mxb) - fminf(mna, mnb);
+      if (e < best || kbest == KVQ_INDEX_NONE) { best = e; kbest = jp; }
+    }
+    // V threshold (Eq 10): keep the pattern iff R_flat <= rho* R_raw
+    if (kind == 1 && a.rho >= 0.0f && kbest != KVQ_INDEX_NONE) {
+      float mx = x[0], mn = x[0];
+#pragma unroll
+      for (int i = 1; i < D; ++i) { mx = fmaxf(mx, x[i]); mn = fminf(mn, x[i]); }
+      const float r_raw = mx - mn;
+      if (!(best <= a.rho * r_raw)) kbest = KVQ_INDEX_NONE;
+    }
+    if (kbest != KVQ_INDEX_NONE) {
+      const float* m = s_tab + kbest * LROW;
+#pragma unroll
+      for (int i = 0; i < D; i += 4) {
+        const float4 mv = *(const float4*)(m + i);
+        x[i] -= mv.x; x[i + 1] -= mv.y; x[i + 2] -= mv.z; x[i + 3] -= mv.w;
+      }
+    }
+    // Eq 1 per group; codes packed into the K record layout (channel d at
+    // bit bits * d of the token's record), then stored or staged (V)
+    uint32_t rec[D * BITS / 32];
+    uint32_t szw[NGL];
+#pragma unroll
+    for (int w = 0; w < D * BITS / 32; ++w) rec[w] = 0u;
+#pragma unroll
+    for (int g = 0; g < NGL; ++g) {
+      const int i0 = g * G;
+      float lo = x[i0], hi = x[i0];
+#pragma unroll
+      for (int i = i0 + 1; i < i0 + G; ++i) { lo = fminf(lo, x[i]); hi = fmaxf(hi, x[i]); }
+      const uint16_t zb = f16_down(lo);
+      const float z = bits2f(zb);
+      const float sv = (hi - z) / qmax;
+      const uint16_t sb = f16_up(sv);
+      const float sf = bits2f(sb);
+      const float inv = sf != 0.0f ? 1.0f / sf : 0.0f;
+#pragma unroll
+      for (int i = i0; i < i0 + G; ++i) {
+        uint32_t c = 0;
+        if (sf != 0.0f) {
+          const float v = rintf((x[i] - z) * inv);
+          c = (uint32_t)fminf(fmaxf(v, 0.0f), qmax);
+        }
+        rec[i / per] |= c << (BITS * (i % per));
+      }
+      szw[g] = (uint32_t)sb | ((uint32_t)zb << 16);
+    }
+    if (valid) {
+      uint32_t* sz_tok = a.r.sz[kind] + ((u * a.tcap) + t) * a.ngroups;
+#pragma unroll
+      for (int g = 0; g < NGL; ++g) sz_tok[g] = szw[g];
+      a.r.idx[kind][u * a.tcap + t] = (uint8_t)kbest;
+      if (kind == 0) {
+        uint4* out = (uint4*)(a.r.codes[0] + (u * a.tcap + t) * (D * BITS / 8));
+#pragma unroll
+        for (int w = 0; w < D * BITS / 32; w += 4) out[w / 4] = make_uint4(rec[w], rec[w + 1], rec[w + 2], rec[w + 3]);
+      }
+    }
+    if (kind == 1) {
+      // V tiles of this chunk (two of 32 tokens): word (wi, d) holds tokens
+      // wi*per .. of channel d.  Tokens before the append keep their bits;
+      // positions after it are zero.
+#pragma unroll
+      for (int w = 0; w < RW; ++w) s_vr[wave][lane][w] = rec[w];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      constexpr int words = D * BITS;                 // words per 32-token tile
+      for (int half = 0; half < 2; ++half) {
+        const int tile = c0 / VT + half, tt0 = max(tile * VT, s_begin), tt1 = min(tile * VT + VT, s_end);
+        if (tt0 >= tt1) continue;
+        uint32_t* tile_out = (uint32_t*)(a.r.codes[1] + ((u * (a.tcap / VT)) + tile) * (VT * D * BITS / 8));
+        for (int w = lane; w < words; w += 64) {
+          const int d = w % D, tok0 = (w / D) * per;
+          uint32_t word = 0, keep = 0;
+          for (int i = 0; i < per; ++i) {
+            const int tk = tile * VT + tok0 + i;
+            const uint32_t msk = ((1u << BITS) - 1u) << (i * BITS);
+            if (tk >= tt0 && tk < tt1)
+              word |= ((s_vr[wave][half * VT + tok0 + i][d / per] >> (BITS * (d % per))) & ((1u << BITS) - 1u))
+                      << (i * BITS);
+            else if (tk < tt0) keep |= msk;
+          }
+          if (keep) word |= tile_out[w] & keep;
+          tile_out[w] = word;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+}
+
 // ---------------------------------------------------------------- one token
 // One wave per (unit, K|V): the token at position t0 (row 0 of the input).
 // The vector, the window state and the pattern table (coalesced, up to
@@ -205,6 +374,16 @@ __global__ void __launch_bounds__(64) encode_token_kernel(EncodeArgs a) {
 hipError_t launch_encode(const EncodeArgs& a, int units, int n_blocks_x, hipStream_t s) {
   if (a.n_new == 1) {
     hipLaunchKernelGGL(encode_token_kernel, dim3(units, 2), dim3(64), 0, s, a);
+    return hipGetLastError();
+  }
+  if (lane_encode_ok(a)) {
+    const int spans = (a.t0 + a.n_new - 1) / LANE_SPAN - a.t0 / LANE_SPAN + 1;
+    const dim3 grid(spans, units, 2), block(LANE_WAVES * 64);
+    const size_t lds = (size_t)a.n_pat * LROW * 4;
+    if (a.bits == 2 && a.group == 32) hipLaunchKernelGGL((encode_lane_kernel<2, 32>), grid, block, lds, s, a);
+    else if (a.bits == 2) hipLaunchKernelGGL((encode_lane_kernel<2, 64>), grid, block, lds, s, a);
+    else if (a.group == 32) hipLaunchKernelGGL((encode_lane_kernel<4, 32>), grid, block, lds, s, a);
+    else hipLaunchKernelGGL((encode_lane_kernel<4, 64>), grid, block, lds, s, a);
     return hipGetLastError();
   }
   dim3 grid(n_blocks_x, units, 2);
