@@ -360,6 +360,10 @@ attn_mfma_kernel(AttnArgs a) {
   f32x4 hacc[NPB > 0 ? NPB : 1];
 #pragma unroll
   for (int cb = 0; cb < (NPB > 0 ? NPB : 1); ++cb) hacc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // with the one-hot path the V zero-point sums sum_t p_t z_tg are a product
+  // of the same p operand and a B of binary16 zero points: rows as hacc,
+  // column g = group (columns >= NG repeat a group and are not read)
+  f32x4 zm = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   // hist A: this lane's row (head n16 / NG, part n16 % NG) takes the low
   // (part 0) or high (part 1) binary16 of each packed word; other rows are 0
   const uint32_t hsel = (n16 / NG >= gq || n16 % NG > 1) ? 0x0C0C0C0Cu
@@ -537,6 +541,8 @@ attn_mfma_kernel(AttnArgs a) {
         for (int cb = 0; cb < NPB; ++cb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) hacc[cb][r] *= al[r / NG];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) zm[r] *= al[r / NG];
       } else if (!KVARN && n_pat > 0) {
         if (n16 == 0)
 #pragma unroll
@@ -557,7 +563,7 @@ attn_mfma_kernel(AttnArgs a) {
       const int t64 = 16 * nb + n16;
       const bool valid = FULL || t64 < nvalid;
       uint32_t vszz[NG];
-      {
+      if constexpr (NPB == 0) {
         const uint32_t* vszp = (const uint32_t*)(tb + TS::O_VS) + t64 * NG;
         if (NG == 4) {
           const u32x4 v4 = *(const u32x4*)vszp;
@@ -583,9 +589,10 @@ attn_mfma_kernel(AttnArgs a) {
         const float p = __builtin_amdgcn_exp2f(sc[nb][s] - m_run[s]);
         l_run[s] += p;
         const float pt = p * tv;              // KVarN: v^ carries the token scale t
+        if constexpr (NPB == 0)
 #pragma unroll
-        for (int g = 0; g < NG; ++g)
-          zacc[s * NG + g] = __builtin_fmaf(pt, bits2f((uint16_t)(vszz[g] >> 16)), zacc[s * NG + g]);
+          for (int g = 0; g < NG; ++g)
+            zacc[s * NG + g] = __builtin_fmaf(pt, bits2f((uint16_t)(vszz[g] >> 16)), zacc[s * NG + g]);
         pk[nb][s] = p;
         s_ps[prow<HB>(head0 + s) + t64] = ldexpf(pt, EP - pv_shift<BITS>(t64 & 31));
         if constexpr (NPB > 0) {
@@ -672,6 +679,20 @@ attn_mfma_kernel(AttnArgs a) {
           }
           hacc[cb] = mfma16(ah, B, hacc[cb]);
         }
+        // B = zero points z_tg (binary16, the high half of each (s, z) word)
+        // of the same tokens for group n16 % NG; tokens past the end read 0
+        const uint32_t* zw = (const uint32_t*)(tb + TS::O_VS) + (32 * kb + 8 * j) * NG + n16 % NG;
+        u32x4 bz;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t w0 = zw[(2 * q) * NG], w1 = zw[(2 * q + 1) * NG];
+          if (!FULL) {
+            w0 = 32 * kb + 8 * j + 2 * q < nvalid ? w0 : 0u;
+            w1 = 32 * kb + 8 * j + 2 * q + 1 < nvalid ? w1 : 0u;
+          }
+          bz[q] = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
+        }
+        zm = mfma16(ah, bz, zm);
       }
       // this lane's word of channels 8*n16 .. 8*n16+7 (word-major V tile)
       const int word = BITS == 2 ? (j >> 1) : j;
@@ -702,8 +723,9 @@ attn_mfma_kernel(AttnArgs a) {
   constexpr int MVR = NPB > 0 ? 16 * NPB : 1;
 #pragma unroll
   for (int s = 0; s < SPL; ++s) l_run[s] = row_sum16(l_run[s]);
+  if constexpr (NPB == 0)
 #pragma unroll
-  for (int r = 0; r < 4; ++r) zacc[r] = row_sum16(zacc[r]);
+    for (int r = 0; r < 4; ++r) zacc[r] = row_sum16(zacc[r]);
   if (n16 == 0)
 #pragma unroll
     for (int s = 0; s < SPL; ++s) s_m[wave * HB + head0 + s] = m_run[s];
@@ -734,14 +756,19 @@ attn_mfma_kernel(AttnArgs a) {
       *(float4*)dst = float4{oacc[0][r] * sc, oacc[1][r] * sc, oacc[2][r] * sc, oacc[3][r] * sc};
       *(float4*)(dst + 4) = float4{oacc[4][r] * sc, oacc[5][r] * sc, oacc[6][r] * sc, oacc[7][r] * sc};
     }
-    if (n16 == 0)
 #pragma unroll
-      for (int s = 0; s < SPL; ++s) {
-        float* lz = s_lz + (wave * HB + head0 + s) * (1 + NG);
+    for (int s = 0; s < SPL; ++s) {
+      float* lz = s_lz + (wave * HB + head0 + s) * (1 + NG);
+      if (n16 == 0) {
         lz[0] = f[s] * l_run[s];
+        if constexpr (NPB == 0)
 #pragma unroll
-        for (int g = 0; g < NG; ++g) lz[1 + g] = f[s] * zacc[s * NG + g];
+          for (int g = 0; g < NG; ++g) lz[1 + g] = f[s] * zacc[s * NG + g];
       }
+      // zm rows (head, hi | lo) carry p 2^15
+      if constexpr (NPB > 0)
+        if (n16 < NG) lz[1 + n16] = (zm[s * NG] + zm[s * NG + 1]) * (f[s] * (1.0f / 32768.0f));
+    }
   }
   if constexpr (NPB > 0) {
     // w = (hi + lo rows) * 2^-15 / 2^-24, relative to the block max
