@@ -12,8 +12,10 @@ Infinity Cache cannot hold them.
 value = algorithmic bytes of a step / step time (effective GB/s); the bytes
 are the packed cache records read by attention, the pattern tables read by
 attention and encode, the new K/V read and records written by encode, q and
-the outputs.  The roofline object covers the attention kernel alone, timed
-with events on the stream it runs on.  A bulk (prefill-style) encode rate is
+the outputs.  The roofline object covers the step's dominant kernel (the
+one-launch decode step), timed with events on the stream it runs on around a
+rotating sample of its launches inside the timed steps (2 of 32 layers per
+step: an event record between launches adds device time of its own).  A bulk (prefill-style) encode rate is
 reported as encode tokens/s.  The CPU oracle is timed on a bounded sample.
 
 Usage: python bench.py [--steps K] [--warmup W] [--context T] [--layers L]
@@ -251,22 +253,31 @@ def main():
 
     enc_bytes = 2 * U * D * in_b + 2 * U * rec + 2 * U * P * D * 4
 
-    # events per layer: [0] before the layer's calls, [1] after them; in the
-    # two-call form [2] sits between the encode and the attention
+    # Events bracket a rotating sample of the layers' launches inside the timed
+    # steps (EV_EVERY-th layer, offset by the step), because an event record
+    # between two launches costs ~6 us of device time on its own.  Per sampled
+    # layer: [0] before the layer's calls, [1] after them; in the two-call form
+    # [2] sits between the encode and the attention.
+    EV_EVERY = max(1, min(16, L))   # at least one sampled layer per step
+
+    def sampled(s, li):
+        return (li - s) % EV_EVERY == 0
+
     def step(s, ev=None):
         for li, c in enumerate(layers):
-            if ev is not None:
-                ev[li][0].record()
+            e = ev[li] if ev is not None and sampled(s, li) else None
+            if e is not None:
+                e[0].record()
             if args.split_step:
                 c.encode_append(kn[s, li][:, :, None, :], vn[s, li][:, :, None, :],
                                 update_patterns=True)
-                if ev is not None:
-                    ev[li][2].record()
+                if e is not None:
+                    e[2].record()
                 c.attn_decode(qs[li], out=out)
             else:
                 c.decode_step(kn[s, li][:, :, None, :], vn[s, li][:, :, None, :], qs[li], out=out)
-            if ev is not None:
-                ev[li][1].record()
+            if e is not None:
+                e[1].record()
 
     for s in range(args.warmup):
         step(s)
@@ -281,15 +292,16 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    layer_ms = [e[0].elapsed_time(e[1]) for st in evs for e in st]
+    used = [evs[s][li] for s in range(args.steps) for li in range(L) if sampled(args.warmup + s, li)]
+    layer_ms = [e[0].elapsed_time(e[1]) for e in used]
     layer_avg_us = 1e3 * sum(layer_ms) / len(layer_ms)
     T_mid = T_start + args.steps // 2 + 1
     step_bytes = L * (attn_bytes(T_mid) + enc_bytes)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     if args.split_step:
         # dominant kernel: the attention launch; the encode launch on its own
-        attn_avg_us = 1e3 * sum(e[2].elapsed_time(e[1]) for st in evs for e in st) / (L * args.steps)
-        enc_avg_us = 1e3 * sum(e[0].elapsed_time(e[2]) for st in evs for e in st) / (L * args.steps)
+        attn_avg_us = 1e3 * sum(e[2].elapsed_time(e[1]) for e in used) / len(used)
+        enc_avg_us = 1e3 * sum(e[0].elapsed_time(e[2]) for e in used) / len(used)
         kern, kern_us, kern_bytes = "attention (split + combine)", attn_avg_us, attn_bytes(T_mid)
     else:
         # dominant kernel: the one-launch step (encode 1 token + attention)
