@@ -188,8 +188,16 @@ def main():
     base = KVCache(B, Hq, H, max_tokens, bits=2, group=32, mode="pattern", max_patterns=P,
                    pattern_window=W, v_alpha=0.05, in_dtype=torch.bfloat16, device=dev)
     nk = min(args.kmeans_tokens, T0)
-    base.init_patterns(k[:, :, :nk].contiguous(), v[:, :, :nk].contiguous(), P)
+    kpre, vpre = k[:, :, :nk].contiguous(), v[:, :, :nk].contiguous()
     torch.cuda.synchronize()
+    # pattern mining (k-means over the prefix, K and V of every unit), one layer
+    i0, i1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    i0.record()
+    base.init_patterns(kpre, vpre, P)
+    i1.record()
+    torch.cuda.synchronize()
+    init_ms = i0.elapsed_time(i1)
+    del kpre, vpre
     # bulk encode rate: the whole prefix in one append (prefill-style)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -355,6 +363,9 @@ def main():
                    "decode_step_tok_s": round(B / (enc_avg_us * 1e-6), 1),
                    "decode_step_avg_us": round(enc_avg_us, 3),
                    "token": "one position's K and V for all 8 kv-heads of one layer"},
+        "pattern_init": {"ms": round(init_ms, 3), "prefix_tokens": nk, "patterns": P,
+                         "what": "k-means (binary64) over the prefix for K and V of all "
+                                 f"{U} (batch, kv-head) units of one layer"},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args, T0, P, W, attn_bytes, enc_bytes, U)

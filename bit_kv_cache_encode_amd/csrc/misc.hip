@@ -189,9 +189,181 @@ __global__ void __launch_bounds__(KM_THREADS) kmeans_kernel(const void* xk, cons
   for (int i = threadIdx.x; i < k * D; i += KM_THREADS) tab[i] = (float)sh.cent[i / D][i % D];
 }
 
+// The same iteration, arithmetic and operation order with the work spread
+// over a 1024-thread block, for prefixes of up to KF_MAXN tokens:
+// * assignment: lane = token, 16 distance chains at a time (each still summed
+//   in channel order); the centroid reads are LDS broadcasts;
+// * update: members of each cluster listed in token order (per 64-token
+//   chunk: ballot counts and ranks, then prefixes over chunks), then one
+//   thread per (pattern, channel) sums its members in that order.
+constexpr int KF_THREADS = 1024;
+constexpr int KF_MAXN = 8192;
+constexpr int KF_PC = 8;    // patterns per distance pass
+
+// 16 consecutive channels of an input row (16-byte aligned) as fp32
+__device__ __forceinline__ void km_load16(const void* x, int64_t idx, int bf16, float (&o)[16]) {
+  if (bf16) {
+    const uint4* p = (const uint4*)((const uint16_t*)x + idx);
+    const uint4 w0 = p[0], w1 = p[1];
+    const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      o[2 * i] = bf16_to_f32((uint16_t)(w[i] & 0xFFFFu));
+      o[2 * i + 1] = bf16_to_f32((uint16_t)(w[i] >> 16));
+    }
+  } else {
+    const float4* p = (const float4*)((const float*)x + idx);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 f = p[i];
+      o[4 * i] = f.x; o[4 * i + 1] = f.y; o[4 * i + 2] = f.z; o[4 * i + 3] = f.w;
+    }
+  }
+}
+
+struct KfShared {
+  double cent[KM_MAXK][D];
+  uint8_t a[KF_MAXN];                   // assignment of each token
+  uint8_t rank[KF_MAXN];                // rank among its cluster's tokens in its chunk
+  uint16_t mem[KF_MAXN];                // tokens grouped by cluster, in token order
+  uint16_t pre[KF_MAXN / 64][KM_MAXK];  // per chunk counts, then exclusive prefixes
+  int off[KM_MAXK];
+  int cnt[KM_MAXK];
+  int changed;
+};
+
+__global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk, const void* xv,
+                                                                  int bf16, int n, int k,
+                                                                  float* tab_k, float* tab_v,
+                                                                  int max_pat) {
+  extern __shared__ unsigned char km_raw[];
+  KfShared& sh = *reinterpret_cast<KfShared*>(km_raw);
+  const int kind = blockIdx.y;
+  const int64_t u = blockIdx.x;
+  const void* x = kind ? xv : xk;
+  float* tab = (kind ? tab_v : tab_k) + u * max_pat * D;
+  const int64_t xrow0 = u * (int64_t)n;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nch = (n + 63) / 64;
+
+  for (int i = tid; i < KM_MAXK * D; i += KF_THREADS) {
+    const int j = i / D, d = i % D;
+    sh.cent[j][d] = j < k ? (double)load_in(x, (xrow0 + (int64_t)j * n / k) * D + d, bf16) : 0.0;
+  }
+  __syncthreads();
+  for (int it = 0; it < KM_ITERS; ++it) {
+    if (tid == 0) sh.changed = 0;
+    __syncthreads();
+    int changed = 0;
+    for (int t = tid; t < n; t += KF_THREADS) {
+      const int64_t row = (xrow0 + t) * D;
+      int best = 0;
+      double bd = INFINITY;
+      for (int p0 = 0; p0 < k; p0 += KF_PC) {
+        double dist[KF_PC];
+#pragma unroll
+        for (int q = 0; q < KF_PC; ++q) dist[q] = 0.0;
+        // channels in blocks of 16; the next block's loads are in flight
+        // while this one is used
+        float xb[16], xn[16];
+        km_load16(x, row, bf16, xb);
+        for (int d0 = 0; d0 < D; d0 += 16) {
+          if (d0 + 16 < D) km_load16(x, row + d0 + 16, bf16, xn);
+#pragma unroll
+          for (int dd = 0; dd < 16; ++dd) {
+            const double xd = (double)xb[dd];
+#pragma unroll
+            for (int q = 0; q < KF_PC; ++q) {
+              const double diff = xd - sh.cent[p0 + q][d0 + dd];
+              dist[q] = dist[q] + diff * diff;
+            }
+          }
+#pragma unroll
+          for (int dd = 0; dd < 16; ++dd) xb[dd] = xn[dd];
+        }
+        // strict '<' in pattern order keeps the lowest index
+#pragma unroll
+        for (int q = 0; q < KF_PC; ++q)
+          if (p0 + q < k && dist[q] < bd) { bd = dist[q]; best = p0 + q; }
+      }
+      if (it == 0 || sh.a[t] != (uint8_t)best) changed = 1;
+      sh.a[t] = (uint8_t)best;
+    }
+    if (changed) atomicOr(&sh.changed, 1);
+    __syncthreads();
+    if (it > 0 && sh.changed == 0) break;
+    // per chunk: member counts per cluster and each token's rank among them
+    for (int c = wave; c < nch; c += KF_THREADS / 64) {
+      const int t = c * 64 + lane;
+      const int at = t < n ? sh.a[t] : -1;
+      int rank = 0;
+      for (int j = 0; j < k; ++j) {
+        const uint64_t m = __ballot(at == j);
+        if (at == j) rank = __popcll(m & ((1ull << lane) - 1ull));
+        if (lane == 0) sh.pre[c][j] = (uint16_t)__popcll(m);
+      }
+      if (t < n) sh.rank[t] = (uint8_t)rank;
+    }
+    __syncthreads();
+    if (tid < k) {
+      int acc = 0;
+      for (int c = 0; c < nch; ++c) {
+        const int v = sh.pre[c][tid];
+        sh.pre[c][tid] = (uint16_t)acc;
+        acc += v;
+      }
+      sh.cnt[tid] = acc;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int o = 0;
+      for (int j = 0; j < k; ++j) { sh.off[j] = o; o += sh.cnt[j]; }
+    }
+    __syncthreads();
+    for (int t = tid; t < n; t += KF_THREADS) {
+      const int j = sh.a[t];
+      sh.mem[sh.off[j] + sh.pre[t >> 6][j] + sh.rank[t]] = (uint16_t)t;
+    }
+    __syncthreads();
+    // centroid = member sum in token order / member count; empty keeps its centroid
+    for (int i = tid; i < k * D; i += KF_THREADS) {
+      const int j = i / D, d = i % D, c = sh.cnt[j];
+      if (c == 0) continue;
+      const uint16_t* m = sh.mem + sh.off[j];
+      // members in blocks of 8 (their loads issued together), summed in order
+      double acc = 0.0;
+      int e = 0;
+      for (; e + 8 <= c; e += 8) {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = load_in(x, (xrow0 + m[e + i]) * D + d, bf16);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc = acc + (double)v[i];
+      }
+      for (; e < c; ++e) acc = acc + (double)load_in(x, (xrow0 + m[e]) * D + d, bf16);
+      sh.cent[j][d] = acc / (double)c;
+    }
+    __syncthreads();
+  }
+  for (int i = tid; i < k * D; i += KF_THREADS) tab[i] = (float)sh.cent[i / D][i % D];
+}
+
 hipError_t launch_kmeans_pair(const void* xk, const void* xv, int bf16, int n_tok, int k,
                               float* tab_k, float* tab_v, int max_pat, int units, uint8_t* assign,
                               hipStream_t s) {
+  if (n_tok <= KF_MAXN && k <= KM_MAXK) {
+    const size_t lds = sizeof(KfShared);
+    static bool fast_attr = false;
+    if (!fast_attr) {
+      hipError_t e = hipFuncSetAttribute((const void*)kmeans_fast_kernel,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      fast_attr = true;
+    }
+    hipLaunchKernelGGL(kmeans_fast_kernel, dim3(units, 2), dim3(KF_THREADS), lds, s, xk, xv, bf16,
+                       n_tok, k, tab_k, tab_v, max_pat);
+    return hipGetLastError();
+  }
   size_t lds = sizeof(KmShared);
   static bool attr_set = false;
   if (!attr_set) {

@@ -1,0 +1,43 @@
+"""GPU pattern mining (kvq_init_patterns, PATTERN mode) against the oracle.
+
+The GPU k-means runs the oracle's Lloyd iteration in binary64 with the same
+operation order (channel-ordered distance sums, lowest index on ties, member
+sums in token order), so the fp32 pattern tables must be bit-identical.
+Cases cover prefixes that end inside a 64-token chunk, 1 / 17 / 64 patterns
+(partial and several 16-pattern distance passes), the largest prefix of the
+block-parallel kernel (8192 tokens) and one beyond it, which takes the
+one-block-per-unit kernel.
+"""
+import numpy as np
+import pytest
+import torch
+
+from bit_kv_cache_encode_amd import synth
+from parity_util import gpu_tab, make_pair, to_dev, to_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("n,P,bf16", [
+    (100, 1, True),
+    (300, 17, False),
+    (777, 64, True),
+    (2048, 32, True),
+    (8192, 24, True),
+    (8193, 8, True),
+])
+def test_kmeans_tables_bit_exact(n, P, bf16):
+    B, Hq, H = 1, 4, 2
+    gpu, ref, dt = make_pair(B, Hq, H, n, max_patterns=max(P, 8), bf16=bf16)
+    k = synth.k_vectors(B, H, n, 128, seed=synth.seed_for("k") + n)
+    v = synth.v_vectors(B, H, n, 128, seed=synth.seed_for("v") + n)
+    assert ref.init_patterns(to_oracle(k, bf16), to_oracle(v, bf16), P) == 0
+    print(f"k-means n={n} P={P} bf16={bf16}", flush=True)
+    gpu.init_patterns(to_dev(k, dt), to_dev(v, dt), P)
+    torch.cuda.synchronize()
+    assert gpu.n_patterns == P
+    for which in (0, 1):
+        g = gpu_tab(gpu, which)[:, :P]
+        r = ref.patterns(which)[:, :P]
+        assert np.array_equal(g.view(np.uint32), r.view(np.uint32)), \
+            f"{'KV'[which]} table differs in {int((g != r).sum())} of {g.size} values"
