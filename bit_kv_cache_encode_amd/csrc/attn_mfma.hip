@@ -79,12 +79,19 @@ __host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes
 // NPB == 0 -> LDS atomics (or no pattern term at all for KVarN).
 // QLO: q needs a binary16 lo part (binary32 queries, or the KVarN rotation);
 // a bfloat16 query is a single binary16 operand (see the exponent choice).
-template <int BITS, int NG, bool KVARN, int NPB, bool QLO>
+// NGS: quantization groups stored per token.  NG = NGS normally; NG = 2 NGS
+// splits each stored group into two virtual groups that share its (s, z)
+// word (s (q_a . c_a + q_b . c_b) = s q_a . c_a + s q_b . c_b, and likewise
+// for z and for p s, p z on the V side), which fills the 16 MFMA rows with
+// 4 q-heads at G = 64 instead of leaving half of an 8-head row block idle.
+template <int BITS, int NG, int NGS, bool KVARN, int NPB, bool QLO>
 __global__ void __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_mfma_kernel(AttnArgs a) {
   static_assert(!(KVARN && NPB), "KVarN has no pattern term");
-  using TS = TileShape<BITS, NG, KVARN>;
-  constexpr int G = D / NG;            // channels per group
+  static_assert(NG == NGS || NG == 2 * NGS, "a stored group spans one or two virtual groups");
+  using TS = TileShape<BITS, NGS, KVARN>;
+  constexpr int VPS = NG / NGS;        // virtual groups per stored group
+  constexpr int G = D / NG;            // channels per (virtual) group
   constexpr int HB = 16 / NG;          // heads per row block
   constexpr int CPG = 16 / NG;         // PV columns per group
   constexpr int SPL = 4 / NG;          // heads per lane in a 16x16 output
@@ -135,8 +142,8 @@ attn_mfma_kernel(AttnArgs a) {
 
   const uint8_t* kcodes = a.r.codes[0] + (int64_t)u * a.tcap * TS::KREC;
   const uint8_t* vcodes = a.r.codes[1] + (int64_t)u * a.tcap * TS::KREC;
-  const uint8_t* ksz = (const uint8_t*)(a.r.sz[0] + (int64_t)u * a.tcap * NG);
-  const uint8_t* vsz = (const uint8_t*)(a.r.sz[1] + (int64_t)u * a.tcap * NG);
+  const uint8_t* ksz = (const uint8_t*)(a.r.sz[0] + (int64_t)u * a.tcap * NGS);
+  const uint8_t* vsz = (const uint8_t*)(a.r.sz[1] + (int64_t)u * a.tcap * NGS);
   const uint8_t* kix_src = KVARN ? (const uint8_t*)(a.r.t16[0] + (int64_t)u * a.tcap)
                                  : a.r.idx[0] + (int64_t)u * a.tcap;
   const uint8_t* vix_src = KVARN ? (const uint8_t*)(a.r.t16[1] + (int64_t)u * a.tcap)
@@ -152,8 +159,8 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < TS::R_VC; ++r) rvc[r] = vc[lane + 64 * r];
     if (lane < TS::P_KS) {
-      rks = ((const u32x4*)(ksz + (int64_t)tile * NG * 4))[lane];
-      rvs = ((const u32x4*)(vsz + (int64_t)tile * NG * 4))[lane];
+      rks = ((const u32x4*)(ksz + (int64_t)tile * NGS * 4))[lane];
+      rvs = ((const u32x4*)(vsz + (int64_t)tile * NGS * 4))[lane];
     }
     const int ix_bytes = KVARN ? 2 : 1;
     if (lane < TS::P_IX) rix = ((const u32x4*)(kix_src + (int64_t)tile * ix_bytes))[lane];
@@ -477,16 +484,17 @@ attn_mfma_kernel(AttnArgs a) {
     for (int nb = 0; nb < 4; ++nb) {
       const int t64 = 16 * nb + n16;
       const bool valid = FULL || t64 < nvalid;
-      uint32_t kszw[NG];
+      uint32_t kszw[NG];   // (s, z) word of each virtual group
       {
-        const uint32_t* kszp = (const uint32_t*)(tb + TS::O_KS) + t64 * NG;
-        if (NG == 4) {
+        const uint32_t* kszp = (const uint32_t*)(tb + TS::O_KS) + t64 * NGS;
+        if (NGS == 4) {
           const u32x4 k4 = *(const u32x4*)kszp;
 #pragma unroll
           for (int g = 0; g < NG; ++g) kszw[g] = k4[g];
         } else {
           const uint2 k2 = *(const uint2*)kszp;
-          kszw[0] = k2.x; kszw[1 % NG] = k2.y;
+#pragma unroll
+          for (int g = 0; g < NG; ++g) kszw[g] = g / VPS == 0 ? k2.x : k2.y;
         }
       }
       float tk = 1.0f;
@@ -564,15 +572,15 @@ attn_mfma_kernel(AttnArgs a) {
       const bool valid = FULL || t64 < nvalid;
       uint32_t vszz[NG];
       if constexpr (NPB == 0) {
-        const uint32_t* vszp = (const uint32_t*)(tb + TS::O_VS) + t64 * NG;
-        if (NG == 4) {
+        const uint32_t* vszp = (const uint32_t*)(tb + TS::O_VS) + t64 * NGS;
+        if (NGS == 4) {
           const u32x4 v4 = *(const u32x4*)vszp;
 #pragma unroll
           for (int g = 0; g < NG; ++g) vszz[g] = valid ? v4[g] : 0u;
         } else {
           const uint2 v2 = *(const uint2*)vszp;
-          vszz[0] = valid ? v2.x : 0u;
-          vszz[1 % NG] = valid ? v2.y : 0u;
+#pragma unroll
+          for (int g = 0; g < NG; ++g) vszz[g] = valid ? (g / VPS == 0 ? v2.x : v2.y) : 0u;
         }
       }
       float tv = 1.0f;
@@ -606,7 +614,7 @@ attn_mfma_kernel(AttnArgs a) {
       vk[nb] = vix;
       // V group scale of this token for group j (lanes j < NG)
       if (j < NG) {
-        const uint32_t sw = ((const uint32_t*)(tb + TS::O_VS))[t64 * NG + j];
+        const uint32_t sw = ((const uint32_t*)(tb + TS::O_VS))[t64 * NGS + j / VPS];
         s_vs[j * VS_STRIDE + t64] = __builtin_bit_cast(_Float16, (uint16_t)(valid ? sw & 0xFFFFu : 0u));
       }
     }
@@ -681,11 +689,11 @@ attn_mfma_kernel(AttnArgs a) {
         }
         // B = zero points z_tg (binary16, the high half of each (s, z) word)
         // of the same tokens for group n16 % NG; tokens past the end read 0
-        const uint32_t* zw = (const uint32_t*)(tb + TS::O_VS) + (32 * kb + 8 * j) * NG + n16 % NG;
+        const uint32_t* zw = (const uint32_t*)(tb + TS::O_VS) + (32 * kb + 8 * j) * NGS + (n16 % NG) / VPS;
         u32x4 bz;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          uint32_t w0 = zw[(2 * q) * NG], w1 = zw[(2 * q + 1) * NG];
+          uint32_t w0 = zw[(2 * q) * NGS], w1 = zw[(2 * q + 1) * NGS];
           if (!FULL) {
             w0 = 32 * kb + 8 * j + 2 * q < nvalid ? w0 : 0u;
             w1 = 32 * kb + 8 * j + 2 * q + 1 < nvalid ? w1 : 0u;
@@ -928,37 +936,37 @@ attn_mfma_kernel(AttnArgs a) {
   if (tid == 0) __hip_atomic_store(&a.r.cnt[cu], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int BITS, int NG, bool KVARN, int NPB, bool QLO>
+template <int BITS, int NG, int NGS, bool KVARN, int NPB, bool QLO>
 static hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
   constexpr int HB = 16 / NG;
   const int npat = pad_pat(KVARN ? 0 : a.n_pat);
-  const MfLds L = mf_lds(HB, NG, npat, TileShape<BITS, NG, KVARN>::BYTES, 16 * NPB);
+  const MfLds L = mf_lds(HB, NG, npat, TileShape<BITS, NGS, KVARN>::BYTES, 16 * NPB);
   static int attr = 0;
   if (L.total > attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel<BITS, NG, KVARN, NPB, QLO>,
+    hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel<BITS, NG, NGS, KVARN, NPB, QLO>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, L.total);
     if (e != hipSuccess) return e;
     attr = L.total;
   }
-  const int n_hb = (a.gq + 16 / NG - 1) / (16 / NG);
-  hipLaunchKernelGGL((attn_mfma_kernel<BITS, NG, KVARN, NPB, QLO>), dim3(a.B * a.Hkv * a.splits * n_hb),
-                     dim3(MF_THREADS), L.total, s, a);
+  const int n_hb = (a.gq + HB - 1) / HB;
+  hipLaunchKernelGGL((attn_mfma_kernel<BITS, NG, NGS, KVARN, NPB, QLO>),
+                     dim3(a.B * a.Hkv * a.splits * n_hb), dim3(MF_THREADS), L.total, s, a);
   return hipGetLastError();
 }
 
-template <int BITS, int NG, bool QLO>
+template <int BITS, int NG, int NGS, bool QLO>
 static hipError_t launch_pattern(const AttnArgs& a, hipStream_t s) {
-  if (a.n_pat <= 0) return launch_one<BITS, NG, false, 0, QLO>(a, s);
-  if (a.n_pat <= 16) return launch_one<BITS, NG, false, 1, QLO>(a, s);
-  if (a.n_pat <= 32) return launch_one<BITS, NG, false, 2, QLO>(a, s);
-  if (a.n_pat <= 64) return launch_one<BITS, NG, false, 4, QLO>(a, s);
-  return launch_one<BITS, NG, false, 0, QLO>(a, s);
+  if (a.n_pat <= 0) return launch_one<BITS, NG, NGS, false, 0, QLO>(a, s);
+  if (a.n_pat <= 16) return launch_one<BITS, NG, NGS, false, 1, QLO>(a, s);
+  if (a.n_pat <= 32) return launch_one<BITS, NG, NGS, false, 2, QLO>(a, s);
+  if (a.n_pat <= 64) return launch_one<BITS, NG, NGS, false, 4, QLO>(a, s);
+  return launch_one<BITS, NG, NGS, false, 0, QLO>(a, s);
 }
 
-template <int BITS, int NG>
+template <int BITS, int NG, int NGS>
 static hipError_t launch_bits_group(const AttnArgs& a, hipStream_t s) {
-  if (a.mode == KVQ_MODE_KVARN) return launch_one<BITS, NG, true, 0, true>(a, s);
-  return a.bf16 ? launch_pattern<BITS, NG, false>(a, s) : launch_pattern<BITS, NG, true>(a, s);
+  if (a.mode == KVQ_MODE_KVARN) return launch_one<BITS, NG, NGS, true, 0, true>(a, s);
+  return a.bf16 ? launch_pattern<BITS, NG, NGS, false>(a, s) : launch_pattern<BITS, NG, NGS, true>(a, s);
 }
 
 bool mfma_attention_supported(int bits, int group, int gq) {
@@ -969,9 +977,12 @@ bool mfma_attention_supported(int bits, int group, int gq) {
   return false;
 }
 
+// Row blocks: 4 q-heads x 4 groups at G = 32; at G = 64, 4 q-heads x 4 virtual
+// half-groups when a unit has at most 4 q-heads, else 8 q-heads x 2 groups.
 hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t s) {
-  if (a.group == 32) return a.bits == 2 ? launch_bits_group<2, 4>(a, s) : launch_bits_group<4, 4>(a, s);
-  return a.bits == 2 ? launch_bits_group<2, 2>(a, s) : launch_bits_group<4, 2>(a, s);
+  if (a.group == 32) return a.bits == 2 ? launch_bits_group<2, 4, 4>(a, s) : launch_bits_group<4, 4, 4>(a, s);
+  if (a.gq <= 4) return a.bits == 2 ? launch_bits_group<2, 4, 2>(a, s) : launch_bits_group<4, 4, 2>(a, s);
+  return a.bits == 2 ? launch_bits_group<2, 2, 2>(a, s) : launch_bits_group<4, 2, 2>(a, s);
 }
 
 }  // namespace kvq

@@ -112,6 +112,12 @@ def test_decode_step_4bit_gqa8_binary32():
     _run(1, 16, 2, 500, 10, bits=4, group=64, P=40, W=6, bf16=False, seed_off=5)
 
 
+def test_decode_step_group64_gqa4():
+    """2-bit group 64 with 4 q-heads per kv-head (each stored group read as two
+    virtual groups sharing its scale and zero point)."""
+    _run(2, 8, 2, 350, 8, group=64, P=20, W=4, seed_off=11)
+
+
 def test_decode_step_gqa7_two_calls():
     """7 q-heads per kv-head at group 32 (two q-head blocks) takes the
     two-call path; results as the separate calls."""

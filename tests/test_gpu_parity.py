@@ -201,6 +201,8 @@ def test_determinism_and_checkpoint():
 @pytest.mark.parametrize("bits,group,gq,mode", [
     (2, 32, 4, "pattern"), (2, 32, 1, "pattern"), (4, 64, 4, "pattern"), (4, 64, 8, "pattern"),
     (2, 64, 2, "pattern"), (4, 32, 3, "pattern"), (2, 32, 4, "kvarn"), (4, 64, 8, "kvarn"),
+    # G = 64 with at most 4 q-heads: virtual half-groups fill the row block
+    (2, 64, 4, "kvarn"), (2, 64, 3, "pattern"),
     # more q-heads per kv-head than one MFMA row block holds: further head blocks
     (2, 32, 7, "pattern"), (4, 32, 8, "pattern"), (2, 64, 12, "pattern"), (2, 32, 16, "pattern"),
     (2, 32, 6, "kvarn")])
