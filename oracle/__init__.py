@@ -42,7 +42,7 @@ class _Cfg(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "batch", "n_q_heads", "n_kv_heads", "head_dim", "max_tokens",
         "bits", "group", "mode", "max_patterns", "pattern_window")] + [
-        ("v_alpha", C.c_double), ("in_dtype", C.c_int32)]
+        ("v_alpha", C.c_double), ("in_dtype", C.c_int32), ("shared_patterns", C.c_int32)]
 
 
 _lib = None
@@ -146,13 +146,14 @@ class RefCache:
 
     def __init__(self, batch, n_q_heads, n_kv_heads, head_dim, max_tokens, bits=2, group=32,
                  mode=PATTERN, max_patterns=64, pattern_window=128, v_alpha=0.05,
-                 in_dtype=IN_F32):
+                 in_dtype=IN_F32, shared_patterns=False):
         self.cfg = _Cfg(batch, n_q_heads, n_kv_heads, head_dim, max_tokens, bits, group, mode,
-                        max_patterns, pattern_window, v_alpha, in_dtype)
+                        max_patterns, pattern_window, v_alpha, in_dtype, int(shared_patterns))
         self._h = lib().kvqref_new(C.byref(self.cfg))
         if not self._h:
             raise ValueError("invalid oracle configuration")
         self.U = batch * n_kv_heads
+        self.PU = n_kv_heads if shared_patterns else self.U   # pattern-table units
         self.tcap = (max_tokens + VTILE - 1) // VTILE * VTILE
 
     def __del__(self):
@@ -239,7 +240,7 @@ class RefCache:
 
     def patterns(self, which):
         return self.region("kv"[which] + "_pat").view(np.float32).reshape(
-            self.U, self.cfg.max_patterns, self.cfg.head_dim)
+            self.PU, self.cfg.max_patterns, self.cfg.head_dim)
 
     def scales(self, which):
         return self.region("kv"[which] + "_scale").view(np.float32).reshape(
@@ -256,7 +257,7 @@ def attn_exact(k, v, q, n_q_heads, sm_scale=0.0):
     v = np.ascontiguousarray(v, dtype=np.float32)
     q = np.ascontiguousarray(q, dtype=np.float32)
     B, H, T, D = k.shape
-    cfg = _Cfg(B, n_q_heads, H, D, T, 2, D, PATTERN, 0, 0, 0.0, IN_F32)
+    cfg = _Cfg(B, n_q_heads, H, D, T, 2, D, PATTERN, 0, 0, 0.0, IN_F32, 0)
     out = np.zeros((B, n_q_heads, D), np.float32)
     rc = lib().kvqref_attn_exact(C.byref(cfg), _ptr(k), _ptr(v), T, _ptr(q), _ptr(out), sm_scale)
     if rc:

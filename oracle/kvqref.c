@@ -28,7 +28,8 @@
  *      the V threshold off (V always uses its nearest pattern).  K has no
  *      threshold.  A rejected V vector stores index NONE (0xFF) and
  *      quantises the raw vector.
- *  R9  Pattern tables are per (batch, kv-head) unit, at most 255 patterns.
+ *  R9  Pattern tables are per (batch, kv-head) unit, at most 255 patterns
+ *      (per kv-head with shared_patterns, R16).
  *  R10 The Chebyshev window covers decode appends only; its centre
  *      fl(fl(lo + hi) * 0.5) is appended after the window's last token is
  *      encoded and serves later tokens; when the table is full the centre is
@@ -52,6 +53,15 @@
  *      words, each holding 32/n consecutive tokens of one channel (token k of
  *      the word at bit n*k); word w of channel d sits at (w*D + d)*4 bytes
  *      of the tile (all channels' first words, then their second words...).
+ *  R16 Batch-shared tables (shared_patterns, PATTERN mode): the pattern
+ *      memory estimate of PatternKV's memory analysis carries no batch factor
+ *      (its share of the KV memory falls as 1/B) and one decode pattern per
+ *      G_pattern steps gives a 1/(B G_pattern) share, i.e. the table and the
+ *      window belong to the kv-head.  k-means then runs per kv-head over the
+ *      B prefixes pooled batch-major (row b*n_tok + t), the window's min / max
+ *      run over every sequence's decode vectors of the window, and each
+ *      closure appends one centre per kv-head; every (batch, kv-head) unit
+ *      encodes and reconstructs against its kv-head's table.
  */
 #include "kvqref.h"
 
@@ -65,7 +75,7 @@
 
 struct kvqref_cache {
   kvqref_cfg cfg;
-  int32_t D, U, NG, tcap, kbytes, vtile;
+  int32_t D, U, PU, NG, tcap, kbytes, vtile;   /* PU: pattern-table units */
   int32_t n_tokens, n_patterns, win_count, dropped;
   int32_t thr_on;
   float rho;
@@ -302,12 +312,19 @@ static int valid_cfg(const kvqref_cfg* g) {
   if (g->pattern_window < 0) return 0;
   if (g->in_dtype != KVQREF_IN_F32 && g->in_dtype != KVQREF_IN_BF16) return 0;
   if (g->v_alpha >= 0.5) return 0;
+  if (g->shared_patterns != 0 && g->shared_patterns != 1) return 0;
+  if (g->shared_patterns && g->mode != KVQREF_PATTERN) return 0;
   return 1;
+}
+
+/* pattern-table (and window) unit of (batch, kv-head) unit u */
+static int64_t pu_of(const kvqref_cache* c, int64_t u) {
+  return c->cfg.shared_patterns ? u % c->cfg.n_kv_heads : u;
 }
 
 static void reset_window(kvqref_cache* c) {
   for (int k = 0; k < 2; ++k)
-    for (int64_t i = 0; i < (int64_t)c->U * c->D; ++i) {
+    for (int64_t i = 0; i < (int64_t)c->PU * c->D; ++i) {
       c->wlo[k][i] = INFINITY;
       c->whi[k][i] = -INFINITY;
     }
@@ -320,6 +337,7 @@ kvqref_cache* kvqref_new(const kvqref_cfg* cfg) {
   c->cfg = *cfg;
   c->D = cfg->head_dim;
   c->U = cfg->batch * cfg->n_kv_heads;
+  c->PU = cfg->shared_patterns ? cfg->n_kv_heads : c->U;
   c->NG = cfg->head_dim / cfg->group;
   c->tcap = (cfg->max_tokens + KVQREF_VTILE - 1) / KVQREF_VTILE * KVQREF_VTILE;
   c->kbytes = c->D * cfg->bits / 8;
@@ -334,9 +352,9 @@ kvqref_cache* kvqref_new(const kvqref_cfg* cfg) {
     memset(c->idx[k], KVQREF_NONE, (size_t)(U * T));
     c->t16[k] = (uint16_t*)calloc((size_t)(U * T), 2);
     c->tie[k] = (uint8_t*)calloc((size_t)(U * T * D), 1);
-    c->pat[k] = (float*)calloc((size_t)(U * (cfg->max_patterns ? cfg->max_patterns : 1) * D), 4);
-    c->wlo[k] = (float*)malloc((size_t)(U * D) * 4);
-    c->whi[k] = (float*)malloc((size_t)(U * D) * 4);
+    c->pat[k] = (float*)calloc((size_t)(c->PU * (cfg->max_patterns ? cfg->max_patterns : 1) * D), 4);
+    c->wlo[k] = (float*)malloc((size_t)(c->PU * D) * 4);
+    c->whi[k] = (float*)malloc((size_t)(c->PU * D) * 4);
     c->cscale[k] = (float*)malloc((size_t)(U * D) * 4);
     for (int64_t i = 0; i < U * D; ++i) c->cscale[k][i] = 1.0f;
   }
@@ -412,7 +430,7 @@ static void store_quantised(kvqref_cache* c, int kind, int64_t u, int32_t t, con
  * section 3.3 V threshold, then Eq 1 on the residual. */
 static void encode_pattern_vec(kvqref_cache* c, int kind, int64_t u, int32_t t, const float* x) {
   int D = c->D;
-  const float* pats = c->pat[kind] + u * (int64_t)c->cfg.max_patterns * D;
+  const float* pats = c->pat[kind] + pu_of(c, u) * (int64_t)c->cfg.max_patterns * D;
   float e = 0.0f;
   int32_t k = kvqref_nearest(x, pats, c->n_patterns, D, &e);
   if (kind == 1 && c->thr_on && k != KVQREF_NONE) {
@@ -470,8 +488,8 @@ int kvqref_set_patterns(kvqref_cache* c, const float* k_tab, const float* v_tab,
   }
   if (n < 0 || n > c->cfg.max_patterns) return -1;
   for (int k = 0; k < 2; ++k)
-    for (int64_t u = 0; u < U; ++u)
-      memcpy(c->pat[k] + u * c->cfg.max_patterns * D, tabs[k] + u * n * D, sizeof(float) * (size_t)(n * D));
+    for (int64_t p = 0; p < c->PU; ++p)
+      memcpy(c->pat[k] + p * c->cfg.max_patterns * D, tabs[k] + p * n * D, sizeof(float) * (size_t)(n * D));
   c->n_patterns = n;
   reset_window(c);
   return 0;
@@ -512,11 +530,21 @@ int kvqref_init_patterns(kvqref_cache* c, const void* k, const void* v, int32_t 
     return 0;
   }
   if (n_pat < 0 || n_pat > c->cfg.max_patterns) { free(rows); return -1; }
+  /* k-means rows of pattern unit p: its own prefix, or (shared tables) the
+   * prefixes of kv-head p in every sequence, batch-major */
+  const int64_t H = c->cfg.n_kv_heads, nb = c->cfg.shared_patterns ? c->cfg.batch : 1;
+  free(rows);
+  rows = (float*)malloc(sizeof(float) * (size_t)(nb * n_tok * D));
   for (int kind = 0; kind < 2; ++kind)
-    for (int64_t u = 0; u < U; ++u) {
-      for (int64_t t = 0; t < n_tok; ++t) load_vec(c, src[kind], u * n_tok + t, rows + t * D);
+    for (int64_t p = 0; p < c->PU; ++p) {
+      for (int64_t b = 0; b < nb; ++b)
+        for (int64_t t = 0; t < n_tok; ++t) {
+          const int64_t u = c->cfg.shared_patterns ? b * H + p : p;
+          load_vec(c, src[kind], u * n_tok + t, rows + (b * n_tok + t) * D);
+        }
       if (n_pat > 0)
-        kvqref_kmeans(rows, n_tok, (int32_t)D, n_pat, c->pat[kind] + u * c->cfg.max_patterns * D, NULL);
+        kvqref_kmeans(rows, (int32_t)(nb * n_tok), (int32_t)D, n_pat,
+                      c->pat[kind] + p * c->cfg.max_patterns * D, NULL);
     }
   free(rows);
   c->n_patterns = n_pat;
@@ -540,8 +568,8 @@ int kvqref_encode_append(kvqref_cache* c, const void* k, const void* v, int32_t 
         if (c->cfg.mode == KVQREF_PATTERN) encode_pattern_vec(c, kind, u, t, x);
         else encode_kvarn_vec(c, kind, u, t, x);
         if (window) {
-          float* lo = c->wlo[kind] + u * D;
-          float* hi = c->whi[kind] + u * D;
+          float* lo = c->wlo[kind] + pu_of(c, u) * D;
+          float* hi = c->whi[kind] + pu_of(c, u) * D;
           for (int i = 0; i < D; ++i) {
             if (x[i] < lo[i]) lo[i] = x[i];
             if (x[i] > hi[i]) hi[i] = x[i];
@@ -551,10 +579,10 @@ int kvqref_encode_append(kvqref_cache* c, const void* k, const void* v, int32_t 
     if (window && ++c->win_count == c->cfg.pattern_window) {
       if (c->n_patterns < c->cfg.max_patterns) {
         for (int kind = 0; kind < 2; ++kind)
-          for (int64_t u = 0; u < U; ++u) {
-            float* m = c->pat[kind] + (u * c->cfg.max_patterns + c->n_patterns) * D;
+          for (int64_t p = 0; p < c->PU; ++p) {
+            float* m = c->pat[kind] + (p * c->cfg.max_patterns + c->n_patterns) * D;
             for (int i = 0; i < D; ++i) {
-              float s = c->wlo[kind][u * D + i] + c->whi[kind][u * D + i];
+              float s = c->wlo[kind][p * D + i] + c->whi[kind][p * D + i];
               m[i] = s * 0.5f;
             }
           }
@@ -577,7 +605,7 @@ static void dequant_vec(const kvqref_cache* c, int kind, int64_t u, int32_t t, f
   if (c->cfg.mode == KVQREF_PATTERN) {
     int k = c->idx[kind][u * c->tcap + t];
     const float* m = (k == KVQREF_NONE) ? NULL
-                     : c->pat[kind] + (u * c->cfg.max_patterns + k) * (int64_t)D;
+                     : c->pat[kind] + (pu_of(c, u) * c->cfg.max_patterns + k) * (int64_t)D;
     for (int d = 0; d < D; ++d) {
       float s = kvqref_f16_to_f32(sz[(d / G) * 2]);
       float z = kvqref_f16_to_f32(sz[(d / G) * 2 + 1]);
@@ -695,9 +723,9 @@ const void* kvqref_region(const kvqref_cache* c, const char* name, int64_t* byte
   if (!strcmp(r, "idx")) { *bytes = U * T; return c->idx[kind]; }
   if (!strcmp(r, "t16")) { *bytes = U * T * 2; return c->t16[kind]; }
   if (!strcmp(r, "tie")) { *bytes = U * T * D; return c->tie[kind]; }
-  if (!strcmp(r, "pat")) { *bytes = U * M * D * 4; return c->pat[kind]; }
-  if (!strcmp(r, "wlo")) { *bytes = U * D * 4; return c->wlo[kind]; }
-  if (!strcmp(r, "whi")) { *bytes = U * D * 4; return c->whi[kind]; }
+  if (!strcmp(r, "pat")) { *bytes = c->PU * M * D * 4; return c->pat[kind]; }
+  if (!strcmp(r, "wlo")) { *bytes = c->PU * D * 4; return c->wlo[kind]; }
+  if (!strcmp(r, "whi")) { *bytes = c->PU * D * 4; return c->whi[kind]; }
   if (!strcmp(r, "scale")) { *bytes = U * D * 4; return c->cscale[kind]; }
   *bytes = 0;
   return NULL;

@@ -40,6 +40,7 @@ typedef struct {
   int32_t bits, group, mode, max_patterns, pattern_window;
   double v_alpha;                 /* <= 0: V threshold disabled */
   int32_t in_dtype;
+  int32_t shared_patterns;        /* PATTERN: 1 = one table and window per kv-head for the batch */
 } kvqref_cfg;
 
 typedef struct kvqref_cache kvqref_cache;
@@ -47,12 +48,14 @@ typedef struct kvqref_cache kvqref_cache;
 kvqref_cache* kvqref_new(const kvqref_cfg* cfg);
 void kvqref_free(kvqref_cache* c);
 
-/* Explicit pattern tables [B][Hkv][n][D] (PATTERN) or channel scales
- * [B][Hkv][D] (KVARN, n ignored).  fp32 host arrays. */
+/* Explicit pattern tables [B][Hkv][n][D] (PATTERN; [Hkv][n][D] with
+ * shared_patterns) or channel scales [B][Hkv][D] (KVARN, n ignored).  fp32
+ * host arrays. */
 int kvqref_set_patterns(kvqref_cache* c, const float* k_tab, const float* v_tab, int32_t n);
 
-/* Prefill mining: per-unit k-means (PATTERN) or channel scales (KVARN) over
- * [B][Hkv][n_tok][D] inputs of the configured dtype. */
+/* Prefill mining: per-unit k-means (PATTERN; per kv-head over the B
+ * prefixes pooled batch-major with shared_patterns) or channel scales (KVARN)
+ * over [B][Hkv][n_tok][D] inputs of the configured dtype. */
 int kvqref_init_patterns(kvqref_cache* c, const void* k, const void* v, int32_t n_tok,
                          int32_t n_patterns);
 
