@@ -28,7 +28,7 @@ class kvq_config(C.Structure):
                 ("head_dim", C.c_int32), ("max_tokens", C.c_int32), ("bits", C.c_int32),
                 ("group", C.c_int32), ("mode", C.c_int32), ("max_patterns", C.c_int32),
                 ("pattern_window", C.c_int32), ("v_alpha", C.c_float), ("in_dtype", C.c_int32),
-                ("max_splits", C.c_int32)]
+                ("max_splits", C.c_int32), ("shared_patterns", C.c_int32)]
 
 
 class kvq_layout(C.Structure):

@@ -26,26 +26,32 @@ class KVCache:
     """A packed 2/4-bit K/V cache for one attention layer.
 
     mode: "pattern" (PatternKV residual encode) or "kvarn" (Hadamard +
-    dual-axis normalisation encode).  Shapes follow include/kvq.h.
+    dual-axis normalisation encode).  shared_patterns (pattern mode): one
+    pattern table and Chebyshev window per kv-head for the whole batch.
+    Shapes follow include/kvq.h.
     """
 
     def __init__(self, batch: int, n_q_heads: int, n_kv_heads: int, max_tokens: int,
                  head_dim: int = 128, bits: int = 2, group: int = 32, mode: str = "pattern",
                  max_patterns: int = 64, pattern_window: int = 128, v_alpha: float = 0.05,
                  in_dtype: torch.dtype = torch.bfloat16, max_splits: int = 0,
-                 device: str | torch.device = "cuda", buffer: torch.Tensor | None = None):
+                 device: str | torch.device = "cuda", buffer: torch.Tensor | None = None,
+                 shared_patterns: bool = False):
         if in_dtype not in _DT:
             raise ValueError("in_dtype must be torch.float32 or torch.bfloat16")
         m = {"pattern": B.MODE_PATTERN, "kvarn": B.MODE_KVARN}[mode]
         self.cfg = B.kvq_config(batch, n_q_heads, n_kv_heads, head_dim, max_tokens, bits, group,
                                 m, max_patterns, pattern_window, v_alpha, _DT[in_dtype],
-                                max_splits)
+                                max_splits, int(shared_patterns))
         self.layout = B.kvq_layout_of(self.cfg)
         self.device = torch.device(device)
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
         self.in_dtype = in_dtype
         self.mode = mode
+        self.shared_patterns = bool(shared_patterns)
+        # pattern-table units: one per kv-head when shared, else per (batch, kv-head)
+        self.pattern_units = n_kv_heads if shared_patterns else batch * n_kv_heads
         if buffer is None:
             buffer = torch.zeros(self.layout.total, dtype=torch.uint8, device=self.device)
         if buffer.numel() < self.layout.total or buffer.dtype != torch.uint8:
@@ -71,7 +77,18 @@ class KVCache:
         for t in (k_tab, v_tab):
             if t.device != self.device or t.dtype != torch.float32 or not t.is_contiguous():
                 raise ValueError("pattern tables must be contiguous fp32 on the cache device")
-        n = k_tab.shape[2] if self.mode == "pattern" else 0
+        c = self.cfg
+        if self.mode == "pattern":
+            lead = (c.n_kv_heads,) if self.shared_patterns else (c.batch, c.n_kv_heads)
+            shp = tuple(k_tab.shape)
+            if self.shared_patterns and len(shp) == 4 and shp[0] == 1:
+                shp = shp[1:]
+            if shp[:-2] != lead or shp[-1] != c.head_dim or tuple(v_tab.shape) != tuple(k_tab.shape):
+                raise ValueError(f"pattern tables: expected {lead} + (n, {c.head_dim}), got "
+                                 f"{tuple(k_tab.shape)} / {tuple(v_tab.shape)}")
+            n = shp[-2]
+        else:
+            n = 0
         B.check("kvq_set_patterns", B.kvq_set_patterns(self.c, _ptr(k_tab), _ptr(v_tab), n,
                                                        _stream(self.device)))
 

@@ -88,7 +88,7 @@ __global__ void __launch_bounds__(AT_THREADS) attn_split_kernel(AttnArgs a) {
     sh.qsum[h][g] = s;
   }
   if (pattern) {
-    const float* mk = a.r.tab[0] + u * a.max_pat * D;
+    const float* mk = a.r.tab[0] + pat_unit(a.r, u) * a.max_pat * D;
     for (int i = tid; i < a.gq * a.n_pat; i += AT_THREADS) {
       int h = i / a.n_pat, j = i % a.n_pat;
       float s = 0.0f;
@@ -202,7 +202,7 @@ __global__ void __launch_bounds__(AT_THREADS) attn_split_kernel(AttnArgs a) {
   }
 
   // ---- epilogue: V pattern term, write the partial
-  const float* mv = a.r.tab[1] + u * a.max_pat * D;
+  const float* mv = a.r.tab[1] + pat_unit(a.r, u) * a.max_pat * D;
   for (int i = 0; i < MAX_GQ / 2; ++i) {
     int h = hh + 2 * i;
     if (h >= a.gq) continue;

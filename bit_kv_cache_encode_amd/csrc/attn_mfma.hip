@@ -193,7 +193,7 @@ attn_mfma_kernel(AttnArgs a) {
   // Completion is awaited before the merge reads them.
   const bool stage_mv = NPB > 0 && Lo.mv_rows > 0;
   if (stage_mv) {
-    const float* mv = a.r.tab[1] + (int64_t)u * a.max_pat * D;
+    const float* mv = a.r.tab[1] + pat_unit(a.r, u) * a.max_pat * D;
     const int n16b = min(n_pat, 16 * NPB) * (D / 4);
     for (int g = wave; g * 64 < n16b; g += MF_WAVES) {
       const int c = g * 64 + lane;
@@ -203,7 +203,7 @@ attn_mfma_kernel(AttnArgs a) {
     }
   }
   const int qm_j = tid >> 2, qm_part = tid & 3;
-  const float* mk = a.r.tab[0] + (int64_t)u * a.max_pat * D;
+  const float* mk = a.r.tab[0] + pat_unit(a.r, u) * a.max_pat * D;
   float4 mkr[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) mkr[k] = float4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -391,7 +391,7 @@ attn_mfma_kernel(AttnArgs a) {
     const float x0 = load_in(e.src[kind], uu * D + lane, e.bf16);
     const float x1 = load_in(e.src[kind], uu * D + lane + 64, e.bf16);
     float wl0 = 0.0f, wl1 = 0.0f, wh0 = 0.0f, wh1 = 0.0f;
-    if (e.win_update) {
+    if (e.win_update && !e.r.pat_h) {
       const float* win = e.r.win[kind] + uu * 2 * D;
       wl0 = win[lane]; wl1 = win[lane + 64];
       wh0 = win[D + lane]; wh1 = win[D + lane + 64];
@@ -404,7 +404,7 @@ attn_mfma_kernel(AttnArgs a) {
     token_append(e, kind, uu, e.t0, lane, x0, x1, wl0, wl1, wh0, wh1, c0, c1, w0, w1, kidx, t16);
     float m0 = 0.0f, m1 = 0.0f;
     if (kidx != KVQ_INDEX_NONE) {
-      const float* mrow = e.r.tab[kind] + (uu * e.max_pat + kidx) * D;
+      const float* mrow = e.r.tab[kind] + (pat_unit(e.r, uu) * e.max_pat + kidx) * D;
       m0 = mrow[lane];
       m1 = mrow[lane + 64];
     }
@@ -727,7 +727,7 @@ attn_mfma_kernel(AttnArgs a) {
   // the M^V rows staged in the prologue have landed once this wave's vector
   // memory operations are done (the barriers below publish them)
   if (stage_mv) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-  const float* mv = a.r.tab[1] + (int64_t)u * a.max_pat * D;
+  const float* mv = a.r.tab[1] + pat_unit(a.r, u) * a.max_pat * D;
   constexpr int MVR = NPB > 0 ? 16 * NPB : 1;
 #pragma unroll
   for (int s = 0; s < SPL; ++s) l_run[s] = row_sum16(l_run[s]);

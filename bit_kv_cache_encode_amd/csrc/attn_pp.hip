@@ -187,7 +187,7 @@ attn_pp_kernel(AttnArgs a) {
   // This thread's 32-channel slice of pattern row tid / 4 of M^K is loaded
   // with q, before anything waits.
   const int qm_j = tid >> 2, qm_part = tid & 3;
-  const float* mk = a.r.tab[0] + (int64_t)u * a.max_pat * D;
+  const float* mk = a.r.tab[0] + pat_unit(a.r, u) * a.max_pat * D;
   float4 mkr[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) mkr[k] = float4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -280,7 +280,7 @@ attn_pp_kernel(AttnArgs a) {
   const int n_steps = t_end > t_begin ? (t_end - t_begin + PP_PAIRS * TILE - 1) / (PP_PAIRS * TILE) + 1 : 0;
   // The V pattern rows of this thread's output channel d = tid % D are loaded
   // at loop exit, so that they arrive while the pairs merge.
-  const float* mv = a.r.tab[1] + (int64_t)u * a.max_pat * D;
+  const float* mv = a.r.tab[1] + pat_unit(a.r, u) * a.max_pat * D;
   constexpr int MVR = NPB > 0 ? 16 * NPB : 1;
   float mvr[MVR];
   // per-pair partial o[HB][D], over the staging

@@ -59,7 +59,7 @@ __global__ void __launch_bounds__(ENC_THREADS) encode_kernel(EncodeArgs a) {
   // The pattern table in the pass-0 row layout, when one pass covers it.
   const bool staged = a.mode == KVQ_MODE_PATTERN && a.n_pat > 0 && a.n_pat <= PAT_PASS;
   if (staged) {
-    const float* tab = a.r.tab[kind] + u * a.max_pat * D;
+    const float* tab = a.r.tab[kind] + pat_unit(a.r, u) * a.max_pat * D;
     const int S = dist_chunks(a.n_pat), ch = D / S;
     for (int i = threadIdx.x; i < PAT_PASS * ch; i += ENC_THREADS) {
       const int row = i / ch, c = i % ch, j = row / S, s = row % S;
@@ -133,10 +133,14 @@ __global__ void __launch_bounds__(ENC_THREADS) encode_kernel(EncodeArgs a) {
       const int d = threadIdx.x;
       float lo = sh.wlo[0][d], hi = sh.whi[0][d];
       for (int w = 1; w < ENC_WAVES; ++w) { lo = fminf(lo, sh.wlo[w][d]); hi = fmaxf(hi, sh.whi[w][d]); }
-      float* win = a.r.win[kind] + u * 2 * D;
-      lo = fminf(lo, win[d]);
-      hi = fmaxf(hi, win[D + d]);
-      if (a.win_close) {
+      float* win = a.r.win[kind] + pat_unit(a.r, u) * 2 * D;
+      if (a.r.pat_h) {
+        // batch-shared window: fold in with order-key atomics; closed later
+        atomicMin((int*)&win[d], f32_order_key(lo));
+        atomicMax((int*)&win[D + d], f32_order_key(hi));
+      } else if (a.win_close) {
+        lo = fminf(lo, win[d]);
+        hi = fmaxf(hi, win[D + d]);
         if (a.close_slot >= 0) {
           float s = lo + hi;
           a.r.tab[kind][(u * a.max_pat + a.close_slot) * D + d] = s * 0.5f;
@@ -144,8 +148,8 @@ __global__ void __launch_bounds__(ENC_THREADS) encode_kernel(EncodeArgs a) {
         win[d] = INFINITY;
         win[D + d] = -INFINITY;
       } else {
-        win[d] = lo;
-        win[D + d] = hi;
+        win[d] = fminf(lo, win[d]);
+        win[D + d] = fmaxf(hi, win[D + d]);
       }
     }
   }
@@ -191,7 +195,7 @@ encode_lane_kernel(EncodeArgs a) {
   const int s_begin = max(span0, a.t0), s_end = min(span0 + LANE_SPAN, t_end);
   const int n_pat = a.n_pat;
   {
-    const float* tab = a.r.tab[kind] + u * a.max_pat * D;
+    const float* tab = a.r.tab[kind] + pat_unit(a.r, u) * a.max_pat * D;
     for (int i = threadIdx.x; i < n_pat * D; i += LANE_WAVES * 64)
       s_tab[(i / D) * LROW + i % D] = tab[i];
   }
@@ -336,15 +340,15 @@ __global__ void __launch_bounds__(64) encode_token_kernel(EncodeArgs a) {
   const int64_t row = u * a.src_rows;
   const float x0 = load_in(a.src[kind], row * D + lane, a.bf16);
   const float x1 = load_in(a.src[kind], row * D + lane + 64, a.bf16);
-  float* win = a.r.win[kind] + u * 2 * D;
+  float* win = a.r.win[kind] + pat_unit(a.r, u) * 2 * D;
   float wl0 = 0.0f, wl1 = 0.0f, wh0 = 0.0f, wh1 = 0.0f;
-  if (a.win_update) {
+  if (a.win_update && !a.r.pat_h) {
     wl0 = win[lane]; wl1 = win[lane + 64];
     wh0 = win[D + lane]; wh1 = win[D + lane + 64];
   }
   const bool staged = a.mode == KVQ_MODE_PATTERN && a.n_pat > 0 && a.n_pat <= PAT_PASS;
   if (staged) {
-    const float4* tab4 = (const float4*)(a.r.tab[kind] + u * a.max_pat * D);
+    const float4* tab4 = (const float4*)(a.r.tab[kind] + pat_unit(a.r, u) * a.max_pat * D);
     const int n4 = a.n_pat * D / 4;
     float4 tr[TOK_TAB4];
 #pragma unroll

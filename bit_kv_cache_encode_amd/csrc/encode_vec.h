@@ -195,7 +195,7 @@ __device__ __forceinline__ void encode_vector(const EncodeArgs& a, int kind, int
                                               int64_t row, uint32_t& c0, uint32_t& c1,
                                               uint32_t& w0, uint32_t& w1, int& kidx,
                                               uint16_t& t16) {
-  const float* tab = a.r.tab[kind] + (a.mode == KVQ_MODE_PATTERN ? u * a.max_pat * D : u * D);
+  const float* tab = a.r.tab[kind] + (a.mode == KVQ_MODE_PATTERN ? pat_unit(a.r, u) * a.max_pat * D : u * D);
   kidx = KVQ_INDEX_NONE;
   t16 = 0;
   if (a.mode == KVQ_MODE_PATTERN) {
@@ -309,11 +309,13 @@ __device__ __forceinline__ void store_token(const EncodeArgs& a, int kind, int64
 // words and index, the V code words of its 32-token tile (written whole, later
 // positions zero, at the tile's first token; OR-ed in afterwards), and the
 // Chebyshev window update (Eq 5) with the window's (lo, hi) state as loaded.
+// A batch-shared window is folded into with atomic min / max of order keys
+// instead; its closure is a separate launch once every unit has folded in.
 __device__ __forceinline__ void token_append(const EncodeArgs& a, int kind, int64_t u, int t,
                                              int lane, float x0, float x1, float wl0, float wl1,
                                              float wh0, float wh1, uint32_t c0, uint32_t c1,
                                              uint32_t w0, uint32_t w1, int kidx, uint16_t t16) {
-  float* win = a.r.win[kind] + u * 2 * D;
+  float* win = a.r.win[kind] + pat_unit(a.r, u) * 2 * D;
   store_token(a, kind, u, t, lane, c0, c1, w0, w1, kidx, t16);
   if (kind == 1) {
     // V word of channel d holding token t: whole tile written on its first
@@ -330,13 +332,19 @@ __device__ __forceinline__ void token_append(const EncodeArgs& a, int kind, int6
       if (c1) atomicOr(&tile_out[wi * D + lane + 64], c1 << bit);
     }
   }
-  if (a.win_update) {
+  if (a.win_update && a.r.pat_h) {
+    int* wk = (int*)win;
+    atomicMin(&wk[lane], f32_order_key(x0));
+    atomicMin(&wk[lane + 64], f32_order_key(x1));
+    atomicMax(&wk[D + lane], f32_order_key(x0));
+    atomicMax(&wk[D + lane + 64], f32_order_key(x1));
+  } else if (a.win_update) {
     // Chebyshev window (Eq 5) over this token
     const float lo0 = fminf(wl0, x0), lo1 = fminf(wl1, x1);
     const float hi0 = fmaxf(wh0, x0), hi1 = fmaxf(wh1, x1);
     if (a.win_close) {
       if (a.close_slot >= 0) {
-        float* dst = a.r.tab[kind] + (u * a.max_pat + a.close_slot) * D;
+        float* dst = a.r.tab[kind] + (pat_unit(a.r, u) * a.max_pat + a.close_slot) * D;
         const float s0 = lo0 + hi0, s1 = lo1 + hi1;
         dst[lane] = s0 * 0.5f;
         dst[lane + 64] = s1 * 0.5f;

@@ -46,7 +46,14 @@ bool cfg_ok(const kvq_config* c) {
   if (!(c->v_alpha < 0.5f) || isnan(c->v_alpha)) return false;
   if (c->in_dtype != KVQ_F32 && c->in_dtype != KVQ_BF16) return false;
   if (c->max_splits < 0) return false;
+  if (c->shared_patterns != 0 && c->shared_patterns != 1) return false;
+  if (c->shared_patterns && c->mode != KVQ_MODE_PATTERN) return false;
   return true;
+}
+
+// pattern-table (and window) units: one per kv-head when the batch shares them
+int64_t pattern_units(const kvq_config& c) {
+  return c.shared_patterns ? c.n_kv_heads : (int64_t)c.batch * c.n_kv_heads;
 }
 
 // Standard normal quantile: Acklam's rational approximation refined by two
@@ -115,6 +122,7 @@ Regions regions_of(const kvq_cache* c, const kvq_layout& L) {
   r.sz[1] = (uint32_t*)(base + L.v_sz);
   r.idx[0] = base + L.k_idx;
   r.idx[1] = base + L.v_idx;
+  r.pat_h = c->cfg.shared_patterns ? c->cfg.n_kv_heads : 0;
   r.t16[0] = (uint16_t*)(base + L.k_t16);
   r.t16[1] = (uint16_t*)(base + L.v_t16);
   r.tab[0] = (float*)(base + L.k_tab);
@@ -146,8 +154,9 @@ int kvq_layout_of(const kvq_config* cfg, kvq_layout* out) {
   L.sz_bytes = U * tcap * L.n_groups * 4;
   L.idx_bytes = pattern ? U * tcap : 0;
   L.t16_bytes = pattern ? 0 : U * tcap * 2;
-  L.tab_bytes = pattern ? U * (uint64_t)cfg->max_patterns * D * 4 : U * D * 4;
-  L.win_bytes = pattern ? U * 2 * D * 4 : 0;
+  const uint64_t PU = (uint64_t)pattern_units(*cfg);
+  L.tab_bytes = pattern ? PU * (uint64_t)cfg->max_patterns * D * 4 : U * D * 4;
+  L.win_bytes = pattern ? PU * 2 * D * 4 : 0;
   // split-K partials: o[D], (m, l) and the per-pattern mass w[max_patterns]
   uint64_t ws_attn = (uint64_t)cfg->batch * cfg->n_q_heads * L.max_splits *
                      (D + 2 + (uint64_t)cfg->max_patterns) * 4;
@@ -190,7 +199,8 @@ int kvq_cache_init(kvq_cache* cache, const kvq_config* cfg, void* base, uint64_t
   hipError_t ec = launch_fill((float*)r.cnt, 0.0f, (int64_t)(L.cnt_bytes / 4), s);
   if (ec != hipSuccess) return dev_fail(ec);
   if (cfg->mode == KVQ_MODE_PATTERN) {
-    hipError_t e = launch_window_reset(r.win[0], r.win[1], cfg->batch * cfg->n_kv_heads, s);
+    hipError_t e = launch_window_reset(r.win[0], r.win[1], (int)pattern_units(*cfg),
+                                       cfg->shared_patterns, s);
     if (e != hipSuccess) return dev_fail(e);
   } else {
     hipError_t e = launch_fill(r.tab[0], 1.0f, (int64_t)(L.tab_bytes / 4), s);
@@ -211,20 +221,21 @@ int kvq_set_patterns(kvq_cache* cache, const float* k_tab, const float* v_tab, i
   hipStream_t s = (hipStream_t)stream;
   Regions r = regions_of(cache, L);
   const size_t units = (size_t)c.batch * c.n_kv_heads;
+  const size_t tab_units = (size_t)pattern_units(c);
   const float* src[2] = {k_tab, v_tab};
   for (int k = 0; k < 2; ++k) {
     hipError_t e;
     if (pattern) {
       if (n == 0) continue;
       e = hipMemcpy2DAsync(r.tab[k], (size_t)c.max_patterns * D * 4, src[k], (size_t)n * D * 4,
-                           (size_t)n * D * 4, units, hipMemcpyDeviceToDevice, s);
+                           (size_t)n * D * 4, tab_units, hipMemcpyDeviceToDevice, s);
     } else {
       e = hipMemcpyAsync(r.tab[k], src[k], units * D * 4, hipMemcpyDeviceToDevice, s);
     }
     if (e != hipSuccess) return dev_fail(e);
   }
   if (pattern) {
-    hipError_t e = launch_window_reset(r.win[0], r.win[1], (int)units, s);
+    hipError_t e = launch_window_reset(r.win[0], r.win[1], (int)tab_units, c.shared_patterns, s);
     if (e != hipSuccess) return dev_fail(e);
     cache->n_patterns = n;
     cache->win_count = 0;
@@ -249,11 +260,15 @@ int kvq_init_patterns(kvq_cache* cache, const void* k, const void* v, int32_t n_
   hipError_t e;
   if (pattern) {
     if (n_patterns > 0) {
-      e = launch_kmeans_pair(k, v, bf16, n_tok, n_patterns, r.tab[0], r.tab[1], c.max_patterns,
-                             units, (uint8_t*)r.ws, s);
+      // shared tables: per kv-head over its prefixes in every sequence,
+      // pooled batch-major
+      const int groups = c.shared_patterns ? c.batch : 1;
+      e = launch_kmeans_pair(k, v, bf16, n_tok, groups, (int64_t)c.n_kv_heads * n_tok, n_patterns,
+                             r.tab[0], r.tab[1], c.max_patterns, (int)pattern_units(c),
+                             (uint8_t*)r.ws, s);
       if (e != hipSuccess) return dev_fail(e);
     }
-    e = launch_window_reset(r.win[0], r.win[1], units, s);
+    e = launch_window_reset(r.win[0], r.win[1], (int)pattern_units(c), c.shared_patterns, s);
     if (e != hipSuccess) return dev_fail(e);
     cache->n_patterns = n_patterns;
     cache->win_count = 0;
@@ -324,6 +339,9 @@ int kvq_encode_append(kvq_cache* cache, const void* k_new, const void* v_new, in
     const int tiles = (a.t0 + chunk - 1) / VT - a.t0 / VT + 1;
     a.tiles_per_block = tiles;
     hipError_t e = launch_encode(a, units, 1, s);
+    // a batch-shared window closes once every unit has folded its vectors in
+    if (e == hipSuccess && a.win_close && c.shared_patterns)
+      e = launch_window_close(a.r, (int)pattern_units(c), c.max_patterns, a.close_slot, s);
     if (e != hipSuccess) return dev_fail(e);
     cache->n_tokens += chunk;
     cache->win_count += chunk;
@@ -458,6 +476,12 @@ int kvq_decode_step(kvq_cache* cache, const void* k_new, const void* v_new, cons
   a.fuse = 1;
   const int st = attn_launch(k, a, stream);
   if (st != KVQ_OK) return st;
+  if (window && e.win_close && c.shared_patterns) {
+    // the new centre serves later tokens only, so it may follow the step
+    hipError_t he = launch_window_close(a.r, (int)pattern_units(c), c.max_patterns, e.close_slot,
+                                        (hipStream_t)stream);
+    if (he != hipSuccess) return dev_fail(he);
+  }
   cache->n_tokens += 1;
   if (window) {
     cache->win_count += 1;

@@ -80,7 +80,25 @@ struct Regions {
   float* win[2];
   float* ws;
   uint32_t* cnt;        // [U] arrival counters of the fused split-K combine
+  int pat_h;            // pattern tables and windows per kv-head (= Hkv) when
+                        // shared by the batch; 0 = per (batch, kv-head) unit
 };
+
+// Pattern-table (and Chebyshev-window) unit of (batch, kv-head) unit u.
+__host__ __device__ inline int64_t pat_unit(const Regions& r, int64_t u) {
+  return r.pat_h ? u % r.pat_h : u;
+}
+
+// Order-preserving integer key of a binary32 value and its inverse: integer
+// min / max of keys = binary32 min / max (non-NaN).  Batch-shared windows hold
+// keys so that every unit folds its vectors in with one atomic each.
+__device__ __forceinline__ int f32_order_key(float f) {
+  const int b = __builtin_bit_cast(int, f);
+  return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float f32_from_order_key(int k) {
+  return __builtin_bit_cast(float, k ^ ((k >> 31) & 0x7FFFFFFF));
+}
 
 struct EncodeArgs {
   Regions r;
@@ -121,7 +139,12 @@ struct DequantArgs {
 
 // Host launchers (each returns the hipError_t of its launch).
 hipError_t launch_fill(float* p, float value, int64_t n, hipStream_t s);
-hipError_t launch_window_reset(float* win_k, float* win_v, int units, hipStream_t s);
+// (lo, hi) = (+inf, -inf) for `units` windows, as binary32 or (keys != 0) as
+// order keys
+hipError_t launch_window_reset(float* win_k, float* win_v, int units, int keys, hipStream_t s);
+// Batch-shared windows: write each window's centre fl(fl(lo + hi) * 0.5) into
+// table slot `slot` (none if slot < 0) and reset the window.
+hipError_t launch_window_close(const Regions& r, int units, int max_pat, int slot, hipStream_t s);
 hipError_t launch_encode(const EncodeArgs& a, int units, int n_blocks_x, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, int units, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
@@ -129,9 +152,11 @@ hipError_t launch_attention_combine(const AttnArgs& a, hipStream_t s);
 bool mfma_attention_supported(int bits, int group, int gq);
 hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_pp(const AttnArgs& a, hipStream_t s);
-hipError_t launch_kmeans_pair(const void* xk, const void* xv, int bf16, int n_tok, int k,
-                              float* tab_k, float* tab_v, int max_pat, int units, uint8_t* assign,
-                              hipStream_t s);
+// k-means per (unit, kind) over `groups` * n_tok rows: row i of unit u is
+// input row (i / n_tok) * group_stride + u * n_tok + i % n_tok.
+hipError_t launch_kmeans_pair(const void* xk, const void* xv, int bf16, int n_tok, int groups,
+                              int64_t group_stride, int k, float* tab_k, float* tab_v, int max_pat,
+                              int units, uint8_t* assign, hipStream_t s);
 hipError_t launch_chan_scale_pair(const void* xk, const void* xv, int bf16, int n_tok, float* sk,
                                   float* sv, int units, hipStream_t s);
 

@@ -24,17 +24,42 @@ hipError_t launch_fill(float* p, float value, int64_t n, hipStream_t s) {
 }
 
 // Window state [U][2][D]: min row = +inf, max row = -inf.
-__global__ void window_reset_kernel(float* wk, float* wv, int units) {
+__global__ void window_reset_kernel(float* wk, float* wv, int units, int keys) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= units * 2 * D) return;
-  float v = ((i / D) & 1) ? -INFINITY : INFINITY;
-  wk[i] = v;
-  wv[i] = v;
+  const float v = ((i / D) & 1) ? -INFINITY : INFINITY;
+  const float w = keys ? __builtin_bit_cast(float, f32_order_key(v)) : v;
+  wk[i] = w;
+  wv[i] = w;
 }
 
-hipError_t launch_window_reset(float* wk, float* wv, int units, hipStream_t s) {
+hipError_t launch_window_reset(float* wk, float* wv, int units, int keys, hipStream_t s) {
   int n = units * 2 * D;
-  hipLaunchKernelGGL(window_reset_kernel, dim3((n + 255) / 256), dim3(256), 0, s, wk, wv, units);
+  hipLaunchKernelGGL(window_reset_kernel, dim3((n + 255) / 256), dim3(256), 0, s, wk, wv, units,
+                     keys);
+  return hipGetLastError();
+}
+
+// Batch-shared Chebyshev windows (Eq 5): every unit of a kv-head has folded
+// its vectors into the window's order keys; the centre of the closed window
+// goes to table slot `slot` and the window starts again.  One block of D
+// threads per (pattern unit, kind).
+__global__ void window_close_kernel(Regions r, int max_pat, int slot) {
+  const int d = threadIdx.x;
+  const int64_t p = blockIdx.x;
+  const int kind = blockIdx.y;
+  int* win = (int*)(r.win[kind] + p * 2 * D);
+  const float lo = f32_from_order_key(win[d]), hi = f32_from_order_key(win[D + d]);
+  if (slot >= 0) {
+    const float s = lo + hi;
+    r.tab[kind][(p * max_pat + slot) * D + d] = s * 0.5f;
+  }
+  win[d] = f32_order_key(INFINITY);
+  win[D + d] = f32_order_key(-INFINITY);
+}
+
+hipError_t launch_window_close(const Regions& r, int units, int max_pat, int slot, hipStream_t s) {
+  hipLaunchKernelGGL(window_close_kernel, dim3(units, 2), dim3(D), 0, s, r, max_pat, slot);
   return hipGetLastError();
 }
 
@@ -76,7 +101,7 @@ __global__ void __launch_bounds__(64) dequant_kernel(DequantArgs a) {
   if (a.mode == KVQ_MODE_PATTERN) {
     int k = a.r.idx[w][u * a.tcap + t];
     if (k != KVQ_INDEX_NONE) {
-      const float* m = a.r.tab[w] + (u * a.max_pat + k) * D;
+      const float* m = a.r.tab[w] + (pat_unit(a.r, u) * a.max_pat + k) * D;
       v[0] = v[0] + m[lane];
       v[1] = v[1] + m[lane + 64];
     }
@@ -117,6 +142,14 @@ constexpr int KM_THREADS = 256;
 constexpr int KM_MAXK = 64;
 constexpr int KM_ITERS = 50;
 
+// Input row of row i of unit u's k-means rows: the unit's own prefix
+// (groups = 1), or the prefixes of its kv-head in every sequence pooled
+// batch-major (group stride Hkv * n_tok).
+__device__ __forceinline__ int64_t km_row(int64_t u, int i, int n_tok, int64_t gstride) {
+  const int g = i / n_tok;
+  return g * gstride + u * n_tok + (i - g * n_tok);
+}
+
 struct KmShared {
   double cent[KM_MAXK][D];
   double sums[KM_MAXK][D];
@@ -125,7 +158,8 @@ struct KmShared {
 };
 
 __global__ void __launch_bounds__(KM_THREADS) kmeans_kernel(const void* xk, const void* xv,
-                                                             int bf16, int n, int k, float* tab_k,
+                                                             int bf16, int n_tok, int groups,
+                                                             int64_t gstride, int k, float* tab_k,
                                                              float* tab_v, int max_pat,
                                                              uint8_t* assign) {
   extern __shared__ unsigned char km_raw[];
@@ -134,13 +168,13 @@ __global__ void __launch_bounds__(KM_THREADS) kmeans_kernel(const void* xk, cons
   const int64_t u = blockIdx.x;
   const void* x = kind ? xv : xk;
   float* tab = (kind ? tab_v : tab_k) + u * max_pat * D;
+  const int n = groups * n_tok;
   uint8_t* a = assign + ((int64_t)kind * gridDim.x + u) * n;
-  const int64_t xrow0 = u * (int64_t)n;
 
   for (int i = threadIdx.x; i < k * D; i += KM_THREADS) {
     int j = i / D, d = i % D;
     int64_t row = (int64_t)j * n / k;
-    sh.cent[j][d] = (double)load_in(x, (xrow0 + row) * D + d, bf16);
+    sh.cent[j][d] = (double)load_in(x, km_row(u, (int)row, n_tok, gstride) * D + d, bf16);
   }
   __syncthreads();
   for (int it = 0; it < KM_ITERS; ++it) {
@@ -149,7 +183,8 @@ __global__ void __launch_bounds__(KM_THREADS) kmeans_kernel(const void* xk, cons
     int changed = 0;
     for (int t = threadIdx.x; t < n; t += KM_THREADS) {
       float xr[D];
-      for (int d = 0; d < D; ++d) xr[d] = load_in(x, (xrow0 + t) * D + d, bf16);
+      const int64_t xr0 = km_row(u, t, n_tok, gstride) * D;
+      for (int d = 0; d < D; ++d) xr[d] = load_in(x, xr0 + d, bf16);
       int best = 0;
       double bd = INFINITY;
       for (int j = 0; j < k; ++j) {
@@ -175,7 +210,7 @@ __global__ void __launch_bounds__(KM_THREADS) kmeans_kernel(const void* xk, cons
       const int d = threadIdx.x;
       for (int t = 0; t < n; ++t) {
         int j = a[t];
-        sh.sums[j][d] = sh.sums[j][d] + (double)load_in(x, (xrow0 + t) * D + d, bf16);
+        sh.sums[j][d] = sh.sums[j][d] + (double)load_in(x, km_row(u, t, n_tok, gstride) * D + d, bf16);
         if (d == 0) sh.cnt[j] += 1;
       }
     }
@@ -233,7 +268,8 @@ struct KfShared {
 };
 
 __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk, const void* xv,
-                                                                  int bf16, int n, int k,
+                                                                  int bf16, int n_tok, int groups,
+                                                                  int64_t gstride, int k,
                                                                   float* tab_k, float* tab_v,
                                                                   int max_pat) {
   extern __shared__ unsigned char km_raw[];
@@ -242,13 +278,14 @@ __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk,
   const int64_t u = blockIdx.x;
   const void* x = kind ? xv : xk;
   float* tab = (kind ? tab_v : tab_k) + u * max_pat * D;
-  const int64_t xrow0 = u * (int64_t)n;
+  const int n = groups * n_tok;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nch = (n + 63) / 64;
 
   for (int i = tid; i < KM_MAXK * D; i += KF_THREADS) {
     const int j = i / D, d = i % D;
-    sh.cent[j][d] = j < k ? (double)load_in(x, (xrow0 + (int64_t)j * n / k) * D + d, bf16) : 0.0;
+    sh.cent[j][d] = j < k ? (double)load_in(x, km_row(u, (int)((int64_t)j * n / k), n_tok, gstride) * D + d, bf16)
+                          : 0.0;
   }
   __syncthreads();
   for (int it = 0; it < KM_ITERS; ++it) {
@@ -256,7 +293,7 @@ __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk,
     __syncthreads();
     int changed = 0;
     for (int t = tid; t < n; t += KF_THREADS) {
-      const int64_t row = (xrow0 + t) * D;
+      const int64_t row = km_row(u, t, n_tok, gstride) * D;
       int best = 0;
       double bd = INFINITY;
       for (int p0 = 0; p0 < k; p0 += KF_PC) {
@@ -336,11 +373,11 @@ __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk,
       for (; e + 8 <= c; e += 8) {
         float v[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = load_in(x, (xrow0 + m[e + i]) * D + d, bf16);
+        for (int i = 0; i < 8; ++i) v[i] = load_in(x, km_row(u, m[e + i], n_tok, gstride) * D + d, bf16);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc = acc + (double)v[i];
       }
-      for (; e < c; ++e) acc = acc + (double)load_in(x, (xrow0 + m[e]) * D + d, bf16);
+      for (; e < c; ++e) acc = acc + (double)load_in(x, km_row(u, m[e], n_tok, gstride) * D + d, bf16);
       sh.cent[j][d] = acc / (double)c;
     }
     __syncthreads();
@@ -348,10 +385,10 @@ __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk,
   for (int i = tid; i < k * D; i += KF_THREADS) tab[i] = (float)sh.cent[i / D][i % D];
 }
 
-hipError_t launch_kmeans_pair(const void* xk, const void* xv, int bf16, int n_tok, int k,
-                              float* tab_k, float* tab_v, int max_pat, int units, uint8_t* assign,
-                              hipStream_t s) {
-  if (n_tok <= KF_MAXN && k <= KM_MAXK) {
+hipError_t launch_kmeans_pair(const void* xk, const void* xv, int bf16, int n_tok, int groups,
+                              int64_t gstride, int k, float* tab_k, float* tab_v, int max_pat,
+                              int units, uint8_t* assign, hipStream_t s) {
+  if ((int64_t)groups * n_tok <= KF_MAXN && k <= KM_MAXK) {
     const size_t lds = sizeof(KfShared);
     static bool fast_attr = false;
     if (!fast_attr) {
@@ -361,7 +398,7 @@ hipError_t launch_kmeans_pair(const void* xk, const void* xv, int bf16, int n_to
       fast_attr = true;
     }
     hipLaunchKernelGGL(kmeans_fast_kernel, dim3(units, 2), dim3(KF_THREADS), lds, s, xk, xv, bf16,
-                       n_tok, k, tab_k, tab_v, max_pat);
+                       n_tok, groups, gstride, k, tab_k, tab_v, max_pat);
     return hipGetLastError();
   }
   size_t lds = sizeof(KmShared);
@@ -373,7 +410,7 @@ hipError_t launch_kmeans_pair(const void* xk, const void* xv, int bf16, int n_to
     attr_set = true;
   }
   hipLaunchKernelGGL(kmeans_kernel, dim3(units, 2), dim3(KM_THREADS), lds, s, xk, xv, bf16,
-                     n_tok, k, tab_k, tab_v, max_pat, assign);
+                     n_tok, groups, gstride, k, tab_k, tab_v, max_pat, assign);
   return hipGetLastError();
 }
 

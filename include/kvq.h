@@ -80,13 +80,20 @@ typedef struct {
   float v_alpha;          /* z-test level of section 3.3; <= 0 disables it */
   int32_t in_dtype;       /* KVQ_F32 or KVQ_BF16 for k, v and q inputs */
   int32_t max_splits;     /* split-K workspace capacity; 0 = derived */
+  int32_t shared_patterns; /* PATTERN mode: 1 = one pattern table and one Chebyshev
+                              window per kv-head, shared by the whole batch (the
+                              batch-free pattern memory of PatternKV's memory
+                              analysis); 0 = per (batch, kv-head) unit */
 } kvq_config;
 
 /* Byte offsets (from the cache base) and sizes of every region. */
 typedef struct {
   uint64_t k_codes, v_codes, k_sz, v_sz, k_idx, v_idx, k_t16, v_t16;
-  uint64_t k_tab, v_tab;  /* PATTERN: fp32 [U][max_patterns][D]; KVARN: fp32 [U][D] */
-  uint64_t k_win, v_win;  /* PATTERN window state: fp32 [U][2][D] (min, max) */
+  uint64_t k_tab, v_tab;  /* PATTERN: fp32 [PU][max_patterns][D]; KVARN: fp32 [U][D];
+                             PU = Hkv with shared_patterns, else U = B * Hkv */
+  uint64_t k_win, v_win;  /* PATTERN window state [PU][2][D] (min, max): fp32, or
+                             with shared_patterns int32 order keys of the fp32
+                             values (atomic min / max across the batch) */
   uint64_t ws;            /* split-K partials */
   uint64_t cnt;           /* split-K arrival counters, uint32 [U], zero between calls */
   uint64_t codes_bytes, sz_bytes, idx_bytes, t16_bytes, tab_bytes, win_bytes, ws_bytes;
@@ -121,8 +128,10 @@ int kvq_cache_init(kvq_cache* cache, const kvq_config* cfg, void* base, uint64_t
 
 /* Prefill pattern mining (PatternKV section 3.1, Eq 4): for every unit and for
  * K and V separately, Euclidean k-means over the n_tok prefix vectors
- * (k: [B][Hkv][n_tok][D], v likewise) into n_patterns centroids: centroid j
- * starts at prefix row floor(j*n_tok/n_patterns); Lloyd iterations run until
+ * (k: [B][Hkv][n_tok][D], v likewise) into n_patterns centroids.  With
+ * shared_patterns the k-means of kv-head h runs over its B prefixes pooled
+ * batch-major (row b*n_tok + t), so N = B*n_tok rows; otherwise N = n_tok.
+ * Centroid j starts at row floor(j*N/n_patterns); Lloyd iterations run until
  * no assignment changes (at most 50), ties go to the lowest index, an empty
  * cluster keeps its centroid; binary64 arithmetic, stored as fp32.
  * KVARN mode instead sets each unit's per-channel scale c_j to the root mean
@@ -134,8 +143,9 @@ int kvq_init_patterns(kvq_cache* cache, const void* k, const void* v, int32_t n_
                       int32_t n_patterns, void* stream);
 
 /* Upload pattern tables mined elsewhere: k_tab and v_tab are fp32 device
- * arrays [B][Hkv][n][D] (PATTERN, n <= max_patterns) or per-channel scales
- * [B][Hkv][D] (KVARN, n ignored).  Resets the Chebyshev window.
+ * arrays [B][Hkv][n][D] (PATTERN, n <= max_patterns; [Hkv][n][D] with
+ * shared_patterns) or per-channel scales [B][Hkv][D] (KVARN, n ignored).
+ * Resets the Chebyshev window.
  * KVQ_EINVAL on a bad n or null pointer. */
 int kvq_set_patterns(kvq_cache* cache, const float* k_tab, const float* v_tab, int32_t n,
                      void* stream);
@@ -149,7 +159,9 @@ int kvq_set_patterns(kvq_cache* cache, const float* k_tab, const float* v_tab, i
  * stores index 0xFF and quantizes the raw vector.  update_patterns != 0 marks
  * decode-stage appends: they feed the Chebyshev window (Eq 5) whose centre
  * fl(fl(min + max) * 0.5) joins the table after every pattern_window-th such
- * token and serves the tokens after it.
+ * token and serves the tokens after it.  With shared_patterns the window of
+ * kv-head h takes its min / max over every sequence's vectors, and each
+ * closure adds one centre to h's table (a second, small launch).
  * KVARN: y = Hadamard(x)/sqrt(D), y~ = y / c, t = rms(y~) stored as binary16,
  * u = y~ / t quantized per group (update_patterns is ignored).
  * KVQ_ECAPACITY if n_tokens + n_new > max_tokens; KVQ_EINVAL on null inputs

@@ -59,10 +59,13 @@ def gpu_codes(cache, which: int, T: int, units=None) -> np.ndarray:
 
 
 def gpu_tab(cache, which: int) -> np.ndarray:
+    """Pattern tables [PU][max_patterns][D] (PU = kv-heads when the batch
+    shares them) or KVarN channel scales [U][D]."""
     c = cache.cfg
     a = cache.region("kv"[which] + "_tab").cpu().numpy().view(np.float32)
-    U = c.batch * c.n_kv_heads
-    return a.reshape(U, c.max_patterns, c.head_dim) if cache.mode == "pattern" else a.reshape(U, c.head_dim)
+    if cache.mode == "pattern":
+        return a.reshape(cache.pattern_units, c.max_patterns, c.head_dim)
+    return a.reshape(c.batch * c.n_kv_heads, c.head_dim)
 
 
 def assert_same_encode(ref: "O.RefCache", cache, T: int, units=None, ref_units=None) -> None:
@@ -93,14 +96,14 @@ def assert_same_encode(ref: "O.RefCache", cache, T: int, units=None, ref_units=N
 
 
 def make_pair(B, Hq, Hkv, max_tokens, *, bits=2, group=32, mode="pattern", max_patterns=32,
-              pattern_window=128, v_alpha=0.05, bf16=True):
+              pattern_window=128, v_alpha=0.05, bf16=True, shared_patterns=False):
     from bit_kv_cache_encode_amd import KVCache
     dt = torch.bfloat16 if bf16 else torch.float32
     gpu = KVCache(B, Hq, Hkv, max_tokens, bits=bits, group=group, mode=mode,
                   max_patterns=max_patterns, pattern_window=pattern_window, v_alpha=v_alpha,
-                  in_dtype=dt)
+                  in_dtype=dt, shared_patterns=shared_patterns)
     ref = O.RefCache(B, Hq, Hkv, 128, max_tokens, bits=bits, group=group,
                      mode=O.PATTERN if mode == "pattern" else O.KVARN,
                      max_patterns=max_patterns, pattern_window=pattern_window, v_alpha=v_alpha,
-                     in_dtype=O.IN_BF16 if bf16 else O.IN_F32)
+                     in_dtype=O.IN_BF16 if bf16 else O.IN_F32, shared_patterns=shared_patterns)
     return gpu, ref, dt

@@ -37,9 +37,10 @@ def test_struct_layout_matches_c(tmp_path):
 #include <stddef.h>
 #include "{HEADER}"
 int main(void) {{
-  printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(kvq_config), sizeof(kvq_layout),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(kvq_config), sizeof(kvq_layout),
          sizeof(kvq_cache), offsetof(kvq_cache, base), offsetof(kvq_cache, rho),
-         offsetof(kvq_layout, total), offsetof(kvq_config, max_splits));
+         offsetof(kvq_layout, total), offsetof(kvq_config, max_splits),
+         offsetof(kvq_config, shared_patterns));
   return 0;
 }}''')
     exe = tmp_path / "probe"
@@ -48,7 +49,7 @@ int main(void) {{
                                        check=True).stdout.split()))
     want = [C.sizeof(B.kvq_config), C.sizeof(B.kvq_layout), C.sizeof(B.kvq_cache),
             B.kvq_cache.base.offset, B.kvq_cache.rho.offset, B.kvq_layout.total.offset,
-            B.kvq_config.max_splits.offset]
+            B.kvq_config.max_splits.offset, B.kvq_config.shared_patterns.offset]
     assert got == want
 
 
@@ -70,13 +71,18 @@ def test_layout_regions():
     assert Lk.record_bytes == 50 and Lk.idx_bytes == 0 and Lk.t16_bytes == U * T * 2
     L4 = B.kvq_layout_of(_cfg(bits=4, group=64))
     assert L4.record_bytes == 73
+    # batch-shared tables: one table and one window per kv-head
+    Ls = B.kvq_layout_of(_cfg(shared_patterns=1))
+    assert Ls.tab_bytes == 8 * 32 * 128 * 4 and Ls.win_bytes == 8 * 2 * 128 * 4
+    assert L.tab_bytes == U * 32 * 128 * 4 and Ls.codes_bytes == L.codes_bytes
     assert offs  # regions exist
 
 
 @pytest.mark.parametrize("bad", [
     dict(head_dim=64), dict(bits=3), dict(group=48), dict(group=4), dict(n_q_heads=12),
     dict(n_q_heads=136), dict(n_q_heads=72, group=16), dict(max_patterns=256), dict(mode=5), dict(in_dtype=7),
-    dict(v_alpha=0.5), dict(max_tokens=0), dict(batch=0), dict(pattern_window=-1)])
+    dict(v_alpha=0.5), dict(max_tokens=0), dict(batch=0), dict(pattern_window=-1),
+    dict(shared_patterns=2), dict(shared_patterns=1, mode=B.MODE_KVARN, max_patterns=0)])
 def test_layout_rejects_bad_configs(bad):
     """(n_q_heads 136 = 17 q-heads per kv-head; 72 at group 16 = 9 q-heads on
     a shape only the VALU attention serves, which holds at most 8.)"""
