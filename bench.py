@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--batch", type=int, default=8)
     ap.add_argument("--kmeans-tokens", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--shared-patterns", action="store_true",
+                    help="one pattern table and Chebyshev window per kv-head for the whole batch")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--split-step", action="store_true",
                     help="run each layer's step as two calls (encode-append, then attention) "
@@ -185,8 +187,11 @@ def main():
 
     # ---- setup (untimed): one layer mined + bulk-encoded, then replicated
     k, v = synth.device_kv(B, H, T0, D, layer=0, device=dev)
+    SH = args.shared_patterns
+    PU = H if SH else U          # pattern-table units
     base = KVCache(B, Hq, H, max_tokens, bits=2, group=32, mode="pattern", max_patterns=P,
-                   pattern_window=W, v_alpha=0.05, in_dtype=torch.bfloat16, device=dev)
+                   pattern_window=W, v_alpha=0.05, in_dtype=torch.bfloat16, device=dev,
+                   shared_patterns=SH)
     nk = min(args.kmeans_tokens, T0)
     kpre, vpre = k[:, :, :nk].contiguous(), v[:, :, :nk].contiguous()
     torch.cuda.synchronize()
@@ -207,9 +212,11 @@ def main():
     bulk_ms = e0.elapsed_time(e1)
     # repeat the bulk encode on a scratch cache to get a warm measurement
     scratch = KVCache(B, Hq, H, T0, bits=2, group=32, mode="pattern", max_patterns=P,
-                      pattern_window=W, v_alpha=0.05, in_dtype=torch.bfloat16, device=dev)
-    scratch.set_patterns(base.region("k_tab").view(torch.float32).view(B, H, P, D).clone(),
-                         base.region("v_tab").view(torch.float32).view(B, H, P, D).clone())
+                      pattern_window=W, v_alpha=0.05, in_dtype=torch.bfloat16, device=dev,
+                      shared_patterns=SH)
+    tab_shape = (H, P, D) if SH else (B, H, P, D)
+    scratch.set_patterns(base.region("k_tab").view(torch.float32).view(tab_shape).clone(),
+                         base.region("v_tab").view(torch.float32).view(tab_shape).clone())
     e0.record()
     scratch.encode_append(k, v)
     e1.record()
@@ -257,9 +264,9 @@ def main():
     in_b = 2
 
     def attn_bytes(T):
-        return 2 * U * T * rec + 2 * U * P * D * 4 + B * Hq * D * (in_b + 4)
+        return 2 * U * T * rec + 2 * PU * P * D * 4 + B * Hq * D * (in_b + 4)
 
-    enc_bytes = 2 * U * D * in_b + 2 * U * rec + 2 * U * P * D * 4
+    enc_bytes = 2 * U * D * in_b + 2 * U * rec + 2 * PU * P * D * 4
 
     # Events bracket a rotating sample of the layers' launches inside the timed
     # steps (EV_EVERY-th layer, offset by the step), because an event record
@@ -336,7 +343,8 @@ def main():
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         tr = json.load(open(TRAFFIC_FILE))
-        if tr.get("source_hash") == attn_source_hash():
+        # counters taken on this kernel, sources and table layout
+        if tr.get("source_hash") == attn_source_hash() and tr.get("kernel") == kern and not SH:
             traffic = tr.get("bytes_per_launch")
 
     res = {
@@ -347,10 +355,13 @@ def main():
         "config": {"workload": (f"decode step of a {L}-layer Llama-3-8B-shaped stack: batch {B}, "
                                 f"{Hq} q / {H} kv heads, head_dim {D}, context {T0}, bf16 in, "
                                 f"2-bit PatternKV codes (group 32, {P} patterns, alpha 0.05, "
-                                f"window {W}); per layer encode-append 1 token + decode attention"
+                                f"window {W}"
+                                + (", tables shared by the batch" if SH else "")
+                                + "); per layer encode-append 1 token + decode attention"
                                 + (" (two calls)" if args.split_step else " in one launch")),
                    "batch": B, "context": T0, "layers": L, "n_q_heads": Hq, "n_kv_heads": H,
-                   "head_dim": D, "bits": 2, "group": 32, "patterns": P},
+                   "head_dim": D, "bits": 2, "group": 32, "patterns": P,
+                   "shared_patterns": SH},
         "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -364,8 +375,11 @@ def main():
                    "decode_step_avg_us": round(enc_avg_us, 3),
                    "token": "one position's K and V for all 8 kv-heads of one layer"},
         "pattern_init": {"ms": round(init_ms, 3), "prefix_tokens": nk, "patterns": P,
-                         "what": "k-means (binary64) over the prefix for K and V of all "
-                                 f"{U} (batch, kv-head) units of one layer"},
+                         "what": ("k-means (binary64) for K and V of each of the "
+                                  f"{H} kv-heads of one layer over its {B} prefixes pooled"
+                                  if SH else
+                                  "k-means (binary64) over the prefix for K and V of all "
+                                  f"{U} (batch, kv-head) units of one layer")},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args, T0, P, W, attn_bytes, enc_bytes, U)

@@ -232,7 +232,8 @@ __global__ void __launch_bounds__(KM_THREADS) kmeans_kernel(const void* xk, cons
 //   chunk: ballot counts and ranks, then prefixes over chunks), then one
 //   thread per (pattern, channel) sums its members in that order.
 constexpr int KF_THREADS = 1024;
-constexpr int KF_MAXN = 8192;
+constexpr int KF_MAXN = 65535;          // rows (uint16 member lists)
+constexpr int KF_LDS_MAX = 160 * 1024;  // a compute unit's LDS
 constexpr int KF_PC = 8;    // patterns per distance pass
 
 // 16 consecutive channels of an input row (16-byte aligned) as fp32
@@ -256,24 +257,34 @@ __device__ __forceinline__ void km_load16(const void* x, int64_t idx, int bf16, 
   }
 }
 
-struct KfShared {
-  double cent[KM_MAXK][D];
-  uint8_t a[KF_MAXN];                   // assignment of each token
-  uint8_t rank[KF_MAXN];                // rank among its cluster's tokens in its chunk
-  uint16_t mem[KF_MAXN];                // tokens grouped by cluster, in token order
-  uint16_t pre[KF_MAXN / 64][KM_MAXK];  // per chunk counts, then exclusive prefixes
-  int off[KM_MAXK];
-  int cnt[KM_MAXK];
-  int changed;
-};
+// LDS layout of the block-parallel k-means for n rows and k patterns (bytes):
+// centroids [k rounded up to KF_PC][D] binary64, then per row its assignment
+// and its rank in its chunk (one byte each), the member lists (uint16), per
+// chunk counts / prefixes [n/64][k] (uint16) and the cluster offsets and
+// counts.  It serves any (n, k) whose total fits a compute unit's LDS.
+struct KfLds { int cent, a, rank, mem, pre, off, cnt, changed, total; };
+__host__ __device__ inline KfLds kf_lds(int n, int k) {
+  KfLds L;
+  const int kr = (k + KF_PC - 1) / KF_PC * KF_PC, nch = (n + 63) / 64;
+  int o = 0;
+  L.cent = o; o += kr * D * 8;
+  L.a = o; o += (n + 15) / 16 * 16;
+  L.rank = o; o += (n + 15) / 16 * 16;
+  L.mem = o; o += (2 * n + 15) / 16 * 16;
+  L.pre = o; o += (2 * nch * k + 15) / 16 * 16;
+  L.off = o; o += 4 * KM_MAXK;
+  L.cnt = o; o += 4 * KM_MAXK;
+  L.changed = o; o += 16;
+  L.total = o;
+  return L;
+}
 
 __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk, const void* xv,
                                                                   int bf16, int n_tok, int groups,
                                                                   int64_t gstride, int k,
                                                                   float* tab_k, float* tab_v,
                                                                   int max_pat) {
-  extern __shared__ unsigned char km_raw[];
-  KfShared& sh = *reinterpret_cast<KfShared*>(km_raw);
+  extern __shared__ __attribute__((aligned(16))) unsigned char km_raw[];
   const int kind = blockIdx.y;
   const int64_t u = blockIdx.x;
   const void* x = kind ? xv : xk;
@@ -281,15 +292,25 @@ __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk,
   const int n = groups * n_tok;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nch = (n + 63) / 64;
+  const int kr = (k + KF_PC - 1) / KF_PC * KF_PC;
+  const KfLds Lo = kf_lds(n, k);
+  double (*cent)[D] = (double (*)[D])(km_raw + Lo.cent);   // [kr][D]
+  uint8_t* s_a = km_raw + Lo.a;                              // [n]
+  uint8_t* s_rank = km_raw + Lo.rank;                        // [n]
+  uint16_t* s_mem = (uint16_t*)(km_raw + Lo.mem);            // [n]
+  uint16_t* s_pre = (uint16_t*)(km_raw + Lo.pre);            // [nch][k]
+  int* s_off = (int*)(km_raw + Lo.off);
+  int* s_cnt = (int*)(km_raw + Lo.cnt);
+  int* s_changed = (int*)(km_raw + Lo.changed);
 
-  for (int i = tid; i < KM_MAXK * D; i += KF_THREADS) {
+  for (int i = tid; i < kr * D; i += KF_THREADS) {
     const int j = i / D, d = i % D;
-    sh.cent[j][d] = j < k ? (double)load_in(x, km_row(u, (int)((int64_t)j * n / k), n_tok, gstride) * D + d, bf16)
-                          : 0.0;
+    cent[j][d] = j < k ? (double)load_in(x, km_row(u, (int)((int64_t)j * n / k), n_tok, gstride) * D + d, bf16)
+                       : 0.0;
   }
   __syncthreads();
   for (int it = 0; it < KM_ITERS; ++it) {
-    if (tid == 0) sh.changed = 0;
+    if (tid == 0) *s_changed = 0;
     __syncthreads();
     int changed = 0;
     for (int t = tid; t < n; t += KF_THREADS) {
@@ -311,7 +332,7 @@ __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk,
             const double xd = (double)xb[dd];
 #pragma unroll
             for (int q = 0; q < KF_PC; ++q) {
-              const double diff = xd - sh.cent[p0 + q][d0 + dd];
+              const double diff = xd - cent[p0 + q][d0 + dd];
               dist[q] = dist[q] + diff * diff;
             }
           }
@@ -323,50 +344,50 @@ __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk,
         for (int q = 0; q < KF_PC; ++q)
           if (p0 + q < k && dist[q] < bd) { bd = dist[q]; best = p0 + q; }
       }
-      if (it == 0 || sh.a[t] != (uint8_t)best) changed = 1;
-      sh.a[t] = (uint8_t)best;
+      if (it == 0 || s_a[t] != (uint8_t)best) changed = 1;
+      s_a[t] = (uint8_t)best;
     }
-    if (changed) atomicOr(&sh.changed, 1);
+    if (changed) atomicOr(s_changed, 1);
     __syncthreads();
-    if (it > 0 && sh.changed == 0) break;
+    if (it > 0 && *s_changed == 0) break;
     // per chunk: member counts per cluster and each token's rank among them
     for (int c = wave; c < nch; c += KF_THREADS / 64) {
       const int t = c * 64 + lane;
-      const int at = t < n ? sh.a[t] : -1;
+      const int at = t < n ? s_a[t] : -1;
       int rank = 0;
       for (int j = 0; j < k; ++j) {
         const uint64_t m = __ballot(at == j);
         if (at == j) rank = __popcll(m & ((1ull << lane) - 1ull));
-        if (lane == 0) sh.pre[c][j] = (uint16_t)__popcll(m);
+        if (lane == 0) s_pre[c * k + j] = (uint16_t)__popcll(m);
       }
-      if (t < n) sh.rank[t] = (uint8_t)rank;
+      if (t < n) s_rank[t] = (uint8_t)rank;
     }
     __syncthreads();
     if (tid < k) {
       int acc = 0;
       for (int c = 0; c < nch; ++c) {
-        const int v = sh.pre[c][tid];
-        sh.pre[c][tid] = (uint16_t)acc;
+        const int v = s_pre[c * k + tid];
+        s_pre[c * k + tid] = (uint16_t)acc;
         acc += v;
       }
-      sh.cnt[tid] = acc;
+      s_cnt[tid] = acc;
     }
     __syncthreads();
     if (tid == 0) {
       int o = 0;
-      for (int j = 0; j < k; ++j) { sh.off[j] = o; o += sh.cnt[j]; }
+      for (int j = 0; j < k; ++j) { s_off[j] = o; o += s_cnt[j]; }
     }
     __syncthreads();
     for (int t = tid; t < n; t += KF_THREADS) {
-      const int j = sh.a[t];
-      sh.mem[sh.off[j] + sh.pre[t >> 6][j] + sh.rank[t]] = (uint16_t)t;
+      const int j = s_a[t];
+      s_mem[s_off[j] + s_pre[(t >> 6) * k + j] + s_rank[t]] = (uint16_t)t;
     }
     __syncthreads();
     // centroid = member sum in token order / member count; empty keeps its centroid
     for (int i = tid; i < k * D; i += KF_THREADS) {
-      const int j = i / D, d = i % D, c = sh.cnt[j];
+      const int j = i / D, d = i % D, c = s_cnt[j];
       if (c == 0) continue;
-      const uint16_t* m = sh.mem + sh.off[j];
+      const uint16_t* m = s_mem + s_off[j];
       // members in blocks of 8 (their loads issued together), summed in order
       double acc = 0.0;
       int e = 0;
@@ -378,24 +399,25 @@ __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk,
         for (int i = 0; i < 8; ++i) acc = acc + (double)v[i];
       }
       for (; e < c; ++e) acc = acc + (double)load_in(x, km_row(u, m[e], n_tok, gstride) * D + d, bf16);
-      sh.cent[j][d] = acc / (double)c;
+      cent[j][d] = acc / (double)c;
     }
     __syncthreads();
   }
-  for (int i = tid; i < k * D; i += KF_THREADS) tab[i] = (float)sh.cent[i / D][i % D];
+  for (int i = tid; i < k * D; i += KF_THREADS) tab[i] = (float)cent[i / D][i % D];
 }
 
 hipError_t launch_kmeans_pair(const void* xk, const void* xv, int bf16, int n_tok, int groups,
                               int64_t gstride, int k, float* tab_k, float* tab_v, int max_pat,
                               int units, uint8_t* assign, hipStream_t s) {
-  if ((int64_t)groups * n_tok <= KF_MAXN && k <= KM_MAXK) {
-    const size_t lds = sizeof(KfShared);
-    static bool fast_attr = false;
-    if (!fast_attr) {
+  const int64_t n = (int64_t)groups * n_tok;
+  if (n <= KF_MAXN && k <= KM_MAXK && kf_lds((int)n, k).total <= KF_LDS_MAX) {
+    const int lds = kf_lds((int)n, k).total;
+    static int fast_attr = 0;
+    if (lds > fast_attr) {
       hipError_t e = hipFuncSetAttribute((const void*)kmeans_fast_kernel,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
       if (e != hipSuccess) return e;
-      fast_attr = true;
+      fast_attr = lds;
     }
     hipLaunchKernelGGL(kmeans_fast_kernel, dim3(units, 2), dim3(KF_THREADS), lds, s, xk, xv, bf16,
                        n_tok, groups, gstride, k, tab_k, tab_v, max_pat);

@@ -4,9 +4,9 @@ The GPU k-means runs the oracle's Lloyd iteration in binary64 with the same
 operation order (channel-ordered distance sums, lowest index on ties, member
 sums in token order), so the fp32 pattern tables must be bit-identical.
 Cases cover prefixes that end inside a 64-token chunk, 1 / 17 / 64 patterns
-(partial and several 16-pattern distance passes), the largest prefix of the
-block-parallel kernel (8192 tokens) and one beyond it, which takes the
-one-block-per-unit kernel.
+(partial and several distance passes), and 16384 tokens: with 32 patterns
+the block-parallel kernel's LDS layout still fits, with 64 it does not and
+the one-block-per-unit kernel runs.
 """
 import numpy as np
 import pytest
@@ -24,10 +24,11 @@ pytestmark = pytest.mark.gpu
     (777, 64, True),
     (2048, 32, True),
     (8192, 24, True),
-    (8193, 8, True),
+    (16384, 32, True),
+    (16384, 64, True),
 ])
 def test_kmeans_tables_bit_exact(n, P, bf16):
-    B, Hq, H = 1, 4, 2
+    B, Hq, H = (1, 4, 2) if n <= 4096 else (1, 4, 1)   # the oracle's k-means is O(n P) per unit
     gpu, ref, dt = make_pair(B, Hq, H, n, max_patterns=max(P, 8), bf16=bf16)
     k = synth.k_vectors(B, H, n, 128, seed=synth.seed_for("k") + n)
     v = synth.v_vectors(B, H, n, 128, seed=synth.seed_for("v") + n)
