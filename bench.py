@@ -38,6 +38,52 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attention.json")
 
 
+# Other workload shapes, measured as attention calls (HIP events over 10 calls
+# after 3 warm-up calls); the caches are filled by the bulk encode.
+ATTN_CONFIGS = {
+    "long4bit": dict(B=1, Hq=32, H=8, T=131072, bits=4, group=64, P=64, mode="pattern"),
+    "kvarn": dict(B=64, Hq=32, H=8, T=16384, bits=2, group=32, P=0, mode="kvarn"),
+    "qwen": dict(B=32, Hq=28, H=4, T=32768, bits=2, group=32, P=64, mode="pattern"),
+}
+
+
+def attn_config(name):
+    import torch
+
+    from bit_kv_cache_encode_amd import KVCache, synth
+    c = ATTN_CONFIGS[name]
+    dev = torch.device("cuda", 0)
+    D = 128
+    B, Hq, H, T = c["B"], c["Hq"], c["H"], c["T"]
+    k, v = synth.device_kv(B, H, T, D, device=dev)
+    cache = KVCache(B, Hq, H, T + 64, bits=c["bits"], group=c["group"], mode=c["mode"],
+                    max_patterns=max(c["P"], 1), device=dev)
+    if c["mode"] == "pattern":
+        cache.init_patterns(k[:, :, :2048].contiguous(), v[:, :, :2048].contiguous(), c["P"])
+    else:
+        cache.init_patterns(k[:, :, :1024].contiguous(), v[:, :, :1024].contiguous(), 0)
+    cache.encode_append(k, v)
+    del k, v
+    q = synth.device_queries(B, Hq, D, device=dev)
+    out = torch.empty((B, Hq, D), device=dev)
+    for _ in range(3):
+        cache.attn_decode(q, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 10
+    e0.record()
+    for _ in range(n):
+        cache.attn_decode(q, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    rec = cache.layout.record_bytes
+    nbytes = 2 * B * H * T * rec + 2 * B * H * c["P"] * D * 4 + B * Hq * D * 6
+    print(json.dumps({"attn_config": name, "shape": c, "us_per_call": round(us, 2),
+                      "algorithmic_bytes": nbytes, "effective_GBs": round(nbytes / us / 1e3, 1),
+                      "frac_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}))
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -61,6 +107,11 @@ def parse():
                     help="with --attn-only: then run plain kernels of known traffic on this many "
                          "MiB (4 reads: sum; 4 writes: fill; 4 copies: negation), whose HBM "
                          "counters calibrate the attention's")
+    ap.add_argument("--attn-config", choices=sorted(ATTN_CONFIGS),
+                    help="secondary measurement: decode attention alone on another workload "
+                         "shape (long4bit: B 1, 131072 tokens, 4-bit G64, 64 patterns; "
+                         "kvarn: 64 samples x 16384, KVarN 2-bit; qwen: B 32, 28 q / 4 kv "
+                         "heads, 32768 tokens, 64 patterns); prints one JSON line")
     ap.add_argument("--traffic-from", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "RAW_DIR"),
                     help="no GPU: summarise three rocprofv3 --pmc runs of --attn-only N "
                          "--calib-copy M (FETCH_SIZE; WRITE_SIZE; TCC_EA0_RDREQ 32B/64B/128B) "
@@ -169,9 +220,12 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(the decode path shards by (batch, kv-head) with no communication; see "
-              "DESIGN.md for the multi-GPU layout)", file=sys.stderr)
+              "(the decode path shards by (batch, kv-head) units with no communication, so "
+              "one GPU's throughput is measured at its real per-GPU shape)", file=sys.stderr)
         sys.exit(2)
+    if args.attn_config:
+        attn_config(args.attn_config)
+        return
     import torch
 
     from bit_kv_cache_encode_amd import KVCache, synth
