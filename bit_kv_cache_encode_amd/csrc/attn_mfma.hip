@@ -21,9 +21,10 @@
 //       LDS atomics.
 //
 // Codes enter the MFMA as binary16 subnormals: a 2-bit (4-bit) field masked
-// in place inside a 32-bit word is the integer code times 2^-24 times a power
-// of 4 (16) that depends only on the field's position; the other operand
-// carries the inverse power, so unpacking a pair of codes is one AND.  p*s
+// in place (K) or rotated near the top of the mantissa first (V) is the
+// integer code times 2^-24 times a power of two fixed by its position; the
+// other operand carries the inverse power, so unpacking a pair of codes is
+// one AND (plus a rotate per V word).  p*s
 // is split into binary16 hi + lo parts (two MFMAs), so products keep about 22
 // bits; q is one binary16 operand when it comes in bfloat16 (exact, see the
 // exponent choice) and hi + lo otherwise; accumulation is fp32.
@@ -114,7 +115,7 @@ attn_mfma_kernel(AttnArgs a) {
   const int t_end = min(a.T, split == 0 ? a.chunk0 : t_begin + a.chunk);
   // fused decode step: split 0 also appends the new token and writes its
   // one-token partial into slot a.splits
-  const bool fuse_here = !KVARN && a.fuse && split == 0;
+  const bool fuse_here = a.fuse && split == 0;
   const int S_tot = a.splits + a.fuse;
   const int n_pat = KVARN ? 0 : a.n_pat;
   const int npat = pad_pat(n_pat);
@@ -381,10 +382,13 @@ attn_mfma_kernel(AttnArgs a) {
   // computed, so the waves of the block finish together whatever their
   // issue priority.
   int cur = first;
-  if constexpr (!KVARN) if (fuse_here && wave < 2) {
+  if (fuse_here && wave < 2) {
     // ---- the new token (position a.enc.t0): wave 0 encodes K, wave 1 V,
     // with the one-token encode of the append path; then its dequantised
-    // vector gives this token's own partial (m = its score, l = 1, o = v^)
+    // vector gives this token's own partial (m = its score, l = 1, o = v^).
+    // KVarN stays in the rotated space of the tiles: score t * (q' . u^)
+    // with q' the prologue's rotated, channel-scaled query and u^ = c s + z,
+    // partial o = t u^ (the combine scales by c_V and rotates back).
     const EncodeArgs& e = a.enc;
     const int kind = wave;
     const int64_t uu = u;
@@ -408,14 +412,20 @@ attn_mfma_kernel(AttnArgs a) {
       m0 = mrow[lane];
       m1 = mrow[lane + 64];
     }
-    const float xh0 = __builtin_fmaf((float)c0, bits2f((uint16_t)(w0 & 0xFFFFu)), bits2f((uint16_t)(w0 >> 16))) + m0;
-    const float xh1 = __builtin_fmaf((float)c1, bits2f((uint16_t)(w1 & 0xFFFFu)), bits2f((uint16_t)(w1 >> 16))) + m1;
+    float xh0 = __builtin_fmaf((float)c0, bits2f((uint16_t)(w0 & 0xFFFFu)), bits2f((uint16_t)(w0 >> 16))) + m0;
+    float xh1 = __builtin_fmaf((float)c1, bits2f((uint16_t)(w1 & 0xFFFFu)), bits2f((uint16_t)(w1 >> 16))) + m1;
+    if (KVARN) {
+      const float tf = bits2f(t16);
+      xh0 *= tf;
+      xh1 *= tf;
+    }
     float* mlp = a.r.ws + (int64_t)a.B * a.Hq * S_tot * D;
     for (int h = 0; h < gq; ++h) {
       const int64_t qrow = (int64_t)b * a.Hq + hq0 + h, row = qrow * S_tot + a.splits;
       if (kind == 0) {
-        float dot = __builtin_fmaf(load_in(a.q, qrow * D + lane, a.bf16), xh0,
-                                   load_in(a.q, qrow * D + lane + 64, a.bf16) * xh1);
+        const float q0 = KVARN ? s_q[h * D + lane] : load_in(a.q, qrow * D + lane, a.bf16);
+        const float q1 = KVARN ? s_q[h * D + lane + 64] : load_in(a.q, qrow * D + lane + 64, a.bf16);
+        float dot = __builtin_fmaf(q0, xh0, q1 * xh1);
         dot = row_sum16(dot);
         dot = (rlane(dot, 0) + rlane(dot, 16)) + (rlane(dot, 32) + rlane(dot, 48));
         if (lane == 0) {
@@ -602,7 +612,7 @@ attn_mfma_kernel(AttnArgs a) {
           for (int g = 0; g < NG; ++g)
             zacc[s * NG + g] = __builtin_fmaf(pt, bits2f((uint16_t)(vszz[g] >> 16)), zacc[s * NG + g]);
         pk[nb][s] = p;
-        s_ps[prow<HB>(head0 + s) + t64] = ldexpf(pt, EP - pv_shift<BITS>(t64 & 31));
+        s_ps[prow<HB>(head0 + s) + t64] = ldexpf(pt, pv_ep<BITS, KVARN>() - pv_shift<BITS, KVARN>(t64 & 31));
         if constexpr (NPB > 0) {
           // p * 2^15 <= 2^15 as binary16 hi + lo (round to nearest even)
           const float x = p * 32768.0f;
@@ -667,23 +677,24 @@ attn_mfma_kernel(AttnArgs a) {
         ah[1] = __builtin_amdgcn_perm(h0[3], h0[2], hsel);
         ah[2] = __builtin_amdgcn_perm(h1[1], h1[0], hsel);
         ah[3] = __builtin_amdgcn_perm(h1[3], h1[2], hsel);
-        // pattern indices of tokens 2p, 2p + 1 in the two 16-bit halves
+        // pattern indices of tokens 2p, 2p + 1 in the high bytes of the two halves
         const uint2 vw = *(const uint2*)(tb + TS::O_VI + 32 * kb + 8 * j);
         uint32_t pr[4];
-        pr[0] = __builtin_amdgcn_perm(0u, vw.x, 0x0C010C00u);
-        pr[1] = __builtin_amdgcn_perm(0u, vw.x, 0x0C030C02u);
-        pr[2] = __builtin_amdgcn_perm(0u, vw.y, 0x0C010C00u);
-        pr[3] = __builtin_amdgcn_perm(0u, vw.y, 0x0C030C02u);
+        pr[0] = __builtin_amdgcn_perm(0u, vw.x, 0x010C000Cu);
+        pr[1] = __builtin_amdgcn_perm(0u, vw.x, 0x030C020Cu);
+        pr[2] = __builtin_amdgcn_perm(0u, vw.y, 0x010C000Cu);
+        pr[3] = __builtin_amdgcn_perm(0u, vw.y, 0x030C020Cu);
 #pragma unroll
         for (int cb = 0; cb < NPB; ++cb) {
-          // B = 2^-24 (binary16 0x0001) where the index equals this column's
-          // pattern, else 0
-          const u16x2 tgt = u16x2{(uint16_t)(16 * cb + n16), (uint16_t)(16 * cb + n16)};
+          // B = 2^-16 (binary16 0x0100: the top of the mantissa, where the
+          // dot product's alignment keeps it whole) where the index equals
+          // this column's pattern, else 0
+          const u16x2 tgt = u16x2{(uint16_t)((16 * cb + n16) << 8), (uint16_t)((16 * cb + n16) << 8)};
           u32x4 B;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const u16x2 d = __builtin_bit_cast(u16x2, pr[q]) ^ tgt;
-            B[q] = __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(u16x2{1, 1}, d));
+            B[q] = __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(u16x2{0x100, 0x100}, d));
           }
           hacc[cb] = mfma16(ah, B, hacc[cb]);
         }
@@ -710,7 +721,7 @@ attn_mfma_kernel(AttnArgs a) {
       const u32x4 w0 = vp[vk], w1 = vp[vk ^ 1];
 #pragma unroll
       for (int bb = 0; bb < 8; ++bb) {
-        const u32x4 B = unpack_v<BITS>(bb < 4 ? w0[bb] : w1[bb - 4], j);
+        const u32x4 B = unpack_v<BITS, KVARN>(bb < 4 ? w0[bb] : w1[bb - 4], j);
         oacc[bb] = mfma16(ahi, B, oacc[bb]);
         oacc[bb] = mfma16(alo, B, oacc[bb]);
       }
@@ -753,7 +764,7 @@ attn_mfma_kernel(AttnArgs a) {
   float* s_ow = (float*)(mf_raw + Lo.tiles);
   float* s_lz = s_ow + MF_WAVES * HB * D;
   {
-    const float oscale = (float)(1 << (24 - EP));
+    const float oscale = (float)(1 << (24 - pv_ep<BITS, KVARN>()));
     const int gcol = n16 / CPG;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -779,14 +790,14 @@ attn_mfma_kernel(AttnArgs a) {
     }
   }
   if constexpr (NPB > 0) {
-    // w = (hi + lo rows) * 2^-15 / 2^-24, relative to the block max
+    // w = (hi + lo rows) * 2^-15 / 2^-16, relative to the block max
 #pragma unroll
     for (int cb = 0; cb < NPB; ++cb) {
       const int pat = 16 * cb + n16;
 #pragma unroll
       for (int s = 0; s < SPL; ++s)
         if (pat < npat)
-          wrow[(head0 + s) * npat + pat] = (hacc[cb][s * NG] + hacc[cb][s * NG + 1]) * (512.0f * f[s]);
+          wrow[(head0 + s) * npat + pat] = (hacc[cb][s * NG] + hacc[cb][s * NG + 1]) * (2.0f * f[s]);
     }
   } else if (!KVARN && n_pat > 0) {
     if (n16 == 0)

@@ -14,8 +14,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int TILE = 64;         // tokens per wave iteration (4 QK column blocks, 2 V tiles)
-constexpr int EQ = 10;           // q operand carries 2^EQ
-constexpr int EP = 4;            // p*s operand carries 2^EP
+constexpr int EQ = 10;           // q operand carries 2^EQ (paired kernel)
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a),
@@ -29,7 +28,9 @@ __device__ __forceinline__ int qk_channel(int j, int c, int i) {
   const int p = i >> 1, e = i & 1;
   return BITS == 2 ? 32 * j + 16 * (c >> 1) + 4 * (c & 1) + 8 * e + p : 32 * j + 8 * c + p + 4 * e;
 }
-// log2 of the power the unpacked code carries in element i
+// Codes enter the MFMA as binary16 subnormals: a field masked in place at
+// bit position b of a 16-bit half is code * 2^(b - 24).  log2 of the power the
+// unpacked K code carries in element i:
 template <int BITS>
 __device__ __forceinline__ int code_shift(int i) {
   const int p = i >> 1;
@@ -48,6 +49,23 @@ __device__ __forceinline__ u32x4 unpack_k(const uint32_t* w, int c) {
   return r;
 }
 
+// The f16 dot product lines the products of a group of 8 elements up on the
+// sum of their exponent fields (a subnormal counts as 2^-14) and truncates
+// about 24 bits below, so a code whose leading bit sits k bits under the top
+// of the 10-bit mantissa keeps only ~24 - k bits, and the error is one-signed.
+// On the K side that error moves scores by a tiny fraction of one code step.
+// On the V side it biases sum_t p_t s_t c_t by up to ~2^-14 of itself when
+// fields sit at the bottom.  In KVarN mode that sum nearly cancels against
+// sum_t p_t z_t, so the bias shows up in full after the inverse rotation:
+// there (PRECISE) V fields are rotated to bit 6 or 8 (2-bit) or 2 or 6
+// (4-bit) before masking, at most 4 (2-bit) or 8 (4-bit) bits under the top,
+// for one rotate more per word.  Otherwise 2-bit fields take the one shift
+// the byte select needs anyway as a rotate to bits 2..8 (at most 8 bits
+// under the top) and 4-bit fields stay in place.
+__device__ __forceinline__ uint32_t rotr32(uint32_t x, int s) {
+  return __builtin_amdgcn_alignbit(x, x, (uint32_t)s);
+}
+
 // ---- V side: lane group j, element i = 2p + e -> token slot of a 32-token tile
 template <int BITS>
 __device__ __forceinline__ int pv_token(int j, int i) {
@@ -55,16 +73,31 @@ __device__ __forceinline__ int pv_token(int j, int i) {
   return BITS == 2 ? 16 * (j >> 1) + 4 * (j & 1) + p + 8 * e : 8 * j + p + 4 * e;
 }
 // power of two the code of token slot tau carries (slot tau & 3 = p)
-template <int BITS>
+template <int BITS, bool PRECISE>
 __device__ __forceinline__ int pv_shift(int tau) {
-  return BITS == 2 ? 2 * (tau & 3) : 4 * (tau & 1);
+  if (BITS == 2) return PRECISE ? 6 + 2 * (tau & 1) : 2 + 2 * (tau & 3);
+  return PRECISE ? 2 + 4 * (tau & 1) : 4 * (tau & 1);
 }
-template <int BITS>
+// the p*s operand carries 2^(pv_ep - shift): at most 2^4
+template <int BITS, bool PRECISE>
+constexpr int pv_ep() { return 4 + (BITS == 2 ? (PRECISE ? 6 : 2) : (PRECISE ? 2 : 0)); }
+template <int BITS, bool PRECISE>
 __device__ __forceinline__ u32x4 unpack_v(uint32_t w, int j) {
   u32x4 r;
-  if (BITS == 2) {
-    const uint32_t x = w >> (8 * (j & 1));
-    r[0] = x & 0x00030003u; r[1] = x & 0x000C000Cu; r[2] = x & 0x00300030u; r[3] = x & 0x00C000C0u;
+  const int sb = 8 * (j & 1);
+  if (BITS == 2 && PRECISE) {
+    // byte j & 1 of each half: fields 0, 1 to bits 6, 8 (rotate left 6),
+    // fields 2, 3 likewise (rotate left 2)
+    const uint32_t xa = rotr32(w, (26 + sb) & 31), xb = rotr32(w, (30 + sb) & 31);
+    r[0] = xa & 0x00C000C0u; r[1] = xa & 0x03000300u; r[2] = xb & 0x00C000C0u; r[3] = xb & 0x03000300u;
+  } else if (BITS == 2) {
+    // byte j & 1 of each half to bits 2..9
+    const uint32_t x = rotr32(w, (30 + sb) & 31);
+    r[0] = x & 0x000C000Cu; r[1] = x & 0x00300030u; r[2] = x & 0x00C000C0u; r[3] = x & 0x03000300u;
+  } else if (PRECISE) {
+    // nibbles 0, 1 to bits 2, 6 (rotate left 2); nibbles 2, 3 likewise (right 6)
+    const uint32_t xa = rotr32(w, 30), xb = rotr32(w, 6);
+    r[0] = xa & 0x003C003Cu; r[1] = xa & 0x03C003C0u; r[2] = xb & 0x003C003Cu; r[3] = xb & 0x03C003C0u;
   } else {
     const uint32_t y = w >> 8;
     r[0] = w & 0x000F000Fu; r[1] = w & 0x00F000F0u; r[2] = y & 0x000F000Fu; r[3] = y & 0x00F000F0u;
@@ -149,17 +182,23 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v + dpp_f<0x140>(v);
 }
 
-// Two fp32 values -> packed binary16 hi parts and lo residuals (both rounded
-// toward zero; hi + lo keeps ~21 significant bits).
+// Two fp32 values -> packed binary16 hi parts and lo residuals, both rounded
+// to nearest even (one v_cvt_pk_f16_f32 each): hi + lo keeps ~22 significant
+// bits and what is left over is unbiased.  (Truncation would leave a
+// one-signed remainder; summed over many tokens whose p s sits in the
+// binary16 subnormal range it becomes a bias, which the KVarN inverse
+// Hadamard gathers into one output channel.)
 // m1 is -1 and z is +0, passed in as values the compiler cannot fold, so that
 // fma(binary16, m1, a) and fma(binary16, p, z) stay single v_fma_mix
 // instructions that read the binary16 operand in place.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void split2(float a, float b, float m1, uint32_t& hi, uint32_t& lo) {
-  auto h = __builtin_amdgcn_cvt_pkrtz(a, b);
+  const f16x2 h = __builtin_convertvector(f32x2{a, b}, f16x2);
   hi = __builtin_bit_cast(uint32_t, h);
   // a - hi is exact
-  auto l = __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf((float)h[0], m1, a),
-                                      __builtin_fmaf((float)h[1], m1, b));
+  const f16x2 l = __builtin_convertvector(
+      f32x2{__builtin_fmaf((float)h[0], m1, a), __builtin_fmaf((float)h[1], m1, b)}, f16x2);
   lo = __builtin_bit_cast(uint32_t, l);
 }
 // p * s with s in binary16 and p >= 0 (exact product rounded once)

@@ -8,7 +8,7 @@
 //
 //  * the first PP_PAIRS waves (score waves) stage the K half of their 64-token
 //    tile, run the QK products, the score epilogue and the online softmax,
-//    and leave p (as p * 2^(EP - shift) for the PV operand and as binary16
+//    and leave p (as p * 2^(pv_ep - shift) for the PV operand and as binary16
 //    hi/lo for the pattern mass) plus the rescale factor of the tile in a slot;
 //  * the other PP_PAIRS waves (value waves) stage the V half of the same tile
 //    one step later and run the PV products, the pattern-mass product and the
@@ -412,7 +412,7 @@ attn_pp_kernel(AttnArgs a) {
               for (int s = 0; s < SPL; ++s) {
                 const float p = __builtin_amdgcn_exp2f(sc[nb][s] - m_run[s]);
                 l_run[s] += p;
-                ps[prow<HB>(head0 + s) + t64] = ldexpf(p, EP - pv_shift<BITS>(t64 & 31));
+                ps[prow<HB>(head0 + s) + t64] = ldexpf(p, pv_ep<BITS, KVARN>() - pv_shift<BITS, KVARN>(t64 & 31));
                 if constexpr (NPB > 0) {
                   // p * 2^15 <= 2^15 as binary16 hi + lo (round to nearest even)
                   const float x = p * 32768.0f;
@@ -472,8 +472,8 @@ attn_pp_kernel(AttnArgs a) {
     const uint32_t hsel = (n16 / NG >= a.gq || n16 % NG > 1) ? 0x0C0C0C0Cu
                           : (n16 % NG == 0 ? 0x05040100u : 0x07060302u);
     // p of this lane's column token t64 = 16 nb + n16 from the PV operand value
-    // p * 2^(EP - shift(t64)); the shift depends on n16 only
-    const float unshift = ldexpf(1.0f, pv_shift<BITS>(n16) - EP);
+    // p * 2^(pv_ep - shift(t64)); the shift depends on n16 only
+    const float unshift = ldexpf(1.0f, pv_shift<BITS, KVARN>(n16) - pv_ep<BITS, KVARN>());
     for (int k = 0; k < n_steps; ++k) {
       const int slot = k & 1;
         const int tile = tile0 + PP_PAIRS * TILE * (k - 1);
@@ -596,23 +596,24 @@ attn_pp_kernel(AttnArgs a) {
               ah[1] = __builtin_amdgcn_perm(h0[3], h0[2], hsel);
               ah[2] = __builtin_amdgcn_perm(h1[1], h1[0], hsel);
               ah[3] = __builtin_amdgcn_perm(h1[3], h1[2], hsel);
-              // pattern indices of tokens 2p, 2p + 1 in the two 16-bit halves
+              // pattern indices of tokens 2p, 2p + 1 in the high bytes of the two halves
               const uint2 vw = *(const uint2*)(vt + PS::V_IX + 32 * kb + 8 * j);
               uint32_t pr[4];
-              pr[0] = __builtin_amdgcn_perm(0u, vw.x, 0x0C010C00u);
-              pr[1] = __builtin_amdgcn_perm(0u, vw.x, 0x0C030C02u);
-              pr[2] = __builtin_amdgcn_perm(0u, vw.y, 0x0C010C00u);
-              pr[3] = __builtin_amdgcn_perm(0u, vw.y, 0x0C030C02u);
+              pr[0] = __builtin_amdgcn_perm(0u, vw.x, 0x010C000Cu);
+              pr[1] = __builtin_amdgcn_perm(0u, vw.x, 0x030C020Cu);
+              pr[2] = __builtin_amdgcn_perm(0u, vw.y, 0x010C000Cu);
+              pr[3] = __builtin_amdgcn_perm(0u, vw.y, 0x030C020Cu);
   #pragma unroll
               for (int cb = 0; cb < NPB; ++cb) {
-                // B = 2^-24 (binary16 0x0001) where the index equals this
-                // column's pattern, else 0
-                const u16x2 tgt = u16x2{(uint16_t)(16 * cb + n16), (uint16_t)(16 * cb + n16)};
+                // B = 2^-16 (binary16 0x0100: the top of the mantissa, where
+                // the dot product's alignment keeps it whole) where the index
+                // equals this column's pattern, else 0
+                const u16x2 tgt = u16x2{(uint16_t)((16 * cb + n16) << 8), (uint16_t)((16 * cb + n16) << 8)};
                 u32x4 Bh;
   #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                   const u16x2 d = __builtin_bit_cast(u16x2, pr[q]) ^ tgt;
-                  Bh[q] = __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(u16x2{1, 1}, d));
+                  Bh[q] = __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(u16x2{0x100, 0x100}, d));
                 }
                 hacc[cb] = mfma16(ah, Bh, hacc[cb]);
               }
@@ -625,7 +626,7 @@ attn_pp_kernel(AttnArgs a) {
             const u32x4 w0 = vp[vk], w1 = vp[vk ^ 1];
   #pragma unroll
             for (int bb = 0; bb < 8; ++bb) {
-              const u32x4 B = unpack_v<BITS>(bb < 4 ? w0[bb] : w1[bb - 4], j);
+              const u32x4 B = unpack_v<BITS, KVARN>(bb < 4 ? w0[bb] : w1[bb - 4], j);
               oacc[bb] = mfma16(ahi, B, oacc[bb]);
               oacc[bb] = mfma16(alo, B, oacc[bb]);
             }
@@ -645,7 +646,7 @@ attn_pp_kernel(AttnArgs a) {
     float f[SPL];
 #pragma unroll
     for (int s = 0; s < SPL; ++s) f[s] = s_f[pair * HB + head0 + s];
-    const float oscale = (float)(1 << (24 - EP));
+    const float oscale = (float)(1 << (24 - pv_ep<BITS, KVARN>()));
     const int gcol = n16 / CPG;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -663,14 +664,14 @@ attn_pp_kernel(AttnArgs a) {
         for (int g = 0; g < NG; ++g)
           s_lz[(pair * HB + head0 + s) * (1 + NG) + 1 + g] = f[s] * zacc[s * NG + g];
     if constexpr (NPB > 0) {
-      // w = (hi + lo rows) * 2^-15 / 2^-24, relative to the block max
+      // w = (hi + lo rows) * 2^-15 / 2^-16, relative to the block max
 #pragma unroll
       for (int cb = 0; cb < NPB; ++cb) {
         const int pat = 16 * cb + n16;
 #pragma unroll
         for (int s = 0; s < SPL; ++s)
           if (pat < npat)
-            wrow[(head0 + s) * npat + pat] = (hacc[cb][s * NG] + hacc[cb][s * NG + 1]) * (512.0f * f[s]);
+            wrow[(head0 + s) * npat + pat] = (hacc[cb][s * NG] + hacc[cb][s * NG + 1]) * (2.0f * f[s]);
       }
     }
     __syncthreads();

@@ -441,10 +441,10 @@ int kvq_decode_step(kvq_cache* cache, const void* k_new, const void* v_new, cons
   const AttnKernel k = cache->n_tokens > 0 && L.max_splits >= 2
                            ? attn_setup(cache, L, q, out, sm_scale, cache->n_tokens, 1, a)
                            : ATTN_VALU;
-  // The fused launch covers the MFMA kernel in PatternKV mode with a
-  // non-empty cache and one q-head block per unit; anything else is the two
+  // The fused launch covers the MFMA kernel (PatternKV and KVarN modes) with
+  // a non-empty cache and one q-head block per unit; anything else is the two
   // calls in sequence.
-  if (k != ATTN_MFMA || c.mode != KVQ_MODE_PATTERN || a.gq > 16 / (D / c.group)) {
+  if (k != ATTN_MFMA || a.gq > 16 / (D / c.group)) {
     int st = kvq_encode_append(cache, k_new, v_new, 1, update_patterns, stream);
     if (st != KVQ_OK) return st;
     return kvq_attn_decode(cache, q, out, sm_scale, stream);
@@ -467,7 +467,7 @@ int kvq_decode_step(kvq_cache* cache, const void* k_new, const void* v_new, cons
   e.max_pat = c.max_patterns;
   e.rho = cache->rho;
   e.tiles_per_block = 1;
-  const bool window = update_patterns && c.pattern_window > 0;
+  const bool window = c.mode == KVQ_MODE_PATTERN && update_patterns && c.pattern_window > 0;
   if (window) {
     e.win_update = 1;
     e.win_close = cache->win_count + 1 == c.pattern_window;

@@ -187,8 +187,9 @@ int kvq_attn_decode(kvq_cache* cache, const void* q, float* out, float sm_scale,
  * decode-stage fusion of PatternKV section 3.4 extended to the append).
  * Cache contents afterwards are identical to the two separate calls; `out`
  * agrees with them to floating-point rounding.  Falls back to the two calls
- * in sequence where the fused launch does not apply (KVARN mode, an empty
- * cache, shapes served by the VALU kernel).
+ * in sequence where the fused launch does not apply (an empty cache, more
+ * q-heads per kv-head than one MFMA row block, shapes served by the VALU
+ * kernel).
  * Errors as kvq_encode_append (n_new = 1) and kvq_attn_decode; nothing is
  * written when a check fails. */
 int kvq_decode_step(kvq_cache* cache, const void* k_new, const void* v_new, const void* q,

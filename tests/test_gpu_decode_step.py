@@ -124,9 +124,12 @@ def test_decode_step_gqa7_two_calls():
     _run(2, 14, 2, 400, 6, P=20, W=4, seed_off=9)
 
 
-def test_decode_step_kvarn_two_calls():
-    """KVarN mode takes the two-call path; results as the separate calls."""
-    _run(2, 8, 2, 300, 6, mode="kvarn", P=0, W=0, seed_off=7)
+@pytest.mark.parametrize("group,bf16", [(32, True), (64, False)])
+def test_decode_step_kvarn(group, bf16):
+    """KVarN mode in one launch: the new token's term in the rotated space
+    (q' . u^ t, partial t u^); group 64 with 4 q-heads takes the virtual
+    half-groups."""
+    _run(2, 8, 2, 300, 6, group=group, mode="kvarn", P=0, W=0, bf16=bf16, seed_off=7)
 
 
 def test_decode_step_capacity_error_writes_nothing():
