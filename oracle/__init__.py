@@ -25,6 +25,7 @@ PATTERN, KVARN = 0, 1
 IN_F32, IN_BF16 = 0, 1
 NONE = 0xFF
 VTILE = 32
+KBLOCK = 128
 
 
 def build(force: bool = True) -> str:
@@ -42,7 +43,8 @@ class _Cfg(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "batch", "n_q_heads", "n_kv_heads", "head_dim", "max_tokens",
         "bits", "group", "mode", "max_patterns", "pattern_window")] + [
-        ("v_alpha", C.c_double), ("in_dtype", C.c_int32), ("shared_patterns", C.c_int32)]
+        ("v_alpha", C.c_double), ("in_dtype", C.c_int32), ("shared_patterns", C.c_int32),
+        ("k_per_channel", C.c_int32)]
 
 
 _lib = None
@@ -146,15 +148,17 @@ class RefCache:
 
     def __init__(self, batch, n_q_heads, n_kv_heads, head_dim, max_tokens, bits=2, group=32,
                  mode=PATTERN, max_patterns=64, pattern_window=128, v_alpha=0.05,
-                 in_dtype=IN_F32, shared_patterns=False):
+                 in_dtype=IN_F32, shared_patterns=False, k_per_channel=False):
         self.cfg = _Cfg(batch, n_q_heads, n_kv_heads, head_dim, max_tokens, bits, group, mode,
-                        max_patterns, pattern_window, v_alpha, in_dtype, int(shared_patterns))
+                        max_patterns, pattern_window, v_alpha, in_dtype, int(shared_patterns),
+                        int(k_per_channel))
         self._h = lib().kvqref_new(C.byref(self.cfg))
         if not self._h:
             raise ValueError("invalid oracle configuration")
         self.U = batch * n_kv_heads
         self.PU = n_kv_heads if shared_patterns else self.U   # pattern-table units
         self.tcap = (max_tokens + VTILE - 1) // VTILE * VTILE
+        self.nblk = (self.tcap + KBLOCK - 1) // KBLOCK
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -246,6 +250,14 @@ class RefCache:
         return self.region("kv"[which] + "_scale").view(np.float32).reshape(
             self.U, self.cfg.head_dim)
 
+    def block_sz(self):
+        """K per channel: binary16 (s, z) [U][block][D][2]."""
+        return self.region("k_bsz").view(np.uint16).reshape(self.U, self.nblk, self.cfg.head_dim, 2)
+
+    def k_tail(self):
+        """K per channel: binary16 residuals of the open block [U][128][D]."""
+        return self.region("k_tail").view(np.uint16).reshape(self.U, KBLOCK, self.cfg.head_dim)
+
     def codes(self, which):
         """Packed code bytes [U][tcap * D * bits / 8] in the stored layout."""
         return self.region("kv"[which] + "_codes").reshape(self.U, -1)
@@ -257,7 +269,7 @@ def attn_exact(k, v, q, n_q_heads, sm_scale=0.0):
     v = np.ascontiguousarray(v, dtype=np.float32)
     q = np.ascontiguousarray(q, dtype=np.float32)
     B, H, T, D = k.shape
-    cfg = _Cfg(B, n_q_heads, H, D, T, 2, D, PATTERN, 0, 0, 0.0, IN_F32, 0)
+    cfg = _Cfg(B, n_q_heads, H, D, T, 2, D, PATTERN, 0, 0, 0.0, IN_F32, 0, 0)
     out = np.zeros((B, n_q_heads, D), np.float32)
     rc = lib().kvqref_attn_exact(C.byref(cfg), _ptr(k), _ptr(v), T, _ptr(q), _ptr(out), sm_scale)
     if rc:

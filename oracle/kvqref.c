@@ -62,6 +62,19 @@
  *      run over every sequence's decode vectors of the window, and each
  *      closure appends one centre per kv-head; every (batch, kv-head) unit
  *      encodes and reconstructs against its kv-head's table.
+ *  R17 K per channel (k_per_channel, PATTERN mode): PatternKV's experiments
+ *      (section 4.1 quantization settings, appendix E) quantise K per channel
+ *      and V per token as KIVI does, K in groups of 128 tokens with a 128-token
+ *      residual that is cleared once its group is quantised.  A K vector
+ *      takes its nearest pattern on arrival (Eq 6, current table, no
+ *      threshold); its residual x - M_k* is rounded to binary16 (nearest-even)
+ *      into the unit's residual buffer at slot t mod 128.  When a block of 128
+ *      tokens is complete, each channel's 128 binary16 residuals (as binary32)
+ *      go through the Eq 1 quantiser (R1-R4 along the token axis): one (s, z)
+ *      per (block, channel), codes in the K layout of R15.  Tokens of the open
+ *      block reconstruct as f32(residual) + M_k*.  Bulk and token-by-token
+ *      appends are the same computation.  V, the Chebyshev window and the
+ *      pattern tables are unchanged.
  */
 #include "kvqref.h"
 
@@ -88,6 +101,9 @@ struct kvqref_cache {
   float* wlo[2];
   float* whi[2];
   float* cscale[2];
+  int32_t nblk;       /* K blocks per unit (k_per_channel) */
+  uint16_t* kbsz;     /* [U][nblk][D][s, z] binary16 */
+  uint16_t* ktail;    /* [U][KBLOCK][D] binary16 residuals of the open block */
 };
 
 /* ------------------------------------------------------------ binary16 */
@@ -314,6 +330,8 @@ static int valid_cfg(const kvqref_cfg* g) {
   if (g->v_alpha >= 0.5) return 0;
   if (g->shared_patterns != 0 && g->shared_patterns != 1) return 0;
   if (g->shared_patterns && g->mode != KVQREF_PATTERN) return 0;
+  if (g->k_per_channel != 0 && g->k_per_channel != 1) return 0;
+  if (g->k_per_channel && g->mode != KVQREF_PATTERN) return 0;
   return 1;
 }
 
@@ -358,6 +376,9 @@ kvqref_cache* kvqref_new(const kvqref_cfg* cfg) {
     c->cscale[k] = (float*)malloc((size_t)(U * D) * 4);
     for (int64_t i = 0; i < U * D; ++i) c->cscale[k][i] = 1.0f;
   }
+  c->nblk = (c->tcap + KVQREF_KBLOCK - 1) / KVQREF_KBLOCK;
+  c->kbsz = (uint16_t*)calloc((size_t)(U * c->nblk * D * 2), 2);
+  c->ktail = (uint16_t*)calloc((size_t)(U * KVQREF_KBLOCK * D), 2);
   reset_window(c);
   return c;
 }
@@ -368,6 +389,8 @@ void kvqref_free(kvqref_cache* c) {
     free(c->codes[k]); free(c->sz[k]); free(c->idx[k]); free(c->t16[k]); free(c->tie[k]);
     free(c->pat[k]); free(c->wlo[k]); free(c->whi[k]); free(c->cscale[k]);
   }
+  free(c->kbsz);
+  free(c->ktail);
   free(c);
 }
 
@@ -426,8 +449,31 @@ static void store_quantised(kvqref_cache* c, int kind, int64_t u, int32_t t, con
   }
 }
 
+/* K per channel (R17): quantise block blk of unit u, channel by channel, from
+ * the binary16 residuals of its 128 tokens. */
+static void quantise_k_block(kvqref_cache* c, int64_t u, int32_t blk) {
+  int D = c->D;
+  float col[KVQREF_KBLOCK];
+  uint8_t codes[KVQREF_KBLOCK], ties[KVQREF_KBLOCK];
+  const uint16_t* tail = c->ktail + u * KVQREF_KBLOCK * D;
+  for (int d = 0; d < D; ++d) {
+    for (int i = 0; i < KVQREF_KBLOCK; ++i) col[i] = kvqref_f16_to_f32(tail[i * D + d]);
+    uint16_t s16, z16;
+    kvqref_quant_group(col, KVQREF_KBLOCK, c->cfg.bits, codes, &s16, &z16, ties);
+    uint16_t* sz = c->kbsz + ((u * c->nblk + blk) * D + d) * 2;
+    sz[0] = s16;
+    sz[1] = z16;
+    for (int i = 0; i < KVQREF_KBLOCK; ++i) {
+      int32_t t = blk * KVQREF_KBLOCK + i;
+      put_code(c, 0, u, t, d, codes[i]);
+      c->tie[0][(u * c->tcap + t) * D + d] = ties[i];
+    }
+  }
+}
+
 /* PatternKV encode of one vector: Eq 6 (nearest pattern, residual), the
- * section 3.3 V threshold, then Eq 1 on the residual. */
+ * section 3.3 V threshold, then Eq 1 on the residual (K per channel: the
+ * residual waits in binary16 for its block, R17). */
 static void encode_pattern_vec(kvqref_cache* c, int kind, int64_t u, int32_t t, const float* x) {
   int D = c->D;
   const float* pats = c->pat[kind] + pu_of(c, u) * (int64_t)c->cfg.max_patterns * D;
@@ -446,6 +492,12 @@ static void encode_pattern_vec(kvqref_cache* c, int kind, int64_t u, int32_t t, 
   float r[MAX_D];
   for (int i = 0; i < D; ++i) r[i] = (k == KVQREF_NONE) ? x[i] : x[i] - pats[(int64_t)k * D + i];
   c->idx[kind][u * c->tcap + t] = (uint8_t)k;
+  if (kind == 0 && c->cfg.k_per_channel) {
+    uint16_t* slot = c->ktail + (u * KVQREF_KBLOCK + t % KVQREF_KBLOCK) * D;
+    for (int i = 0; i < D; ++i) slot[i] = kvqref_f16_round(r[i], 0);
+    if (t % KVQREF_KBLOCK == KVQREF_KBLOCK - 1) quantise_k_block(c, u, t / KVQREF_KBLOCK);
+    return;
+  }
   store_quantised(c, kind, u, t, r);
 }
 
@@ -606,6 +658,23 @@ static void dequant_vec(const kvqref_cache* c, int kind, int64_t u, int32_t t, f
     int k = c->idx[kind][u * c->tcap + t];
     const float* m = (k == KVQREF_NONE) ? NULL
                      : c->pat[kind] + (pu_of(c, u) * c->cfg.max_patterns + k) * (int64_t)D;
+    if (kind == 0 && c->cfg.k_per_channel) {
+      const int32_t blk = t / KVQREF_KBLOCK;
+      const int closed = (int64_t)(blk + 1) * KVQREF_KBLOCK <= c->n_tokens;
+      const uint16_t* bsz = c->kbsz + (u * c->nblk + blk) * (int64_t)D * 2;
+      const uint16_t* res = c->ktail + (u * KVQREF_KBLOCK + t % KVQREF_KBLOCK) * (int64_t)D;
+      for (int d = 0; d < D; ++d) {
+        float r;
+        if (closed) {
+          float q = (float)get_code(c, kind, u, t, d);
+          r = fmaf(q, kvqref_f16_to_f32(bsz[d * 2]), kvqref_f16_to_f32(bsz[d * 2 + 1]));
+        } else {
+          r = kvqref_f16_to_f32(res[d]);
+        }
+        out[d] = m ? r + m[d] : r;
+      }
+      return;
+    }
     for (int d = 0; d < D; ++d) {
       float s = kvqref_f16_to_f32(sz[(d / G) * 2]);
       float z = kvqref_f16_to_f32(sz[(d / G) * 2 + 1]);
@@ -727,6 +796,8 @@ const void* kvqref_region(const kvqref_cache* c, const char* name, int64_t* byte
   if (!strcmp(r, "wlo")) { *bytes = c->PU * D * 4; return c->wlo[kind]; }
   if (!strcmp(r, "whi")) { *bytes = c->PU * D * 4; return c->whi[kind]; }
   if (!strcmp(r, "scale")) { *bytes = U * D * 4; return c->cscale[kind]; }
+  if (!strcmp(name, "k_bsz")) { *bytes = U * c->nblk * D * 4; return c->kbsz; }
+  if (!strcmp(name, "k_tail")) { *bytes = U * KVQREF_KBLOCK * D * 2; return c->ktail; }
   *bytes = 0;
   return NULL;
 }

@@ -34,6 +34,7 @@ enum { KVQREF_PATTERN = 0, KVQREF_KVARN = 1 };
 enum { KVQREF_IN_F32 = 0, KVQREF_IN_BF16 = 1 };
 enum { KVQREF_NONE = 0xFF };      /* stored pattern index meaning "raw" */
 enum { KVQREF_VTILE = 32 };       /* tokens per V code tile */
+enum { KVQREF_KBLOCK = 128 };     /* tokens per K block with k_per_channel */
 
 typedef struct {
   int32_t batch, n_q_heads, n_kv_heads, head_dim, max_tokens;
@@ -41,6 +42,8 @@ typedef struct {
   double v_alpha;                 /* <= 0: V threshold disabled */
   int32_t in_dtype;
   int32_t shared_patterns;        /* PATTERN: 1 = one table and window per kv-head for the batch */
+  int32_t k_per_channel;          /* PATTERN: 1 = K quantised per channel over 128-token blocks,
+                                     the open block's residuals held in binary16 (R17) */
 } kvqref_cfg;
 
 typedef struct kvqref_cache kvqref_cache;
