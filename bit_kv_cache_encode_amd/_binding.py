@@ -28,7 +28,8 @@ class kvq_config(C.Structure):
                 ("head_dim", C.c_int32), ("max_tokens", C.c_int32), ("bits", C.c_int32),
                 ("group", C.c_int32), ("mode", C.c_int32), ("max_patterns", C.c_int32),
                 ("pattern_window", C.c_int32), ("v_alpha", C.c_float), ("in_dtype", C.c_int32),
-                ("max_splits", C.c_int32), ("shared_patterns", C.c_int32)]
+                ("max_splits", C.c_int32), ("shared_patterns", C.c_int32),
+                ("k_per_channel", C.c_int32)]
 
 
 class kvq_layout(C.Structure):
@@ -37,7 +38,8 @@ class kvq_layout(C.Structure):
         "k_tab", "v_tab", "k_win", "v_win", "ws", "cnt",
         "codes_bytes", "sz_bytes", "idx_bytes", "t16_bytes", "tab_bytes", "win_bytes",
         "ws_bytes", "cnt_bytes", "total")] + [(n, C.c_int32) for n in (
-        "token_cap", "n_groups", "record_bytes", "max_splits")]
+        "token_cap", "n_groups", "record_bytes", "max_splits")] + [
+        (n, C.c_uint64) for n in ("k_bsz", "k_tail", "bsz_bytes", "tail_bytes")]
 
 
 class kvq_cache(C.Structure):

@@ -28,6 +28,8 @@ class KVCache:
     mode: "pattern" (PatternKV residual encode) or "kvarn" (Hadamard +
     dual-axis normalisation encode).  shared_patterns (pattern mode): one
     pattern table and Chebyshev window per kv-head for the whole batch.
+    k_per_channel (pattern mode): K quantized per channel over 128-token
+    blocks, the open block's residuals held in binary16.
     Shapes follow include/kvq.h.
     """
 
@@ -36,13 +38,13 @@ class KVCache:
                  max_patterns: int = 64, pattern_window: int = 128, v_alpha: float = 0.05,
                  in_dtype: torch.dtype = torch.bfloat16, max_splits: int = 0,
                  device: str | torch.device = "cuda", buffer: torch.Tensor | None = None,
-                 shared_patterns: bool = False):
+                 shared_patterns: bool = False, k_per_channel: bool = False):
         if in_dtype not in _DT:
             raise ValueError("in_dtype must be torch.float32 or torch.bfloat16")
         m = {"pattern": B.MODE_PATTERN, "kvarn": B.MODE_KVARN}[mode]
         self.cfg = B.kvq_config(batch, n_q_heads, n_kv_heads, head_dim, max_tokens, bits, group,
                                 m, max_patterns, pattern_window, v_alpha, _DT[in_dtype],
-                                max_splits, int(shared_patterns))
+                                max_splits, int(shared_patterns), int(k_per_channel))
         self.layout = B.kvq_layout_of(self.cfg)
         self.device = torch.device(device)
         if self.device.type == "cuda" and self.device.index is None:
@@ -50,6 +52,7 @@ class KVCache:
         self.in_dtype = in_dtype
         self.mode = mode
         self.shared_patterns = bool(shared_patterns)
+        self.k_per_channel = bool(k_per_channel)
         # pattern-table units: one per kv-head when shared, else per (batch, kv-head)
         self.pattern_units = n_kv_heads if shared_patterns else batch * n_kv_heads
         if buffer is None:
@@ -178,15 +181,15 @@ class KVCache:
                 "v_sz": L.sz_bytes, "k_idx": L.idx_bytes, "v_idx": L.idx_bytes,
                 "k_t16": L.t16_bytes, "v_t16": L.t16_bytes, "k_tab": L.tab_bytes,
                 "v_tab": L.tab_bytes, "k_win": L.win_bytes, "v_win": L.win_bytes,
-                "ws": L.ws_bytes, "cnt": L.cnt_bytes}[name]
+                "ws": L.ws_bytes, "cnt": L.cnt_bytes, "k_bsz": L.bsz_bytes,
+                "k_tail": L.tail_bytes}[name]
         off = getattr(L, name)
         return self.buf[off:off + size]
 
     def clone(self) -> "KVCache":
         """An independent cache with a copy of this one's buffer and state."""
         other = KVCache.__new__(KVCache)
-        other.cfg, other.layout, other.device = self.cfg, self.layout, self.device
-        other.in_dtype, other.mode = self.in_dtype, self.mode
+        other.__dict__.update({k: v for k, v in self.__dict__.items() if k not in ("buf", "c")})
         other.buf = self.buf.clone()
         other.c = B.kvq_cache()
         C.memmove(C.addressof(other.c), C.addressof(self.c), C.sizeof(B.kvq_cache))

@@ -123,14 +123,31 @@ __global__ void __launch_bounds__(AT_THREADS) attn_split_kernel(AttnArgs a) {
         const uint32_t* src = (const uint32_t*)(kcodes + (int64_t)t * (D * bits / 8));
         for (int w = 0; w < rec_words; ++w) rec[w] = src[w];
         float tot = 0.0f;
-        for (int g = 0; g < NG; ++g) {
-          float dot = 0.0f;
-          for (int dd = g * G; dd < (g + 1) * G; ++dd)
-            dot = __builtin_fmaf(sh.q[h][dd], (float)code_at(rec, dd, bits), dot);
-          uint32_t p = ksz[(int64_t)t * NG + g];
-          float s = bits2f((uint16_t)(p & 0xFFFF)), z = bits2f((uint16_t)(p >> 16));
-          tot = __builtin_fmaf(s, dot, tot);
-          tot = __builtin_fmaf(z, sh.qsum[h][g], tot);
+        if (a.r.kch) {
+          // K per channel: (s, z) of the token's block for each channel, or
+          // the open block's binary16 residual
+          if (t < a.kclosed) {
+            const uint32_t* bsz = a.r.kbsz + (u * kch_blocks(a.tcap) + t / KBLOCK) * D;
+            for (int dd = 0; dd < D; ++dd) {
+              const uint32_t p = bsz[dd];
+              const float kv = __builtin_fmaf((float)code_at(rec, dd, bits), bits2f((uint16_t)(p & 0xFFFF)),
+                                              bits2f((uint16_t)(p >> 16)));
+              tot = __builtin_fmaf(sh.q[h][dd], kv, tot);
+            }
+          } else {
+            const uint16_t* res = a.r.ktail + (u * KBLOCK + t % KBLOCK) * D;
+            for (int dd = 0; dd < D; ++dd) tot = __builtin_fmaf(sh.q[h][dd], bits2f(res[dd]), tot);
+          }
+        } else {
+          for (int g = 0; g < NG; ++g) {
+            float dot = 0.0f;
+            for (int dd = g * G; dd < (g + 1) * G; ++dd)
+              dot = __builtin_fmaf(sh.q[h][dd], (float)code_at(rec, dd, bits), dot);
+            uint32_t p = ksz[(int64_t)t * NG + g];
+            float s = bits2f((uint16_t)(p & 0xFFFF)), z = bits2f((uint16_t)(p >> 16));
+            tot = __builtin_fmaf(s, dot, tot);
+            tot = __builtin_fmaf(z, sh.qsum[h][g], tot);
+          }
         }
         if (pattern) {
           int k = a.r.idx[0][u * a.tcap + t];

@@ -278,11 +278,13 @@ encode_lane_kernel(EncodeArgs a) {
       szw[g] = (uint32_t)sb | ((uint32_t)zb << 16);
     }
     if (valid) {
-      uint32_t* sz_tok = a.r.sz[kind] + ((u * a.tcap) + t) * a.ngroups;
-#pragma unroll
-      for (int g = 0; g < NGL; ++g) sz_tok[g] = szw[g];
       a.r.idx[kind][u * a.tcap + t] = (uint8_t)kbest;
-      if (kind == 0) {
+      // K per channel keeps only the index here (its block quantizer runs later)
+      uint32_t* sz_tok = a.r.sz[kind] + ((u * a.tcap) + t) * a.ngroups;
+      if (!(kind == 0 && a.r.kch))
+#pragma unroll
+        for (int g = 0; g < NGL; ++g) sz_tok[g] = szw[g];
+      if (kind == 0 && !a.r.kch) {
         uint4* out = (uint4*)(a.r.codes[0] + (u * a.tcap + t) * (D * BITS / 8));
 #pragma unroll
         for (int w = 0; w < D * BITS / 32; w += 4) out[w / 4] = make_uint4(rec[w], rec[w + 1], rec[w + 2], rec[w + 3]);

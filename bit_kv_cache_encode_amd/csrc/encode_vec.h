@@ -284,13 +284,15 @@ __device__ __forceinline__ void encode_vector(const EncodeArgs& a, int kind, int
 __device__ __forceinline__ void store_token(const EncodeArgs& a, int kind, int64_t u, int t,
                                             int lane, uint32_t c0, uint32_t c1, uint32_t w0,
                                             uint32_t w1, int kidx, uint16_t t16) {
-  uint32_t* sz_tok = a.r.sz[kind] + ((u * a.tcap) + t) * a.ngroups;
-  if (lane % a.group == 0) sz_tok[lane / a.group] = w0;
-  if ((lane + 64) % a.group == 0 && a.group <= 64) sz_tok[(lane + 64) / a.group] = w1;
   if (lane == 0) {
     if (a.mode == KVQ_MODE_PATTERN) a.r.idx[kind][u * a.tcap + t] = (uint8_t)kidx;
     else a.r.t16[kind][u * a.tcap + t] = t16;
   }
+  // K per channel keeps only the index here; its block quantizer runs later
+  if (kind == 0 && a.r.kch) return;
+  uint32_t* sz_tok = a.r.sz[kind] + ((u * a.tcap) + t) * a.ngroups;
+  if (lane % a.group == 0) sz_tok[lane / a.group] = w0;
+  if ((lane + 64) % a.group == 0 && a.group <= 64) sz_tok[(lane + 64) / a.group] = w1;
   if (kind == 0) {
     // token-major record: channel d's code at bit bits*d; lanes OR their
     // shifted codes into 32-bit words

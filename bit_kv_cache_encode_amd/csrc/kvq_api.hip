@@ -48,6 +48,8 @@ bool cfg_ok(const kvq_config* c) {
   if (c->max_splits < 0) return false;
   if (c->shared_patterns != 0 && c->shared_patterns != 1) return false;
   if (c->shared_patterns && c->mode != KVQ_MODE_PATTERN) return false;
+  if (c->k_per_channel != 0 && c->k_per_channel != 1) return false;
+  if (c->k_per_channel && (c->mode != KVQ_MODE_PATTERN || gq > MAX_GQ)) return false;
   return true;
 }
 
@@ -131,10 +133,33 @@ Regions regions_of(const kvq_cache* c, const kvq_layout& L) {
   r.win[1] = (float*)(base + L.v_win);
   r.ws = (float*)(base + L.ws);
   r.cnt = (uint32_t*)(base + L.cnt);
+  r.kch = c->cfg.k_per_channel;
+  r.kbsz = (uint32_t*)(base + L.k_bsz);
+  r.ktail = (uint16_t*)(base + L.k_tail);
   return r;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// K per channel after an encode launch of tokens [a.t0, a.t0 + a.n_new): the
+// blocks it completes, then the open block's residuals.
+hipError_t kch_after(const EncodeArgs& a, int units, hipStream_t s) {
+  KchArgs k;
+  memset(&k, 0, sizeof(k));
+  k.r = a.r;
+  k.src = a.src[0];
+  k.src_rows = a.src_rows;
+  k.t0 = a.t0;
+  k.n_new = a.n_new;
+  k.blk0 = a.t0 / KBLOCK;
+  k.blk1 = (a.t0 + a.n_new) / KBLOCK;
+  k.tail0 = k.blk1 * KBLOCK > a.t0 ? k.blk1 * KBLOCK : a.t0;
+  k.tcap = a.tcap;
+  k.bits = a.bits;
+  k.bf16 = a.bf16;
+  k.max_pat = a.max_pat;
+  return launch_kch_append(k, units, s);
+}
 
 }  // namespace
 
@@ -180,6 +205,12 @@ int kvq_layout_of(const kvq_config* cfg, kvq_layout* out) {
   L.ws = place(L.ws_bytes);
   L.cnt_bytes = (uint64_t)cfg->batch * cfg->n_q_heads * 4;   // one per (unit, q-head block) at most
   L.cnt = place(L.cnt_bytes);
+  // K per channel: block scales and the open block's residuals (placed last,
+  // so that the other offsets do not depend on the option)
+  L.bsz_bytes = cfg->k_per_channel ? U * (uint64_t)kch_blocks(tcap) * D * 4 : 0;
+  L.tail_bytes = cfg->k_per_channel ? U * (uint64_t)KBLOCK * D * 2 : 0;
+  L.k_bsz = place(L.bsz_bytes);
+  L.k_tail = place(L.tail_bytes);
   L.total = off;
   *out = L;
   return KVQ_OK;
@@ -316,6 +347,7 @@ int kvq_encode_append(kvq_cache* cache, const void* k_new, const void* v_new, in
     int tpb = (int)(((int64_t)tiles * units * 2 + 2047) / 2048);
     a.tiles_per_block = tpb < 1 ? 1 : tpb;
     hipError_t e = launch_encode(a, units, (tiles + a.tiles_per_block - 1) / a.tiles_per_block, s);
+    if (e == hipSuccess && c.k_per_channel) e = kch_after(a, units, s);
     if (e != hipSuccess) return dev_fail(e);
     cache->n_tokens += n_new;
     return KVQ_OK;
@@ -339,6 +371,7 @@ int kvq_encode_append(kvq_cache* cache, const void* k_new, const void* v_new, in
     const int tiles = (a.t0 + chunk - 1) / VT - a.t0 / VT + 1;
     a.tiles_per_block = tiles;
     hipError_t e = launch_encode(a, units, 1, s);
+    if (e == hipSuccess && c.k_per_channel) e = kch_after(a, units, s);
     // a batch-shared window closes once every unit has folded its vectors in
     if (e == hipSuccess && a.win_close && c.shared_patterns)
       e = launch_window_close(a.r, (int)pattern_units(c), c.max_patterns, a.close_slot, s);
@@ -383,11 +416,12 @@ static AttnKernel attn_setup(const kvq_cache* cache, const kvq_layout& L, const 
   a.mode = c.mode;
   a.n_pat = cache->n_patterns;
   a.max_pat = c.max_patterns;
+  a.kclosed = T / KBLOCK * KBLOCK;
   const float sm = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)D);
   a.qscale = sm * 1.4426950408889634f;
   const int units = c.batch * c.n_kv_heads;
   const char* kenv = getenv("KVQ_ATTN_KERNEL");
-  const bool mfma_ok = mfma_attention_supported(c.bits, c.group, a.gq);
+  const bool mfma_ok = mfma_attention_supported(c.bits, c.group, a.gq) && !c.k_per_channel;
   // the paired kernel serves one q-head block per unit
   const bool pp_ok = mfma_ok && a.gq <= 16 / (D / c.group);
   // (the VALU kernel holds at most MAX_GQ q-heads per kv-head)
@@ -444,7 +478,7 @@ int kvq_decode_step(kvq_cache* cache, const void* k_new, const void* v_new, cons
   // The fused launch covers the MFMA kernel (PatternKV and KVarN modes) with
   // a non-empty cache and one q-head block per unit; anything else is the two
   // calls in sequence.
-  if (k != ATTN_MFMA || a.gq > 16 / (D / c.group)) {
+  if (k != ATTN_MFMA || a.gq > 16 / (D / c.group) || c.k_per_channel) {
     int st = kvq_encode_append(cache, k_new, v_new, 1, update_patterns, stream);
     if (st != KVQ_OK) return st;
     return kvq_attn_decode(cache, q, out, sm_scale, stream);
@@ -516,6 +550,7 @@ int kvq_dequant(const kvq_cache* cache, int32_t which, int32_t tok0, int32_t n, 
   a.bits = c.bits;
   a.mode = c.mode;
   a.max_pat = c.max_patterns;
+  a.n_closed = cache->n_tokens / KBLOCK * KBLOCK;
   hipError_t e = launch_dequant(a, c.batch * c.n_kv_heads, (hipStream_t)stream);
   if (e != hipSuccess) return dev_fail(e);
   return KVQ_OK;

@@ -82,7 +82,14 @@ struct Regions {
   uint32_t* cnt;        // [U] arrival counters of the fused split-K combine
   int pat_h;            // pattern tables and windows per kv-head (= Hkv) when
                         // shared by the batch; 0 = per (batch, kv-head) unit
+  int kch;              // K quantized per channel over KVQ_KBLOCK-token blocks
+  uint32_t* kbsz;       // kch: [U][tcap / KBLOCK][D] packed (s | z << 16)
+  uint16_t* ktail;      // kch: [U][KBLOCK][D] binary16 residuals of the open block
 };
+
+constexpr int KBLOCK = KVQ_KBLOCK;
+// K blocks per unit (token capacity rounded up to whole blocks)
+__host__ __device__ inline int kch_blocks(int tcap) { return (tcap + KBLOCK - 1) / KBLOCK; }
 
 // Pattern-table (and Chebyshev-window) unit of (batch, kv-head) unit u.
 __host__ __device__ inline int64_t pat_unit(const Regions& r, int64_t u) {
@@ -129,15 +136,31 @@ struct AttnArgs {
   // merges splits + 1 partials).  The splits cover tokens [0, T).
   int fuse;
   EncodeArgs enc;
+  int kclosed;          // K per channel: tokens in complete blocks (multiple of KBLOCK)
 };
 
 struct DequantArgs {
   Regions r;
   float* out;           // [U][n][D]
   int which, tok0, n, tcap, ngroups, group, bits, mode, max_pat;
+  int n_closed;         // kch: tokens in complete K blocks (a multiple of KBLOCK)
+};
+
+// K per channel after an append of tokens [t0, t0 + n_new) whose indices are
+// stored: quantize the complete blocks [blk0, blk1) and write the residuals of
+// tokens [tail0, t0 + n_new) of the open block.  Row t - t0 of unit u's input
+// is at src + (u * src_rows + t - t0) * D; residuals of tokens before t0 come
+// from the open-block buffer.
+struct KchArgs {
+  Regions r;
+  const void* src;
+  int src_rows, t0, n_new, blk0, blk1, tail0, tcap, bits, bf16, max_pat;
 };
 
 // Host launchers (each returns the hipError_t of its launch).
+// K per channel: the complete blocks, then (a second launch, after the first
+// has read the buffer) the open block's residuals.
+hipError_t launch_kch_append(const KchArgs& a, int units, hipStream_t s);
 hipError_t launch_fill(float* p, float value, int64_t n, hipStream_t s);
 // (lo, hi) = (+inf, -inf) for `units` windows, as binary32 or (keys != 0) as
 // order keys

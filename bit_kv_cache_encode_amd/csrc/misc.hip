@@ -89,13 +89,31 @@ __global__ void __launch_bounds__(64) dequant_kernel(DequantArgs a) {
   const int w = a.which;
   const uint32_t* sz = a.r.sz[w] + (u * a.tcap + t) * a.ngroups;
   float v[2];
+  if (w == 0 && a.r.kch) {
+    // K per channel: a complete block's (s, z) of the channel, or the open
+    // block's binary16 residual
+    const uint32_t* bsz = a.r.kbsz + (u * kch_blocks(a.tcap) + t / KBLOCK) * D;
+    const uint16_t* res = a.r.ktail + (u * KBLOCK + t % KBLOCK) * D;
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    int d = lane + 64 * k;
-    uint32_t p = sz[d / a.group];
-    float s = bits2f((uint16_t)(p & 0xFFFF)), z = bits2f((uint16_t)(p >> 16));
-    float q = (float)read_code(a.r.codes[w], w, u, t, d, a.tcap, a.bits);
-    v[k] = __builtin_fmaf(q, s, z);
+    for (int k = 0; k < 2; ++k) {
+      const int d = lane + 64 * k;
+      if (t < a.n_closed) {
+        const uint32_t p = bsz[d];
+        const float s = bits2f((uint16_t)(p & 0xFFFF)), z = bits2f((uint16_t)(p >> 16));
+        v[k] = __builtin_fmaf((float)read_code(a.r.codes[0], 0, u, t, d, a.tcap, a.bits), s, z);
+      } else {
+        v[k] = bits2f(res[d]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      int d = lane + 64 * k;
+      uint32_t p = sz[d / a.group];
+      float s = bits2f((uint16_t)(p & 0xFFFF)), z = bits2f((uint16_t)(p >> 16));
+      float q = (float)read_code(a.r.codes[w], w, u, t, d, a.tcap, a.bits);
+      v[k] = __builtin_fmaf(q, s, z);
+    }
   }
   float* out = a.out + (u * a.n + j) * D;
   if (a.mode == KVQ_MODE_PATTERN) {
@@ -130,6 +148,81 @@ __global__ void __launch_bounds__(64) dequant_kernel(DequantArgs a) {
 hipError_t launch_dequant(const DequantArgs& a, int units, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
   hipLaunchKernelGGL(dequant_kernel, dim3(a.n, units), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ K per channel
+// Binary16 residual (nearest-even) of token t >= a.t0 of unit u, channel d:
+// x - M_k* with the index the encode stored, or x for index NONE.
+__device__ __forceinline__ uint16_t kch_residual(const KchArgs& a, int64_t u, int t, int d) {
+  const float x = load_in(a.src, (u * a.src_rows + (t - a.t0)) * D + d, a.bf16);
+  const int k = a.r.idx[0][u * a.tcap + t];
+  if (k == KVQ_INDEX_NONE) return h2bits((_Float16)x);
+  const float m = a.r.tab[0][(pat_unit(a.r, u) * a.max_pat + k) * D + d];
+  return h2bits((_Float16)(x - m));
+}
+
+// One block per (unit, complete block): thread d gathers channel d's 128
+// residuals (the open-block buffer before this append, recomputed from the
+// input after), runs the Eq 1 quantizer down the channel (z rounded down, s
+// rounded up, codes from the stored values), then thread i packs token i's
+// record (channel c at bit bits * c).
+__global__ void __launch_bounds__(KBLOCK) kch_block_kernel(KchArgs a) {
+  __shared__ uint16_t s_r[KBLOCK][D];
+  __shared__ uint8_t s_c[KBLOCK][D + 4];   // rows 33 words apart
+  const int d = threadIdx.x;
+  const int64_t u = blockIdx.x;
+  const int blk = a.blk0 + blockIdx.y, tb = blk * KBLOCK;
+  for (int i = 0; i < KBLOCK; ++i) {
+    const int t = tb + i;
+    s_r[i][d] = t < a.t0 ? a.r.ktail[(u * KBLOCK + i) * D + d] : kch_residual(a, u, t, d);
+  }
+  float lo = bits2f(s_r[0][d]), hi = lo;
+  for (int i = 1; i < KBLOCK; ++i) {
+    const float v = bits2f(s_r[i][d]);
+    lo = fminf(lo, v);
+    hi = fmaxf(hi, v);
+  }
+  const float qmax = (float)((1 << a.bits) - 1);
+  const uint16_t zb = f16_down(lo);
+  const float z = bits2f(zb);
+  const uint16_t sb = f16_up((hi - z) / qmax);
+  const float sf = bits2f(sb);
+  const float inv = sf != 0.0f ? 1.0f / sf : 0.0f;
+  for (int i = 0; i < KBLOCK; ++i) {
+    uint32_t c = 0;
+    if (sf != 0.0f) {
+      const float v = rintf((bits2f(s_r[i][d]) - z) * inv);
+      c = (uint32_t)fminf(fmaxf(v, 0.0f), qmax);
+    }
+    s_c[i][d] = (uint8_t)c;
+  }
+  a.r.kbsz[(u * kch_blocks(a.tcap) + blk) * D + d] = (uint32_t)sb | ((uint32_t)zb << 16);
+  __syncthreads();
+  const int per = 32 / a.bits;
+  uint32_t* out = (uint32_t*)(a.r.codes[0] + (u * a.tcap + tb + d) * (D * a.bits / 8));
+  for (int w = 0; w < D / per; ++w) {
+    uint32_t word = 0;
+    for (int i = 0; i < per; ++i) word |= (uint32_t)s_c[d][w * per + i] << (a.bits * i);
+    out[w] = word;
+  }
+}
+
+// Residuals of this append's tokens in the open block, one thread per channel.
+__global__ void __launch_bounds__(D) kch_tail_kernel(KchArgs a) {
+  const int d = threadIdx.x;
+  const int64_t u = blockIdx.x;
+  for (int t = a.tail0; t < a.t0 + a.n_new; ++t)
+    a.r.ktail[(u * KBLOCK + t % KBLOCK) * D + d] = kch_residual(a, u, t, d);
+}
+
+hipError_t launch_kch_append(const KchArgs& a, int units, hipStream_t s) {
+  if (a.blk1 > a.blk0) {
+    hipLaunchKernelGGL(kch_block_kernel, dim3(units, a.blk1 - a.blk0), dim3(KBLOCK), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.tail0 < a.t0 + a.n_new) hipLaunchKernelGGL(kch_tail_kernel, dim3(units), dim3(D), 0, s, a);
   return hipGetLastError();
 }
 

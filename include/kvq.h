@@ -44,6 +44,17 @@
  *  - idx (PATTERN): one byte per token, the stored pattern index k* of
  *    section 3.2, 0xFF when the raw vector was quantized.
  *  - t16 (KVARN): one binary16 token scale per token.
+ *  - k_per_channel (PATTERN): K is quantized per channel over blocks of
+ *    KVQ_KBLOCK = 128 tokens instead of per token and group (PatternKV's
+ *    experimental setting, section 4.1, after KIVI; appendix E: groups of 128
+ *    with a 128-token residual cleared once its group is quantized).  A K
+ *    vector takes its nearest pattern on arrival (idx as above); its residual
+ *    x - M_k*, rounded to binary16 (nearest-even), waits in k_tail (slot
+ *    t mod 128).  When a block is complete each channel's 128 residuals go
+ *    through the Eq 1 quantizer along the token axis: k_bsz holds one packed
+ *    (s | z << 16) word per block and channel, the codes keep the K layout
+ *    above.  Tokens of the open block reconstruct as residual + M_k*.  The K
+ *    sz region is unused; V is unchanged.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -65,6 +76,7 @@ extern "C" {
 #define KVQ_BF16 1
 #define KVQ_INDEX_NONE 0xFF
 #define KVQ_VTILE 32
+#define KVQ_KBLOCK 128      /* tokens per K block with k_per_channel */
 
 typedef struct {
   int32_t batch;          /* B */
@@ -84,6 +96,9 @@ typedef struct {
                               window per kv-head, shared by the whole batch (the
                               batch-free pattern memory of PatternKV's memory
                               analysis); 0 = per (batch, kv-head) unit */
+  int32_t k_per_channel;  /* PATTERN mode: 1 = K quantized per channel over 128-token
+                             blocks with a binary16 residual for the open block
+                             (see the stored format above); 0 = per token */
 } kvq_config;
 
 /* Byte offsets (from the cache base) and sizes of every region. */
@@ -103,6 +118,9 @@ typedef struct {
   int32_t n_groups;       /* head_dim / group */
   int32_t record_bytes;   /* stored bytes per token per unit and kind */
   int32_t max_splits;
+  uint64_t k_bsz;         /* k_per_channel: packed (s | z << 16) [U][token_cap / 128][D] */
+  uint64_t k_tail;        /* k_per_channel: binary16 residuals [U][128][D] of the open block */
+  uint64_t bsz_bytes, tail_bytes;   /* 0 without k_per_channel */
 } kvq_layout;
 
 typedef struct {
@@ -164,6 +182,8 @@ int kvq_set_patterns(kvq_cache* cache, const float* k_tab, const float* v_tab, i
  * closure adds one centre to h's table (a second, small launch).
  * KVARN: y = Hadamard(x)/sqrt(D), y~ = y / c, t = rms(y~) stored as binary16,
  * u = y~ / t quantized per group (update_patterns is ignored).
+ * k_per_channel: K residuals go to the open block's binary16 buffer, and every
+ * block this append completes is quantized per channel (two more launches).
  * KVQ_ECAPACITY if n_tokens + n_new > max_tokens; KVQ_EINVAL on null inputs
  * or n_new < 0. */
 int kvq_encode_append(kvq_cache* cache, const void* k_new, const void* v_new, int32_t n_new,
@@ -189,7 +209,7 @@ int kvq_attn_decode(kvq_cache* cache, const void* q, float* out, float sm_scale,
  * agrees with them to floating-point rounding.  Falls back to the two calls
  * in sequence where the fused launch does not apply (an empty cache, more
  * q-heads per kv-head than one MFMA row block, shapes served by the VALU
- * kernel).
+ * kernel, k_per_channel).
  * Errors as kvq_encode_append (n_new = 1) and kvq_attn_decode; nothing is
  * written when a check fails. */
 int kvq_decode_step(kvq_cache* cache, const void* k_new, const void* v_new, const void* q,
@@ -198,7 +218,8 @@ int kvq_decode_step(kvq_cache* cache, const void* k_new, const void* v_new, cons
 /* Dequantize tokens tok0 .. tok0+n-1 of K (which = 0) or V (which = 1) into
  * fp32 out [B][Hkv][n][D]: PATTERN x^ = fl(fmaf(q, s, z) + M_k*) (the index
  * restore of section 3.2), or fmaf(q, s, z) alone for index 0xFF; KVARN
- * x^ = Hadamard(fl(fl(fmaf(q, s, z) * t) * c)) / sqrt(D).
+ * x^ = Hadamard(fl(fl(fmaf(q, s, z) * t) * c)) / sqrt(D); k_per_channel K
+ * in the open block x^ = fl(residual + M_k*).
  * KVQ_EINVAL on a bad `which` or a span outside [0, n_tokens). */
 int kvq_dequant(const kvq_cache* cache, int32_t which, int32_t tok0, int32_t n, float* out,
                 void* stream);

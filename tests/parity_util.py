@@ -95,15 +95,44 @@ def assert_same_encode(ref: "O.RefCache", cache, T: int, units=None, ref_units=N
             assert np.array_equal(gt, rt), f"{'KV'[which]} t16 differ at {np.argwhere(gt != rt)[:5]}"
 
 
+def assert_same_kch(ref: "O.RefCache", cache, T: int) -> None:
+    """K per channel: K indices, the complete blocks' codes (ties excused)
+    and (s, z) words, the open block's residuals, and V bit-exact for
+    tokens < T."""
+    c = cache.cfg
+    U, D = c.batch * c.n_kv_heads, c.head_dim
+    closed, nblk = T // O.KBLOCK * O.KBLOCK, T // O.KBLOCK
+    gi, ri = gpu_idx(cache, 0)[:, :T], ref.idx(0)[:, :T]
+    assert np.array_equal(gi, ri), f"K idx differ at {np.argwhere(gi != ri)[:5]}"
+    if closed:
+        gc = gpu_codes(cache, 0, closed)
+        rc = O.unpack_codes(ref.codes(0), 0, closed, D, c.bits)
+        bad = (gc != rc) & (ref.ties(0)[:, :closed] == 0)
+        assert not bad.any(), f"K codes differ at {np.argwhere(bad)[:5]}"
+        gb = cache.region("k_bsz").cpu().numpy().view(np.uint16).reshape(U, -1, D, 2)[:, :nblk]
+        rb = ref.block_sz()[:, :nblk]
+        assert np.array_equal(gb, rb), f"K block (s, z) differ at {np.argwhere(gb != rb)[:5]}"
+    if T % O.KBLOCK:
+        gt = cache.region("k_tail").cpu().numpy().view(np.uint16).reshape(U, O.KBLOCK, D)[:, :T % O.KBLOCK]
+        rt = ref.k_tail()[:, :T % O.KBLOCK]
+        assert np.array_equal(gt, rt), f"K residuals differ at {np.argwhere(gt != rt)[:5]}"
+    gc, rc = gpu_codes(cache, 1, T), O.unpack_codes(ref.codes(1), 1, T, D, c.bits)
+    assert np.array_equal(gc, rc), f"V codes differ at {np.argwhere(gc != rc)[:5]}"
+    assert np.array_equal(gpu_sz(cache, 1)[:, :T], ref.sz(1)[:, :T]), "V scales differ"
+    assert np.array_equal(gpu_idx(cache, 1)[:, :T], ref.idx(1)[:, :T]), "V idx differ"
+
+
 def make_pair(B, Hq, Hkv, max_tokens, *, bits=2, group=32, mode="pattern", max_patterns=32,
-              pattern_window=128, v_alpha=0.05, bf16=True, shared_patterns=False):
+              pattern_window=128, v_alpha=0.05, bf16=True, shared_patterns=False,
+              k_per_channel=False):
     from bit_kv_cache_encode_amd import KVCache
     dt = torch.bfloat16 if bf16 else torch.float32
     gpu = KVCache(B, Hq, Hkv, max_tokens, bits=bits, group=group, mode=mode,
                   max_patterns=max_patterns, pattern_window=pattern_window, v_alpha=v_alpha,
-                  in_dtype=dt, shared_patterns=shared_patterns)
+                  in_dtype=dt, shared_patterns=shared_patterns, k_per_channel=k_per_channel)
     ref = O.RefCache(B, Hq, Hkv, 128, max_tokens, bits=bits, group=group,
                      mode=O.PATTERN if mode == "pattern" else O.KVARN,
                      max_patterns=max_patterns, pattern_window=pattern_window, v_alpha=v_alpha,
-                     in_dtype=O.IN_BF16 if bf16 else O.IN_F32, shared_patterns=shared_patterns)
+                     in_dtype=O.IN_BF16 if bf16 else O.IN_F32, shared_patterns=shared_patterns,
+                     k_per_channel=k_per_channel)
     return gpu, ref, dt

@@ -37,10 +37,11 @@ def test_struct_layout_matches_c(tmp_path):
 #include <stddef.h>
 #include "{HEADER}"
 int main(void) {{
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(kvq_config), sizeof(kvq_layout),
-         sizeof(kvq_cache), offsetof(kvq_cache, base), offsetof(kvq_cache, rho),
-         offsetof(kvq_layout, total), offsetof(kvq_config, max_splits),
-         offsetof(kvq_config, shared_patterns));
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(kvq_config),
+         sizeof(kvq_layout), sizeof(kvq_cache), offsetof(kvq_cache, base),
+         offsetof(kvq_cache, rho), offsetof(kvq_layout, total), offsetof(kvq_config, max_splits),
+         offsetof(kvq_config, shared_patterns), offsetof(kvq_config, k_per_channel),
+         offsetof(kvq_layout, k_bsz), offsetof(kvq_layout, tail_bytes));
   return 0;
 }}''')
     exe = tmp_path / "probe"
@@ -49,7 +50,9 @@ int main(void) {{
                                        check=True).stdout.split()))
     want = [C.sizeof(B.kvq_config), C.sizeof(B.kvq_layout), C.sizeof(B.kvq_cache),
             B.kvq_cache.base.offset, B.kvq_cache.rho.offset, B.kvq_layout.total.offset,
-            B.kvq_config.max_splits.offset, B.kvq_config.shared_patterns.offset]
+            B.kvq_config.max_splits.offset, B.kvq_config.shared_patterns.offset,
+            B.kvq_config.k_per_channel.offset, B.kvq_layout.k_bsz.offset,
+            B.kvq_layout.tail_bytes.offset]
     assert got == want
 
 
@@ -76,13 +79,24 @@ def test_layout_regions():
     assert Ls.tab_bytes == 8 * 32 * 128 * 4 and Ls.win_bytes == 8 * 2 * 128 * 4
     assert L.tab_bytes == U * 32 * 128 * 4 and Ls.codes_bytes == L.codes_bytes
     assert offs  # regions exist
+    # K per channel: block scales and the open block's residuals, placed after
+    # every other region so that the others keep their offsets
+    assert L.bsz_bytes == 0 and L.tail_bytes == 0
+    Lc = B.kvq_layout_of(_cfg(k_per_channel=1, max_tokens=4000))
+    assert Lc.token_cap == 4032 and Lc.bsz_bytes == U * 32 * 128 * 4
+    assert Lc.tail_bytes == U * 128 * 128 * 2
+    assert Lc.k_bsz % 256 == 0 and Lc.k_tail % 256 == 0 and Lc.k_bsz >= Lc.cnt + Lc.cnt_bytes
+    assert Lc.k_tail + Lc.tail_bytes <= Lc.total
+    L0 = B.kvq_layout_of(_cfg(max_tokens=4000))
+    assert all(getattr(Lc, n) == getattr(L0, n) for n in ("k_codes", "v_codes", "k_sz", "ws", "cnt"))
 
 
 @pytest.mark.parametrize("bad", [
     dict(head_dim=64), dict(bits=3), dict(group=48), dict(group=4), dict(n_q_heads=12),
     dict(n_q_heads=136), dict(n_q_heads=72, group=16), dict(max_patterns=256), dict(mode=5), dict(in_dtype=7),
     dict(v_alpha=0.5), dict(max_tokens=0), dict(batch=0), dict(pattern_window=-1),
-    dict(shared_patterns=2), dict(shared_patterns=1, mode=B.MODE_KVARN, max_patterns=0)])
+    dict(shared_patterns=2), dict(shared_patterns=1, mode=B.MODE_KVARN, max_patterns=0),
+    dict(k_per_channel=2), dict(k_per_channel=1, mode=B.MODE_KVARN, max_patterns=0)])
 def test_layout_rejects_bad_configs(bad):
     """(n_q_heads 136 = 17 q-heads per kv-head; 72 at group 16 = 9 q-heads on
     a shape only the VALU attention serves, which holds at most 8.)"""
