@@ -40,10 +40,14 @@ constexpr int MF_THREADS = MF_WAVES * 64;
 
 // Dynamic LDS layout of a block (bytes); npat = padded pattern count.
 struct MfLds {
-  int q, qsum, qe, next, qm, mv, mv_rows, ps, ph, vs, w, alpha, m, o, z, l, wsum, M, last, tiles, total;
+  int q, qsum, qe, next, qm, qa, mv, mv_rows, ps, ph, vs, w, alpha, m, o, z, l, wsum, M, last, tiles,
+      total;
 };
 // mv_rows: rows of M^V staged for the pattern term (0 without the one-hot path)
-__host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes, int mv_rows) {
+// kch: K per channel, which keeps the per-lane q operands of the QK product
+// (64 lanes x 32 fp32, quad-major) for the per-tile q * s operand
+__host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes, int mv_rows,
+                                        bool kch = false) {
   const bool hist_mfma = mv_rows > 0;
   MfLds L;
   int o = 0;
@@ -52,6 +56,7 @@ __host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes
   L.qe = o; o = al16(o + HB * 4);
   L.next = o; o = al16(o + 4);
   L.qm = o; o = al16(o + HB * 256 * 4);
+  L.qa = o; o = al16(o + (kch ? 64 * 32 * 4 : 0));
   const int pw = HB == 4 ? ptab_words<4>() : ptab_words<8>();
   L.ps = o; o = al16(o + MF_WAVES * pw * 4);
   L.ph = o; o = al16(o + (hist_mfma ? MF_WAVES * pw * 4 : 0));
@@ -85,12 +90,13 @@ __host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes
 // word (s (q_a . c_a + q_b . c_b) = s q_a . c_a + s q_b . c_b, and likewise
 // for z and for p s, p z on the V side), which fills the 16 MFMA rows with
 // 4 q-heads at G = 64 instead of leaving half of an 8-head row block idle.
-template <int BITS, int NG, int NGS, bool KVARN, int NPB, bool QLO>
+template <int BITS, int NG, int NGS, bool KVARN, int NPB, bool QLO, bool KCH>
 __global__ void __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_mfma_kernel(AttnArgs a) {
   static_assert(!(KVARN && NPB), "KVarN has no pattern term");
   static_assert(NG == NGS || NG == 2 * NGS, "a stored group spans one or two virtual groups");
-  using TS = TileShape<BITS, NGS, KVARN>;
+  static_assert(!KCH || (!KVARN && QLO), "K per channel: PatternKV mode, q * s needs a lo part");
+  using TS = TileShape<BITS, NGS, KVARN, KCH>;
   constexpr int VPS = NG / NGS;        // virtual groups per stored group
   constexpr int G = D / NG;            // channels per (virtual) group
   constexpr int HB = 16 / NG;          // heads per row block
@@ -119,13 +125,14 @@ attn_mfma_kernel(AttnArgs a) {
   const int S_tot = a.splits + a.fuse;
   const int n_pat = KVARN ? 0 : a.n_pat;
   const int npat = pad_pat(n_pat);
-  const MfLds Lo = mf_lds(HB, NG, npat, TS::BYTES, 16 * NPB);
+  const MfLds Lo = mf_lds(HB, NG, npat, TS::BYTES, 16 * NPB, KCH);
   float* s_q = (float*)(mf_raw + Lo.q);            // [HB][D]
   float* s_qsum = (float*)(mf_raw + Lo.qsum);      // [HB][NG]
   int* s_qe = (int*)(mf_raw + Lo.qe);              // [HB]: max |q| bits, then the exponent
   int* s_next = (int*)(mf_raw + Lo.next);          // next unclaimed tile of the block
   float* s_mv = (float*)(mf_raw + Lo.mv);          // [16 NPB][D] rows of M^V
   float* s_qm = (float*)(mf_raw + Lo.qm);          // [HB][256]; entry 0xFF (no pattern) is 0
+  float4* s_qa = (float4*)(mf_raw + Lo.qa);        // K per channel: [8 quads][64 lanes]
   float* s_ps = (float*)(mf_raw + Lo.ps) + wave * ptab_words<HB>();
   uint32_t* s_ph = (uint32_t*)(mf_raw + Lo.ph) + wave * ptab_words<HB>();
   _Float16* s_vs = (_Float16*)(mf_raw + Lo.vs) + wave * NG * VS_STRIDE;
@@ -160,9 +167,12 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < TS::R_VC; ++r) rvc[r] = vc[lane + 64 * r];
     if (lane < TS::P_KS) {
-      rks = ((const u32x4*)(ksz + (int64_t)tile * NGS * 4))[lane];
-      rvs = ((const u32x4*)(vsz + (int64_t)tile * NGS * 4))[lane];
+      // K per channel: the words of the tile's block (a tile never straddles
+      // a block); those of an open block are not read
+      rks = KCH ? ((const u32x4*)(a.r.kbsz + ((int64_t)u * kch_blocks(a.tcap) + tile / KBLOCK) * D))[lane]
+                : ((const u32x4*)(ksz + (int64_t)tile * NGS * 4))[lane];
     }
+    if (lane < TILE * NGS * 4 / 16) rvs = ((const u32x4*)(vsz + (int64_t)tile * NGS * 4))[lane];
     const int ix_bytes = KVARN ? 2 : 1;
     if (lane < TS::P_IX) rix = ((const u32x4*)(kix_src + (int64_t)tile * ix_bytes))[lane];
     else if (lane < 2 * TS::P_IX)
@@ -174,10 +184,8 @@ attn_mfma_kernel(AttnArgs a) {
     for (int r = 0; r < TS::R_KC; ++r) t4[TS::O_KC / 16 + kpiece<BITS>(lane + 64 * r)] = rkc[r];
 #pragma unroll
     for (int r = 0; r < TS::R_VC; ++r) t4[TS::O_VC / 16 + vpiece(lane + 64 * r)] = rvc[r];
-    if (lane < TS::P_KS) {
-      t4[TS::O_KS / 16 + lane] = rks;
-      t4[TS::O_VS / 16 + lane] = rvs;
-    }
+    if (lane < TS::P_KS) t4[TS::O_KS / 16 + lane] = rks;
+    if (lane < TILE * NGS * 4 / 16) t4[TS::O_VS / 16 + lane] = rvs;
     if (lane < 2 * TS::P_IX) t4[TS::O_KI / 16 + lane] = rix;
   };
 
@@ -324,8 +332,31 @@ attn_mfma_kernel(AttnArgs a) {
   const float k_m1 = __builtin_fmaf(a.qscale, 0.0f, -1.0f);
   const float k_z = a.qscale * 0.0f;
   // QK A operands: row m = n16 -> (h, g); element i of chunk c -> channel.
+  // K per channel: the operand is q * s with s the channel's scale in the
+  // tile's block, so it is rebuilt per tile from this lane's q values, kept
+  // in LDS with the power 2^(e_h - shift - KCH_E) (s < 2^13 in the input
+  // domain, so q * s stays under 2^15).
+  constexpr int KCH_E = 13;
   u32x4 aq_hi[4], aq_lo[QLO ? 4 : 1];
-  {
+  if constexpr (KCH) {
+    if (tid < 64) {
+      const int h = n16 / NG, g = n16 % NG;
+      const int eh = s_qe[h];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int pq = 0; pq < 2; ++pq) {
+          float v[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int i = 2 * (2 * pq + (k >> 1)) + (k & 1), ch = qk_channel<BITS>(j, c, i);
+            v[k] = (ch / G == g) ? ldexpf(s_q[h * D + ch], eh - code_shift<BITS>(i) - KCH_E) : 0.0f;
+          }
+          s_qa[(2 * c + pq) * 64 + lane] = float4{v[0], v[1], v[2], v[3]};
+        }
+    }
+    __syncthreads();
+  } else {
     const int h = n16 / NG, g = n16 % NG;
     const int eh = s_qe[h];
 #pragma unroll
@@ -354,7 +385,7 @@ attn_mfma_kernel(AttnArgs a) {
   // powers) times the softmax scale
   float dsc[SPL];
 #pragma unroll
-  for (int s = 0; s < SPL; ++s) dsc[s] = a.qscale * ldexpf(1.0f, 24 - s_qe[head0 + s]);
+  for (int s = 0; s < SPL; ++s) dsc[s] = a.qscale * ldexpf(1.0f, 24 + (KCH ? KCH_E : 0) - s_qe[head0 + s]);
 
   float m_run[SPL], l_run[SPL], zacc[4];
 #pragma unroll
@@ -458,10 +489,54 @@ attn_mfma_kernel(AttnArgs a) {
     auto tile_body = [&](auto full_tag) {
       constexpr bool FULL = decltype(full_tag)::value;
 
+    // ---- K per channel: a tile of a complete block rebuilds the operand
+    // q * s (hi + lo) and its heads' sum_d q_d z_d; a tile of the open block
+    // scores against the binary16 residuals instead (below).
+    bool open_tile = false;
+    float zq[SPL];
+    if constexpr (KCH) {
+      open_tile = tile >= a.kclosed;
+      if (!open_tile) {
+        const uint32_t* bw = (const uint32_t*)(tb + TS::O_KS);   // [D] (s | z << 16)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          // channels of elements (p, e): qk_channel(j, c, 2p + e), runs of 4 in p
+          const u32x4 w0 = *(const u32x4*)(bw + qk_channel<BITS>(j, c, 0));
+          const u32x4 w1 = *(const u32x4*)(bw + qk_channel<BITS>(j, c, 1));
+          const float4 qa0 = s_qa[(2 * c) * 64 + lane], qa1 = s_qa[(2 * c + 1) * 64 + lane];
+          const float qv[8] = {qa0.x, qa0.y, qa0.z, qa0.w, qa1.x, qa1.y, qa1.z, qa1.w};
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const float x0 = mul_h(qv[2 * p], (uint16_t)(w0[p] & 0xFFFFu), k_z);
+            const float x1 = mul_h(qv[2 * p + 1], (uint16_t)(w1[p] & 0xFFFFu), k_z);
+            uint32_t hi, lo;
+            split2(x0, x1, k_m1, hi, lo);
+            aq_hi[c][p] = hi;
+            aq_lo[QLO ? c : 0][p] = lo;
+          }
+        }
+        // sum_d q_hd z_d: channels 8 n16 .. 8 n16 + 7 per lane, summed over the row
+        const u32x4 z0 = *(const u32x4*)(bw + 8 * n16), z1 = *(const u32x4*)(bw + 8 * n16 + 4);
+#pragma unroll
+        for (int s = 0; s < SPL; ++s) {
+          const float4 q0 = *(const float4*)(s_q + (head0 + s) * D + 8 * n16);
+          const float4 q1 = *(const float4*)(s_q + (head0 + s) * D + 8 * n16 + 4);
+          float acc = mul_h(q0.x, (uint16_t)(z0[0] >> 16), k_z);
+          acc = __builtin_fmaf(q0.y, bits2f((uint16_t)(z0[1] >> 16)), acc);
+          acc = __builtin_fmaf(q0.z, bits2f((uint16_t)(z0[2] >> 16)), acc);
+          acc = __builtin_fmaf(q0.w, bits2f((uint16_t)(z0[3] >> 16)), acc);
+          acc = __builtin_fmaf(q1.x, bits2f((uint16_t)(z1[0] >> 16)), acc);
+          acc = __builtin_fmaf(q1.y, bits2f((uint16_t)(z1[1] >> 16)), acc);
+          acc = __builtin_fmaf(q1.z, bits2f((uint16_t)(z1[2] >> 16)), acc);
+          acc = __builtin_fmaf(q1.w, bits2f((uint16_t)(z1[3] >> 16)), acc);
+          zq[s] = row_sum16(acc) * a.qscale;
+        }
+      }
+    }
     // ---- QK: four independent accumulators (one per 16-token column block)
     // so consecutive MFMAs never wait on each other.
-    f32x4 C[4];
-    {
+    f32x4 C[4] = {};
+    if (!open_tile) {
       // this lane's K words of column block nb: 32 channels of token 16 nb + n16
       auto load_kw = [&](int nb, uint32_t* kw) {
         const int t64 = 16 * nb + n16;
@@ -494,6 +569,37 @@ attn_mfma_kernel(AttnArgs a) {
     for (int nb = 0; nb < 4; ++nb) {
       const int t64 = 16 * nb + n16;
       const bool valid = FULL || t64 < nvalid;
+      if constexpr (KCH) {
+        const int kix = tb[TS::O_KI + t64];   // 0xFF (no pattern) reads a 0 entry
+#pragma unroll
+        for (int s = 0; s < SPL; ++s) {
+          const float qm = s_qm[(head0 + s) * 256 + kix];
+          float v;
+          if (!open_tile) {
+            float dot = 0.0f;
+#pragma unroll
+            for (int g = 0; g < NG; ++g) dot += C[nb][s * NG + g];
+            v = __builtin_fmaf(dot, dsc[s], zq[s] + qm);
+          } else {
+            // open block: q . residual over the whole vector (a rare tile)
+            const uint4* res = (const uint4*)(a.r.ktail + ((int64_t)u * KBLOCK + (tile + t64) % KBLOCK) * D);
+            const float* qh = s_q + (head0 + s) * D;
+            float acc = 0.0f;
+            for (int d8 = 0; d8 < D / 8; ++d8) {
+              const uint4 r8 = res[d8];
+              const uint32_t rw[4] = {r8.x, r8.y, r8.z, r8.w};
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                acc = __builtin_fmaf(qh[8 * d8 + 2 * k], bits2f((uint16_t)(rw[k] & 0xFFFFu)), acc);
+                acc = __builtin_fmaf(qh[8 * d8 + 2 * k + 1], bits2f((uint16_t)(rw[k] >> 16)), acc);
+              }
+            }
+            v = __builtin_fmaf(acc, a.qscale, qm);
+          }
+          sc[nb][s] = valid ? v : -INFINITY;
+        }
+        continue;
+      }
       uint32_t kszw[NG];   // (s, z) word of each virtual group
       {
         const uint32_t* kszp = (const uint32_t*)(tb + TS::O_KS) + t64 * NGS;
@@ -947,20 +1053,20 @@ attn_mfma_kernel(AttnArgs a) {
   if (tid == 0) __hip_atomic_store(&a.r.cnt[cu], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int BITS, int NG, int NGS, bool KVARN, int NPB, bool QLO>
+template <int BITS, int NG, int NGS, bool KVARN, int NPB, bool QLO, bool KCH = false>
 static hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
   constexpr int HB = 16 / NG;
   const int npat = pad_pat(KVARN ? 0 : a.n_pat);
-  const MfLds L = mf_lds(HB, NG, npat, TileShape<BITS, NGS, KVARN>::BYTES, 16 * NPB);
+  const MfLds L = mf_lds(HB, NG, npat, TileShape<BITS, NGS, KVARN, KCH>::BYTES, 16 * NPB, KCH);
   static int attr = 0;
   if (L.total > attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel<BITS, NG, NGS, KVARN, NPB, QLO>,
+    hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel<BITS, NG, NGS, KVARN, NPB, QLO, KCH>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, L.total);
     if (e != hipSuccess) return e;
     attr = L.total;
   }
   const int n_hb = (a.gq + HB - 1) / HB;
-  hipLaunchKernelGGL((attn_mfma_kernel<BITS, NG, NGS, KVARN, NPB, QLO>),
+  hipLaunchKernelGGL((attn_mfma_kernel<BITS, NG, NGS, KVARN, NPB, QLO, KCH>),
                      dim3(a.B * a.Hkv * a.splits * n_hb), dim3(MF_THREADS), L.total, s, a);
   return hipGetLastError();
 }
@@ -974,9 +1080,20 @@ static hipError_t launch_pattern(const AttnArgs& a, hipStream_t s) {
   return launch_one<BITS, NG, NGS, false, 0, QLO>(a, s);
 }
 
+// K per channel: the q * s operand always has a lo part
+template <int BITS, int NG, int NGS>
+static hipError_t launch_kch(const AttnArgs& a, hipStream_t s) {
+  if (a.n_pat <= 0) return launch_one<BITS, NG, NGS, false, 0, true, true>(a, s);
+  if (a.n_pat <= 16) return launch_one<BITS, NG, NGS, false, 1, true, true>(a, s);
+  if (a.n_pat <= 32) return launch_one<BITS, NG, NGS, false, 2, true, true>(a, s);
+  if (a.n_pat <= 64) return launch_one<BITS, NG, NGS, false, 4, true, true>(a, s);
+  return launch_one<BITS, NG, NGS, false, 0, true, true>(a, s);
+}
+
 template <int BITS, int NG, int NGS>
 static hipError_t launch_bits_group(const AttnArgs& a, hipStream_t s) {
   if (a.mode == KVQ_MODE_KVARN) return launch_one<BITS, NG, NGS, true, 0, true>(a, s);
+  if (a.r.kch) return launch_kch<BITS, NG, NGS>(a, s);
   return a.bf16 ? launch_pattern<BITS, NG, NGS, false>(a, s) : launch_pattern<BITS, NG, NGS, true>(a, s);
 }
 

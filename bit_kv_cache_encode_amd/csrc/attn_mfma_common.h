@@ -108,11 +108,13 @@ __device__ __forceinline__ u32x4 unpack_v(uint32_t w, int j) {
 // Per-wave LDS copy of one 64-token tile, byte offsets.  Every segment is
 // contiguous in the cache and 16-byte aligned, so the copy is plain 16-byte
 // loads per lane.
-template <int BITS, int NG, bool KVARN>
+template <int BITS, int NG, bool KVARN, bool KCH = false>
 struct TileShape {
   static constexpr int KREC = D * BITS / 8;
   static constexpr int KC = TILE * KREC;            // K codes
-  static constexpr int KS = TILE * NG * 4;          // K (s, z) words
+  // K (s, z) words: per token and group, or (K per channel) the tile's block's
+  // word for each channel
+  static constexpr int KS = KCH ? D * 4 : TILE * NG * 4;
   static constexpr int VC = 2 * VT * D * BITS / 8;  // two V code tiles
   static constexpr int VS = TILE * NG * 4;          // V (s, z) words
   static constexpr int IX = KVARN ? 2 * TILE : TILE;// K idx or t16; V likewise

@@ -49,7 +49,7 @@ bool cfg_ok(const kvq_config* c) {
   if (c->shared_patterns != 0 && c->shared_patterns != 1) return false;
   if (c->shared_patterns && c->mode != KVQ_MODE_PATTERN) return false;
   if (c->k_per_channel != 0 && c->k_per_channel != 1) return false;
-  if (c->k_per_channel && (c->mode != KVQ_MODE_PATTERN || gq > MAX_GQ)) return false;
+  if (c->k_per_channel && c->mode != KVQ_MODE_PATTERN) return false;
   return true;
 }
 
@@ -421,9 +421,9 @@ static AttnKernel attn_setup(const kvq_cache* cache, const kvq_layout& L, const 
   a.qscale = sm * 1.4426950408889634f;
   const int units = c.batch * c.n_kv_heads;
   const char* kenv = getenv("KVQ_ATTN_KERNEL");
-  const bool mfma_ok = mfma_attention_supported(c.bits, c.group, a.gq) && !c.k_per_channel;
-  // the paired kernel serves one q-head block per unit
-  const bool pp_ok = mfma_ok && a.gq <= 16 / (D / c.group);
+  const bool mfma_ok = mfma_attention_supported(c.bits, c.group, a.gq);
+  // the paired kernel serves one q-head block per unit (and K per token)
+  const bool pp_ok = mfma_ok && a.gq <= 16 / (D / c.group) && !c.k_per_channel;
   // (the VALU kernel holds at most MAX_GQ q-heads per kv-head)
   const bool valu_ok = a.gq <= MAX_GQ;
   const AttnKernel k = (!mfma_ok || (valu_ok && kenv && strcmp(kenv, "valu") == 0)) ? ATTN_VALU

@@ -102,3 +102,37 @@ def test_kch_decode_appends_with_window(fused_call):
         assert err <= ATTN_TOL, f"step {s}: attention err {err}"
         assert gpu.n_patterns == ref.n_patterns
     _check(gpu, ref, B, Hq, T0 + steps, True, step=3)
+
+
+@pytest.mark.parametrize("bits,group,gq,npat", [(2, 32, 4, 32), (2, 64, 4, 16), (2, 64, 8, 24),
+                                                (4, 32, 7, 64), (4, 64, 3, 8), (2, 32, 16, 0)])
+@pytest.mark.parametrize("blocks", [1, 256])
+def test_kch_attention_kernels_agree(monkeypatch, bits, group, gq, npat, blocks):
+    """The matrix-core kernel (q * s operand per tile of a complete block,
+    VALU scores for the open block) and the VALU kernel match the oracle:
+    several blocks plus an open one, one or many splits, virtual groups at
+    G = 64, several q-head blocks (7 and 16 q-heads per kv-head)."""
+    B, H, T = 2, 2, 3 * 128 + 70
+    gpu, ref, dt = make_pair(B, gq * H, H, 512, bits=bits, group=group, max_patterns=max(npat, 1),
+                             k_per_channel=True)
+    k, v = _kv(B, H, T, off=gq + bits)
+    if npat:
+        assert ref.init_patterns(to_oracle(k[:, :, :128], True), to_oracle(v[:, :, :128], True), npat) == 0
+        gpu.init_patterns(to_dev(k[:, :, :128], dt), to_dev(v[:, :, :128], dt), npat)
+    assert ref.encode_append(to_oracle(k, True), to_oracle(v, True)) == 0
+    gpu.encode_append(to_dev(k, dt), to_dev(v, dt))
+    monkeypatch.setenv("KVQ_ATTN_BLOCKS", str(blocks))
+    for step, qmul in ((0, 1.0), (1, 6.0)):
+        q = synth.queries(B, gq * H, D, step=step) * np.float32(qmul)
+        want = ref.attn_decode(to_oracle(q, True))
+        errs = {}
+        for kern in ("", "valu") if gq <= 8 else ("",):
+            if kern:
+                monkeypatch.setenv("KVQ_ATTN_KERNEL", kern)
+            else:
+                monkeypatch.delenv("KVQ_ATTN_KERNEL", raising=False)
+            print(f"k per channel kernels bits={bits} group={group} gq={gq} kern={kern or 'mfma'}",
+                  flush=True)
+            got = gpu.attn_decode(to_dev(q, dt)).cpu().numpy()
+            errs[kern or "mfma"] = float(np.abs(got - want).max())
+        assert max(errs.values()) <= ATTN_TOL, errs
