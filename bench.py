@@ -44,6 +44,9 @@ ATTN_CONFIGS = {
     "long4bit": dict(B=1, Hq=32, H=8, T=131072, bits=4, group=64, P=64, mode="pattern"),
     "kvarn": dict(B=64, Hq=32, H=8, T=16384, bits=2, group=32, P=0, mode="kvarn"),
     "qwen": dict(B=32, Hq=28, H=4, T=32768, bits=2, group=32, P=64, mode="pattern"),
+    # K per channel over 128-token blocks (PatternKV's KIVI-style setting): the
+    # 32k context plus 64 tokens in the open block
+    "kivi": dict(B=8, Hq=32, H=8, T=32832, bits=2, group=32, P=32, mode="pattern", kch=True),
 }
 
 
@@ -56,8 +59,9 @@ def attn_config(name):
     D = 128
     B, Hq, H, T = c["B"], c["Hq"], c["H"], c["T"]
     k, v = synth.device_kv(B, H, T, D, device=dev)
+    kch = c.get("kch", False)
     cache = KVCache(B, Hq, H, T + 64, bits=c["bits"], group=c["group"], mode=c["mode"],
-                    max_patterns=max(c["P"], 1), device=dev)
+                    max_patterns=max(c["P"], 1), device=dev, k_per_channel=kch)
     if c["mode"] == "pattern":
         cache.init_patterns(k[:, :, :2048].contiguous(), v[:, :, :2048].contiguous(), c["P"])
     else:
@@ -78,10 +82,29 @@ def attn_config(name):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / n
     rec = cache.layout.record_bytes
-    nbytes = 2 * B * H * T * rec + 2 * B * H * c["P"] * D * 4 + B * Hq * D * 6
-    print(json.dumps({"attn_config": name, "shape": c, "us_per_call": round(us, 2),
-                      "algorithmic_bytes": nbytes, "effective_GBs": round(nbytes / us / 1e3, 1),
-                      "frac_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}))
+    if kch:
+        # K: codes + index per token, one (s, z) word per channel and complete
+        # block, binary16 residuals of the open block; V per token as usual
+        closed = T // 128 * 128
+        k_bytes = T * (D * c["bits"] // 8 + 1) + closed // 128 * D * 4 + (T - closed) * D * 2
+        nbytes = B * H * (k_bytes + T * rec) + 2 * B * H * c["P"] * D * 4 + B * Hq * D * 6
+    else:
+        nbytes = 2 * B * H * T * rec + 2 * B * H * c["P"] * D * 4 + B * Hq * D * 6
+    res = {"attn_config": name, "shape": c, "us_per_call": round(us, 2),
+           "algorithmic_bytes": nbytes, "effective_GBs": round(nbytes / us / 1e3, 1),
+           "frac_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+    if kch:
+        # a decode step here is the append of one token (encode, the open
+        # block's residual write) and the attention: separate launches
+        kn, vn = synth.device_kv(B, H, 1, D, layer=1, device=dev)
+        steps = 10
+        e0.record()
+        for _ in range(steps):
+            cache.decode_step(kn, vn, q, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        res["decode_step_us"] = round(e0.elapsed_time(e1) * 1e3 / steps, 2)
+    print(json.dumps(res))
 
 
 def parse():
@@ -111,7 +134,9 @@ def parse():
                     help="secondary measurement: decode attention alone on another workload "
                          "shape (long4bit: B 1, 131072 tokens, 4-bit G64, 64 patterns; "
                          "kvarn: 64 samples x 16384, KVarN 2-bit; qwen: B 32, 28 q / 4 kv "
-                         "heads, 32768 tokens, 64 patterns); prints one JSON line")
+                         "heads, 32768 tokens, 64 patterns; kivi: the step's shapes with K "
+                         "quantised per channel over 128-token blocks, 32832 tokens); prints one "
+                         "JSON line")
     ap.add_argument("--traffic-from", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "RAW_DIR"),
                     help="no GPU: summarise three rocprofv3 --pmc runs of --attn-only N "
                          "--calib-copy M (FETCH_SIZE; WRITE_SIZE; TCC_EA0_RDREQ 32B/64B/128B) "

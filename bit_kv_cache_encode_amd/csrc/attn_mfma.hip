@@ -195,7 +195,9 @@ attn_mfma_kernel(AttnArgs a) {
   const int n_tiles = (t_end - t_begin + TILE - 1) / TILE;
   // in the fused step waves 0 and 1 of split 0 encode the new token first and
   // take their tiles from the counter afterwards
-  const int first = !fuse_here ? wave : (wave < 2 ? n_tiles : wave - 2);
+  // K per channel: a wave takes both tiles of a 128-token block (splits start
+  // on block boundaries), so the q * s operand serves two tiles
+  const int first = KCH ? 2 * wave : !fuse_here ? wave : (wave < 2 ? n_tiles : wave - 2);
   if (first < n_tiles) issue(t_begin + TILE * first);
   // M^V rows for the pattern term go straight to LDS (no registers held
   // through the loop); 16 bytes per lane, one kilobyte per wave instruction.
@@ -413,6 +415,9 @@ attn_mfma_kernel(AttnArgs a) {
   // computed, so the waves of the block finish together whatever their
   // issue priority.
   int cur = first;
+  // K per channel: block whose q * s operand and z sums are in registers
+  int kch_built = -1;
+  float zq[SPL];
   if (fuse_here && wave < 2) {
     // ---- the new token (position a.enc.t0): wave 0 encodes K, wave 1 V,
     // with the one-token encode of the append path; then its dequantised
@@ -481,8 +486,13 @@ attn_mfma_kernel(AttnArgs a) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     int nxt = 0;
-    if (lane == 0) nxt = atomicAdd(s_next, 1);
-    nxt = __builtin_amdgcn_readfirstlane(nxt);
+    if (KCH && (cur & 1) == 0 && cur + 1 < n_tiles) {
+      nxt = cur + 1;
+    } else {
+      if (lane == 0) nxt = atomicAdd(s_next, 1);
+      nxt = __builtin_amdgcn_readfirstlane(nxt);
+      if (KCH) nxt *= 2;
+    }
     if (nxt < n_tiles) issue(t_begin + TILE * nxt);
     cur = nxt;
     const int nvalid = t_end - tile;
@@ -493,10 +503,10 @@ attn_mfma_kernel(AttnArgs a) {
     // q * s (hi + lo) and its heads' sum_d q_d z_d; a tile of the open block
     // scores against the binary16 residuals instead (below).
     bool open_tile = false;
-    float zq[SPL];
     if constexpr (KCH) {
       open_tile = tile >= a.kclosed;
-      if (!open_tile) {
+      if (!open_tile && tile / KBLOCK != kch_built) {
+        kch_built = tile / KBLOCK;
         const uint32_t* bw = (const uint32_t*)(tb + TS::O_KS);   // [D] (s | z << 16)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {

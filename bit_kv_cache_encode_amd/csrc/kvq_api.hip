@@ -439,6 +439,9 @@ static AttnKernel attn_setup(const kvq_cache* cache, const kvq_layout& L, const 
   const int lead = reserve ? FUSED_LEAD_TOKENS : 0;
   int chunk = (a.T + lead + want - 1) / want;
   chunk = (chunk + ATTN_MIN_CHUNK - 1) / ATTN_MIN_CHUNK * ATTN_MIN_CHUNK;
+  // K per channel: splits start on block boundaries (the MFMA kernel hands
+  // out both tiles of a block to one wave)
+  if (c.k_per_channel) chunk = (chunk + KBLOCK - 1) / KBLOCK * KBLOCK;
   int chunk0 = chunk - lead < ATTN_MIN_CHUNK ? ATTN_MIN_CHUNK : chunk - lead;
   a.chunk = chunk;
   a.chunk0 = chunk0;
