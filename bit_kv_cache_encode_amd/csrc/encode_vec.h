@@ -237,6 +237,12 @@ __device__ __forceinline__ void encode_vector(const EncodeArgs& a, int kind, int
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
+    if (kind == 0 && a.kch_tail_direct) {
+      // K per channel: the residual waits in binary16 (nearest-even) for its block
+      uint16_t* slot = a.r.ktail + (u * KBLOCK + a.t0 % KBLOCK) * D;
+      slot[lane] = h2bits((_Float16)r0);
+      slot[lane + 64] = h2bits((_Float16)r1);
+    }
     quantize_pair(r0, r1, lane, a.group, a.bits, c0, c1, w0, w1);
   } else {
     // KVarN reading: FWHT (stages h = 1..64), 1/sqrt(D), channel scale,

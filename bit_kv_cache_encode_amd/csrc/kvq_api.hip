@@ -154,6 +154,7 @@ hipError_t kch_after(const EncodeArgs& a, int units, hipStream_t s) {
   k.blk0 = a.t0 / KBLOCK;
   k.blk1 = (a.t0 + a.n_new) / KBLOCK;
   k.tail0 = k.blk1 * KBLOCK > a.t0 ? k.blk1 * KBLOCK : a.t0;
+  if (a.kch_tail_direct) k.tail0 = a.t0 + a.n_new;   // the encode wrote it
   k.tcap = a.tcap;
   k.bits = a.bits;
   k.bf16 = a.bf16;
@@ -341,6 +342,7 @@ int kvq_encode_append(kvq_cache* cache, const void* k_new, const void* v_new, in
     a.n_new = n_new;
     a.t0 = cache->n_tokens;
     a.n_pat = cache->n_patterns;
+    a.kch_tail_direct = c.k_per_channel && n_new == 1 && (a.t0 + 1) % KBLOCK != 0;
     const int tiles = (a.t0 + n_new - 1) / VT - a.t0 / VT + 1;
     // about 2048 blocks in all, so that each block's pattern-table copy
     // serves many tokens
@@ -368,6 +370,7 @@ int kvq_encode_append(kvq_cache* cache, const void* k_new, const void* v_new, in
     a.win_update = 1;
     a.win_close = cache->win_count + chunk == c.pattern_window;
     a.close_slot = cache->n_patterns < c.max_patterns ? cache->n_patterns : -1;
+    a.kch_tail_direct = c.k_per_channel && chunk == 1 && (a.t0 + 1) % KBLOCK != 0;
     const int tiles = (a.t0 + chunk - 1) / VT - a.t0 / VT + 1;
     a.tiles_per_block = tiles;
     hipError_t e = launch_encode(a, units, 1, s);

@@ -118,6 +118,8 @@ struct EncodeArgs {
   int win_update;       // accumulate the Chebyshev window over these tokens
   int win_close;        // this call ends a window
   int close_slot;       // table slot for the new centre, -1 = dropped
+  int kch_tail_direct;  // K per channel, one token that leaves its block open:
+                        // the encode stores its binary16 residual itself
 };
 
 struct AttnArgs {

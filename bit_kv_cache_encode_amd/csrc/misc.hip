@@ -162,20 +162,48 @@ __device__ __forceinline__ uint16_t kch_residual(const KchArgs& a, int64_t u, in
   return h2bits((_Float16)(x - m));
 }
 
+// OR of this lane's value and the N lanes before it within its 16-lane DPP
+// row (row_shr with zeros shifted in)
+template <int N>
+__device__ __forceinline__ uint32_t or_shr(uint32_t v) {
+  return v | (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x110 + N, 0xF, 0xF, true);
+}
+
 // One block per (unit, complete block): thread d gathers channel d's 128
 // residuals (the open-block buffer before this append, recomputed from the
 // input after), runs the Eq 1 quantizer down the channel (z rounded down, s
-// rounded up, codes from the stored values), then thread i packs token i's
-// record (channel c at bit bits * c).
+// rounded up, codes from the stored values), and for each token the 32/bits
+// channels of one record word (consecutive lanes of a DPP row) OR their
+// shifted codes together; the row's last lane of each word stores it.
 __global__ void __launch_bounds__(KBLOCK) kch_block_kernel(KchArgs a) {
   __shared__ uint16_t s_r[KBLOCK][D];
-  __shared__ uint8_t s_c[KBLOCK][D + 4];   // rows 33 words apart
+  __shared__ int s_k[KBLOCK];              // pattern index of each token
   const int d = threadIdx.x;
   const int64_t u = blockIdx.x;
   const int blk = a.blk0 + blockIdx.y, tb = blk * KBLOCK;
-  for (int i = 0; i < KBLOCK; ++i) {
-    const int t = tb + i;
-    s_r[i][d] = t < a.t0 ? a.r.ktail[(u * KBLOCK + i) * D + d] : kch_residual(a, u, t, d);
+  s_k[d] = a.r.idx[0][u * a.tcap + tb + d];
+  __syncthreads();
+  // residuals, 8 tokens' loads in flight at a time
+  const float* tab = a.r.tab[0] + pat_unit(a.r, u) * a.max_pat * D + d;
+  for (int i0 = 0; i0 < KBLOCK; i0 += 8) {
+    float x[8], m[8];
+    uint16_t old[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int t = tb + i0 + e, k = s_k[i0 + e];
+      if (t < a.t0) {
+        old[e] = a.r.ktail[(u * KBLOCK + i0 + e) * D + d];
+      } else {
+        x[e] = load_in(a.src, (u * a.src_rows + (t - a.t0)) * D + d, a.bf16);
+        m[e] = k == KVQ_INDEX_NONE ? 0.0f : tab[(int64_t)k * D];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int t = tb + i0 + e, k = s_k[i0 + e];
+      // x - M_k* (x alone for index NONE), binary16 nearest-even
+      s_r[i0 + e][d] = t < a.t0 ? old[e] : h2bits((_Float16)(k == KVQ_INDEX_NONE ? x[e] : x[e] - m[e]));
+    }
   }
   float lo = bits2f(s_r[0][d]), hi = lo;
   for (int i = 1; i < KBLOCK; ++i) {
@@ -189,22 +217,20 @@ __global__ void __launch_bounds__(KBLOCK) kch_block_kernel(KchArgs a) {
   const uint16_t sb = f16_up((hi - z) / qmax);
   const float sf = bits2f(sb);
   const float inv = sf != 0.0f ? 1.0f / sf : 0.0f;
+  a.r.kbsz[(u * kch_blocks(a.tcap) + blk) * D + d] = (uint32_t)sb | ((uint32_t)zb << 16);
+  const int per = 32 / a.bits;             // channels per record word: 16 or 8
+  const int sh = a.bits * (d % per);
+  uint32_t* rec = (uint32_t*)(a.r.codes[0] + (u * a.tcap + tb) * (D * a.bits / 8)) + d / per;
+  const int rec_words = D * a.bits / 32;
   for (int i = 0; i < KBLOCK; ++i) {
     uint32_t c = 0;
     if (sf != 0.0f) {
       const float v = rintf((bits2f(s_r[i][d]) - z) * inv);
       c = (uint32_t)fminf(fmaxf(v, 0.0f), qmax);
     }
-    s_c[i][d] = (uint8_t)c;
-  }
-  a.r.kbsz[(u * kch_blocks(a.tcap) + blk) * D + d] = (uint32_t)sb | ((uint32_t)zb << 16);
-  __syncthreads();
-  const int per = 32 / a.bits;
-  uint32_t* out = (uint32_t*)(a.r.codes[0] + (u * a.tcap + tb + d) * (D * a.bits / 8));
-  for (int w = 0; w < D / per; ++w) {
-    uint32_t word = 0;
-    for (int i = 0; i < per; ++i) word |= (uint32_t)s_c[d][w * per + i] << (a.bits * i);
-    out[w] = word;
+    uint32_t w = or_shr<4>(or_shr<2>(or_shr<1>(c << sh)));
+    if (per == 16) w = or_shr<8>(w);
+    if (d % per == per - 1) rec[i * rec_words] = w;
   }
 }
 

@@ -136,3 +136,21 @@ def test_kch_attention_kernels_agree(monkeypatch, bits, group, gq, npat, blocks)
             got = gpu.attn_decode(to_dev(q, dt)).cpu().numpy()
             errs[kern or "mfma"] = float(np.abs(got - want).max())
         assert max(errs.values()) <= ATTN_TOL, errs
+
+
+def test_kch_single_token_appends_without_patterns():
+    """One-token appends store their residual from the encode itself (no
+    pattern table here, so the residual is the raw vector); the 128th token
+    closes the block through the block quantiser instead."""
+    B, H, Hq, T0, steps = 2, 2, 8, 120, 12
+    gpu, ref, dt = make_pair(B, Hq, H, 256, max_patterns=0, pattern_window=0, k_per_channel=True)
+    k, v = _kv(B, H, T0 + steps, off=17)
+    assert ref.encode_append(to_oracle(k[:, :, :T0], True), to_oracle(v[:, :, :T0], True)) == 0
+    gpu.encode_append(to_dev(k[:, :, :T0], dt), to_dev(v[:, :, :T0], dt))
+    for s in range(steps):
+        t = T0 + s
+        kn, vn = k[:, :, t:t + 1].copy(), v[:, :, t:t + 1].copy()
+        assert ref.encode_append(to_oracle(kn, True), to_oracle(vn, True)) == 0
+        print(f"k per channel single token {t}", flush=True)
+        gpu.encode_append(to_dev(kn, dt), to_dev(vn, dt))
+        _check(gpu, ref, B, Hq, t + 1, True, step=s)
