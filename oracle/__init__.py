@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvqref.c")
 _LIB = os.path.join(_HERE, "libkvqref.so")
 
-PATTERN, KVARN = 0, 1
+PATTERN, KVARN, NSN = 0, 1, 2
 IN_F32, IN_BF16 = 0, 1
 NONE = 0xFF
 VTILE = 32
@@ -237,7 +237,12 @@ class RefCache:
         return self.region("kv"[which] + "_idx").reshape(self.U, self.tcap)
 
     def t16(self, which):
+        """KVARN token scale, or NSN first norm n1 (binary16 bits)."""
         return self.region("kv"[which] + "_t16").view(np.uint16).reshape(self.U, self.tcap)
+
+    def t2(self, which):
+        """NSN second norm n2 (binary16 bits)."""
+        return self.region("kv"[which] + "_t2").view(np.uint16).reshape(self.U, self.tcap)
 
     def ties(self, which):
         return self.region("kv"[which] + "_tie").reshape(self.U, self.tcap, self.cfg.head_dim)

@@ -75,6 +75,18 @@
  *      block reconstruct as f32(residual) + M_k*.  Bulk and token-by-token
  *      appends are the same computation.  V, the Chebyshev window and the
  *      pattern tables are unchanged.
+ *  R18 NSN scalar mode (NSNQuant, abstract: token-wise normalisation,
+ *      channel-wise centring, token-wise normalisation, with a Hadamard
+ *      transform; its vector-quantisation codebook is out of scope, so the
+ *      normalised vector goes through the Eq 1 quantiser, at 1, 2 or 4 bits):
+ *      n1 = sqrtf(fl(ss(x) * (1/D))) with ss the halving-fold sum of squares
+ *      (as R11), stored as RNE binary16; a = x * fl(1/n1); b = a - mu with mu
+ *      the unit's channel centre; n2 likewise from b, stored as RNE binary16;
+ *      y = FWHT(b * fl(1/n2)) * fp32(1/sqrt(D)); Eq 1 on y.  A zero n1 or n2
+ *      gives zero codes and scales from that point.  Reconstruction:
+ *      w = FWHT(fmaf(q, s, z)) * fp32(1/sqrt(D)), x^ = fl(fl(fl(w * n2) + mu) * n1).
+ *      mu = mean over the prefix tokens of x / rms(x) in binary64 (tokens with
+ *      rms 0 skipped), rounded to fp32; 0 before any init.
  */
 #include "kvqref.h"
 
@@ -95,7 +107,8 @@ struct kvqref_cache {
   uint8_t* codes[2];
   uint16_t* sz[2];
   uint8_t* idx[2];
-  uint16_t* t16[2];
+  uint16_t* t16[2];   /* KVARN: token scale t; NSN: first norm n1 */
+  uint16_t* t2[2];    /* NSN: second norm n2 */
   uint8_t* tie[2];
   float* pat[2];
   float* wlo[2];
@@ -319,11 +332,11 @@ static int valid_cfg(const kvqref_cfg* g) {
   if (g->batch <= 0 || g->n_kv_heads <= 0 || g->n_q_heads <= 0) return 0;
   if (g->n_q_heads % g->n_kv_heads) return 0;
   if (g->head_dim <= 0 || g->head_dim > MAX_D || g->max_tokens <= 0) return 0;
-  if (g->bits != 2 && g->bits != 4) return 0;
+  if (g->bits != 2 && g->bits != 4 && !(g->bits == 1 && g->mode == KVQREF_NSN)) return 0;
   if (g->group <= 0 || g->head_dim % g->group) return 0;
   if ((g->group * g->bits) % 8) return 0;
-  if (g->mode != KVQREF_PATTERN && g->mode != KVQREF_KVARN) return 0;
-  if (g->mode == KVQREF_KVARN && (g->head_dim & (g->head_dim - 1))) return 0;
+  if (g->mode != KVQREF_PATTERN && g->mode != KVQREF_KVARN && g->mode != KVQREF_NSN) return 0;
+  if (g->mode != KVQREF_PATTERN && (g->head_dim & (g->head_dim - 1))) return 0;
   if (g->max_patterns < 0 || g->max_patterns > 255) return 0;
   if (g->pattern_window < 0) return 0;
   if (g->in_dtype != KVQREF_IN_F32 && g->in_dtype != KVQREF_IN_BF16) return 0;
@@ -369,12 +382,13 @@ kvqref_cache* kvqref_new(const kvqref_cfg* cfg) {
     c->idx[k] = (uint8_t*)malloc((size_t)(U * T));
     memset(c->idx[k], KVQREF_NONE, (size_t)(U * T));
     c->t16[k] = (uint16_t*)calloc((size_t)(U * T), 2);
+    c->t2[k] = (uint16_t*)calloc((size_t)(U * T), 2);
     c->tie[k] = (uint8_t*)calloc((size_t)(U * T * D), 1);
     c->pat[k] = (float*)calloc((size_t)(c->PU * (cfg->max_patterns ? cfg->max_patterns : 1) * D), 4);
     c->wlo[k] = (float*)malloc((size_t)(c->PU * D) * 4);
     c->whi[k] = (float*)malloc((size_t)(c->PU * D) * 4);
     c->cscale[k] = (float*)malloc((size_t)(U * D) * 4);
-    for (int64_t i = 0; i < U * D; ++i) c->cscale[k][i] = 1.0f;
+    for (int64_t i = 0; i < U * D; ++i) c->cscale[k][i] = cfg->mode == KVQREF_NSN ? 0.0f : 1.0f;
   }
   c->nblk = (c->tcap + KVQREF_KBLOCK - 1) / KVQREF_KBLOCK;
   c->kbsz = (uint16_t*)calloc((size_t)(U * c->nblk * D * 2), 2);
@@ -386,7 +400,7 @@ kvqref_cache* kvqref_new(const kvqref_cfg* cfg) {
 void kvqref_free(kvqref_cache* c) {
   if (!c) return;
   for (int k = 0; k < 2; ++k) {
-    free(c->codes[k]); free(c->sz[k]); free(c->idx[k]); free(c->t16[k]); free(c->tie[k]);
+    free(c->codes[k]); free(c->sz[k]); free(c->idx[k]); free(c->t16[k]); free(c->t2[k]); free(c->tie[k]);
     free(c->pat[k]); free(c->wlo[k]); free(c->whi[k]); free(c->cscale[k]);
   }
   free(c->kbsz);
@@ -530,11 +544,48 @@ static void encode_kvarn_vec(kvqref_cache* c, int kind, int64_t u, int32_t t, co
   store_quantised(c, kind, u, t, v);
 }
 
+/* Root mean square by the halving-fold sum of squares (R11): sqrtf(fl(ss * (1/D))). */
+static float rms_fold(const float* x, int D) {
+  float v[MAX_D];
+  for (int i = 0; i < D; ++i) v[i] = x[i] * x[i];
+  for (int h = D / 2; h >= 1; h >>= 1)
+    for (int i = 0; i < h; ++i) v[i] = v[i] + v[i + h];
+  return sqrtf(v[0] * (1.0f / (float)D));
+}
+
+/* NSN scalar encode of one vector (reading R18). */
+static void encode_nsn_vec(kvqref_cache* c, int kind, int64_t u, int32_t t, const float* x) {
+  int D = c->D;
+  const float* mu = c->cscale[kind] + u * D;
+  float y[MAX_D];
+  uint16_t n1b = kvqref_f16_round(rms_fold(x, D), 0), n2b = 0;
+  float n1 = kvqref_f16_to_f32(n1b);
+  if (n1 != 0.0f) {
+    float i1 = 1.0f / n1;
+    for (int i = 0; i < D; ++i) y[i] = x[i] * i1 - mu[i];
+    /* (two roundings: the product, then the difference; contraction is off) */
+    n2b = kvqref_f16_round(rms_fold(y, D), 0);
+  }
+  float n2 = kvqref_f16_to_f32(n2b);
+  c->t16[kind][u * c->tcap + t] = n1b;
+  c->t2[kind][u * c->tcap + t] = n2b;
+  if (n1 == 0.0f || n2 == 0.0f) {
+    for (int i = 0; i < D; ++i) y[i] = 0.0f;
+  } else {
+    float i2 = 1.0f / n2;
+    for (int i = 0; i < D; ++i) y[i] = y[i] * i2;
+    kvqref_fwht_f32(y, D);
+    const float isd = (float)(1.0 / sqrt((double)D));
+    for (int i = 0; i < D; ++i) y[i] = y[i] * isd;
+  }
+  store_quantised(c, kind, u, t, y);
+}
+
 int kvqref_set_patterns(kvqref_cache* c, const float* k_tab, const float* v_tab, int32_t n) {
   if (!c) return -1;
   int64_t U = c->U, D = c->D;
   const float* tabs[2] = {k_tab, v_tab};
-  if (c->cfg.mode == KVQREF_KVARN) {
+  if (c->cfg.mode != KVQREF_PATTERN) {
     for (int k = 0; k < 2; ++k) memcpy(c->cscale[k], tabs[k], sizeof(float) * (size_t)(U * D));
     return 0;
   }
@@ -553,6 +604,28 @@ int kvqref_init_patterns(kvqref_cache* c, const void* k, const void* v, int32_t 
   int64_t U = c->U, D = c->D;
   const void* src[2] = {k, v};
   float* rows = (float*)malloc(sizeof(float) * (size_t)(n_tok * D));
+  if (c->cfg.mode == KVQREF_NSN) {
+    /* channel centre: mean over the prefix of x / rms(x), binary64 */
+    double* acc = (double*)malloc(sizeof(double) * D);
+    for (int kind = 0; kind < 2; ++kind)
+      for (int64_t u = 0; u < U; ++u) {
+        for (int64_t t = 0; t < n_tok; ++t) load_vec(c, src[kind], u * n_tok + t, rows + t * D);
+        memset(acc, 0, sizeof(double) * D);
+        int64_t cnt = 0;
+        for (int64_t t = 0; t < n_tok; ++t) {
+          double ss = 0.0;
+          for (int i = 0; i < D; ++i) ss += (double)rows[t * D + i] * rows[t * D + i];
+          double r = sqrt(ss / (double)D);
+          if (!(r > 0.0)) continue;
+          for (int i = 0; i < D; ++i) acc[i] += rows[t * D + i] / r;
+          cnt++;
+        }
+        for (int i = 0; i < D; ++i) c->cscale[kind][u * D + i] = cnt ? (float)(acc[i] / (double)cnt) : 0.0f;
+      }
+    free(acc);
+    free(rows);
+    return 0;
+  }
   if (c->cfg.mode == KVQREF_KVARN) {
     double* y = (double*)malloc(sizeof(double) * D);
     double* acc = (double*)malloc(sizeof(double) * D);
@@ -618,6 +691,7 @@ int kvqref_encode_append(kvqref_cache* c, const void* k, const void* v, int32_t 
       for (int64_t u = 0; u < U; ++u) {
         load_vec(c, src[kind], u * n_new + j, x);
         if (c->cfg.mode == KVQREF_PATTERN) encode_pattern_vec(c, kind, u, t, x);
+        else if (c->cfg.mode == KVQREF_NSN) encode_nsn_vec(c, kind, u, t, x);
         else encode_kvarn_vec(c, kind, u, t, x);
         if (window) {
           float* lo = c->wlo[kind] + pu_of(c, u) * D;
@@ -685,6 +759,19 @@ static void dequant_vec(const kvqref_cache* c, int kind, int64_t u, int32_t t, f
     return;
   }
   const float* cs = c->cscale[kind] + u * D;
+  if (c->cfg.mode == KVQREF_NSN) {
+    for (int d = 0; d < D; ++d) {
+      float s = kvqref_f16_to_f32(sz[(d / G) * 2]);
+      float z = kvqref_f16_to_f32(sz[(d / G) * 2 + 1]);
+      out[d] = fmaf((float)get_code(c, kind, u, t, d), s, z);
+    }
+    kvqref_fwht_f32(out, D);
+    const float isd = (float)(1.0 / sqrt((double)D));
+    const float n1 = kvqref_f16_to_f32(c->t16[kind][u * c->tcap + t]);
+    const float n2 = kvqref_f16_to_f32(c->t2[kind][u * c->tcap + t]);
+    for (int d = 0; d < D; ++d) out[d] = ((out[d] * isd) * n2 + cs[d]) * n1;
+    return;
+  }
   float tf = kvqref_f16_to_f32(c->t16[kind][u * c->tcap + t]);
   for (int d = 0; d < D; ++d) {
     float s = kvqref_f16_to_f32(sz[(d / G) * 2]);
@@ -791,6 +878,7 @@ const void* kvqref_region(const kvqref_cache* c, const char* name, int64_t* byte
   if (!strcmp(r, "sz")) { *bytes = U * T * c->NG * 4; return c->sz[kind]; }
   if (!strcmp(r, "idx")) { *bytes = U * T; return c->idx[kind]; }
   if (!strcmp(r, "t16")) { *bytes = U * T * 2; return c->t16[kind]; }
+  if (!strcmp(r, "t2")) { *bytes = U * T * 2; return c->t2[kind]; }
   if (!strcmp(r, "tie")) { *bytes = U * T * D; return c->tie[kind]; }
   if (!strcmp(r, "pat")) { *bytes = c->PU * M * D * 4; return c->pat[kind]; }
   if (!strcmp(r, "wlo")) { *bytes = c->PU * D * 4; return c->wlo[kind]; }

@@ -30,7 +30,7 @@
 extern "C" {
 #endif
 
-enum { KVQREF_PATTERN = 0, KVQREF_KVARN = 1 };
+enum { KVQREF_PATTERN = 0, KVQREF_KVARN = 1, KVQREF_NSN = 2 };
 enum { KVQREF_IN_F32 = 0, KVQREF_IN_BF16 = 1 };
 enum { KVQREF_NONE = 0xFF };      /* stored pattern index meaning "raw" */
 enum { KVQREF_VTILE = 32 };       /* tokens per V code tile */
@@ -52,8 +52,8 @@ kvqref_cache* kvqref_new(const kvqref_cfg* cfg);
 void kvqref_free(kvqref_cache* c);
 
 /* Explicit pattern tables [B][Hkv][n][D] (PATTERN; [Hkv][n][D] with
- * shared_patterns) or channel scales [B][Hkv][D] (KVARN, n ignored).  fp32
- * host arrays. */
+ * shared_patterns), channel scales [B][Hkv][D] (KVARN, n ignored) or channel
+ * centres [B][Hkv][D] (NSN, n ignored).  fp32 host arrays. */
 int kvqref_set_patterns(kvqref_cache* c, const float* k_tab, const float* v_tab, int32_t n);
 
 /* Prefill mining: per-unit k-means (PATTERN; per kv-head over the B
