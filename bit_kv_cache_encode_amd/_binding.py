@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvq.so")
 
 KVQ_OK, KVQ_EINVAL, KVQ_ECAPACITY, KVQ_ESTATE, KVQ_EDEVICE = 0, -1, -2, -3, -4
-MODE_PATTERN, MODE_KVARN = 0, 1
+MODE_PATTERN, MODE_KVARN, MODE_NSN = 0, 1, 2
 F32, BF16 = 0, 1
 INDEX_NONE = 0xFF
 VTILE = 32
@@ -39,7 +39,8 @@ class kvq_layout(C.Structure):
         "codes_bytes", "sz_bytes", "idx_bytes", "t16_bytes", "tab_bytes", "win_bytes",
         "ws_bytes", "cnt_bytes", "total")] + [(n, C.c_int32) for n in (
         "token_cap", "n_groups", "record_bytes", "max_splits")] + [
-        (n, C.c_uint64) for n in ("k_bsz", "k_tail", "bsz_bytes", "tail_bytes")]
+        (n, C.c_uint64) for n in ("k_bsz", "k_tail", "bsz_bytes", "tail_bytes", "k_t2", "v_t2",
+                                  "t2_bytes")]
 
 
 class kvq_cache(C.Structure):

@@ -25,8 +25,9 @@ def _stream(device) -> int:
 class KVCache:
     """A packed 2/4-bit K/V cache for one attention layer.
 
-    mode: "pattern" (PatternKV residual encode) or "kvarn" (Hadamard +
-    dual-axis normalisation encode).  shared_patterns (pattern mode): one
+    mode: "pattern" (PatternKV residual encode), "kvarn" (Hadamard +
+    dual-axis normalisation encode) or "nsn" (token norm, channel centre,
+    token norm, Hadamard; also 1-bit codes).  shared_patterns (pattern mode): one
     pattern table and Chebyshev window per kv-head for the whole batch.
     k_per_channel (pattern mode): K quantized per channel over 128-token
     blocks, the open block's residuals held in binary16.
@@ -41,7 +42,7 @@ class KVCache:
                  shared_patterns: bool = False, k_per_channel: bool = False):
         if in_dtype not in _DT:
             raise ValueError("in_dtype must be torch.float32 or torch.bfloat16")
-        m = {"pattern": B.MODE_PATTERN, "kvarn": B.MODE_KVARN}[mode]
+        m = {"pattern": B.MODE_PATTERN, "kvarn": B.MODE_KVARN, "nsn": B.MODE_NSN}[mode]
         self.cfg = B.kvq_config(batch, n_q_heads, n_kv_heads, head_dim, max_tokens, bits, group,
                                 m, max_patterns, pattern_window, v_alpha, _DT[in_dtype],
                                 max_splits, int(shared_patterns), int(k_per_channel))
@@ -182,7 +183,7 @@ class KVCache:
                 "k_t16": L.t16_bytes, "v_t16": L.t16_bytes, "k_tab": L.tab_bytes,
                 "v_tab": L.tab_bytes, "k_win": L.win_bytes, "v_win": L.win_bytes,
                 "ws": L.ws_bytes, "cnt": L.cnt_bytes, "k_bsz": L.bsz_bytes,
-                "k_tail": L.tail_bytes}[name]
+                "k_tail": L.tail_bytes, "k_t2": L.t2_bytes, "v_t2": L.t2_bytes}[name]
         off = getattr(L, name)
         return self.buf[off:off + size]
 

@@ -34,6 +34,12 @@ struct AttnShared {
   uint32_t vsz[AT_TILE][MAX_NG];
   float tv[AT_TILE];
   uint8_t vidx[AT_TILE];
+  // NSN: sm_scale * log2(e) * (q . mu_K) per head, the sums sum_t p_t n1_t,
+  // each V token's n1 and the rotated V centre Hadamard(mu_V) / sqrt(D)
+  float qmu[MAX_GQ];
+  float s1[MAX_GQ];
+  float tn1[AT_TILE];
+  float muv[D];
 };
 
 __device__ __forceinline__ uint32_t code_at(const uint32_t* words, int d, int bits) {
@@ -50,6 +56,7 @@ __global__ void __launch_bounds__(AT_THREADS) attn_split_kernel(AttnArgs a) {
   const int hq0 = hk * a.gq;
   const int t_begin = split * a.chunk, t_end = min(a.T, t_begin + a.chunk);
   const bool pattern = a.mode == KVQ_MODE_PATTERN;
+  const bool nsn = a.mode == KVQ_MODE_NSN;
   const int G = a.group, NG = a.ngroups, bits = a.bits;
   const int rec_words = D * bits / 32;
 
@@ -59,8 +66,29 @@ __global__ void __launch_bounds__(AT_THREADS) attn_split_kernel(AttnArgs a) {
     sh.q[h][d] = load_in(a.q, ((int64_t)b * a.Hq + hq0 + h) * D + d, a.bf16);
   }
   __syncthreads();
+  if (nsn) {
+    // q . mu_K in the original space (the rotation is orthonormal), and the
+    // V centre rotated like the V partials
+    const float* muk = a.r.tab[0] + u * D;
+    for (int h = tid; h < a.gq; h += AT_THREADS) {
+      float s = 0.0f;
+      for (int dd = 0; dd < D; ++dd) s = __builtin_fmaf(sh.q[h][dd], muk[dd], s);
+      sh.qmu[h] = s * a.qscale;
+    }
+    if (tid < D) sh.muv[tid] = a.r.tab[1][u * D + tid];
+    __syncthreads();
+    for (int hstep = 1; hstep < D; hstep <<= 1) {
+      float v = 0.0f;
+      if (tid < D) v = (tid & hstep) ? sh.muv[tid ^ hstep] - sh.muv[tid] : sh.muv[tid] + sh.muv[tid ^ hstep];
+      __syncthreads();
+      if (tid < D) sh.muv[tid] = v;
+      __syncthreads();
+    }
+    if (tid < D) sh.muv[tid] *= (float)(1.0 / __builtin_sqrt(128.0));
+    __syncthreads();
+  }
   if (!pattern) {
-    // q' = Hadamard(q) / sqrt(D) * c_K
+    // q' = Hadamard(q) / sqrt(D) * c_K (NSN: no channel scale)
     for (int hstep = 1; hstep < D; hstep <<= 1) {
       float v[MAX_GQ * D / AT_THREADS];
       int n = 0;
@@ -76,7 +104,7 @@ __global__ void __launch_bounds__(AT_THREADS) attn_split_kernel(AttnArgs a) {
     }
     const float* ck = a.r.tab[0] + u * D;
     const float isd = (float)(1.0 / __builtin_sqrt(128.0));
-    for (int i = tid; i < a.gq * D; i += AT_THREADS) sh.q[i / D][i % D] *= isd * ck[i % D];
+    for (int i = tid; i < a.gq * D; i += AT_THREADS) sh.q[i / D][i % D] *= nsn ? isd : isd * ck[i % D];
     __syncthreads();
   }
   for (int i = tid; i < a.gq * D; i += AT_THREADS) sh.q[i / D][i % D] *= a.qscale;
@@ -100,6 +128,7 @@ __global__ void __launch_bounds__(AT_THREADS) attn_split_kernel(AttnArgs a) {
   if (tid < MAX_GQ) {
     sh.m[tid] = -INFINITY;
     sh.l[tid] = 0.0f;
+    sh.s1[tid] = 0.0f;
   }
   __syncthreads();
 
@@ -152,6 +181,10 @@ __global__ void __launch_bounds__(AT_THREADS) attn_split_kernel(AttnArgs a) {
         if (pattern) {
           int k = a.r.idx[0][u * a.tcap + t];
           if (k != KVQ_INDEX_NONE) tot += sh.qm[h][k];
+        } else if (nsn) {
+          // k^ rotated = n1 n2 (s c + z) + n1 Hadamard(mu_K) / sqrt(D)
+          const float n1 = bits2f(a.r.t16[0][u * a.tcap + t]), n2 = bits2f(a.r.t2[0][u * a.tcap + t]);
+          tot = __builtin_fmaf(tot, n1 * n2, n1 * sh.qmu[h]);
         } else {
           tot *= bits2f(a.r.t16[0][u * a.tcap + t]);
         }
@@ -164,7 +197,11 @@ __global__ void __launch_bounds__(AT_THREADS) attn_split_kernel(AttnArgs a) {
       if (tid < nvalid) {
         for (int g = 0; g < NG; ++g) sh.vsz[tid][g] = vsz[(int64_t)t * NG + g];
         sh.vidx[tid] = pattern ? a.r.idx[1][u * a.tcap + t] : (uint8_t)KVQ_INDEX_NONE;
-        sh.tv[tid] = pattern ? 1.0f : bits2f(a.r.t16[1][u * a.tcap + t]);
+        const float t1 = pattern ? 1.0f : bits2f(a.r.t16[1][u * a.tcap + t]);
+        sh.tv[tid] = nsn ? t1 * bits2f(a.r.t2[1][u * a.tcap + t]) : t1;
+        sh.tn1[tid] = nsn ? t1 : 0.0f;
+      } else {
+        sh.tn1[tid] = 0.0f;
       }
     }
     __syncthreads();
@@ -180,6 +217,13 @@ __global__ void __launch_bounds__(AT_THREADS) attn_split_kernel(AttnArgs a) {
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) ps += __shfl_xor(ps, o, 64);
       sh.p[h][lane] = p;
+      if (nsn) {
+        // sum_t p_t n1_t, rescaled like l
+        float p1 = p * sh.tn1[lane];
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) p1 += __shfl_xor(p1, o, 64);
+        if (lane == 0) sh.s1[h] = sh.s1[h] * alpha + p1;
+      }
       if (pattern) {
         for (int j = lane; j < a.n_pat; j += 64) sh.w[h][j] *= alpha;
         __builtin_amdgcn_wave_barrier();
@@ -226,6 +270,7 @@ __global__ void __launch_bounds__(AT_THREADS) attn_split_kernel(AttnArgs a) {
     float o = acc[i];
     if (pattern)
       for (int j = 0; j < a.n_pat; ++j) o = __builtin_fmaf(sh.w[h][j], mv[(int64_t)j * D + d], o);
+    if (nsn) o = __builtin_fmaf(sh.s1[h], sh.muv[d], o);
     const int64_t row = ((int64_t)b * a.Hq + hq0 + h) * a.splits + split;
     a.r.ws[row * D + d] = o;
     if (d == 0) {
@@ -260,7 +305,7 @@ __global__ void __launch_bounds__(D) attn_combine_kernel(AttnArgs a) {
   }
   const int b = row0 / a.Hq, hq = row0 % a.Hq;
   const int64_t u = (int64_t)b * a.Hkv + hq / a.gq;
-  buf[d] = r * a.r.tab[1][u * D + d];
+  buf[d] = a.mode == KVQ_MODE_NSN ? r : r * a.r.tab[1][u * D + d];
   __syncthreads();
   for (int h = 1; h < D; h <<= 1) {
     float mine = buf[d], other = buf[d ^ h];

@@ -438,7 +438,7 @@ attn_mfma_kernel(AttnArgs a) {
     }
     uint32_t c0, c1, w0, w1;
     int kidx;
-    uint16_t t16;
+    uint32_t t16;
     float* sx = (float*)tb;   // this wave's tile buffer is idle until its first tile
     encode_vector<true>(e, kind, uu, x0, x1, lane, sx, nullptr, uu, c0, c1, w0, w1, kidx, t16);
     token_append(e, kind, uu, e.t0, lane, x0, x1, wl0, wl1, wh0, wh1, c0, c1, w0, w1, kidx, t16);
@@ -451,7 +451,7 @@ attn_mfma_kernel(AttnArgs a) {
     float xh0 = __builtin_fmaf((float)c0, bits2f((uint16_t)(w0 & 0xFFFFu)), bits2f((uint16_t)(w0 >> 16))) + m0;
     float xh1 = __builtin_fmaf((float)c1, bits2f((uint16_t)(w1 & 0xFFFFu)), bits2f((uint16_t)(w1 >> 16))) + m1;
     if (KVARN) {
-      const float tf = bits2f(t16);
+      const float tf = bits2f((uint16_t)t16);
       xh0 *= tf;
       xh1 *= tf;
     }

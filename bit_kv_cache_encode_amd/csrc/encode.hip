@@ -90,7 +90,7 @@ __global__ void __launch_bounds__(ENC_THREADS) encode_kernel(EncodeArgs a) {
       }
       uint32_t c0, c1, w0, w1;
       int kidx;
-      uint16_t t16;
+      uint32_t t16;
       encode_vector<false>(a, kind, u, x0, x1, lane, sh.x[wave], staged ? s_tab : nullptr, row,
                            c0, c1, w0, w1, kidx, t16);
       store_token(a, kind, u, t, lane, c0, c1, w0, w1, kidx, t16);
@@ -371,7 +371,7 @@ __global__ void __launch_bounds__(64) encode_token_kernel(EncodeArgs a) {
   }
   uint32_t c0, c1, w0, w1;
   int kidx;
-  uint16_t t16;
+  uint32_t t16;
   encode_vector<true>(a, kind, u, x0, x1, lane, sx, staged ? stab : nullptr, row, c0, c1, w0, w1,
                       kidx, t16);
   token_append(a, kind, u, t, lane, x0, x1, wl0, wl1, wh0, wh1, c0, c1, w0, w1, kidx, t16);

@@ -56,13 +56,29 @@ __device__ __forceinline__ uint32_t wave_min_u(uint32_t v) {
   v = min(v, dpp_u<0x140>(v));
   return min(min(rlane_u(v, 0), rlane_u(v, 16)), min(rlane_u(v, 32), rlane_u(v, 48)));
 }
-// OR over aligned groups of W <= 16 lanes
+// OR over aligned groups of W <= 32 lanes
 __device__ __forceinline__ uint32_t group_or(uint32_t v, int W) {
   if (W >= 2) v |= dpp_u<0xB1>(v);
   if (W >= 4) v |= dpp_u<0x4E>(v);
   if (W >= 8) v |= dpp_u<0x141>(v);
   if (W >= 16) v |= dpp_u<0x140>(v);
+  if (W >= 32) v |= (uint32_t)__shfl_xor((int)v, 16, 64);
   return v;
+}
+
+// Root mean square of the 128 channels a wave holds (lane l: channels l and
+// l + 64) by the halving-fold sum of squares: v[i] += v[i + 64], then + 32,
+// ..., + 1; sqrtf(fl(ss * (1/128))).  Every lane gets it.
+__device__ __forceinline__ float rms_fold(float x0, float x1, int lane) {
+  float v = x0 * x0;
+  const float v1 = x1 * x1;
+  v = v + v1;
+#pragma unroll
+  for (int h = 32; h >= 1; h >>= 1) {
+    const float o = __shfl_down(v, h, 64);
+    if (lane < h) v = v + o;
+  }
+  return sqrtf(__shfl(v, 0, 64) * (1.0f / 128.0f));
 }
 
 // ---------------------------------------------------------------- Eq 1 quantizer
@@ -194,7 +210,7 @@ __device__ __forceinline__ void encode_vector(const EncodeArgs& a, int kind, int
                                               float x1, int lane, float* sx, const float* tab_lds,
                                               int64_t row, uint32_t& c0, uint32_t& c1,
                                               uint32_t& w0, uint32_t& w1, int& kidx,
-                                              uint16_t& t16) {
+                                              uint32_t& t16) {
   const float* tab = a.r.tab[kind] + (a.mode == KVQ_MODE_PATTERN ? pat_unit(a.r, u) * a.max_pat * D : u * D);
   kidx = KVQ_INDEX_NONE;
   t16 = 0;
@@ -244,6 +260,39 @@ __device__ __forceinline__ void encode_vector(const EncodeArgs& a, int kind, int
       slot[lane + 64] = h2bits((_Float16)r1);
     }
     quantize_pair(r0, r1, lane, a.group, a.bits, c0, c1, w0, w1);
+  } else if (a.mode == KVQ_MODE_NSN) {
+    // NSN reading: n1 = rms(x), b = x * fl(1/n1) - mu, n2 = rms(b),
+    // y = FWHT(b * fl(1/n2)) * fp32(1/sqrt(D)), Eq 1 on y; t16 carries
+    // n1 | n2 << 16 (binary16, nearest-even)
+    const uint16_t n1b = h2bits((_Float16)rms_fold(x0, x1, lane));
+    const float n1 = bits2f(n1b);
+    float b0 = 0.0f, b1 = 0.0f;
+    uint16_t n2b = 0;
+    if (n1 != 0.0f) {
+      const float i1 = 1.0f / n1;
+      b0 = x0 * i1 - tab[lane];
+      b1 = x1 * i1 - tab[lane + 64];
+      n2b = h2bits((_Float16)rms_fold(b0, b1, lane));
+    }
+    const float n2 = bits2f(n2b);
+    float y0 = 0.0f, y1 = 0.0f;
+    if (n1 != 0.0f && n2 != 0.0f) {
+      const float i2 = 1.0f / n2;
+      y0 = b0 * i2;
+      y1 = b1 * i2;
+#pragma unroll
+      for (int h = 1; h < 64; h <<= 1) {
+        const float p0 = __shfl_xor(y0, h, 64), p1 = __shfl_xor(y1, h, 64);
+        if (lane & h) { y0 = p0 - y0; y1 = p1 - y1; }
+        else { y0 = y0 + p0; y1 = y1 + p1; }
+      }
+      const float a0 = y0 + y1, a1 = y0 - y1;   // stage h = 64 (in-lane)
+      const float isd = (float)(1.0 / __builtin_sqrt(128.0));
+      y0 = a0 * isd;
+      y1 = a1 * isd;
+    }
+    t16 = (uint32_t)n1b | ((uint32_t)n2b << 16);
+    quantize_pair(y0, y1, lane, a.group, a.bits, c0, c1, w0, w1);
   } else {
     // KVarN reading: FWHT (stages h = 1..64), 1/sqrt(D), channel scale,
     // token RMS (halving-fold sum), then Eq 1 on u = y~ / t.
@@ -289,10 +338,11 @@ __device__ __forceinline__ void encode_vector(const EncodeArgs& a, int kind, int
 // Store a token's (s, z) words, index / token scale and (K) packed record.
 __device__ __forceinline__ void store_token(const EncodeArgs& a, int kind, int64_t u, int t,
                                             int lane, uint32_t c0, uint32_t c1, uint32_t w0,
-                                            uint32_t w1, int kidx, uint16_t t16) {
+                                            uint32_t w1, int kidx, uint32_t t16) {
   if (lane == 0) {
     if (a.mode == KVQ_MODE_PATTERN) a.r.idx[kind][u * a.tcap + t] = (uint8_t)kidx;
-    else a.r.t16[kind][u * a.tcap + t] = t16;
+    else a.r.t16[kind][u * a.tcap + t] = (uint16_t)t16;
+    if (a.mode == KVQ_MODE_NSN) a.r.t2[kind][u * a.tcap + t] = (uint16_t)(t16 >> 16);
   }
   // K per channel keeps only the index here; its block quantizer runs later
   if (kind == 0 && a.r.kch) return;
@@ -322,7 +372,7 @@ __device__ __forceinline__ void store_token(const EncodeArgs& a, int kind, int64
 __device__ __forceinline__ void token_append(const EncodeArgs& a, int kind, int64_t u, int t,
                                              int lane, float x0, float x1, float wl0, float wl1,
                                              float wh0, float wh1, uint32_t c0, uint32_t c1,
-                                             uint32_t w0, uint32_t w1, int kidx, uint16_t t16) {
+                                             uint32_t w0, uint32_t w1, int kidx, uint32_t t16) {
   float* win = a.r.win[kind] + pat_unit(a.r, u) * 2 * D;
   store_token(a, kind, u, t, lane, c0, c1, w0, w1, kidx, t16);
   if (kind == 1) {

@@ -35,12 +35,15 @@ bool cfg_ok(const kvq_config* c) {
   // up to MAX_GQ q-heads per kv-head on every path; up to 16 where the MFMA
   // attention serves the shape (q-head blocks)
   const int gq = c->n_q_heads / c->n_kv_heads;
-  if (gq > MAX_GQ && !(gq <= 16 && mfma_attention_supported(c->bits, c->group, gq))) return false;
+  if (gq > MAX_GQ && !(gq <= 16 && c->mode != KVQ_MODE_NSN && mfma_attention_supported(c->bits, c->group, gq)))
+    return false;
   if (c->head_dim != D) return false;
   if (c->max_tokens <= 0 || c->max_tokens > (1 << 28)) return false;
-  if (c->bits != 2 && c->bits != 4) return false;
+  // 1-bit codes in NSN mode (served by the VALU attention)
+  if (c->bits != 2 && c->bits != 4 && !(c->bits == 1 && c->mode == KVQ_MODE_NSN)) return false;
   if (c->group < 8 || c->group > D || D % c->group) return false;
-  if (c->mode != KVQ_MODE_PATTERN && c->mode != KVQ_MODE_KVARN) return false;
+  if (c->mode != KVQ_MODE_PATTERN && c->mode != KVQ_MODE_KVARN && c->mode != KVQ_MODE_NSN) return false;
+  if (c->group * c->bits % 8) return false;
   if (c->max_patterns < 0 || c->max_patterns > 255) return false;
   if (c->pattern_window < 0) return false;
   if (!(c->v_alpha < 0.5f) || isnan(c->v_alpha)) return false;
@@ -127,6 +130,8 @@ Regions regions_of(const kvq_cache* c, const kvq_layout& L) {
   r.pat_h = c->cfg.shared_patterns ? c->cfg.n_kv_heads : 0;
   r.t16[0] = (uint16_t*)(base + L.k_t16);
   r.t16[1] = (uint16_t*)(base + L.v_t16);
+  r.t2[0] = (uint16_t*)(base + L.k_t2);
+  r.t2[1] = (uint16_t*)(base + L.v_t2);
   r.tab[0] = (float*)(base + L.k_tab);
   r.tab[1] = (float*)(base + L.v_tab);
   r.win[0] = (float*)(base + L.k_win);
@@ -188,7 +193,8 @@ int kvq_layout_of(const kvq_config* cfg, kvq_layout* out) {
                      (D + 2 + (uint64_t)cfg->max_patterns) * 4;
   uint64_t ws_init = 2 * U * (uint64_t)tcap;       // k-means assignments (one byte per token)
   L.ws_bytes = ws_attn > ws_init ? ws_attn : ws_init;
-  L.record_bytes = (int)(D * cfg->bits / 8 + L.n_groups * 4 + (pattern ? 1 : 2));
+  L.record_bytes = (int)(D * cfg->bits / 8 + L.n_groups * 4 +
+                         (pattern ? 1 : cfg->mode == KVQ_MODE_NSN ? 4 : 2));
   uint64_t off = 0;
   auto place = [&](uint64_t bytes) { uint64_t at = off; off = align256(off + bytes); return at; };
   L.k_codes = place(L.codes_bytes);
@@ -212,6 +218,10 @@ int kvq_layout_of(const kvq_config* cfg, kvq_layout* out) {
   L.tail_bytes = cfg->k_per_channel ? U * (uint64_t)KBLOCK * D * 2 : 0;
   L.k_bsz = place(L.bsz_bytes);
   L.k_tail = place(L.tail_bytes);
+  // NSN: the second norm (after every other region)
+  L.t2_bytes = cfg->mode == KVQ_MODE_NSN ? U * tcap * 2 : 0;
+  L.k_t2 = place(L.t2_bytes);
+  L.v_t2 = place(L.t2_bytes);
   L.total = off;
   *out = L;
   return KVQ_OK;
@@ -235,8 +245,10 @@ int kvq_cache_init(kvq_cache* cache, const kvq_config* cfg, void* base, uint64_t
                                        cfg->shared_patterns, s);
     if (e != hipSuccess) return dev_fail(e);
   } else {
-    hipError_t e = launch_fill(r.tab[0], 1.0f, (int64_t)(L.tab_bytes / 4), s);
-    if (e == hipSuccess) e = launch_fill(r.tab[1], 1.0f, (int64_t)(L.tab_bytes / 4), s);
+    // KVARN channel scales start at 1, NSN channel centres at 0
+    const float v0 = cfg->mode == KVQ_MODE_NSN ? 0.0f : 1.0f;
+    hipError_t e = launch_fill(r.tab[0], v0, (int64_t)(L.tab_bytes / 4), s);
+    if (e == hipSuccess) e = launch_fill(r.tab[1], v0, (int64_t)(L.tab_bytes / 4), s);
     if (e != hipSuccess) return dev_fail(e);
   }
   return KVQ_OK;
@@ -304,6 +316,9 @@ int kvq_init_patterns(kvq_cache* cache, const void* k, const void* v, int32_t n_
     if (e != hipSuccess) return dev_fail(e);
     cache->n_patterns = n_patterns;
     cache->win_count = 0;
+  } else if (c.mode == KVQ_MODE_NSN) {
+    e = launch_chan_centre_pair(k, v, bf16, n_tok, r.tab[0], r.tab[1], units, s);
+    if (e != hipSuccess) return dev_fail(e);
   } else {
     e = launch_chan_scale_pair(k, v, bf16, n_tok, r.tab[0], r.tab[1], units, s);
     if (e != hipSuccess) return dev_fail(e);
@@ -424,7 +439,7 @@ static AttnKernel attn_setup(const kvq_cache* cache, const kvq_layout& L, const 
   a.qscale = sm * 1.4426950408889634f;
   const int units = c.batch * c.n_kv_heads;
   const char* kenv = getenv("KVQ_ATTN_KERNEL");
-  const bool mfma_ok = mfma_attention_supported(c.bits, c.group, a.gq);
+  const bool mfma_ok = mfma_attention_supported(c.bits, c.group, a.gq) && c.mode != KVQ_MODE_NSN;
   // the paired kernel serves one q-head block per unit (and K per token)
   const bool pp_ok = mfma_ok && a.gq <= 16 / (D / c.group) && !c.k_per_channel;
   // (the VALU kernel holds at most MAX_GQ q-heads per kv-head)

@@ -75,7 +75,8 @@ struct Regions {
   uint8_t* codes[2];
   uint32_t* sz[2];      // [U][tcap][NG] packed (s | z << 16)
   uint8_t* idx[2];
-  uint16_t* t16[2];
+  uint16_t* t16[2];     // KVARN token scale; NSN first norm n1
+  uint16_t* t2[2];      // NSN second norm n2
   float* tab[2];
   float* win[2];
   float* ws;
@@ -184,5 +185,7 @@ hipError_t launch_kmeans_pair(const void* xk, const void* xv, int bf16, int n_to
                               int units, uint8_t* assign, hipStream_t s);
 hipError_t launch_chan_scale_pair(const void* xk, const void* xv, int bf16, int n_tok, float* sk,
                                   float* sv, int units, hipStream_t s);
+hipError_t launch_chan_centre_pair(const void* xk, const void* xv, int bf16, int n_tok, float* mk,
+                                   float* mv, int units, hipStream_t s);
 
 }  // namespace kvq

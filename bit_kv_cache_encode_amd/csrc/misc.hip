@@ -127,6 +127,24 @@ __global__ void __launch_bounds__(64) dequant_kernel(DequantArgs a) {
     out[lane + 64] = v[1];
     return;
   }
+  if (a.mode == KVQ_MODE_NSN) {
+    // NSN inverse: y = FWHT(fmaf(q, s, z)) * fp32(1/sqrt(D));
+    // x^ = fl(fl(fl(y * n2) + mu) * n1)
+    float x0 = v[0], x1 = v[1];
+#pragma unroll
+    for (int h = 1; h < 64; h <<= 1) {
+      float p0 = __shfl_xor(x0, h, 64), p1 = __shfl_xor(x1, h, 64);
+      if (lane & h) { x0 = p0 - x0; x1 = p1 - x1; }
+      else { x0 = x0 + p0; x1 = x1 + p1; }
+    }
+    const float a0 = x0 + x1, a1 = x0 - x1;
+    const float isd = (float)(1.0 / __builtin_sqrt(128.0));
+    const float n1 = bits2f(a.r.t16[w][u * a.tcap + t]), n2 = bits2f(a.r.t2[w][u * a.tcap + t]);
+    const float* mu = a.r.tab[w] + u * D;
+    out[lane] = ((a0 * isd) * n2 + mu[lane]) * n1;
+    out[lane + 64] = ((a1 * isd) * n2 + mu[lane + 64]) * n1;
+    return;
+  }
   // KVarN inverse: y^ = fl(fl(w * t) * c); x^ = FWHT(y^) * fp32(1/sqrt(D)).
   const float tf = bits2f(a.r.t16[w][u * a.tcap + t]);
   const float* c = a.r.tab[w] + u * D;
@@ -597,6 +615,41 @@ __global__ void __launch_bounds__(D) chan_scale_kernel(const void* xk, const voi
 hipError_t launch_chan_scale_pair(const void* xk, const void* xv, int bf16, int n_tok, float* sk,
                                   float* sv, int units, hipStream_t s) {
   hipLaunchKernelGGL(chan_scale_kernel, dim3(units, 2), dim3(D), 0, s, xk, xv, bf16, n_tok, sk, sv);
+  return hipGetLastError();
+}
+
+// NSN channel centre: mu_j = mean over prefix tokens of x_j / rms(x) (tokens
+// with rms 0 skipped; no tokens: 0), binary64.  One block of 128 threads per
+// (unit, kind).
+__global__ void __launch_bounds__(D) chan_centre_kernel(const void* xk, const void* xv, int bf16,
+                                                        int n, float* mk, float* mv) {
+  __shared__ double red[D];
+  const int kind = blockIdx.y, d = threadIdx.x;
+  const int64_t u = blockIdx.x;
+  const void* x = kind ? xv : xk;
+  double acc = 0.0;
+  int cnt = 0;
+  for (int t = 0; t < n; ++t) {
+    const double v = (double)load_in(x, (u * n + t) * D + d, bf16);
+    red[d] = v * v;
+    __syncthreads();
+    for (int h = D / 2; h >= 1; h >>= 1) {
+      if (d < h) red[d] += red[d + h];
+      __syncthreads();
+    }
+    const double r = sqrt(red[0] / (double)D);
+    __syncthreads();
+    if (r > 0.0) {
+      acc += v / r;
+      cnt++;
+    }
+  }
+  (kind ? mv : mk)[u * D + d] = cnt ? (float)(acc / (double)cnt) : 0.0f;
+}
+
+hipError_t launch_chan_centre_pair(const void* xk, const void* xv, int bf16, int n_tok, float* mk,
+                                   float* mv, int units, hipStream_t s) {
+  hipLaunchKernelGGL(chan_centre_kernel, dim3(units, 2), dim3(D), 0, s, xk, xv, bf16, n_tok, mk, mv);
   return hipGetLastError();
 }
 

@@ -43,7 +43,16 @@
  *    clamp(rint((r - z) * fl(1/s)), 0, 2^bits - 1), 0 when s == 0.
  *  - idx (PATTERN): one byte per token, the stored pattern index k* of
  *    section 3.2, 0xFF when the raw vector was quantized.
- *  - t16 (KVARN): one binary16 token scale per token.
+ *  - t16 (KVARN): one binary16 token scale per token; (NSN) the first norm n1.
+ *  - t2 (NSN): the second norm n2, one binary16 per token.
+ *  - NSN mode (a scalar reading of NSNQuant's double normalisation, arXiv
+ *    2505.18231, abstract): n1 = rms(x), a = x * fl(1/n1) - mu (mu the
+ *    unit's channel centre, the tables), n2 = rms(a), y = Hadamard(a *
+ *    fl(1/n2)) / sqrt(D), Eq 1 on y with 1, 2 or 4 bits; rms is
+ *    sqrtf(fl(ss * (1/D))) with ss the halving-fold sum of squares, n1 and
+ *    n2 are stored as nearest-even binary16 (a zero one gives zero codes and
+ *    scales).  x^ = fl(fl(fl(w * n2) + mu) * n1), w = Hadamard(fmaf(q, s, z))
+ *    / sqrt(D).
  *  - k_per_channel (PATTERN): K is quantized per channel over blocks of
  *    KVQ_KBLOCK = 128 tokens instead of per token and group (PatternKV's
  *    experimental setting, section 4.1, after KIVI; appendix E: groups of 128
@@ -72,6 +81,7 @@ extern "C" {
 
 #define KVQ_MODE_PATTERN 0  /* PatternKV residual encode */
 #define KVQ_MODE_KVARN 1    /* Hadamard + dual-axis normalisation encode */
+#define KVQ_MODE_NSN 2      /* token norm, channel centre, token norm, Hadamard */
 #define KVQ_F32 0
 #define KVQ_BF16 1
 #define KVQ_INDEX_NONE 0xFF
@@ -84,9 +94,9 @@ typedef struct {
   int32_t n_kv_heads;     /* Hkv; q-head hq attends to kv-head hq / (Hq/Hkv) */
   int32_t head_dim;       /* D, must be 128 */
   int32_t max_tokens;     /* token capacity per unit */
-  int32_t bits;           /* 2 or 4 */
+  int32_t bits;           /* 2 or 4; also 1 in NSN mode */
   int32_t group;          /* channels per quantization group (Eq 1 scope) */
-  int32_t mode;           /* KVQ_MODE_PATTERN or KVQ_MODE_KVARN */
+  int32_t mode;           /* KVQ_MODE_PATTERN, KVQ_MODE_KVARN or KVQ_MODE_NSN */
   int32_t max_patterns;   /* pattern table capacity per unit and kind, <= 255 */
   int32_t pattern_window; /* G_pattern of Eq 5 (0 = no decode-time patterns) */
   float v_alpha;          /* z-test level of section 3.3; <= 0 disables it */
@@ -121,6 +131,8 @@ typedef struct {
   uint64_t k_bsz;         /* k_per_channel: packed (s | z << 16) [U][token_cap / 128][D] */
   uint64_t k_tail;        /* k_per_channel: binary16 residuals [U][128][D] of the open block */
   uint64_t bsz_bytes, tail_bytes;   /* 0 without k_per_channel */
+  uint64_t k_t2, v_t2;    /* NSN: binary16 second norm n2 [U][token_cap] */
+  uint64_t t2_bytes;      /* 0 outside NSN mode */
 } kvq_layout;
 
 typedef struct {
@@ -155,14 +167,17 @@ int kvq_cache_init(kvq_cache* cache, const kvq_config* cfg, void* base, uint64_t
  * KVARN mode instead sets each unit's per-channel scale c_j to the root mean
  * square over the prefix of (y_j / rms(y)) with y the orthonormal Hadamard
  * rotation of the token (0 becomes 1): the channel axis of KVarN's dual-axis
- * normalisation (arXiv 2606.03458, abstract).  Resets the Chebyshev window.
+ * normalisation (arXiv 2606.03458, abstract).  NSN mode sets each unit's
+ * channel centre mu to the mean over the prefix of x / rms(x) (binary64,
+ * stored as fp32).  Resets the Chebyshev window.
  * KVQ_EINVAL if n_tok < 1 or n_patterns > max_patterns. */
 int kvq_init_patterns(kvq_cache* cache, const void* k, const void* v, int32_t n_tok,
                       int32_t n_patterns, void* stream);
 
 /* Upload pattern tables mined elsewhere: k_tab and v_tab are fp32 device
  * arrays [B][Hkv][n][D] (PATTERN, n <= max_patterns; [Hkv][n][D] with
- * shared_patterns) or per-channel scales [B][Hkv][D] (KVARN, n ignored).
+ * shared_patterns), per-channel scales [B][Hkv][D] (KVARN, n ignored) or
+ * channel centres [B][Hkv][D] (NSN, n ignored).
  * Resets the Chebyshev window.
  * KVQ_EINVAL on a bad n or null pointer. */
 int kvq_set_patterns(kvq_cache* cache, const float* k_tab, const float* v_tab, int32_t n,
@@ -182,6 +197,7 @@ int kvq_set_patterns(kvq_cache* cache, const float* k_tab, const float* v_tab, i
  * closure adds one centre to h's table (a second, small launch).
  * KVARN: y = Hadamard(x)/sqrt(D), y~ = y / c, t = rms(y~) stored as binary16,
  * u = y~ / t quantized per group (update_patterns is ignored).
+ * NSN: as described with the stored format above (update_patterns ignored).
  * k_per_channel: K residuals go to the open block's binary16 buffer, and every
  * block this append completes is quantized per channel (two more launches).
  * KVQ_ECAPACITY if n_tokens + n_new > max_tokens; KVQ_EINVAL on null inputs
@@ -218,7 +234,8 @@ int kvq_decode_step(kvq_cache* cache, const void* k_new, const void* v_new, cons
 /* Dequantize tokens tok0 .. tok0+n-1 of K (which = 0) or V (which = 1) into
  * fp32 out [B][Hkv][n][D]: PATTERN x^ = fl(fmaf(q, s, z) + M_k*) (the index
  * restore of section 3.2), or fmaf(q, s, z) alone for index 0xFF; KVARN
- * x^ = Hadamard(fl(fl(fmaf(q, s, z) * t) * c)) / sqrt(D); k_per_channel K
+ * x^ = Hadamard(fl(fl(fmaf(q, s, z) * t) * c)) / sqrt(D); NSN as in the
+ * stored format above; k_per_channel K
  * in the open block x^ = fl(residual + M_k*).
  * KVQ_EINVAL on a bad `which` or a span outside [0, n_tokens). */
 int kvq_dequant(const kvq_cache* cache, int32_t which, int32_t tok0, int32_t n, float* out,

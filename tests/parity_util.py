@@ -93,6 +93,11 @@ def assert_same_encode(ref: "O.RefCache", cache, T: int, units=None, ref_units=N
             gt = gpu_t16(cache, which)[units, :T]
             rt = ref.t16(which)[ref_units, :T]
             assert np.array_equal(gt, rt), f"{'KV'[which]} t16 differ at {np.argwhere(gt != rt)[:5]}"
+            if cache.mode == "nsn":
+                L = cache.layout
+                g2 = cache.region("kv"[which] + "_t2").cpu().numpy().view(np.uint16).reshape(-1, L.token_cap)
+                g2, r2 = g2[units, :T], ref.t2(which)[ref_units, :T]
+                assert np.array_equal(g2, r2), f"{'KV'[which]} n2 differ at {np.argwhere(g2 != r2)[:5]}"
 
 
 def assert_same_kch(ref: "O.RefCache", cache, T: int) -> None:
@@ -131,7 +136,7 @@ def make_pair(B, Hq, Hkv, max_tokens, *, bits=2, group=32, mode="pattern", max_p
                   max_patterns=max_patterns, pattern_window=pattern_window, v_alpha=v_alpha,
                   in_dtype=dt, shared_patterns=shared_patterns, k_per_channel=k_per_channel)
     ref = O.RefCache(B, Hq, Hkv, 128, max_tokens, bits=bits, group=group,
-                     mode=O.PATTERN if mode == "pattern" else O.KVARN,
+                     mode={"pattern": O.PATTERN, "kvarn": O.KVARN, "nsn": O.NSN}[mode],
                      max_patterns=max_patterns, pattern_window=pattern_window, v_alpha=v_alpha,
                      in_dtype=O.IN_BF16 if bf16 else O.IN_F32, shared_patterns=shared_patterns,
                      k_per_channel=k_per_channel)

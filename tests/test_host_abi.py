@@ -87,6 +87,13 @@ def test_layout_regions():
     assert Lc.tail_bytes == U * 128 * 128 * 2
     assert Lc.k_bsz % 256 == 0 and Lc.k_tail % 256 == 0 and Lc.k_bsz >= Lc.cnt + Lc.cnt_bytes
     assert Lc.k_tail + Lc.tail_bytes <= Lc.total
+    # NSN: the second norm after every other region; 1-bit codes allowed there
+    Ln = B.kvq_layout_of(_cfg(mode=B.MODE_NSN, max_patterns=0))
+    assert Ln.t2_bytes == U * T * 2 and Ln.t16_bytes == U * T * 2 and L.t2_bytes == 0
+    assert Ln.record_bytes == 32 + 16 + 4 and Ln.tab_bytes == U * 128 * 4
+    assert Ln.v_t2 + Ln.t2_bytes <= Ln.total
+    L1 = B.kvq_layout_of(_cfg(mode=B.MODE_NSN, max_patterns=0, bits=1, group=8))
+    assert L1.codes_bytes == U * T * 16 and L1.n_groups == 16
     L0 = B.kvq_layout_of(_cfg(max_tokens=4000))
     assert all(getattr(Lc, n) == getattr(L0, n) for n in ("k_codes", "v_codes", "k_sz", "ws", "cnt"))
 
@@ -96,7 +103,9 @@ def test_layout_regions():
     dict(n_q_heads=136), dict(n_q_heads=72, group=16), dict(max_patterns=256), dict(mode=5), dict(in_dtype=7),
     dict(v_alpha=0.5), dict(max_tokens=0), dict(batch=0), dict(pattern_window=-1),
     dict(shared_patterns=2), dict(shared_patterns=1, mode=B.MODE_KVARN, max_patterns=0),
-    dict(k_per_channel=2), dict(k_per_channel=1, mode=B.MODE_KVARN, max_patterns=0)])
+    dict(k_per_channel=2), dict(k_per_channel=1, mode=B.MODE_KVARN, max_patterns=0),
+    dict(bits=1), dict(bits=1, mode=B.MODE_KVARN, max_patterns=0), dict(mode=3),
+    dict(mode=B.MODE_NSN, max_patterns=0, n_q_heads=96)])
 def test_layout_rejects_bad_configs(bad):
     """(n_q_heads 136 = 17 q-heads per kv-head; 72 at group 16 = 9 q-heads on
     a shape only the VALU attention serves, which holds at most 8.)"""
