@@ -43,6 +43,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attention.json")
 ATTN_CONFIGS = {
     "long4bit": dict(B=1, Hq=32, H=8, T=131072, bits=4, group=64, P=64, mode="pattern"),
     "kvarn": dict(B=64, Hq=32, H=8, T=16384, bits=2, group=32, P=0, mode="kvarn"),
+    # the same breadth workload in the NSN scalar mode (52-byte records)
+    "nsn": dict(B=64, Hq=32, H=8, T=16384, bits=2, group=32, P=0, mode="nsn"),
     "qwen": dict(B=32, Hq=28, H=4, T=32768, bits=2, group=32, P=64, mode="pattern"),
     # K per channel over 128-token blocks (PatternKV's KIVI-style setting): the
     # 32k context plus 64 tokens in the open block
@@ -134,7 +136,8 @@ def parse():
                     help="secondary measurement: decode attention alone on another workload "
                          "shape (long4bit: B 1, 131072 tokens, 4-bit G64, 64 patterns; "
                          "kvarn: 64 samples x 16384, KVarN 2-bit; qwen: B 32, 28 q / 4 kv "
-                         "heads, 32768 tokens, 64 patterns; kivi: the step's shapes with K "
+                         "heads, 32768 tokens, 64 patterns; nsn: the kvarn shape in the NSN "
+                         "scalar mode; kivi: the step's shapes with K "
                          "quantised per channel over 128-token blocks, 32832 tokens); prints one "
                          "JSON line")
     ap.add_argument("--traffic-from", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "RAW_DIR"),

@@ -41,13 +41,15 @@ constexpr int MF_THREADS = MF_WAVES * 64;
 // Dynamic LDS layout of a block (bytes); npat = padded pattern count.
 struct MfLds {
   int q, qsum, qe, next, qm, qa, mv, mv_rows, ps, ph, vs, w, alpha, m, o, z, l, wsum, M, last, tiles,
-      total;
+      nsn, total;
 };
 // mv_rows: rows of M^V staged for the pattern term (0 without the one-hot path)
 // kch: K per channel, which keeps the per-lane q operands of the QK product
 // (64 lanes x 32 fp32, quad-major) for the per-tile q * s operand
+// nsn: NSN mode, which keeps q . mu_K and sum p n1 per head and the rotated
+// V centre
 __host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes, int mv_rows,
-                                        bool kch = false) {
+                                        bool kch = false, bool nsn = false) {
   const bool hist_mfma = mv_rows > 0;
   MfLds L;
   int o = 0;
@@ -70,8 +72,10 @@ __host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes
   L.wsum = o; o = al16(o + HB * npat * 4);
   L.M = o; o = al16(o + HB * 4);
   L.last = o; o = al16(o + 16);
-  // the tile buffers, reused after the loop for per-wave o[HB][D] and (l, z[NG])
-  const int part_bytes = MF_WAVES * HB * (D + 1 + NG) * 4;
+  L.nsn = o; o = al16(o + (nsn ? (2 * HB + D) * 4 : 0));
+  // the tile buffers, reused after the loop for per-wave o[HB][D] and (l, z[NG]
+  // and with NSN sum p n1)
+  const int part_bytes = MF_WAVES * HB * (D + 1 + NG + (nsn ? 1 : 0)) * 4;
   L.tiles = o; o = al16(o + (MF_WAVES * tile_bytes > part_bytes ? MF_WAVES * tile_bytes : part_bytes));
   // M^V rows are staged only where they fit the 160 KiB of a compute unit
   L.mv = o;
@@ -90,13 +94,16 @@ __host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes
 // word (s (q_a . c_a + q_b . c_b) = s q_a . c_a + s q_b . c_b, and likewise
 // for z and for p s, p z on the V side), which fills the 16 MFMA rows with
 // 4 q-heads at G = 64 instead of leaving half of an 8-head row block idle.
-template <int BITS, int NG, int NGS, bool KVARN, int NPB, bool QLO, bool KCH>
+template <int BITS, int NG, int NGS, bool KVARN, int NPB, bool QLO, bool KCH, bool NSNM>
 __global__ void __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_mfma_kernel(AttnArgs a) {
   static_assert(!(KVARN && NPB), "KVarN has no pattern term");
   static_assert(NG == NGS || NG == 2 * NGS, "a stored group spans one or two virtual groups");
   static_assert(!KCH || (!KVARN && QLO), "K per channel: PatternKV mode, q * s needs a lo part");
-  using TS = TileShape<BITS, NGS, KVARN, KCH>;
+  static_assert(!NSNM || KVARN, "NSN is a rotated mode");
+  using TS = TileShape<BITS, NGS, KVARN, KCH, NSNM>;
+  // per-wave (l, z[NG]) partial rows, with NSN also sum p n1
+  constexpr int LZ = 1 + NG + (NSNM ? 1 : 0);
   constexpr int VPS = NG / NGS;        // virtual groups per stored group
   constexpr int G = D / NG;            // channels per (virtual) group
   constexpr int HB = 16 / NG;          // heads per row block
@@ -125,7 +132,7 @@ attn_mfma_kernel(AttnArgs a) {
   const int S_tot = a.splits + a.fuse;
   const int n_pat = KVARN ? 0 : a.n_pat;
   const int npat = pad_pat(n_pat);
-  const MfLds Lo = mf_lds(HB, NG, npat, TS::BYTES, 16 * NPB, KCH);
+  const MfLds Lo = mf_lds(HB, NG, npat, TS::BYTES, 16 * NPB, KCH, NSNM);
   float* s_q = (float*)(mf_raw + Lo.q);            // [HB][D]
   float* s_qsum = (float*)(mf_raw + Lo.qsum);      // [HB][NG]
   int* s_qe = (int*)(mf_raw + Lo.qe);              // [HB]: max |q| bits, then the exponent
@@ -133,6 +140,9 @@ attn_mfma_kernel(AttnArgs a) {
   float* s_mv = (float*)(mf_raw + Lo.mv);          // [16 NPB][D] rows of M^V
   float* s_qm = (float*)(mf_raw + Lo.qm);          // [HB][256]; entry 0xFF (no pattern) is 0
   float4* s_qa = (float4*)(mf_raw + Lo.qa);        // K per channel: [8 quads][64 lanes]
+  float* s_qmu = (float*)(mf_raw + Lo.nsn);        // NSN: [HB] qscale (q . mu_K)
+  float* s_s1 = s_qmu + HB;                        // NSN: [HB] block sum p n1
+  float* s_muv = s_s1 + HB;                        // NSN: [D] Hadamard(mu_V) / sqrt(D)
   float* s_ps = (float*)(mf_raw + Lo.ps) + wave * ptab_words<HB>();
   uint32_t* s_ph = (uint32_t*)(mf_raw + Lo.ph) + wave * ptab_words<HB>();
   _Float16* s_vs = (_Float16*)(mf_raw + Lo.vs) + wave * NG * VS_STRIDE;
@@ -156,6 +166,9 @@ attn_mfma_kernel(AttnArgs a) {
                                  : a.r.idx[0] + (int64_t)u * a.tcap;
   const uint8_t* vix_src = KVARN ? (const uint8_t*)(a.r.t16[1] + (int64_t)u * a.tcap)
                                  : a.r.idx[1] + (int64_t)u * a.tcap;
+  // NSN: the second norms follow the first in the tile's index section
+  const uint8_t* kt2_src = (const uint8_t*)(a.r.t2[0] + (int64_t)u * a.tcap);
+  const uint8_t* vt2_src = (const uint8_t*)(a.r.t2[1] + (int64_t)u * a.tcap);
 
   // ---------------------------------------------------------------- tile copy
   u32x4 rkc[TS::R_KC], rvc[TS::R_VC], rks, rvs, rix;
@@ -174,9 +187,20 @@ attn_mfma_kernel(AttnArgs a) {
     }
     if (lane < TILE * NGS * 4 / 16) rvs = ((const u32x4*)(vsz + (int64_t)tile * NGS * 4))[lane];
     const int ix_bytes = KVARN ? 2 : 1;
-    if (lane < TS::P_IX) rix = ((const u32x4*)(kix_src + (int64_t)tile * ix_bytes))[lane];
-    else if (lane < 2 * TS::P_IX)
+    if (NSNM) {
+      // [K t16 | K t2 | V t16 | V t2], 8 pieces each (one fixed source per
+      // lane range: a select over the four would become a private table)
+      constexpr int Q = TS::P_IX / 2;
+      const int64_t o = (int64_t)tile * ix_bytes;
+      if (lane < Q) rix = ((const u32x4*)(kix_src + o))[lane];
+      else if (lane < 2 * Q) rix = ((const u32x4*)(kt2_src + o))[lane - Q];
+      else if (lane < 3 * Q) rix = ((const u32x4*)(vix_src + o))[lane - 2 * Q];
+      else if (lane < 4 * Q) rix = ((const u32x4*)(vt2_src + o))[lane - 3 * Q];
+    } else if (lane < TS::P_IX) {
+      rix = ((const u32x4*)(kix_src + (int64_t)tile * ix_bytes))[lane];
+    } else if (lane < 2 * TS::P_IX) {
       rix = ((const u32x4*)(vix_src + (int64_t)tile * ix_bytes))[lane - TS::P_IX];
+    }
   };
   auto commit = [&]() {
     u32x4* t4 = (u32x4*)tb;
@@ -237,6 +261,27 @@ attn_mfma_kernel(AttnArgs a) {
   if (tid < HB) { s_l[tid] = 0.0f; s_qe[tid] = 0; }
   if (tid == 0) *s_next = fuse_here ? MF_WAVES - 2 : MF_WAVES;
   __syncthreads();
+  if constexpr (NSNM) {
+    // q . mu_K in the original space (the rotation is orthonormal): wave h
+    // < HB reduces head h; the V centre is rotated like the V partials
+    if (wave < HB) {
+      const float* muk = a.r.tab[0] + (int64_t)u * D;
+      float pq = __builtin_fmaf(s_q[wave * D + lane], muk[lane], s_q[wave * D + lane + 64] * muk[lane + 64]);
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) pq += __shfl_xor(pq, o, 64);
+      if (lane == 0) s_qmu[wave] = pq * a.qscale;
+    }
+    if (tid < D) s_muv[tid] = a.r.tab[1][(int64_t)u * D + tid];
+    __syncthreads();
+    for (int hs = 1; hs < D; hs <<= 1) {
+      float v = 0.0f;
+      if (tid < D) v = (tid & hs) ? s_muv[tid ^ hs] - s_muv[tid] : s_muv[tid] + s_muv[tid ^ hs];
+      __syncthreads();
+      if (tid < D) s_muv[tid] = v;
+      __syncthreads();
+    }
+    if (tid < D) s_muv[tid] *= (float)(1.0 / __builtin_sqrt(128.0));
+  }
   if (KVARN) {
     for (int hs = 1; hs < D; hs <<= 1) {
       float v[HB * D / MF_THREADS];
@@ -257,7 +302,7 @@ attn_mfma_kernel(AttnArgs a) {
     const float* ck = a.r.tab[0] + (int64_t)u * D;
     for (int i = tid; i < HB * D; i += MF_THREADS) {
       float v = s_q[i];
-      if (KVARN) v = v * isd * ck[i % D];
+      if (KVARN) v = NSNM ? v * isd : v * isd * ck[i % D];
       s_q[i] = v;
     }
   }
@@ -390,6 +435,10 @@ attn_mfma_kernel(AttnArgs a) {
   for (int s = 0; s < SPL; ++s) dsc[s] = a.qscale * ldexpf(1.0f, 24 + (KCH ? KCH_E : 0) - s_qe[head0 + s]);
 
   float m_run[SPL], l_run[SPL], zacc[4];
+  // NSN: running sum_t p_t n1_t per head, and qscale (q . mu_K) per head
+  float s1_run[SPL], qmu_r[SPL];
+#pragma unroll
+  for (int s = 0; s < SPL; ++s) { s1_run[s] = 0.0f; qmu_r[s] = NSNM ? s_qmu[head0 + s] : 0.0f; }
 #pragma unroll
   for (int s = 0; s < SPL; ++s) { m_run[s] = -INFINITY; l_run[s] = 0.0f; }
 #pragma unroll
@@ -623,10 +672,15 @@ attn_mfma_kernel(AttnArgs a) {
           for (int g = 0; g < NG; ++g) kszw[g] = g / VPS == 0 ? k2.x : k2.y;
         }
       }
-      float tk = 1.0f;
+      float tk = 1.0f, tk1 = 0.0f;
       int kix = KVQ_INDEX_NONE;
       if (KVARN) {
         tk = bits2f(((const uint16_t*)(tb + TS::O_KI))[t64]);
+        if (NSNM) {
+          // NSN: k^ rotated = n1 n2 (s c + z) + n1 Hadamard(mu_K) / sqrt(D)
+          tk1 = tk;
+          tk *= bits2f(((const uint16_t*)(tb + TS::O_KI + 2 * TILE))[t64]);
+        }
       } else {
         kix = tb[TS::O_KI + t64];   // 0xFF (no pattern) reads a 0 entry
       }
@@ -641,7 +695,7 @@ attn_mfma_kernel(AttnArgs a) {
           zt = __builtin_fmaf(bits2f((uint16_t)(kszw[g] >> 16)), qsum[r], zt);
         }
         float v = __builtin_fmaf(dot, dsc[s], zt);
-        if (KVARN) v *= tk;
+        if (KVARN) v = NSNM ? __builtin_fmaf(v, tk, tk1 * qmu_r[s]) : v * tk;
         sc[nb][s] = valid ? v : -INFINITY;
       }
     }
@@ -662,6 +716,7 @@ attn_mfma_kernel(AttnArgs a) {
       for (int s = 0; s < SPL; ++s) {
         al[s] = __builtin_amdgcn_exp2f(m_run[s] - mnew[s]);
         l_run[s] *= al[s];
+        if constexpr (NSNM) s1_run[s] *= al[s];
         m_run[s] = mnew[s];
       }
 #pragma unroll
@@ -709,11 +764,16 @@ attn_mfma_kernel(AttnArgs a) {
           for (int g = 0; g < NG; ++g) vszz[g] = valid ? (g / VPS == 0 ? v2.x : v2.y) : 0u;
         }
       }
-      float tv = 1.0f;
+      float tv = 1.0f, tn1 = 0.0f;
       int vix = KVQ_INDEX_NONE;
       if (KVARN) {
         const float t = bits2f(((const uint16_t*)(tb + TS::O_VI))[t64]);
         tv = valid ? t : 0.0f;
+        if (NSNM) {
+          // NSN: v^ rotated = n1 n2 (s c + z) + n1 Hadamard(mu_V) / sqrt(D)
+          tn1 = tv;
+          tv *= bits2f(((const uint16_t*)(tb + TS::O_VI + 2 * TILE))[t64]);
+        }
       } else {
         const int vi = tb[TS::O_VI + t64];
         vix = valid ? vi : KVQ_INDEX_NONE;
@@ -722,6 +782,7 @@ attn_mfma_kernel(AttnArgs a) {
       for (int s = 0; s < SPL; ++s) {
         const float p = __builtin_amdgcn_exp2f(sc[nb][s] - m_run[s]);
         l_run[s] += p;
+        if constexpr (NSNM) s1_run[s] = __builtin_fmaf(p, tn1, s1_run[s]);
         const float pt = p * tv;              // KVarN: v^ carries the token scale t
         if constexpr (NPB == 0)
 #pragma unroll
@@ -858,6 +919,9 @@ attn_mfma_kernel(AttnArgs a) {
   constexpr int MVR = NPB > 0 ? 16 * NPB : 1;
 #pragma unroll
   for (int s = 0; s < SPL; ++s) l_run[s] = row_sum16(l_run[s]);
+  if constexpr (NSNM)
+#pragma unroll
+    for (int s = 0; s < SPL; ++s) s1_run[s] = row_sum16(s1_run[s]);
   if constexpr (NPB == 0)
 #pragma unroll
     for (int r = 0; r < 4; ++r) zacc[r] = row_sum16(zacc[r]);
@@ -893,9 +957,10 @@ attn_mfma_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int s = 0; s < SPL; ++s) {
-      float* lz = s_lz + (wave * HB + head0 + s) * (1 + NG);
+      float* lz = s_lz + (wave * HB + head0 + s) * LZ;
       if (n16 == 0) {
         lz[0] = f[s] * l_run[s];
+        if constexpr (NSNM) lz[1 + NG] = f[s] * s1_run[s];
         if constexpr (NPB == 0)
 #pragma unroll
           for (int g = 0; g < NG; ++g) lz[1 + g] = f[s] * zacc[s * NG + g];
@@ -933,13 +998,14 @@ attn_mfma_kernel(AttnArgs a) {
       }
       s_wsum[e] = acc;
     }
-  if (tid < HB * (1 + NG)) {
+  if (tid < HB * LZ) {
     float acc = 0.0f;
 #pragma unroll
-    for (int w = 0; w < MF_WAVES; ++w) acc += s_lz[w * HB * (1 + NG) + tid];
-    const int h = tid / (1 + NG), k = tid % (1 + NG);
+    for (int w = 0; w < MF_WAVES; ++w) acc += s_lz[w * HB * LZ + tid];
+    const int h = tid / LZ, k = tid % LZ;
     if (k == 0) s_l[h] = acc;
-    else s_z[h * NG + k - 1] = acc;
+    else if (k <= NG) s_z[h * NG + k - 1] = acc;
+    else s_s1[h] = acc;
   }
   __syncthreads();
 
@@ -953,6 +1019,8 @@ attn_mfma_kernel(AttnArgs a) {
     const int h = i / D, d = i % D;
     const int64_t row = ((int64_t)b * a.Hq + hq0 + h) * S + split;
     float o = s_z[h * NG + d / G];
+    // NSN: the centre term sum_t p_t n1_t Hadamard(mu_V) / sqrt(D)
+    if constexpr (NSNM) o = __builtin_fmaf(s_s1[h], s_muv[d], o);
 #pragma unroll
     for (int w = 0; w < MF_WAVES; ++w) o += s_ow[(w * HB + h) * D + d];
     if constexpr (NPB > 0) {
@@ -1039,7 +1107,7 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < OPT; ++k) {
       const int i = tid + k * MF_THREADS;
-      s_o[i] = r_out[k] * a.r.tab[1][(int64_t)u * D + i % D];
+      s_o[i] = NSNM ? r_out[k] : r_out[k] * a.r.tab[1][(int64_t)u * D + i % D];
     }
     __syncthreads();
     for (int hs = 1; hs < D; hs <<= 1) {
@@ -1063,20 +1131,20 @@ attn_mfma_kernel(AttnArgs a) {
   if (tid == 0) __hip_atomic_store(&a.r.cnt[cu], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int BITS, int NG, int NGS, bool KVARN, int NPB, bool QLO, bool KCH = false>
+template <int BITS, int NG, int NGS, bool KVARN, int NPB, bool QLO, bool KCH = false, bool NSNM = false>
 static hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
   constexpr int HB = 16 / NG;
   const int npat = pad_pat(KVARN ? 0 : a.n_pat);
-  const MfLds L = mf_lds(HB, NG, npat, TileShape<BITS, NGS, KVARN, KCH>::BYTES, 16 * NPB, KCH);
+  const MfLds L = mf_lds(HB, NG, npat, TileShape<BITS, NGS, KVARN, KCH, NSNM>::BYTES, 16 * NPB, KCH, NSNM);
   static int attr = 0;
   if (L.total > attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel<BITS, NG, NGS, KVARN, NPB, QLO, KCH>,
+    hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel<BITS, NG, NGS, KVARN, NPB, QLO, KCH, NSNM>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, L.total);
     if (e != hipSuccess) return e;
     attr = L.total;
   }
   const int n_hb = (a.gq + HB - 1) / HB;
-  hipLaunchKernelGGL((attn_mfma_kernel<BITS, NG, NGS, KVARN, NPB, QLO, KCH>),
+  hipLaunchKernelGGL((attn_mfma_kernel<BITS, NG, NGS, KVARN, NPB, QLO, KCH, NSNM>),
                      dim3(a.B * a.Hkv * a.splits * n_hb), dim3(MF_THREADS), L.total, s, a);
   return hipGetLastError();
 }
@@ -1103,6 +1171,7 @@ static hipError_t launch_kch(const AttnArgs& a, hipStream_t s) {
 template <int BITS, int NG, int NGS>
 static hipError_t launch_bits_group(const AttnArgs& a, hipStream_t s) {
   if (a.mode == KVQ_MODE_KVARN) return launch_one<BITS, NG, NGS, true, 0, true>(a, s);
+  if (a.mode == KVQ_MODE_NSN) return launch_one<BITS, NG, NGS, true, 0, true, false, true>(a, s);
   if (a.r.kch) return launch_kch<BITS, NG, NGS>(a, s);
   return a.bf16 ? launch_pattern<BITS, NG, NGS, false>(a, s) : launch_pattern<BITS, NG, NGS, true>(a, s);
 }

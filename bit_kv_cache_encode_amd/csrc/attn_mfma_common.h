@@ -108,7 +108,7 @@ __device__ __forceinline__ u32x4 unpack_v(uint32_t w, int j) {
 // Per-wave LDS copy of one 64-token tile, byte offsets.  Every segment is
 // contiguous in the cache and 16-byte aligned, so the copy is plain 16-byte
 // loads per lane.
-template <int BITS, int NG, bool KVARN, bool KCH = false>
+template <int BITS, int NG, bool KVARN, bool KCH = false, bool NSNM = false>
 struct TileShape {
   static constexpr int KREC = D * BITS / 8;
   static constexpr int KC = TILE * KREC;            // K codes
@@ -117,7 +117,8 @@ struct TileShape {
   static constexpr int KS = KCH ? D * 4 : TILE * NG * 4;
   static constexpr int VC = 2 * VT * D * BITS / 8;  // two V code tiles
   static constexpr int VS = TILE * NG * 4;          // V (s, z) words
-  static constexpr int IX = KVARN ? 2 * TILE : TILE;// K idx or t16; V likewise
+  // K idx or t16 (NSN: t16 then t2); V likewise
+  static constexpr int IX = KVARN ? 2 * TILE * (NSNM ? 2 : 1) : TILE;
   static constexpr int O_KC = 0, O_KS = KC, O_VC = O_KS + KS, O_VS = O_VC + VC;
   static constexpr int O_KI = O_VS + VS, O_VI = O_KI + IX;
   static constexpr int BYTES = O_VI + IX;

@@ -35,8 +35,7 @@ bool cfg_ok(const kvq_config* c) {
   // up to MAX_GQ q-heads per kv-head on every path; up to 16 where the MFMA
   // attention serves the shape (q-head blocks)
   const int gq = c->n_q_heads / c->n_kv_heads;
-  if (gq > MAX_GQ && !(gq <= 16 && c->mode != KVQ_MODE_NSN && mfma_attention_supported(c->bits, c->group, gq)))
-    return false;
+  if (gq > MAX_GQ && !(gq <= 16 && mfma_attention_supported(c->bits, c->group, gq))) return false;
   if (c->head_dim != D) return false;
   if (c->max_tokens <= 0 || c->max_tokens > (1 << 28)) return false;
   // 1-bit codes in NSN mode (served by the VALU attention)
@@ -439,9 +438,10 @@ static AttnKernel attn_setup(const kvq_cache* cache, const kvq_layout& L, const 
   a.qscale = sm * 1.4426950408889634f;
   const int units = c.batch * c.n_kv_heads;
   const char* kenv = getenv("KVQ_ATTN_KERNEL");
-  const bool mfma_ok = mfma_attention_supported(c.bits, c.group, a.gq) && c.mode != KVQ_MODE_NSN;
-  // the paired kernel serves one q-head block per unit (and K per token)
-  const bool pp_ok = mfma_ok && a.gq <= 16 / (D / c.group) && !c.k_per_channel;
+  const bool mfma_ok = mfma_attention_supported(c.bits, c.group, a.gq);
+  // the paired kernel serves one q-head block per unit (K per token, no NSN)
+  const bool pp_ok = mfma_ok && a.gq <= 16 / (D / c.group) && !c.k_per_channel &&
+                     c.mode != KVQ_MODE_NSN;
   // (the VALU kernel holds at most MAX_GQ q-heads per kv-head)
   const bool valu_ok = a.gq <= MAX_GQ;
   const AttnKernel k = (!mfma_ok || (valu_ok && kenv && strcmp(kenv, "valu") == 0)) ? ATTN_VALU
@@ -499,7 +499,7 @@ int kvq_decode_step(kvq_cache* cache, const void* k_new, const void* v_new, cons
   // The fused launch covers the MFMA kernel (PatternKV and KVarN modes) with
   // a non-empty cache and one q-head block per unit; anything else is the two
   // calls in sequence.
-  if (k != ATTN_MFMA || a.gq > 16 / (D / c.group) || c.k_per_channel) {
+  if (k != ATTN_MFMA || a.gq > 16 / (D / c.group) || c.k_per_channel || c.mode == KVQ_MODE_NSN) {
     int st = kvq_encode_append(cache, k_new, v_new, 1, update_patterns, stream);
     if (st != KVQ_OK) return st;
     return kvq_attn_decode(cache, q, out, sm_scale, stream);

@@ -90,3 +90,29 @@ def test_nsn_token_appends(fused_call):
         err = float(np.abs(got.cpu().numpy() - want).max())
         assert err <= ATTN_TOL, f"step {s}: attention err {err}"
     _check(gpu, ref, B, Hq, T0 + steps, True, step=5)
+
+
+@pytest.mark.parametrize("bits,group,gq", [(2, 32, 4), (4, 64, 8), (2, 64, 4), (2, 32, 16)])
+@pytest.mark.parametrize("blocks", [1, 256])
+def test_nsn_attention_kernels_agree(monkeypatch, bits, group, gq, blocks):
+    """The matrix-core kernel (rotated query, n1 n2 token scale, q . mu_K and
+    sum p n1 centre terms) and the VALU kernel match the oracle over several
+    splits and q-head blocks."""
+    B, H, T = 2, 2, 700
+    gpu, ref, dt, k, v = _setup(B, gq * H, H, T, bits, group, True, off=gq + bits)
+    assert ref.encode_append(to_oracle(k, True), to_oracle(v, True)) == 0
+    gpu.encode_append(to_dev(k, dt), to_dev(v, dt))
+    monkeypatch.setenv("KVQ_ATTN_BLOCKS", str(blocks))
+    for step, qmul in ((0, 1.0), (1, 6.0)):
+        q = synth.queries(B, gq * H, D, step=step) * np.float32(qmul)
+        want = ref.attn_decode(to_oracle(q, True))
+        errs = {}
+        for kern in ("", "valu") if gq <= 8 else ("",):
+            if kern:
+                monkeypatch.setenv("KVQ_ATTN_KERNEL", kern)
+            else:
+                monkeypatch.delenv("KVQ_ATTN_KERNEL", raising=False)
+            print(f"nsn kernels bits={bits} group={group} gq={gq} kern={kern or 'mfma'}", flush=True)
+            got = gpu.attn_decode(to_dev(q, dt)).cpu().numpy()
+            errs[kern or "mfma"] = float(np.abs(got - want).max())
+        assert max(errs.values()) <= ATTN_TOL, errs
