@@ -22,10 +22,11 @@
  *  - The library never allocates device memory: the caller owns one device
  *    buffer per cache (kvq_layout_of().total bytes, 256-byte aligned) and
  *    frees it.  The split-K workspace of the attention lives in that buffer.
- *  - Supported shapes: head_dim 128; bits 2 or 4; group divides 128 and is a
- *    multiple of 8; max_patterns <= 255; n_q_heads a multiple of
- *    n_kv_heads with at most 8 q-heads per kv-head, or at most 16 where
- *    group is 32 or 64 (served by the matrix-core attention).
+ *  - Supported shapes: head_dim 128; bits 2 or 4 (also 1 in NSN mode); group
+ *    divides 128 and is a multiple of 8; max_patterns <= 255; n_q_heads a
+ *    multiple of n_kv_heads with at most 8 q-heads per kv-head, or at most 16
+ *    where bits is 2 or 4 and group is 32 or 64 (served by the matrix-core
+ *    attention).  shared_patterns and k_per_channel are PATTERN-mode options.
  *  - Domain: finite K/V inputs with |x| < 4096 and queries with
  *    |q| * sm_scale < 40.  Outside it results are unspecified (no error is
  *    raised; checking would need a device sync).
