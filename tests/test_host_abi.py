@@ -105,7 +105,7 @@ def test_layout_regions():
     dict(shared_patterns=2), dict(shared_patterns=1, mode=B.MODE_KVARN, max_patterns=0),
     dict(k_per_channel=2), dict(k_per_channel=1, mode=B.MODE_KVARN, max_patterns=0),
     dict(bits=1), dict(bits=1, mode=B.MODE_KVARN, max_patterns=0), dict(mode=3),
-    dict(mode=B.MODE_NSN, max_patterns=0, n_q_heads=96)])
+    dict(mode=B.MODE_NSN, max_patterns=0, bits=1, group=8, n_q_heads=96)])
 def test_layout_rejects_bad_configs(bad):
     """(n_q_heads 136 = 17 q-heads per kv-head; 72 at group 16 = 9 q-heads on
     a shape only the VALU attention serves, which holds at most 8.)"""
