@@ -100,31 +100,34 @@ def assert_same_encode(ref: "O.RefCache", cache, T: int, units=None, ref_units=N
                 assert np.array_equal(g2, r2), f"{'KV'[which]} n2 differ at {np.argwhere(g2 != r2)[:5]}"
 
 
-def assert_same_kch(ref: "O.RefCache", cache, T: int) -> None:
+def assert_same_kch(ref: "O.RefCache", cache, T: int, units=None, ref_units=None) -> None:
     """K per channel: K indices, the complete blocks' codes (ties excused)
     and (s, z) words, the open block's residuals, and V bit-exact for
-    tokens < T."""
+    tokens < T.  units: GPU units to compare; ref_units: matching oracle units."""
     c = cache.cfg
     U, D = c.batch * c.n_kv_heads, c.head_dim
+    units = list(range(U)) if units is None else list(units)
+    ref_units = units if ref_units is None else list(ref_units)
     closed, nblk = T // O.KBLOCK * O.KBLOCK, T // O.KBLOCK
-    gi, ri = gpu_idx(cache, 0)[:, :T], ref.idx(0)[:, :T]
+    gi, ri = gpu_idx(cache, 0)[units, :T], ref.idx(0)[ref_units, :T]
     assert np.array_equal(gi, ri), f"K idx differ at {np.argwhere(gi != ri)[:5]}"
     if closed:
-        gc = gpu_codes(cache, 0, closed)
-        rc = O.unpack_codes(ref.codes(0), 0, closed, D, c.bits)
-        bad = (gc != rc) & (ref.ties(0)[:, :closed] == 0)
+        gc = gpu_codes(cache, 0, closed, units)
+        rc = O.unpack_codes(ref.codes(0)[ref_units], 0, closed, D, c.bits)
+        bad = (gc != rc) & (ref.ties(0)[ref_units, :closed] == 0)
         assert not bad.any(), f"K codes differ at {np.argwhere(bad)[:5]}"
-        gb = cache.region("k_bsz").cpu().numpy().view(np.uint16).reshape(U, -1, D, 2)[:, :nblk]
-        rb = ref.block_sz()[:, :nblk]
+        gb = cache.region("k_bsz").cpu().numpy().view(np.uint16).reshape(U, -1, D, 2)[units, :nblk]
+        rb = ref.block_sz()[ref_units, :nblk]
         assert np.array_equal(gb, rb), f"K block (s, z) differ at {np.argwhere(gb != rb)[:5]}"
     if T % O.KBLOCK:
-        gt = cache.region("k_tail").cpu().numpy().view(np.uint16).reshape(U, O.KBLOCK, D)[:, :T % O.KBLOCK]
-        rt = ref.k_tail()[:, :T % O.KBLOCK]
+        gt = cache.region("k_tail").cpu().numpy().view(np.uint16).reshape(U, O.KBLOCK, D)
+        gt, rt = gt[units, :T % O.KBLOCK], ref.k_tail()[ref_units, :T % O.KBLOCK]
         assert np.array_equal(gt, rt), f"K residuals differ at {np.argwhere(gt != rt)[:5]}"
-    gc, rc = gpu_codes(cache, 1, T), O.unpack_codes(ref.codes(1), 1, T, D, c.bits)
+    gc = gpu_codes(cache, 1, T, units)
+    rc = O.unpack_codes(ref.codes(1)[ref_units], 1, T, D, c.bits)
     assert np.array_equal(gc, rc), f"V codes differ at {np.argwhere(gc != rc)[:5]}"
-    assert np.array_equal(gpu_sz(cache, 1)[:, :T], ref.sz(1)[:, :T]), "V scales differ"
-    assert np.array_equal(gpu_idx(cache, 1)[:, :T], ref.idx(1)[:, :T]), "V idx differ"
+    assert np.array_equal(gpu_sz(cache, 1)[units, :T], ref.sz(1)[ref_units, :T]), "V scales differ"
+    assert np.array_equal(gpu_idx(cache, 1)[units, :T], ref.idx(1)[ref_units, :T]), "V idx differ"
 
 
 def make_pair(B, Hq, Hkv, max_tokens, *, bits=2, group=32, mode="pattern", max_patterns=32,

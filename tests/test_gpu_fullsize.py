@@ -185,3 +185,74 @@ def test_streaming_qwen_fullsize():
         assert_same_encode(ref, gpu, T0 + S, units=[b * H + h], ref_units=[0])
     for b, h, s, err, qerr in report:
         print(f"unit ({b},{h}) step {s}: |gpu - oracle| {err:.2e}, |gpu - exact fp32| {qerr:.3e}")
+
+
+def test_kivi_fullsize():
+    """The step's shapes with K per channel over 128-token blocks: batch 8,
+    32 q / 8 kv heads, 32768-token prefix then 64 single-token decode appends
+    (an open block), 2-bit group 32, 32 patterns, window 128."""
+    from parity_util import assert_same_kch
+    dev = torch.device("cuda", 0)
+    B, Hq, H, T, S, P = 8, 32, 8, 32768, 64, 32
+    gq = Hq // H
+    k, v = synth.device_kv(B, H, T + S, D, device=dev, dtype=torch.bfloat16)
+    gpu = KVCache(B, Hq, H, T + S + 64, bits=2, group=32, mode="pattern", max_patterns=P,
+                  pattern_window=128, v_alpha=0.05, in_dtype=torch.bfloat16, k_per_channel=True)
+    gpu.init_patterns(k[:, :, :2048].contiguous(), v[:, :, :2048].contiguous(), P)
+    gpu.encode_append(k[:, :, :T].contiguous(), v[:, :, :T].contiguous())
+    for s in range(S):
+        gpu.encode_append(k[:, :, T + s:T + s + 1].contiguous(), v[:, :, T + s:T + s + 1].contiguous(),
+                          update_patterns=True)
+    q = synth.device_queries(B, Hq, D, device=dev, dtype=torch.bfloat16)
+    out = gpu.attn_decode(q)
+    torch.cuda.synchronize()
+    for (b, h) in [(0, 0), (5, 3), (7, 7)]:
+        ref = _unit_ref(gq, T + S + 64, bits=2, group=32, mode=O.PATTERN, max_patterns=P,
+                        pattern_window=128, v_alpha=0.05, k_per_channel=True)
+        ku, vu = _unit_in(k, b, h), _unit_in(v, b, h)
+        assert ref.init_patterns(ku[:, :, :2048], vu[:, :, :2048], P) == 0
+        assert ref.encode_append(ku[:, :, :T], vu[:, :, :T]) == 0
+        for s in range(S):
+            assert ref.encode_append(ku[:, :, T + s:T + s + 1], vu[:, :, T + s:T + s + 1], update=1) == 0
+        print(f"k per channel full size unit ({b},{h})", flush=True)
+        assert_same_kch(ref, gpu, T + S, units=[b * H + h], ref_units=[0])
+        err = _check_unit_attn(out, ref, q, b, h, gq)
+        print(f"unit ({b},{h}): attention err {err:.2e}")
+
+
+def test_nsn_breadth_fullsize():
+    """64 samples x 16384 tokens, 8 kv heads, the NSN scalar mode at 2 bits
+    (group 32), centres from the first 256 tokens."""
+    dev = torch.device("cuda", 0)
+    B, Hq, H, T, n_init = 64, 32, 8, 16384, 256
+    gq = Hq // H
+    k, v = synth.device_kv(B, H, T, D, device=dev, dtype=torch.bfloat16)
+    gpu = KVCache(B, Hq, H, T, bits=2, group=32, mode="nsn", max_patterns=0, in_dtype=torch.bfloat16)
+    gpu.init_patterns(k[:, :, :n_init].contiguous(), v[:, :, :n_init].contiguous(), 0)
+    torch.cuda.synchronize()
+    samples = [(0, 0), (40, 2), (63, 7)]
+    refs = {}
+    mk, mv = gpu_tab(gpu, 0).copy(), gpu_tab(gpu, 1).copy()
+    for (b, h) in samples:
+        u = b * H + h
+        ref = O.RefCache(1, gq, 1, D, T, bits=2, group=32, mode=O.NSN, max_patterns=0,
+                         in_dtype=O.IN_BF16)
+        ku, vu = _unit_in(k, b, h), _unit_in(v, b, h)
+        assert ref.init_patterns(ku[:, :, :n_init], vu[:, :, :n_init], 0) == 0
+        # centres agree within rounding (binary64 sums in another order)
+        np.testing.assert_allclose(mk[u], ref.scales(0)[0], rtol=1e-6, atol=1e-7)
+        np.testing.assert_allclose(mv[u], ref.scales(1)[0], rtol=1e-6, atol=1e-7)
+        mk[u], mv[u] = ref.scales(0)[0], ref.scales(1)[0]
+        refs[(b, h)] = (ref, ku, vu)
+    # the sampled units encode with the oracle's centres (oracle -> GPU only)
+    gpu.set_patterns(torch.from_numpy(mk.reshape(B, H, D)).to(dev),
+                     torch.from_numpy(mv.reshape(B, H, D)).to(dev))
+    gpu.encode_append(k, v)
+    q = synth.device_queries(B, Hq, D, device=dev, dtype=torch.bfloat16)
+    out = gpu.attn_decode(q)
+    torch.cuda.synchronize()
+    for (b, h), (ref, ku, vu) in refs.items():
+        assert ref.encode_append(ku, vu) == 0
+        print(f"nsn full size unit ({b},{h})", flush=True)
+        assert_same_encode(ref, gpu, T, units=[b * H + h], ref_units=[0])
+        _check_unit_attn(out, ref, q, b, h, gq)
