@@ -221,7 +221,8 @@ attn_mfma_kernel(AttnArgs a) {
   // take their tiles from the counter afterwards
   // K per channel: a wave takes both tiles of a 128-token block (splits start
   // on block boundaries), so the q * s operand serves two tiles
-  const int first = KCH ? 2 * wave : !fuse_here ? wave : (wave < 2 ? n_tiles : wave - 2);
+  const int first = !fuse_here ? (KCH ? 2 * wave : wave)
+                                : (wave < 2 ? n_tiles : (KCH ? 2 * (wave - 2) : wave - 2));
   if (first < n_tiles) issue(t_begin + TILE * first);
   // M^V rows for the pattern term go straight to LDS (no registers held
   // through the loop); 16 bytes per lane, one kilobyte per wave instruction.
@@ -499,6 +500,13 @@ attn_mfma_kernel(AttnArgs a) {
     }
     float xh0 = __builtin_fmaf((float)c0, bits2f((uint16_t)(w0 & 0xFFFFu)), bits2f((uint16_t)(w0 >> 16))) + m0;
     float xh1 = __builtin_fmaf((float)c1, bits2f((uint16_t)(w1 & 0xFFFFu)), bits2f((uint16_t)(w1 >> 16))) + m1;
+    if (KCH && kind == 0) {
+      // K per channel: the token stays in its open block as the binary16
+      // residual this lane just stored, plus its pattern
+      const uint16_t* slot = e.r.ktail + (uu * KBLOCK + e.t0 % KBLOCK) * D;
+      xh0 = bits2f(slot[lane]) + m0;
+      xh1 = bits2f(slot[lane + 64]) + m1;
+    }
     if (KVARN) {
       const float tf = bits2f((uint16_t)t16);
       xh0 *= tf;
@@ -524,7 +532,7 @@ attn_mfma_kernel(AttnArgs a) {
     }
     int nx = 0;
     if (lane == 0) nx = atomicAdd(s_next, 1);
-    cur = __builtin_amdgcn_readfirstlane(nx);
+    cur = __builtin_amdgcn_readfirstlane(nx) * (KCH ? 2 : 1);
     if (cur < n_tiles) issue(t_begin + TILE * cur);
   }
   for (; cur < n_tiles;) {

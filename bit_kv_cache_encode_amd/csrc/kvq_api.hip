@@ -499,7 +499,9 @@ int kvq_decode_step(kvq_cache* cache, const void* k_new, const void* v_new, cons
   // The fused launch covers the MFMA kernel (PatternKV and KVarN modes) with
   // a non-empty cache and one q-head block per unit; anything else is the two
   // calls in sequence.
-  if (k != ATTN_MFMA || a.gq > 16 / (D / c.group) || c.k_per_channel || c.mode == KVQ_MODE_NSN) {
+  // K per channel: a token that completes its block needs the block kernel
+  const bool kch_close = c.k_per_channel && (cache->n_tokens + 1) % KBLOCK == 0;
+  if (k != ATTN_MFMA || a.gq > 16 / (D / c.group) || kch_close || c.mode == KVQ_MODE_NSN) {
     int st = kvq_encode_append(cache, k_new, v_new, 1, update_patterns, stream);
     if (st != KVQ_OK) return st;
     return kvq_attn_decode(cache, q, out, sm_scale, stream);
@@ -522,6 +524,7 @@ int kvq_decode_step(kvq_cache* cache, const void* k_new, const void* v_new, cons
   e.max_pat = c.max_patterns;
   e.rho = cache->rho;
   e.tiles_per_block = 1;
+  e.kch_tail_direct = c.k_per_channel;   // the token leaves its block open (checked above)
   const bool window = c.mode == KVQ_MODE_PATTERN && update_patterns && c.pattern_window > 0;
   if (window) {
     e.win_update = 1;

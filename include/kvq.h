@@ -226,7 +226,7 @@ int kvq_attn_decode(kvq_cache* cache, const void* q, float* out, float sm_scale,
  * agrees with them to floating-point rounding.  Falls back to the two calls
  * in sequence where the fused launch does not apply (an empty cache, more
  * q-heads per kv-head than one MFMA row block, shapes served by the VALU
- * kernel, k_per_channel).
+ * kernel, NSN mode, a k_per_channel token that completes its block).
  * Errors as kvq_encode_append (n_new = 1) and kvq_attn_decode; nothing is
  * written when a check fails. */
 int kvq_decode_step(kvq_cache* cache, const void* k_new, const void* v_new, const void* q,
