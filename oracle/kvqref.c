@@ -87,6 +87,13 @@
  *      w = FWHT(fmaf(q, s, z)) * fp32(1/sqrt(D)), x^ = fl(fl(fl(w * n2) + mu) * n1).
  *      mu = mean over the prefix tokens of x / rms(x) in binary64 (tokens with
  *      rms 0 skipped), rounded to fp32; 0 before any init.
+ *
+ * Parity unpinned: R12 (the KVarN channel-scale definition; the pages give
+ * no formula) and R13's convergence details (start rows, pass limit, empty
+ * clusters) beyond the textbook Lloyd iteration are checked only for
+ * self-consistency, since no printed numbers exist to pin them.  The other
+ * readings are pinned by the test suite against independent computations,
+ * closed forms and hand-derived bytes.
  */
 #include "kvqref.h"
 
