@@ -88,12 +88,14 @@
  *      mu = mean over the prefix tokens of x / rms(x) in binary64 (tokens with
  *      rms 0 skipped), rounded to fp32; 0 before any init.
  *
- * Parity unpinned: R12 (the KVarN channel-scale definition; the pages give
- * no formula) and R13's convergence details (start rows, pass limit, empty
- * clusters) beyond the textbook Lloyd iteration are checked only for
- * self-consistency, since no printed numbers exist to pin them.  The other
- * readings are pinned by the test suite against independent computations,
- * closed forms and hand-derived bytes.
+ * Pins of R12 and R13 (no printed numbers exist for them): the channel
+ * scale equals a closed form on prefixes built in the rotated space (each
+ * row a token magnitude times a channel profile times random signs), which
+ * fixes the transform's order, the per-token normalisation and the RMS; the
+ * k-means empty-cluster rule is fixed by a hand-traced Lloyd run in which a
+ * strided start leaves a cluster empty.  The other readings are pinned by
+ * the test suite against independent computations, closed forms and
+ * hand-derived bytes.
  */
 #include "kvqref.h"
 

@@ -42,3 +42,21 @@ def test_kmeans_tables_bit_exact(n, P, bf16):
         r = ref.patterns(which)[:, :P]
         assert np.array_equal(g.view(np.uint32), r.view(np.uint32)), \
             f"{'KV'[which]} table differs in {int((g != r).sum())} of {g.size} values"
+
+
+def test_kmeans_empty_cluster_trace():
+    """The hand-traced Lloyd run of the oracle pins (rows 5, 15, 5, 7 in every
+    channel, 2 patterns): the strided start leaves cluster 1 empty on the
+    first pass, it keeps its centroid, and the run ends at (15, 17/3)."""
+    D = 128
+    x = np.repeat(np.array([[5.0], [15.0], [5.0], [7.0]], np.float32), D, axis=1)[None, None]
+    gpu, ref, dt = make_pair(1, 1, 1, 4, max_patterns=8, bf16=False)
+    assert ref.init_patterns(x, x, 2) == 0
+    print("k-means empty-cluster trace", flush=True)
+    gpu.init_patterns(to_dev(x, dt), to_dev(x, dt), 2)
+    torch.cuda.synchronize()
+    want = np.stack([np.full(D, 15.0, np.float32), np.full(D, np.float32(17.0 / 3.0), np.float32)])
+    for which in (0, 1):
+        g = gpu_tab(gpu, which)[0, :2]
+        assert np.array_equal(ref.patterns(which)[0, :2], want)
+        assert np.array_equal(g.view(np.uint32), want.view(np.uint32))

@@ -90,6 +90,29 @@ def test_shape_variants(bits, group, gq, npat):
     _check_attn(ref, gpu, synth.queries(B, gq * H, 128, step=3), bf16=True)
 
 
+def test_kvarn_channel_scale_closed_form():
+    """GPU channel scales on the oracle pin's closed-form prefix: rows built in
+    the rotated space as a_t (sigma * eps_t), so c = sigma / rms(sigma)
+    whatever the token magnitudes a_t (KVarN abstract, reading R12)."""
+    import math
+    from scipy.linalg import hadamard
+    D, T = 128, 64
+    rng = np.random.default_rng(77)
+    sig = [rng.permutation(np.linspace(0.3, 4.0, D)) for _ in range(2)]
+    rows = []
+    for s_ in sig:
+        y = rng.uniform(0.5, 9.0, (T, 1)) * s_ * rng.choice([-1.0, 1.0], (T, D))
+        rows.append((y @ hadamard(D).T.astype(np.float64) / math.sqrt(D)).astype(np.float32))
+    k, v = rows[0][None, None], rows[1][None, None]
+    gpu, _, dt = make_pair(1, 4, 1, 128, mode="kvarn", max_patterns=0, bf16=False)
+    print("KVarN channel scale, closed form", flush=True)
+    gpu.init_patterns(to_dev(k, dt), to_dev(v, dt), 0)
+    torch.cuda.synchronize()
+    for which in (0, 1):
+        want = sig[which] / math.sqrt((sig[which] ** 2).mean())
+        np.testing.assert_allclose(gpu_tab(gpu, which).reshape(D), want, rtol=2e-6, atol=0)
+
+
 def test_kvarn_mode():
     """Hadamard + dual-axis normalisation encode, with oracle channel scales."""
     B, Hq, H, T = 2, 8, 2, 150

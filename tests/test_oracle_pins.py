@@ -409,3 +409,87 @@ def test_config_validation(ref):
     c = O.RefCache(1, 1, 1, 128, 4)
     x = np.zeros((1, 1, 5, 128), np.float32)
     assert c.encode_append(x, x) == -2 and c.n_tokens == 0
+
+
+# --------------------------------------------------------------- KVarN channel scale (R12)
+def _sylvester_rows(sigma_rows):
+    """x = H y / sqrt(D) with scipy's Sylvester Hadamard matrix, i.e. the
+    orthonormal inverse of y = H x / sqrt(D) (H is symmetric, H H = D I)."""
+    from scipy.linalg import hadamard
+    D = sigma_rows.shape[-1]
+    return (sigma_rows @ hadamard(D).T.astype(np.float64)) / math.sqrt(D)
+
+
+def test_kvarn_channel_scale_closed_form(ref):
+    """KVarN abstract, dual-axis variance normalisation (reading R12): the
+    channel scale is the RMS over prefix tokens of the rotated row divided by
+    its own RMS.  Rows built in the rotated space as y_t = a_t (prof_t * eps_t),
+    with eps_t in {+1,-1}^D, a random positive token magnitude a_t and the
+    profile prof_t = sigma for the first half of the tokens and tau for the
+    second, have y_tj / rms(y_t) = prof_tj eps_tj / rms(prof_t), so
+    c_j = sqrt((sigma_j^2 / ms(sigma) + tau_j^2 / ms(tau)) / 2) exactly
+    (ms = mean square over channels).  The profiles are random permutations of
+    distinct values, so a transform in another order (bit-reversed or
+    sequency order), a missed or mis-signed butterfly stage, swapped channels,
+    a mean |y| in place of the RMS, or a global instead of a per-token
+    normalisation all move c away from this value."""
+    D, T = 128, 96
+    rng = np.random.default_rng(1203)
+    B = 2
+    k = np.zeros((B, 1, T, D), np.float32)
+    v = np.zeros((B, 1, T, D), np.float32)
+    want = np.zeros((2, B, D))
+    for kind, arr in enumerate((k, v)):
+        for b in range(B):
+            sigma = rng.permutation(np.linspace(0.2, 5.0, D))
+            tau = rng.permutation(np.geomspace(0.05, 8.0, D))
+            prof = np.where(np.arange(T)[:, None] < T // 2, sigma[None], tau[None])
+            eps = rng.choice([-1.0, 1.0], (T, D))
+            a = rng.uniform(0.1, 20.0, (T, 1))
+            arr[b, 0] = _sylvester_rows(a * prof * eps).astype(np.float32)
+            want[kind, b] = np.sqrt((sigma ** 2 / (sigma ** 2).mean()
+                                     + tau ** 2 / (tau ** 2).mean()) / 2)
+    c = O.RefCache(B, 1, 1, D, T, mode=O.KVARN, max_patterns=0)
+    c.init_patterns(k, v, 0)
+    for kind in range(2):
+        got = c.scales(kind)[:B].astype(np.float64)
+        np.testing.assert_allclose(got, want[kind], rtol=2e-6, atol=0)
+    # the same construction with one profile (tau = sigma): c = sigma / rms(sigma)
+    sigma = rng.permutation(np.linspace(0.5, 3.0, D))
+    eps = rng.choice([-1.0, 1.0], (T, D))
+    x = _sylvester_rows(sigma * eps).astype(np.float32)[None, None]
+    c1 = O.RefCache(1, 1, 1, D, T, mode=O.KVARN, max_patterns=0)
+    c1.init_patterns(x, x, 0)
+    np.testing.assert_allclose(c1.scales(0)[0], sigma / math.sqrt((sigma ** 2).mean()),
+                               rtol=2e-6, atol=0)
+    # an all-zero prefix has no token to normalise: every scale is 1
+    z = np.zeros((1, 1, 8, D), np.float32)
+    c2 = O.RefCache(1, 1, 1, D, 8, mode=O.KVARN, max_patterns=0)
+    c2.init_patterns(z, z, 0)
+    assert np.array_equal(c2.scales(0)[0], np.ones(D, np.float32))
+
+
+# --------------------------------------------------------------- k-means empty cluster (R13)
+def test_kmeans_empty_cluster_keeps_centroid(ref):
+    """Eq 4 Lloyd iteration with reading R13's empty-cluster rule, traced by
+    hand on one-dimensional rows x = (5, 15, 5, 7), k = 2.  Strided start:
+    centroids x[0] = 5 and x[2] = 5.  Pass 1: every row is equidistant, ties
+    go to index 0, so cluster 1 is empty; c0 = 32/4 = 8 and c1 keeps 5.
+    Pass 2: 5 -> 1, 15 -> 0, 5 -> 1, 7 -> 0 (1 < 4); c0 = 11, c1 = 5.
+    Pass 3: 7 -> 1 (16 > 4); c0 = 15, c1 = 17/3.  Pass 4 repeats pass 3's
+    assignment and stops.  Resetting an empty centroid to 0 would stop at
+    (8, 0) after pass 2; moving it to the farthest row would give (17/3, 15)."""
+    x = np.array([[5.0], [15.0], [5.0], [7.0]], np.float32)
+    cent, a, it = O.kmeans(x, 2)
+    assert np.array_equal(cent[:, 0], np.array([15.0, np.float32(17.0 / 3.0)], np.float32))
+    assert list(a) == [1, 0, 1, 1]
+    assert it == 4
+    # the same trace in every channel of a 128-wide row, so the cache's
+    # pattern init (which the GPU k-means is compared with) sees it too
+    D = 128
+    rows = np.repeat(x, D, axis=1)[None, None]
+    c = O.RefCache(1, 1, 1, D, 4, max_patterns=2)
+    c.init_patterns(rows, rows, 2)
+    pk = c.patterns(0)[0, :2]
+    assert np.array_equal(pk[0], np.full(D, 15.0, np.float32))
+    assert np.array_equal(pk[1], np.full(D, np.float32(17.0 / 3.0), np.float32))
