@@ -10,13 +10,13 @@ cache.  The 32 layer caches (6.9 GB) are distinct buffers, so the 256 MB
 Infinity Cache cannot hold them.
 
 value = algorithmic bytes of a step / step time (effective GB/s); the bytes
-are the packed cache records read by attention, the pattern tables read by
-attention and encode, the new K/V read and records written by encode, q and
-the outputs.  The roofline object covers the step's dominant kernel (the
-one-launch decode step), timed with events on the stream it runs on around a
-rotating sample of its launches inside the timed steps (2 of 32 layers per
-step: an event record between launches adds device time of its own).  A bulk (prefill-style) encode rate is
-reported as encode tokens/s.  The CPU oracle is timed on a bounded sample.
+are the packed cache records and pattern tables read by attention, the new
+K/V read and records written by encode, q and the outputs.  The roofline
+object covers the step's dominant kernel (the one-launch decode step, the only
+kernel of the timed region), timed with one event pair on the stream it runs
+on around the whole timed region.  A bulk (prefill-style) encode rate is
+reported as encode tokens/s.  The CPU oracle is timed on a bounded sample, on
+one core and on every usable core.
 
 Usage: python bench.py [--steps K] [--warmup W] [--context T] [--layers L]
        [--no-cpu-baseline] [--gpus 1]
@@ -230,7 +230,7 @@ def traffic_summary(args):
         out["kernel"] = "decode step in one launch: encode 1 token + attention (split + combine)"
         out["algorithmic_bytes_per_launch"] = (2 * 64 * (args.context + 1) * 49 + 2 * 64 * 32 * 128 * 4
                                                + 8 * 32 * 128 * 6
-                                               + 2 * 64 * 128 * 2 + 2 * 64 * 49 + 2 * 64 * 32 * 128 * 4)
+                                               + 2 * 64 * 128 * 2 + 2 * 64 * 49)
     else:
         out["kernel"] = "attention (split + combine)"
     flag = "" if not args.split_step else " --split-step"
@@ -348,17 +348,21 @@ def main():
     def attn_bytes(T):
         return 2 * U * T * rec + 2 * PU * P * D * 4 + B * Hq * D * (in_b + 4)
 
-    enc_bytes = 2 * U * D * in_b + 2 * U * rec + 2 * PU * P * D * 4
+    # the new token's K/V in and its records out; the pattern tables the encode
+    # reads are the ones the attention reads in the same launch, counted there
+    enc_bytes = 2 * U * D * in_b + 2 * U * rec
 
-    # Events bracket a rotating sample of the layers' launches inside the timed
-    # steps (EV_EVERY-th layer, offset by the step), because an event record
-    # between two launches costs ~6 us of device time on its own.  Per sampled
-    # layer: [0] before the layer's calls, [1] after them; in the two-call form
-    # [2] sits between the encode and the attention.
-    EV_EVERY = max(1, min(16, L))   # at least one sampled layer per step
+    # The one-launch step is the only kernel of the timed region: one event pair
+    # on its stream around the whole region gives its average launch duration
+    # (with the few-microsecond gaps between back-to-back launches), and so it
+    # can never exceed the step time per layer.  The two-call form (a
+    # profiling aid) brackets a rotating sample of layers instead (an event
+    # record between two launches costs device time of its own): per sampled
+    # layer [0] before the encode, [2] between it and the attention, [1] after.
+    EV_EVERY = max(1, min(16, L))
 
     def sampled(s, li):
-        return (li - s) % EV_EVERY == 0
+        return args.split_step and (li - s) % EV_EVERY == 0
 
     def step(s, ev=None):
         for li, c in enumerate(layers):
@@ -382,28 +386,36 @@ def main():
     T_start = layers[0].n_tokens
     evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)]
             for _ in range(L)] for _ in range(args.steps)]
+    stream = torch.cuda.current_stream(dev)    # the stream the library launches on
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    r0.record(stream)
     for s in range(args.steps):
         step(args.warmup + s, evs[s])
+    r1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    used = [evs[s][li] for s in range(args.steps) for li in range(L) if sampled(args.warmup + s, li)]
-    layer_ms = [e[0].elapsed_time(e[1]) for e in used]
-    layer_avg_us = 1e3 * sum(layer_ms) / len(layer_ms)
+    region_ms = r0.elapsed_time(r1)
+    layer_avg_us = 1e3 * region_ms / (args.steps * L)
     T_mid = T_start + args.steps // 2 + 1
     step_bytes = L * (attn_bytes(T_mid) + enc_bytes)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     if args.split_step:
         # dominant kernel: the attention launch; the encode launch on its own
+        used = [evs[s][li] for s in range(args.steps) for li in range(L) if sampled(args.warmup + s, li)]
         attn_avg_us = 1e3 * sum(e[2].elapsed_time(e[1]) for e in used) / len(used)
         enc_avg_us = 1e3 * sum(e[0].elapsed_time(e[2]) for e in used) / len(used)
         kern, kern_us, kern_bytes = "attention (split + combine)", attn_avg_us, attn_bytes(T_mid)
+        timing = ("HIP events around the attention launch of a rotating sample of layers "
+                  f"(every {EV_EVERY}th) inside the timed steps")
     else:
         # dominant kernel: the one-launch step (encode 1 token + attention)
         kern = "decode step in one launch: encode 1 token + attention (split + combine)"
         kern_us, kern_bytes = layer_avg_us, attn_bytes(T_mid) + enc_bytes
+        timing = (f"one HIP event pair on the launch stream around the timed region "
+                  f"({args.steps * L} launches, nothing else launched): device time / launches")
         # the single-token encode as its own launch, on a copy of one layer,
         # with the device kept busy while the host queues the launches
         enc_copy = layers[0].clone()
@@ -448,9 +460,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": kern,
-                     "avg_launch_us": round(kern_us, 3),
+                     "avg_launch_us": round(kern_us, 3), "timing": timing,
                      "algorithmic_bytes_per_launch": kern_bytes},
-        "layer_step_avg_us": round(layer_avg_us, 3),
+        "layer_step_avg_us": round(ms_step * 1e3 / L, 3),
         "encode": {"bulk_tok_s": round(B * T0 / (bulk_ms * 1e-3), 1),
                    "bulk_tokens": B * T0, "bulk_ms": round(bulk_ms, 3),
                    "decode_step_tok_s": round(B / (enc_avg_us * 1e-6), 1),
@@ -468,27 +480,42 @@ def main():
     print(json.dumps(res))
 
 
-def cpu_baseline(args, T0, P, W, attn_bytes, enc_bytes, U):
-    """The oracle, as it stands, on a bounded sample of the same workload: one
-    (batch, kv-head) unit at the same context, decode steps (encode 1 token
-    with the Chebyshev window on + 4-q-head attention) repeated until the time
-    budget is spent."""
+def _host_cpu():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cores": usable}
+
+
+def _oracle_unit_steps(args, T0, P, W, attn_bytes, enc_bytes, U, unit, seconds):
+    """Decode steps of one oracle cache (one (batch, kv-head) unit with its 4
+    q-heads at the workload's context) until `seconds` of stepping are spent.
+    Returns (steps, seconds, bytes)."""
     import oracle as O
     from bit_kv_cache_encode_amd import synth
 
-    D, rep = 128, 4
-    n_max = 4096
-    k = synth.k_vectors(1, 1, T0 + n_max, D)
-    v = synth.v_vectors(1, 1, T0 + n_max, D)
+    D, rep, n_max = 128, 4, 4096
+    k = synth.k_vectors(1, 1, T0 + n_max, D, seed=synth.seed_for("k") + 17 * unit)
+    v = synth.v_vectors(1, 1, T0 + n_max, D, seed=synth.seed_for("v") + 17 * unit)
     kb, vb = synth.f32_to_bf16_bits(k), synth.f32_to_bf16_bits(v)
-    q = synth.f32_to_bf16_bits(synth.queries(1, rep, D))
+    del k, v
+    q = synth.f32_to_bf16_bits(synth.queries(1, rep, D, step=unit))
     r = O.RefCache(1, rep, 1, D, T0 + n_max, max_patterns=P, pattern_window=W,
                    in_dtype=O.IN_BF16)
     nk = min(args.kmeans_tokens, T0)
     r.init_patterns(kb[:, :, :nk], vb[:, :, :nk], P)
     r.encode_append(kb[:, :, :T0], vb[:, :, :T0])
     steps, secs, nbytes = 0, 0.0, 0.0
-    while secs < args.cpu_seconds and steps < n_max:
+    while secs < seconds and steps < n_max:
         t = T0 + steps
         t_start = time.perf_counter()
         r.encode_append(kb[:, :, t:t + 1], vb[:, :, t:t + 1], update=1)
@@ -496,11 +523,38 @@ def cpu_baseline(args, T0, P, W, attn_bytes, enc_bytes, U):
         secs += time.perf_counter() - t_start
         nbytes += (attn_bytes(t + 1) + enc_bytes) / U
         steps += 1
-    return {"value": round(nbytes / secs / 1e9, 5), "unit": "GB/s", "cores": 1,
+    return steps, secs, nbytes
+
+
+def cpu_baseline(args, T0, P, W, attn_bytes, enc_bytes, U):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    (batch, kv-head) units at the same context, each stepping decode steps
+    (encode 1 token with the Chebyshev window on + 4-q-head attention) for a
+    time budget.  Run once on one core, then on every usable core with one
+    unit per thread (the oracle is C called through ctypes, which releases the
+    interpreter lock, and each unit is an independent cache)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    host = _host_cpu()
+    st, ss, sb = _oracle_unit_steps(args, T0, P, W, attn_bytes, enc_bytes, U, 0, args.cpu_seconds)
+    single = sb / ss / 1e9
+    n = max(1, min(16, host["usable_cores"]))
+    t_all = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=n) as ex:
+        res = list(ex.map(lambda i: _oracle_unit_steps(args, T0, P, W, attn_bytes, enc_bytes, U,
+                                                       1 + i, args.cpu_seconds), range(n)))
+    t_all = time.perf_counter() - t_all
+    # aggregate rate: every thread's bytes over the longest thread's stepping time
+    tot_bytes = sum(r[2] for r in res)
+    span = max(r[1] for r in res)
+    return {"value": round(tot_bytes / span / 1e9, 5), "unit": "GB/s", "cores": n,
             "kind": "oracle",
-            "sample": (f"{steps} decode steps (encode 1 token + 4-q-head attention) on one of "
-                       f"the {U} (batch, kv-head) units at context {T0}; single-threaded C "
-                       f"oracle, {secs:.1f} s timed; bytes counted as in value")}
+            "single_core_value": round(single, 5),
+            "host": host,
+            "sample": (f"{n} threads, one (batch, kv-head) unit of the {U} each at context {T0}, "
+                       f"{sum(r[0] for r in res)} decode steps in all (encode 1 token + 4-q-head "
+                       f"attention), {span:.1f} s of stepping per thread ({t_all:.1f} s with set-up); "
+                       f"single core: {st} steps in {ss:.1f} s; C oracle, bytes counted as in value")}
 
 
 if __name__ == "__main__":

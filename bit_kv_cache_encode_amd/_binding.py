@@ -13,6 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvq.so")
 
 KVQ_OK, KVQ_EINVAL, KVQ_ECAPACITY, KVQ_ESTATE, KVQ_EDEVICE = 0, -1, -2, -3, -4
+ATTN_AUTO, ATTN_VALU = 0, 1
 MODE_PATTERN, MODE_KVARN, MODE_NSN = 0, 1, 2
 F32, BF16 = 0, 1
 INDEX_NONE = 0xFF
@@ -46,7 +47,7 @@ class kvq_layout(C.Structure):
 class kvq_cache(C.Structure):
     _fields_ = [("cfg", kvq_config), ("base", C.c_void_p), ("n_tokens", C.c_int32),
                 ("n_patterns", C.c_int32), ("win_count", C.c_int32), ("dropped", C.c_int32),
-                ("rho", C.c_float)]
+                ("rho", C.c_float), ("attn_kernel", C.c_int32), ("attn_blocks", C.c_int32)]
 
 
 class KvqError(RuntimeError):

@@ -175,6 +175,31 @@ class KVCache:
     def rho(self) -> float:
         return self.c.rho
 
+    @property
+    def attn_kernel(self) -> str:
+        """Attention kernel: "auto" (the matrix-core kernel wherever it
+        applies) or "valu" (the vector kernel, a cross-check).  Set from the
+        environment variable KVQ_ATTN_KERNEL when the cache is created."""
+        return "valu" if self.c.attn_kernel == B.ATTN_VALU else "auto"
+
+    @attn_kernel.setter
+    def attn_kernel(self, name: str) -> None:
+        if name not in ("auto", "valu"):
+            raise ValueError("attn_kernel must be 'auto' or 'valu'")
+        self.c.attn_kernel = B.ATTN_VALU if name == "valu" else B.ATTN_AUTO
+
+    @property
+    def attn_blocks(self) -> int:
+        """Target grid size of the attention, 0 = the default (256).  Set
+        from the environment variable KVQ_ATTN_BLOCKS when the cache is created."""
+        return self.c.attn_blocks
+
+    @attn_blocks.setter
+    def attn_blocks(self, n: int) -> None:
+        if int(n) < 0:
+            raise ValueError("attn_blocks must be >= 0")
+        self.c.attn_blocks = int(n)
+
     def region(self, name: str) -> torch.Tensor:
         """uint8 view of a region of the cache buffer (e.g. "k_codes")."""
         L = self.layout

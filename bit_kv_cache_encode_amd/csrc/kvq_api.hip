@@ -235,6 +235,11 @@ int kvq_cache_init(kvq_cache* cache, const kvq_config* cfg, void* base, uint64_t
   cache->cfg = *cfg;
   cache->base = base;
   cache->rho = cfg->v_alpha > 0.0f ? rho_star(D, cfg->v_alpha) : -1.0f;
+  // attention kernel and grid: read from the environment here, once per cache
+  const char* kenv = getenv("KVQ_ATTN_KERNEL");
+  cache->attn_kernel = (kenv && strcmp(kenv, "valu") == 0) ? KVQ_ATTN_VALU : KVQ_ATTN_AUTO;
+  const char* benv = getenv("KVQ_ATTN_BLOCKS");
+  cache->attn_blocks = benv && atoi(benv) > 0 ? atoi(benv) : 0;
   hipStream_t s = (hipStream_t)stream;
   Regions r = regions_of(cache, L);
   hipError_t ec = launch_fill((float*)r.cnt, 0.0f, (int64_t)(L.cnt_bytes / 4), s);
@@ -407,12 +412,12 @@ int kvq_encode_append(kvq_cache* cache, const void* k_new, const void* v_new, in
 
 // Attention arguments over the cache's first T tokens and the kernel choice.
 // `reserve` partial slots per (b, q-head) are kept free for a fused step.
-// Kernel choice: the MFMA kernels cover groups of 32 / 64 channels with up
-// to 16/(128/group) q-heads per kv-head.  The single-role MFMA kernel is the
-// default; KVQ_ATTN_KERNEL=pp selects the paired score/value-wave kernel and
-// KVQ_ATTN_KERNEL=valu the VALU kernel (used to cross-check them).
-// KVQ_ATTN_BLOCKS sets the target grid size.
-enum AttnKernel { ATTN_MFMA, ATTN_PP, ATTN_VALU };
+// Kernel choice: the MFMA kernel covers groups of 32 / 64 channels with up
+// to 16 q-heads per kv-head and is the default wherever it applies; the
+// cache's attn_kernel field may select the VALU kernel (a cross-check) and
+// attn_blocks the target grid size (both fixed at kvq_cache_init from the
+// environment unless the caller changes them).
+enum AttnKernel { ATTN_MFMA, ATTN_VALU };
 static AttnKernel attn_setup(const kvq_cache* cache, const kvq_layout& L, const void* q, float* out,
                              float sm_scale, int T, int reserve, AttnArgs& a) {
   const kvq_config& c = cache->cfg;
@@ -437,19 +442,14 @@ static AttnKernel attn_setup(const kvq_cache* cache, const kvq_layout& L, const 
   const float sm = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)D);
   a.qscale = sm * 1.4426950408889634f;
   const int units = c.batch * c.n_kv_heads;
-  const char* kenv = getenv("KVQ_ATTN_KERNEL");
   const bool mfma_ok = mfma_attention_supported(c.bits, c.group, a.gq);
-  // the paired kernel serves one q-head block per unit (K per token, no NSN)
-  const bool pp_ok = mfma_ok && a.gq <= 16 / (D / c.group) && !c.k_per_channel &&
-                     c.mode != KVQ_MODE_NSN;
   // (the VALU kernel holds at most MAX_GQ q-heads per kv-head)
   const bool valu_ok = a.gq <= MAX_GQ;
-  const AttnKernel k = (!mfma_ok || (valu_ok && kenv && strcmp(kenv, "valu") == 0)) ? ATTN_VALU
-                       : (pp_ok && kenv && strcmp(kenv, "pp") == 0) ? ATTN_PP : ATTN_MFMA;
+  const AttnKernel k = (!mfma_ok || (valu_ok && cache->attn_kernel == KVQ_ATTN_VALU)) ? ATTN_VALU
+                                                                                     : ATTN_MFMA;
   // one 8-wave MFMA block per compute unit
-  int target = k == ATTN_VALU ? ATTN_TARGET_BLOCKS : (k == ATTN_PP ? 768 : 256);
-  const char* benv = getenv("KVQ_ATTN_BLOCKS");
-  if (benv && atoi(benv) > 0) target = atoi(benv);
+  int target = k == ATTN_VALU ? ATTN_TARGET_BLOCKS : 256;
+  if (cache->attn_blocks > 0) target = cache->attn_blocks;
   int want = (target + units - 1) / units;
   if (want > L.max_splits - reserve) want = L.max_splits - reserve;
   if (want < 1) want = 1;
@@ -469,7 +469,6 @@ static AttnKernel attn_setup(const kvq_cache* cache, const kvq_layout& L, const 
 
 static int attn_launch(AttnKernel k, const AttnArgs& a, void* stream) {
   hipError_t e = k == ATTN_MFMA ? launch_attention_mfma(a, (hipStream_t)stream)
-               : k == ATTN_PP   ? launch_attention_pp(a, (hipStream_t)stream)
                                 : launch_attention(a, (hipStream_t)stream);
   return e == hipSuccess ? KVQ_OK : dev_fail(e);
 }

@@ -177,7 +177,6 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_combine(const AttnArgs& a, hipStream_t s);
 bool mfma_attention_supported(int bits, int group, int gq);
 hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t s);
-hipError_t launch_attention_pp(const AttnArgs& a, hipStream_t s);
 // k-means per (unit, kind) over `groups` * n_tok rows: row i of unit u is
 // input row (i / n_tok) * group_stride + u * n_tok + i % n_tok.
 hipError_t launch_kmeans_pair(const void* xk, const void* xv, int bf16, int n_tok, int groups,

@@ -144,7 +144,18 @@ typedef struct {
   int32_t win_count;      /* decode appends in the open Chebyshev window */
   int32_t dropped;        /* window centres dropped because the table was full */
   float rho;              /* binary32 rho*(head_dim, v_alpha) of Eq 10 */
+  int32_t attn_kernel;    /* attention kernel: KVQ_ATTN_AUTO (the matrix-core kernel
+                             wherever it applies) or KVQ_ATTN_VALU (the vector
+                             kernel, a cross-check, for at most 8 q-heads per
+                             kv-head); kvq_cache_init sets it from the environment
+                             variable KVQ_ATTN_KERNEL ("valu"), callers may change it */
+  int32_t attn_blocks;    /* target grid size of the attention (0 = the default: one
+                             8-wave block per compute unit, 256); kvq_cache_init sets
+                             it from KVQ_ATTN_BLOCKS, callers may change it */
 } kvq_cache;
+
+#define KVQ_ATTN_AUTO 0
+#define KVQ_ATTN_VALU 1
 
 /* Layout of a cache for `cfg`.  Host only; touches no device.
  * KVQ_EINVAL if the configuration is not supported. */

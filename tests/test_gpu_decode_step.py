@@ -43,15 +43,15 @@ def _used_bytes(cache):
 
 
 def _run(B, Hq, H, T0, steps, *, bits=2, group=32, mode="pattern", P=16, W=8, bf16=True,
-         blocks=None, monkeypatch=None, seed_off=0):
+         blocks=None, seed_off=0):
     dt = torch.bfloat16 if bf16 else torch.float32
-    if blocks is not None:
-        monkeypatch.setenv("KVQ_ATTN_BLOCKS", str(blocks))
     gq = Hq // H
     k = synth.k_vectors(B, H, T0 + steps, D, seed=synth.seed_for("k") + seed_off)
     v = synth.v_vectors(B, H, T0 + steps, D, seed=synth.seed_for("v") + seed_off)
     fused = KVCache(B, Hq, H, T0 + steps, bits=bits, group=group, mode=mode, max_patterns=P,
                     pattern_window=W, v_alpha=0.05, in_dtype=dt)
+    if blocks is not None:
+        fused.attn_blocks = blocks
     ref = O.RefCache(B, Hq, H, D, T0 + steps, bits=bits, group=group,
                      mode=O.PATTERN if mode == "pattern" else O.KVARN, max_patterns=P,
                      pattern_window=W, v_alpha=0.05, in_dtype=O.IN_BF16 if bf16 else O.IN_F32)
@@ -101,10 +101,10 @@ def test_decode_step_llama_gqa4(T0):
 
 
 @pytest.mark.parametrize("blocks", [1, 40, 4096])
-def test_decode_step_split_counts(monkeypatch, blocks):
+def test_decode_step_split_counts(blocks):
     """One split per unit up to many; 16 patterns grow to 19 (the one-hot
     path changes width mid-stream)."""
-    _run(2, 8, 2, 700, 12, P=20, W=4, blocks=blocks, monkeypatch=monkeypatch, seed_off=3)
+    _run(2, 8, 2, 700, 12, P=20, W=4, blocks=blocks, seed_off=3)
 
 
 def test_decode_step_4bit_gqa8_binary32():

@@ -256,3 +256,91 @@ def test_nsn_breadth_fullsize():
         print(f"nsn full size unit ({b},{h})", flush=True)
         assert_same_encode(ref, gpu, T, units=[b * H + h], ref_units=[0])
         _check_unit_attn(out, ref, q, b, h, gq)
+
+
+def _used_regions(cache):
+    """Device views of a cache's used contents (token-indexed regions cut at
+    n_tokens, tables at n_patterns, the window state whole)."""
+    c, L = cache.cfg, cache.layout
+    U, T, tc = c.batch * c.n_kv_heads, cache.n_tokens, L.token_cap
+    rec = D * c.bits // 8
+    out = {}
+    for w in "kv":
+        if w == "k":
+            out["k_codes"] = cache.region("k_codes").view(U, tc * rec)[:, :T * rec]
+        else:
+            out["v_codes"] = cache.region("v_codes").view(U, tc // 32, -1)[:, :(T + 31) // 32]
+        out[w + "_sz"] = cache.region(w + "_sz").view(U, tc, -1)[:, :T]
+        out[w + "_idx"] = cache.region(w + "_idx").view(U, tc)[:, :T]
+        out[w + "_tab"] = cache.region(w + "_tab").view(cache.pattern_units, c.max_patterns, -1)[
+            :, :cache.n_patterns]
+        out[w + "_win"] = cache.region(w + "_win")
+    return out
+
+
+@pytest.mark.parametrize("shape", ["llama8b_ctx32k_2bit", "long_ctx128k_4bit"])
+def test_decode_step_fullsize(shape):
+    """The kernel the benchmark times: the one-launch decode step
+    (kvq_decode_step, default grid) at full size, 130 steps with the
+    Chebyshev window at 128 (PatternKV section 3.1, Eq 5), so the 128th step
+    closes a window and the table grows by one pattern (Llama shape: 32 -> 33,
+    which moves the pattern-mass product to a wider instantiation; long
+    context: 64 -> 65, past the one-hot path).  Every step also runs through a
+    copy of the cache driven by the two separate calls; the two caches' used
+    contents must stay byte-identical and their outputs within 2e-3.  The
+    oracle reproduces sampled units at steps 0, 126, 127 (the closing step),
+    128 and 129."""
+    dev = torch.device("cuda", 0)
+    if shape == "llama8b_ctx32k_2bit":
+        B, Hq, H, T0, bits, group, P = 8, 32, 8, 32768, 2, 32, 32
+        samples = [(0, 0), (3, 5), (7, 7)]
+    else:
+        B, Hq, H, T0, bits, group, P = 1, 32, 8, 131072, 4, 64, 64
+        samples = [(0, 1), (0, 6)]
+    W, steps, gq = 128, 130, Hq // H
+    check = {0, 126, 127, 128, 129}
+    maxp = P + 2
+    k, v = synth.device_kv(B, H, T0 + steps, D, device=dev, dtype=torch.bfloat16)
+    gpu = KVCache(B, Hq, H, T0 + steps, bits=bits, group=group, mode="pattern",
+                  max_patterns=maxp, pattern_window=W, v_alpha=0.05, in_dtype=torch.bfloat16)
+    nk = 2048
+    gpu.init_patterns(k[:, :, :nk].contiguous(), v[:, :, :nk].contiguous(), P)
+    gpu.encode_append(k[:, :, :T0].contiguous(), v[:, :, :T0].contiguous())
+    split = gpu.clone()
+    outs = {}
+    for s in range(steps):
+        t = T0 + s
+        kn, vn = k[:, :, t:t + 1].contiguous(), v[:, :, t:t + 1].contiguous()
+        q = synth.device_queries(B, Hq, D, step=s + 1, device=dev, dtype=torch.bfloat16)
+        out_f = gpu.decode_step(kn, vn, q)
+        split.encode_append(kn, vn, update_patterns=True)
+        out_s = split.attn_decode(q)
+        d = float((out_f - out_s).abs().max())
+        assert d <= ATTN_TOL, f"step {s}: one-launch vs two calls differ by {d}"
+        if s in check:
+            outs[s] = (q, out_f.clone())
+    torch.cuda.synchronize()
+    print(f"{shape}: {steps} steps, patterns {gpu.n_patterns}", flush=True)
+    assert gpu.n_patterns == split.n_patterns == P + 1
+    a, b_ = _used_regions(gpu), _used_regions(split)
+    for name in a:
+        assert torch.equal(a[name], b_[name]), f"{name} differs between the one-launch step and the two calls"
+    errs = []
+    for (b, h) in samples:
+        u = b * H + h
+        ref = _unit_ref(gq, T0 + steps, bits=bits, group=group, mode=O.PATTERN,
+                        max_patterns=maxp, pattern_window=W, v_alpha=0.05)
+        ku, vu = _unit_in(k, b, h), _unit_in(v, b, h)
+        assert ref.init_patterns(ku[:, :, :nk], vu[:, :, :nk], P) == 0
+        assert ref.encode_append(ku[:, :, :T0], vu[:, :, :T0]) == 0
+        for s in range(steps):
+            assert ref.encode_append(ku[:, :, T0 + s:T0 + s + 1], vu[:, :, T0 + s:T0 + s + 1],
+                                     update=1) == 0
+            if s in check:
+                errs.append(_check_unit_attn(outs[s][1], ref, outs[s][0], b, h, gq))
+        assert ref.n_patterns == P + 1
+        for which in (0, 1):
+            assert np.array_equal(gpu_tab(gpu, which)[u, :P + 1], ref.patterns(which)[0, :P + 1]), \
+                f"unit {u}: {'KV'[which]} table differs after the window closure"
+        assert_same_encode(ref, gpu, T0 + steps, units=[u], ref_units=[0])
+    print(f"{shape}: max attention err {max(errs):.2e} over {len(errs)} checks", flush=True)

@@ -107,7 +107,7 @@ def test_kch_decode_appends_with_window(fused_call):
 @pytest.mark.parametrize("bits,group,gq,npat", [(2, 32, 4, 32), (2, 64, 4, 16), (2, 64, 8, 24),
                                                 (4, 32, 7, 64), (4, 64, 3, 8), (2, 32, 16, 0)])
 @pytest.mark.parametrize("blocks", [1, 256])
-def test_kch_attention_kernels_agree(monkeypatch, bits, group, gq, npat, blocks):
+def test_kch_attention_kernels_agree(bits, group, gq, npat, blocks):
     """The matrix-core kernel (q * s operand per tile of a complete block,
     VALU scores for the open block) and the VALU kernel match the oracle:
     several blocks plus an open one, one or many splits, virtual groups at
@@ -121,16 +121,13 @@ def test_kch_attention_kernels_agree(monkeypatch, bits, group, gq, npat, blocks)
         gpu.init_patterns(to_dev(k[:, :, :128], dt), to_dev(v[:, :, :128], dt), npat)
     assert ref.encode_append(to_oracle(k, True), to_oracle(v, True)) == 0
     gpu.encode_append(to_dev(k, dt), to_dev(v, dt))
-    monkeypatch.setenv("KVQ_ATTN_BLOCKS", str(blocks))
+    gpu.attn_blocks = blocks
     for step, qmul in ((0, 1.0), (1, 6.0)):
         q = synth.queries(B, gq * H, D, step=step) * np.float32(qmul)
         want = ref.attn_decode(to_oracle(q, True))
         errs = {}
         for kern in ("", "valu") if gq <= 8 else ("",):
-            if kern:
-                monkeypatch.setenv("KVQ_ATTN_KERNEL", kern)
-            else:
-                monkeypatch.delenv("KVQ_ATTN_KERNEL", raising=False)
+            gpu.attn_kernel = kern or "auto"
             print(f"k per channel kernels bits={bits} group={group} gq={gq} kern={kern or 'mfma'}",
                   flush=True)
             got = gpu.attn_decode(to_dev(q, dt)).cpu().numpy()

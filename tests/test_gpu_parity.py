@@ -231,9 +231,9 @@ def test_determinism_and_checkpoint():
     (2, 32, 6, "kvarn")])
 @pytest.mark.parametrize("blocks", [1, 40, 4096])
 @pytest.mark.parametrize("bf16", [True, False])
-def test_attention_kernels_agree(monkeypatch, bits, group, gq, mode, blocks, bf16):
-    """The single-role MFMA kernel (default), the paired score/value-wave MFMA
-    kernel and the VALU kernel all match the oracle, for one block per unit up
+def test_attention_kernels_agree(bits, group, gq, mode, blocks, bf16):
+    """The MFMA kernel (default) and the VALU kernel both match the oracle,
+    for one block per unit up
     to many splits, ragged lengths, bfloat16 and binary32 inputs (a binary32
     query takes the binary16 hi + lo operand path)."""
     B, H, T = 2, 2, 1000
@@ -249,16 +249,13 @@ def test_attention_kernels_agree(monkeypatch, bits, group, gq, mode, blocks, bf1
                          torch.from_numpy(ref.scales(1).reshape(B, H, 128).copy()).cuda())
     ref.encode_append(to_oracle(k, bf16), to_oracle(v, bf16))
     gpu.encode_append(to_dev(k, dt), to_dev(v, dt))
-    monkeypatch.setenv("KVQ_ATTN_BLOCKS", str(blocks))
+    gpu.attn_blocks = blocks
     for step, qmul in ((0, 1.0), (1, 6.0)):          # flat and peaked softmax
         q = synth.queries(B, gq * H, 128, step=step) * np.float32(qmul)
         want = ref.attn_decode(to_oracle(q, bf16))
         errs = {}
-        for kern in ("", "pp", "valu") if gq <= 8 else ("", "pp"):
-            if kern:
-                monkeypatch.setenv("KVQ_ATTN_KERNEL", kern)
-            else:
-                monkeypatch.delenv("KVQ_ATTN_KERNEL", raising=False)
+        for kern in ("", "valu") if gq <= 8 else ("",):
+            gpu.attn_kernel = kern or "auto"
             got = gpu.attn_decode(to_dev(q, dt)).cpu().numpy()
             errs[kern or "default"] = float(np.abs(got - want).max())
         assert max(errs.values()) <= ATTN_TOL, errs
@@ -285,7 +282,7 @@ def test_attention_query_dynamic_range(bf16):
     assert np.abs(got - want).max() <= ATTN_TOL
 
 
-def test_attention_repeated_calls_reset_counters(monkeypatch):
+def test_attention_repeated_calls_reset_counters():
     """The fused combine's arrival counters return to zero after each call, so
     repeated calls (and calls after appends) keep matching the oracle."""
     B, Hq, H = 2, 8, 2
@@ -293,7 +290,7 @@ def test_attention_repeated_calls_reset_counters(monkeypatch):
     k, v = _inputs(B, H, 3000)
     ref.init_patterns(to_oracle(k[:, :, :512], True), to_oracle(v[:, :, :512], True), 16)
     gpu.init_patterns(to_dev(k[:, :, :512], dt), to_dev(v[:, :, :512], dt), 16)
-    monkeypatch.setenv("KVQ_ATTN_BLOCKS", "64")
+    gpu.attn_blocks = 64
     pos = 0
     for n in (1000, 1, 999, 1000):
         ref.encode_append(to_oracle(k[:, :, pos:pos + n], True), to_oracle(v[:, :, pos:pos + n], True))
