@@ -12,7 +12,8 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvq.so")
 
-KVQ_OK, KVQ_EINVAL, KVQ_ECAPACITY, KVQ_ESTATE, KVQ_EDEVICE = 0, -1, -2, -3, -4
+KVQ_OK, KVQ_EINVAL, KVQ_ECAPACITY, KVQ_ESTATE, KVQ_EDEVICE, KVQ_ESCRATCH = 0, -1, -2, -3, -4, -5
+NOALLOC_SCRATCH_BYTES, NOALLOC_COUNTER_BYTES = 8 << 20, 64 << 10
 ATTN_AUTO, ATTN_VALU = 0, 1
 MODE_PATTERN, MODE_KVARN, MODE_NSN = 0, 1, 2
 F32, BF16 = 0, 1
@@ -20,7 +21,8 @@ INDEX_NONE = 0xFF
 VTILE = 32
 
 EXPORTS = ("kvq_layout_of", "kvq_cache_init", "kvq_init_patterns", "kvq_set_patterns",
-           "kvq_encode_append", "kvq_attn_decode", "kvq_decode_step", "kvq_dequant", "kvq_strerror",
+           "kvq_encode_append", "kvq_attn_decode", "kvq_attn_decode_noalloc", "kvq_decode_step",
+           "kvq_dequant", "kvq_strerror",
            "kvq_last_device_error")
 
 
@@ -79,6 +81,7 @@ def lib():
             "kvq_set_patterns": (I, [C.POINTER(kvq_cache), P, P, I, P]),
             "kvq_encode_append": (I, [C.POINTER(kvq_cache), P, P, I, I, P]),
             "kvq_attn_decode": (I, [C.POINTER(kvq_cache), P, P, C.c_float, P]),
+            "kvq_attn_decode_noalloc": (I, [C.POINTER(kvq_cache), P, P, C.c_float, P]),
             "kvq_decode_step": (I, [C.POINTER(kvq_cache), P, P, P, P, C.c_float, C.c_int32, P]),
             "kvq_dequant": (I, [C.POINTER(kvq_cache), I, I, I, P, P]),
             "kvq_strerror": (C.c_char_p, [I]),
@@ -121,6 +124,10 @@ def kvq_encode_append(cache, k_ptr, v_ptr, n_new, update_patterns, stream) -> in
 
 def kvq_attn_decode(cache, q_ptr, out_ptr, sm_scale, stream) -> int:
     return lib().kvq_attn_decode(C.byref(cache), q_ptr, out_ptr, sm_scale, stream)
+
+
+def kvq_attn_decode_noalloc(cache, q_ptr, out_ptr, sm_scale, stream) -> int:
+    return lib().kvq_attn_decode_noalloc(C.byref(cache), q_ptr, out_ptr, sm_scale, stream)
 
 
 def kvq_decode_step(cache, k_ptr, v_ptr, q_ptr, out_ptr, sm_scale, update_patterns, stream) -> int:

@@ -5,6 +5,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kvq_internal.h"
 
 using namespace kvq;
@@ -483,6 +485,66 @@ int kvq_attn_decode(kvq_cache* cache, const void* q, float* out, float sm_scale,
   return attn_launch(k, a, stream);
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------- no-allocation attention
+// Split-K workspace of kvq_attn_decode_noalloc: arrival counters in the first
+// KVQ_NOALLOC_COUNTER_BYTES, partials after them.  One copy per GPU, held
+// until the process ends; every such call on a GPU shares it.  Host code
+// never passes the array's name to a kernel: its device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[KVQ_NOALLOC_COUNTER_BYTES + KVQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[SCRATCH_MAX_DEVICES];
+
+// The current device's scratch address; its first use on a device clears the
+// counters (a fill kernel on `s`, so the call stays capturable).
+int scratch_of_current_device(void** out, hipStream_t s) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return dev_fail(e);
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return KVQ_EINVAL;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return dev_fail(e != hipSuccess ? e : hipErrorInvalidSymbol);
+    e = launch_fill((float*)p, 0.0f, (int64_t)(KVQ_NOALLOC_COUNTER_BYTES / 4), s);
+    if (e != hipSuccess) return dev_fail(e);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVQ_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int kvq_attn_decode_noalloc(kvq_cache* cache, const void* q, float* out, float sm_scale,
+                            void* stream) {
+  kvq_layout L;
+  if (!cache || !cache->base || kvq_layout_of(&cache->cfg, &L) != KVQ_OK) return KVQ_EINVAL;
+  if (!q || !out || !aligned16(q) || !aligned16(out)) return KVQ_EINVAL;
+  if (cache->n_tokens <= 0) return KVQ_ESTATE;
+  AttnArgs a;
+  const AttnKernel k = attn_setup(cache, L, q, out, sm_scale, cache->n_tokens, 0, a);
+  const kvq_config& c = cache->cfg;
+  // partials o[D] and (m, l) per (b, q-head, split); at most one arrival
+  // counter per (b, q-head)
+  const uint64_t ws_need = (uint64_t)c.batch * c.n_q_heads * a.splits * (D + 2) * 4;
+  const uint64_t cnt_need = (uint64_t)c.batch * c.n_q_heads * 4;
+  if (ws_need > KVQ_NOALLOC_SCRATCH_BYTES || cnt_need > KVQ_NOALLOC_COUNTER_BYTES) return KVQ_ESCRATCH;
+  void* p = nullptr;
+  const int st = scratch_of_current_device(&p, (hipStream_t)stream);
+  if (st != KVQ_OK) return st;
+  a.r.cnt = (uint32_t*)p;
+  a.r.ws = (float*)((unsigned char*)p + KVQ_NOALLOC_COUNTER_BYTES);
+  return attn_launch(k, a, stream);
+}
+
 int kvq_decode_step(kvq_cache* cache, const void* k_new, const void* v_new, const void* q,
                     float* out, float sm_scale, int32_t update_patterns, void* stream) {
   kvq_layout L;
@@ -586,6 +648,9 @@ const char* kvq_strerror(int status) {
     case KVQ_ECAPACITY: return "append exceeds the cache's max_tokens";
     case KVQ_ESTATE: return "operation not valid in the cache's current state";
     case KVQ_EDEVICE: return "HIP launch or runtime call failed";
+    case KVQ_ESCRATCH:
+      return "split-K workspace exceeds the static scratch of kvq_attn_decode_noalloc "
+             "(KVQ_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

@@ -79,6 +79,7 @@ extern "C" {
 #define KVQ_ECAPACITY (-2)  /* append would exceed max_tokens */
 #define KVQ_ESTATE (-3)     /* call not valid in the cache's state */
 #define KVQ_EDEVICE (-4)    /* a HIP launch or runtime call failed */
+#define KVQ_ESCRATCH (-5)   /* kvq_attn_decode_noalloc: workspace beyond its static scratch */
 
 #define KVQ_MODE_PATTERN 0  /* PatternKV residual encode */
 #define KVQ_MODE_KVARN 1    /* Hadamard + dual-axis normalisation encode */
@@ -225,6 +226,27 @@ int kvq_encode_append(kvq_cache* cache, const void* k_new, const void* v_new, in
  * (sm_scale <= 0 means 1/sqrt(D)).  Split-K over tokens with a combine pass.
  * KVQ_ESTATE if the cache is empty; KVQ_EINVAL on null pointers. */
 int kvq_attn_decode(kvq_cache* cache, const void* q, float* out, float sm_scale, void* stream);
+
+/* kvq_attn_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same kernels and results, with the split-K partials and arrival
+ * counters in a static device array of the library instead of the cache
+ * buffer's workspace region (which it leaves untouched).  The array holds
+ * KVQ_NOALLOC_SCRATCH_BYTES of partials (B * Hq * splits * (D + 2) * 4
+ * bytes; splits is about 256 / (B * Hkv) with the default grid, and
+ * attn_blocks raises it) and KVQ_NOALLOC_COUNTER_BYTES of counters
+ * (B * Hq * 4 bytes).  Each GPU has its own copy, kept until the process
+ * ends; the first call on a device (which must be the calling thread's
+ * current device) looks up its address and clears its counters on `stream`.
+ * Every call on a GPU shares that GPU's copy: calls that overlap on one GPU
+ * (different streams, or different threads without ordering) race.  No call
+ * to hipMalloc, hipFree or any allocating routine.
+ * Errors as kvq_attn_decode, plus KVQ_ESCRATCH (nothing launched) when the
+ * call's workspace exceeds the scratch. */
+#define KVQ_NOALLOC_SCRATCH_BYTES (8u << 20)
+#define KVQ_NOALLOC_COUNTER_BYTES (64u << 10)
+int kvq_attn_decode_noalloc(kvq_cache* cache, const void* q, float* out, float sm_scale,
+                            void* stream);
 
 /* One decode step in one launch: append one token per unit (k_new, v_new:
  * [B][Hkv][1][D], encoded exactly as kvq_encode_append with n_new = 1) and

@@ -157,8 +157,26 @@ def test_error_paths_fail_before_launch():
     bad = _cfg(bits=3)
     assert lib.kvq_cache_init(C.byref(cache), C.byref(bad), C.c_void_p(1 << 20), 1 << 30,
                               None) == B.KVQ_EINVAL
-    for s in (0, -1, -2, -3, -4, -99):
+    for s in (0, -1, -2, -3, -4, -5, -99):
         assert B.kvq_strerror(s)
+
+
+def test_noalloc_error_paths_fail_before_launch():
+    """kvq_attn_decode_noalloc checks its arguments and its workspace need
+    against the static scratch before touching the device."""
+    lib = B.lib()
+    p = C.c_void_p(1 << 24)
+    empty = _fake_cache(n_tokens=0)
+    assert lib.kvq_attn_decode_noalloc(C.byref(empty), p, p, 0.0, None) == B.KVQ_ESTATE
+    c = _fake_cache(n_tokens=100)
+    assert lib.kvq_attn_decode_noalloc(C.byref(c), None, p, 0.0, None) == B.KVQ_EINVAL
+    assert lib.kvq_attn_decode_noalloc(C.byref(c), p, C.c_void_p((1 << 24) + 4), 0.0,
+                                       None) == B.KVQ_EINVAL
+    # 520 x 32 (batch, q-head) rows: 66560 bytes of counters and 8.65 MB of
+    # partials at one split, beyond the 64 KiB + 8 MiB scratch
+    wide = _fake_cache(n_tokens=100, batch=520)
+    assert lib.kvq_attn_decode_noalloc(C.byref(wide), p, p, 0.0, None) == B.KVQ_ESCRATCH
+    assert "scratch" in B.kvq_strerror(B.KVQ_ESCRATCH)
 
 
 def test_product_path_has_no_cpu_fallback(monkeypatch, tmp_path):
