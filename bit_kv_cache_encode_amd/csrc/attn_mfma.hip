@@ -40,9 +40,11 @@ constexpr int MF_THREADS = MF_WAVES * 64;
 
 // Dynamic LDS layout of a block (bytes); npat = padded pattern count.
 struct MfLds {
-  int q, qsum, qe, next, qm, qa, mv, mv_rows, ps, ph, vs, w, alpha, m, o, z, l, wsum, M, last, tiles,
+  int q, qsum, qe, next, qm, qa, mv, mv_rows, ps, ph, vs, vz, w, alpha, m, o, z, l, wsum, M, last, tiles,
       nsn, total;
 };
+// binary16 per row of the p hi / lo tables of the pattern-mass product
+constexpr int PH_STRIDE = 72;
 // mv_rows: rows of M^V staged for the pattern term (0 without the one-hot path)
 // kch: K per channel, which keeps the per-lane q operands of the QK product
 // (64 lanes x 32 fp32, quad-major) for the per-tile q * s operand
@@ -61,8 +63,10 @@ __host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes
   L.qa = o; o = al16(o + (kch ? 64 * 32 * 4 : 0));
   const int pw = HB == 4 ? ptab_words<4>() : ptab_words<8>();
   L.ps = o; o = al16(o + MF_WAVES * pw * 4);
-  L.ph = o; o = al16(o + (hist_mfma ? MF_WAVES * pw * 4 : 0));
+  // one shared zero row, then per wave HB rows of p hi and HB rows of p lo
+  L.ph = o; o = al16(o + (hist_mfma ? (1 + MF_WAVES * 2 * HB) * PH_STRIDE * 2 : 0));
   L.vs = o; o = al16(o + MF_WAVES * NG * VS_STRIDE * 2);
+  L.vz = o; o = al16(o + (hist_mfma ? MF_WAVES * NG * VS_STRIDE * 2 : 0));
   L.w = o; o = al16(o + MF_WAVES * HB * npat * 4);
   L.alpha = o; o = al16(o + MF_WAVES * HB * 4);
   L.m = o; o = al16(o + MF_WAVES * HB * 4);
@@ -110,6 +114,10 @@ attn_mfma_kernel(AttnArgs a) {
   constexpr int CPG = 16 / NG;         // PV columns per group
   constexpr int SPL = 4 / NG;          // heads per lane in a 16x16 output
   constexpr int KW = BITS;             // dwords of a lane's 32-channel K slice
+  // p * s as binary16 hi + lo (two PV products) in the rotated modes, whose
+  // V sums cancel against the zero-point sums; one binary16 operand (an
+  // fp16 P.V product with fp32 accumulation) otherwise
+  constexpr bool PLO = KVARN;
   constexpr int VTB = VT * D * BITS / 8;
   extern __shared__ __attribute__((aligned(16))) unsigned char mf_raw[];
 
@@ -144,8 +152,11 @@ attn_mfma_kernel(AttnArgs a) {
   float* s_s1 = s_qmu + HB;                        // NSN: [HB] block sum p n1
   float* s_muv = s_s1 + HB;                        // NSN: [D] Hadamard(mu_V) / sqrt(D)
   float* s_ps = (float*)(mf_raw + Lo.ps) + wave * ptab_words<HB>();
-  uint32_t* s_ph = (uint32_t*)(mf_raw + Lo.ph) + wave * ptab_words<HB>();
-  _Float16* s_vs = (_Float16*)(mf_raw + Lo.vs) + wave * NG * VS_STRIDE;
+  // pattern-mass operand rows: p 2^15 as binary16 hi [HB][PH_STRIDE], then lo
+  _Float16* s_phh = (_Float16*)(mf_raw + Lo.ph) + (1 + wave * 2 * HB) * PH_STRIDE;
+  _Float16* s_phl = s_phh + HB * PH_STRIDE;
+  _Float16* s_vs = (_Float16*)(mf_raw + Lo.vs) + wave * NG * VS_STRIDE;   // V scales [g][token]
+  _Float16* s_vz = (_Float16*)(mf_raw + Lo.vz) + wave * NG * VS_STRIDE;   // V zero points [g][token]
   float* s_w = (float*)(mf_raw + Lo.w);            // [WAVES][HB][npat]
   float* s_alpha = (float*)(mf_raw + Lo.alpha);    // [WAVES][HB]
   float* s_m = (float*)(mf_raw + Lo.m);            // [WAVES][HB]
@@ -259,6 +270,7 @@ attn_mfma_kernel(AttnArgs a) {
   for (int i = tid; i < HB * npat; i += MF_THREADS) s_wsum[i] = 0.0f;
   for (int i = tid; i < HB * 256; i += MF_THREADS) s_qm[i] = 0.0f;
   if (tid < HB * NG) s_z[tid] = 0.0f;
+  if (NPB > 0 && tid < PH_STRIDE) ((_Float16*)(mf_raw + Lo.ph))[tid] = (_Float16)0.0f;
   if (tid < HB) { s_l[tid] = 0.0f; s_qe[tid] = 0; }
   if (tid == 0) *s_next = fuse_here ? MF_WAVES - 2 : MF_WAVES;
   __syncthreads();
@@ -455,10 +467,11 @@ attn_mfma_kernel(AttnArgs a) {
   // of the same p operand and a B of binary16 zero points: rows as hacc,
   // column g = group (columns >= NG repeat a group and are not read)
   f32x4 zm = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  // hist A: this lane's row (head n16 / NG, part n16 % NG) takes the low
-  // (part 0) or high (part 1) binary16 of each packed word; other rows are 0
-  const uint32_t hsel = (n16 / NG >= gq || n16 % NG > 1) ? 0x0C0C0C0Cu
-                        : (n16 % NG == 0 ? 0x05040100u : 0x07060302u);
+  // hist A: this lane's row (head n16 / NG, part n16 % NG) reads the hi
+  // (part 0) or lo (part 1) table of its head; other rows read the zero row
+  const _Float16* ph_row = (n16 / NG >= gq || n16 % NG > 1)
+                               ? (const _Float16*)(mf_raw + Lo.ph)
+                               : (n16 % NG == 0 ? s_phh : s_phl) + (n16 / NG) * PH_STRIDE;
 
   // Tiles are handed out dynamically: each wave starts with tile `wave` and
   // claims its next one from the block counter while the current one is
@@ -803,7 +816,8 @@ attn_mfma_kernel(AttnArgs a) {
           const float x = p * 32768.0f;
           const _Float16 hi = (_Float16)x;
           const _Float16 lo = (_Float16)__builtin_fmaf((float)hi, k_m1, x);
-          s_ph[prow<HB>(head0 + s) + t64] = (uint32_t)h2bits(hi) | ((uint32_t)h2bits(lo) << 16);
+          s_phh[(head0 + s) * PH_STRIDE + t64] = hi;
+          s_phl[(head0 + s) * PH_STRIDE + t64] = lo;
         }
       }
       vk[nb] = vix;
@@ -811,6 +825,8 @@ attn_mfma_kernel(AttnArgs a) {
       if (j < NG) {
         const uint32_t sw = ((const uint32_t*)(tb + TS::O_VS))[t64 * NGS + j / VPS];
         s_vs[j * VS_STRIDE + t64] = __builtin_bit_cast(_Float16, (uint16_t)(valid ? sw & 0xFFFFu : 0u));
+        if constexpr (NPB > 0)
+          s_vz[j * VS_STRIDE + t64] = __builtin_bit_cast(_Float16, (uint16_t)(valid ? sw >> 16 : 0u));
       }
     }
     // V pattern mass: the tile's LDS adds are issued back to back so their
@@ -830,7 +846,7 @@ attn_mfma_kernel(AttnArgs a) {
     // ---- PV over the two 32-token V tiles
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      u32x4 ahi, alo;
+      u32x4 ahi, alo = {};
       {
         // rows of heads >= gq hold finite values that are never stored
         const int h = n16 / NG, g = n16 % NG;
@@ -847,21 +863,19 @@ attn_mfma_kernel(AttnArgs a) {
         for (int p = 0; p < 4; ++p) {
           const float x0 = mul_h(pa[p], (uint16_t)(va[p >> 1] >> (16 * (p & 1))), k_z);
           const float x1 = mul_h(pb[p], (uint16_t)(vb[p >> 1] >> (16 * (p & 1))), k_z);
-          uint32_t hi, lo;
-          split2(x0, x1, k_m1, hi, lo);
-          ahi[p] = hi;
-          alo[p] = lo;
+          if constexpr (PLO) {
+            uint32_t hi, lo;
+            split2(x0, x1, k_m1, hi, lo);
+            ahi[p] = hi;
+            alo[p] = lo;
+          } else {
+            ahi[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, f16x2));
+          }
         }
       }
       if constexpr (NPB > 0) {
         // element i = 2p + e of lane group j <-> token 32 kb + 8 j + i
-        const u32x4 h0 = *(const u32x4*)(s_ph + prow<HB>(n16 / NG) + 32 * kb + 8 * j);
-        const u32x4 h1 = *(const u32x4*)(s_ph + prow<HB>(n16 / NG) + 32 * kb + 8 * j + 4);
-        u32x4 ah;
-        ah[0] = __builtin_amdgcn_perm(h0[1], h0[0], hsel);
-        ah[1] = __builtin_amdgcn_perm(h0[3], h0[2], hsel);
-        ah[2] = __builtin_amdgcn_perm(h1[1], h1[0], hsel);
-        ah[3] = __builtin_amdgcn_perm(h1[3], h1[2], hsel);
+        const u32x4 ah = *(const u32x4*)(ph_row + 32 * kb + 8 * j);
         // pattern indices of tokens 2p, 2p + 1 in the high bytes of the two halves
         const uint2 vw = *(const uint2*)(tb + TS::O_VI + 32 * kb + 8 * j);
         uint32_t pr[4];
@@ -883,19 +897,9 @@ attn_mfma_kernel(AttnArgs a) {
           }
           hacc[cb] = mfma16(ah, B, hacc[cb]);
         }
-        // B = zero points z_tg (binary16, the high half of each (s, z) word)
-        // of the same tokens for group n16 % NG; tokens past the end read 0
-        const uint32_t* zw = (const uint32_t*)(tb + TS::O_VS) + (32 * kb + 8 * j) * NGS + (n16 % NG) / VPS;
-        u32x4 bz;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t w0 = zw[(2 * q) * NGS], w1 = zw[(2 * q + 1) * NGS];
-          if (!FULL) {
-            w0 = 32 * kb + 8 * j + 2 * q < nvalid ? w0 : 0u;
-            w1 = 32 * kb + 8 * j + 2 * q + 1 < nvalid ? w1 : 0u;
-          }
-          bz[q] = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
-        }
+        // B = zero points z_tg (binary16) of the same tokens for group
+        // n16 % NG, staged per group like the scales (0 past the end)
+        const u32x4 bz = *(const u32x4*)(s_vz + (n16 % NG) * VS_STRIDE + 32 * kb + 8 * j);
         zm = mfma16(ah, bz, zm);
       }
       // this lane's word of channels 8*n16 .. 8*n16+7 (word-major V tile)
@@ -908,7 +912,7 @@ attn_mfma_kernel(AttnArgs a) {
       for (int bb = 0; bb < 8; ++bb) {
         const u32x4 B = unpack_v<BITS, KVARN>(bb < 4 ? w0[bb] : w1[bb - 4], j);
         oacc[bb] = mfma16(ahi, B, oacc[bb]);
-        oacc[bb] = mfma16(alo, B, oacc[bb]);
+        if constexpr (PLO) oacc[bb] = mfma16(alo, B, oacc[bb]);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
