@@ -40,19 +40,19 @@ constexpr int MF_THREADS = MF_WAVES * 64;
 
 // Dynamic LDS layout of a block (bytes); npat = padded pattern count.
 struct MfLds {
-  int q, qsum, qe, next, qm, qa, mv, mv_rows, ps, ph, vs, vz, w, alpha, m, o, z, l, wsum, M, last, tiles,
+  int q, qsum, qe, next, qm, qa, ps, ph, vs, vz, w, alpha, m, o, z, l, wsum, M, last, tiles,
       nsn, total;
 };
 // binary16 per row of the p hi / lo tables of the pattern-mass product
 constexpr int PH_STRIDE = 72;
-// mv_rows: rows of M^V staged for the pattern term (0 without the one-hot path)
+// hist_mfma: the pattern masses are a one-hot MFMA product (p hi / lo rows,
+// V zero points staged per group)
 // kch: K per channel, which keeps the per-lane q operands of the QK product
 // (64 lanes x 32 fp32, quad-major) for the per-tile q * s operand
 // nsn: NSN mode, which keeps q . mu_K and sum p n1 per head and the rotated
 // V centre
-__host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes, int mv_rows,
+__host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes, bool hist_mfma,
                                         bool kch = false, bool nsn = false) {
-  const bool hist_mfma = mv_rows > 0;
   MfLds L;
   int o = 0;
   L.q = o; o = al16(o + HB * D * 4);
@@ -81,10 +81,6 @@ __host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes
   // and with NSN sum p n1)
   const int part_bytes = MF_WAVES * HB * (D + 1 + NG + (nsn ? 1 : 0)) * 4;
   L.tiles = o; o = al16(o + (MF_WAVES * tile_bytes > part_bytes ? MF_WAVES * tile_bytes : part_bytes));
-  // M^V rows are staged only where they fit the 160 KiB of a compute unit
-  L.mv = o;
-  L.mv_rows = (mv_rows > 0 && o + mv_rows * D * 4 <= 160 * 1024) ? mv_rows : 0;
-  o = al16(o + L.mv_rows * D * 4);
   L.total = o;
   return L;
 }
@@ -140,12 +136,11 @@ attn_mfma_kernel(AttnArgs a) {
   const int S_tot = a.splits + a.fuse;
   const int n_pat = KVARN ? 0 : a.n_pat;
   const int npat = pad_pat(n_pat);
-  const MfLds Lo = mf_lds(HB, NG, npat, TS::BYTES, 16 * NPB, KCH, NSNM);
+  const MfLds Lo = mf_lds(HB, NG, npat, TS::BYTES, NPB > 0, KCH, NSNM);
   float* s_q = (float*)(mf_raw + Lo.q);            // [HB][D]
   float* s_qsum = (float*)(mf_raw + Lo.qsum);      // [HB][NG]
   int* s_qe = (int*)(mf_raw + Lo.qe);              // [HB]: max |q| bits, then the exponent
   int* s_next = (int*)(mf_raw + Lo.next);          // next unclaimed tile of the block
-  float* s_mv = (float*)(mf_raw + Lo.mv);          // [16 NPB][D] rows of M^V
   float* s_qm = (float*)(mf_raw + Lo.qm);          // [HB][256]; entry 0xFF (no pattern) is 0
   float4* s_qa = (float4*)(mf_raw + Lo.qa);        // K per channel: [8 quads][64 lanes]
   float* s_qmu = (float*)(mf_raw + Lo.nsn);        // NSN: [HB] qscale (q . mu_K)
@@ -224,30 +219,20 @@ attn_mfma_kernel(AttnArgs a) {
     if (lane < 2 * TS::P_IX) t4[TS::O_KI / 16 + lane] = rix;
   };
 
-  // Prologue loads are all issued before anything waits on them: the first
-  // tile, q (below), and this thread's 32-channel slice of pattern row
-  // tid / 4 of M^K (for q' . M^K).
-  const int n_tiles = (t_end - t_begin + TILE - 1) / TILE;
-  // in the fused step waves 0 and 1 of split 0 encode the new token first and
-  // take their tiles from the counter afterwards
-  // K per channel: a wave takes both tiles of a 128-token block (splits start
-  // on block boundaries), so the q * s operand serves two tiles
-  const int first = !fuse_here ? (KCH ? 2 * wave : wave)
-                                : (wave < 2 ? n_tiles : (KCH ? 2 * (wave - 2) : wave - 2));
-  if (first < n_tiles) issue(t_begin + TILE * first);
-  // M^V rows for the pattern term go straight to LDS (no registers held
-  // through the loop); 16 bytes per lane, one kilobyte per wave instruction.
-  // Completion is awaited before the merge reads them.
-  const bool stage_mv = NPB > 0 && Lo.mv_rows > 0;
-  if (stage_mv) {
-    const float* mv = a.r.tab[1] + pat_unit(a.r, u) * a.max_pat * D;
-    const int n16b = min(n_pat, 16 * NPB) * (D / 4);
-    for (int g = wave; g * 64 < n16b; g += MF_WAVES) {
-      const int c = g * 64 + lane;
-      if (c < n16b)
-        __builtin_amdgcn_global_load_lds((const void*)(mv + 4 * c),
-                                         (__attribute__((address_space(3))) void*)(s_mv + 256 * g), 16, 0, 0);
-    }
+  // Prologue loads, oldest first: a wave waits for a load with a count of the
+  // loads issued after it, so each can be used without waiting for the later
+  // ones: q (one or two elements per thread), this thread's 32-channel slice
+  // of pattern row tid / 4 of M^K (for q' . M^K), then the first tile.
+  // q is read as one aligned dword for either input type and converted where
+  // it is used
+  constexpr int QPT = HB * D / MF_THREADS;
+  uint32_t qraw[QPT];
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) {
+    const int i = tid + k * MF_THREADS, h = min(i / D, gq - 1), d = i % D;
+    const int64_t e = ((int64_t)b * a.Hq + hq0 + h) * D + d;
+    const uint32_t* qw = (const uint32_t*)a.q + (a.bf16 ? e >> 1 : e);
+    qraw[k] = *qw;
   }
   const int qm_j = tid >> 2, qm_part = tid & 3;
   const float* mk = a.r.tab[0] + pat_unit(a.r, u) * a.max_pat * D;
@@ -259,13 +244,26 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) mkr[k] = m4[k];
   }
-
-  // ---------------------------------------------------------------- prologue
-  for (int i = tid; i < HB * D; i += MF_THREADS) {
-    const int h = i / D, d = i % D;
-    s_q[i] = h < gq ? load_in(a.q, ((int64_t)b * a.Hq + hq0 + h) * D + d, a.bf16) : 0.0f;
+  // q goes to LDS before the first tile is issued: a wait for it then counts
+  // only the M^K loads after it (with the tile's loads behind a branch, the
+  // count would fall back to waiting for every load)
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) {
+    const int i = tid + k * MF_THREADS;
+    const uint32_t bits = !a.bf16 ? qraw[k] : (i & 1) ? (qraw[k] & 0xFFFF0000u) : (qraw[k] << 16);
+    s_q[i] = i / D < gq ? __builtin_bit_cast(float, bits) : 0.0f;
     s_o[i] = 0.0f;
   }
+  const int n_tiles = (t_end - t_begin + TILE - 1) / TILE;
+  // in the fused step waves 0 and 1 of split 0 encode the new token first and
+  // take their tiles from the counter afterwards
+  // K per channel: a wave takes both tiles of a 128-token block (splits start
+  // on block boundaries), so the q * s operand serves two tiles
+  const int first = !fuse_here ? (KCH ? 2 * wave : wave)
+                                : (wave < 2 ? n_tiles : (KCH ? 2 * (wave - 2) : wave - 2));
+  if (first < n_tiles) issue(t_begin + TILE * first);
+
+  // ---------------------------------------------------------------- prologue
   for (int i = tid; i < MF_WAVES * HB * npat; i += MF_THREADS) s_w[i] = 0.0f;
   for (int i = tid; i < HB * npat; i += MF_THREADS) s_wsum[i] = 0.0f;
   for (int i = tid; i < HB * 256; i += MF_THREADS) s_qm[i] = 0.0f;
@@ -357,9 +355,12 @@ attn_mfma_kernel(AttnArgs a) {
   // q' . M^K_j: four threads per pattern j (32 channels each), all heads;
   // patterns beyond the first MF_THREADS / 4 take further passes
   if (!KVARN && n_pat > 0) {
-    for (int j0 = 0; j0 < n_pat; j0 += MF_THREADS / 4) {
+    // with the one-hot path (at most 64 patterns) one pass covers the table
+    const int passes = NPB > 0 ? 1 : (n_pat + MF_THREADS / 4 - 1) / (MF_THREADS / 4);
+    for (int pass = 0; pass < passes; ++pass) {
+      const int j0 = pass * (MF_THREADS / 4);
       const int jj = j0 + qm_j;
-      if (j0 > 0) {
+      if (NPB == 0 && j0 > 0) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) mkr[k] = float4{0.0f, 0.0f, 0.0f, 0.0f};
         if (jj < n_pat) {
@@ -426,8 +427,10 @@ attn_mfma_kernel(AttnArgs a) {
         float v2[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
+          // unconditional read and a select (no branch around the LDS read)
           const int i = 2 * p + e, ch = qk_channel<BITS>(j, c, i);
-          v2[e] = (ch / G == g) ? ldexpf(s_q[h * D + ch], eh - code_shift<BITS>(i)) : 0.0f;
+          const float qv = ldexpf(s_q[h * D + ch], eh - code_shift<BITS>(i));
+          v2[e] = (ch / G == g) ? qv : 0.0f;
         }
         uint32_t hi, lo;
         split2(v2[0], v2[1], k_m1, hi, lo);
@@ -924,11 +927,15 @@ attn_mfma_kernel(AttnArgs a) {
   }
 
   // ---------------------------------------------------------------- merge waves
-  // the M^V rows staged in the prologue have landed once this wave's vector
-  // memory operations are done (the barriers below publish them)
-  if (stage_mv) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  // The M^V column of this thread's first output row (the pattern term), read
+  // from global memory now so that the loads overlap the merge below.
   const float* mv = a.r.tab[1] + pat_unit(a.r, u) * a.max_pat * D;
   constexpr int MVR = NPB > 0 ? 16 * NPB : 1;
+  float mvr[MVR];
+  if constexpr (NPB > 0) {
+#pragma unroll
+    for (int jj = 0; jj < MVR; ++jj) mvr[jj] = jj < n_pat ? mv[(int64_t)jj * D + tid % D] : 0.0f;
+  }
 #pragma unroll
   for (int s = 0; s < SPL; ++s) l_run[s] = row_sum16(l_run[s]);
   if constexpr (NSNM)
@@ -1036,11 +1043,11 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int w = 0; w < MF_WAVES; ++w) o += s_ow[(w * HB + h) * D + d];
     if constexpr (NPB > 0) {
-      // separate loops keep each one's loads in a single address space
-      if (stage_mv) {
+      // the first output row of this thread uses the registers loaded above
+      if (i == tid) {
 #pragma unroll
         for (int jj = 0; jj < MVR; ++jj)
-          if (jj < n_pat) o = __builtin_fmaf(s_wsum[h * npat + jj], s_mv[jj * D + d], o);
+          if (jj < n_pat) o = __builtin_fmaf(s_wsum[h * npat + jj], mvr[jj], o);
       } else {
 #pragma unroll
         for (int jj = 0; jj < MVR; ++jj)
@@ -1147,7 +1154,7 @@ template <int BITS, int NG, int NGS, bool KVARN, int NPB, bool QLO, bool KCH = f
 static hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
   constexpr int HB = 16 / NG;
   const int npat = pad_pat(KVARN ? 0 : a.n_pat);
-  const MfLds L = mf_lds(HB, NG, npat, TileShape<BITS, NGS, KVARN, KCH, NSNM>::BYTES, 16 * NPB, KCH, NSNM);
+  const MfLds L = mf_lds(HB, NG, npat, TileShape<BITS, NGS, KVARN, KCH, NSNM>::BYTES, NPB > 0, KCH, NSNM);
   static int attr = 0;
   if (L.total > attr) {
     hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel<BITS, NG, NGS, KVARN, NPB, QLO, KCH, NSNM>,
