@@ -109,6 +109,103 @@ def attn_config(name):
     print(json.dumps(res))
 
 
+def streaming(args):
+    """The streaming-accumulation workload: a Qwen2.5-7B-shaped layer (28 q / 4
+    kv heads, head_dim 128), batch 32, a 32768-token prefix, then 256 decode
+    steps (append one token with the Chebyshev window on, then attend) whose K
+    mean drifts (step j adds 0.01 j u, u ~ N(0, I) per unit); 2-bit group 32,
+    64 k-means patterns growing by one per 128 decode steps.  Prints one JSON
+    line: the time per step, and at sampled steps the error of the quantised
+    attention against fp32 attention over the unquantised inputs (max abs and
+    relative L2 over every (batch, q-head) output), GPU-vs-oracle parity on
+    one unit, and V utilisation (the share of V vectors that keep their
+    pattern under the section 3.3 threshold)."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+    from bit_kv_cache_encode_amd import KVCache, synth
+
+    dev = torch.device("cuda", 0)
+    B, Hq, H, D, T0, S, P, W = 32, 28, 4, 128, args.context, 256, 64, 128
+    gq = Hq // H
+    k, v = synth.device_kv(B, H, T0 + S, D, device=dev, dtype=torch.float32)
+    drift = torch.from_numpy(synth.drift_dirs(B, H, D)).to(dev)
+    ramp = torch.arange(1, S + 1, device=dev, dtype=torch.float32)
+    k[:, :, T0:] += 0.01 * ramp[None, None, :, None] * drift[:, :, None, :]
+    k, v = k.to(torch.bfloat16), v.to(torch.bfloat16)
+    cache = KVCache(B, Hq, H, T0 + S, bits=2, group=32, mode="pattern", max_patterns=P + 2,
+                    pattern_window=W, v_alpha=0.05, in_dtype=torch.bfloat16, device=dev)
+    cache.init_patterns(k[:, :, :2048].contiguous(), v[:, :, :2048].contiguous(), P)
+    cache.encode_append(k[:, :, :T0].contiguous(), v[:, :, :T0].contiguous())
+    qs = [synth.device_queries(B, Hq, D, step=s, device=dev) for s in range(S)]
+    kn = [k[:, :, T0 + s:T0 + s + 1].contiguous() for s in range(S)]
+    vn = [v[:, :, T0 + s:T0 + s + 1].contiguous() for s in range(S)]
+    sample = sorted({0, 63, 127, 128, 191, S - 1})
+    out = torch.empty((B, Hq, D), device=dev)
+    saved = {}
+    # timed pass: the 256 steps back to back, outputs of sampled steps kept
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(S):
+        cache.decode_step(kn[s], vn[s], qs[s], out=out)
+        if s in sample:
+            saved[s] = out.clone()
+    e1.record()
+    torch.cuda.synchronize()
+    us_step = e0.elapsed_time(e1) * 1e3 / S
+    vidx = cache.region("v_idx").view(B * H, -1)[:, :T0 + S].cpu().numpy()
+    # exact fp32 attention over the unquantised (bf16) inputs, per sampled step
+    kf = k.float().view(B * H, T0 + S, D)
+    vf = v.float().view(B * H, T0 + S, D)
+    records = []
+    # one unit through the oracle
+    ref = O.RefCache(1, gq, 1, D, T0 + S, bits=2, group=32, mode=O.PATTERN, max_patterns=P + 2,
+                     pattern_window=W, v_alpha=0.05, in_dtype=O.IN_BF16)
+    ku = k[0:1, 0:1].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    vu = v[0:1, 0:1].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    ref.init_patterns(ku[:, :, :2048], vu[:, :, :2048], P)
+    ref.encode_append(ku[:, :, :T0], vu[:, :, :T0])
+    for s in range(S):
+        ref.encode_append(ku[:, :, T0 + s:T0 + s + 1], vu[:, :, T0 + s:T0 + s + 1], update=1)
+        if s not in sample:
+            continue
+        n = T0 + s + 1
+        q = qs[s].float().view(B * H, gq, D)
+        kt = kf[:, :n].transpose(1, 2).contiguous()
+        sc = torch.matmul(q, kt) / (D ** 0.5)
+        pr = torch.softmax(sc, dim=-1)
+        exact = torch.matmul(pr, vf[:, :n].contiguous()).view(B, Hq, D)
+        del kt, sc, pr
+        got = saved[s]
+        diff = (got - exact).abs()
+        want_u = ref.attn_decode(qs[s][0:1, 0:gq].contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
+        par = float(np.abs(got[0:1, 0:gq].cpu().numpy() - want_u).max())
+        used = vidx[:, :n]
+        dec = vidx[:, T0:n]
+        records.append({
+            "step": s, "tokens": n, "patterns": None,
+            "max_abs_err_vs_fp32": round(float(diff.max()), 5),
+            "rel_l2_err_vs_fp32": round(float(diff.norm() / exact.norm()), 5),
+            "gpu_vs_oracle_unit0": float(f"{par:.3e}"),
+            "v_utilisation_all": round(float((used != 0xFF).mean()), 4),
+            "v_utilisation_decode": round(float((dec != 0xFF).mean()), 4)})
+    for r in records:
+        r["patterns"] = P + (r["step"] + 1) // W
+    assert cache.n_patterns == P + S // W and ref.n_patterns == cache.n_patterns
+    res = {"mode": "streaming",
+           "workload": (f"Qwen2.5-7B-shaped layer: batch {B}, {Hq} q / {H} kv heads, head_dim {D}, "
+                        f"prefix {T0}, then {S} decode steps (append 1 token with the Chebyshev "
+                        f"window {W} on + attention) with drifting K mean; 2-bit group 32, "
+                        f"{P} k-means patterns -> {cache.n_patterns}"),
+           "us_per_step": round(us_step, 2), "steps": S,
+           "errors": "max abs and relative L2 over all (batch, q-head) outputs against fp32 "
+                     "attention over the unquantised bf16 inputs; gpu_vs_oracle on unit (0, 0)",
+           "records": records}
+    print(json.dumps(res))
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +237,11 @@ def parse():
                          "scalar mode; kivi: the step's shapes with K "
                          "quantised per channel over 128-token blocks, 32832 tokens); prints one "
                          "JSON line")
+    ap.add_argument("--streaming", action="store_true",
+                    help="the streaming-accumulation workload (Qwen2.5-7B shape, batch 32, "
+                         "32768-token prefix, 256 drifting decode steps): per-step time and, at "
+                         "sampled steps, error against fp32 attention, oracle parity on one unit "
+                         "and V utilisation; prints one JSON line")
     ap.add_argument("--traffic-from", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "RAW_DIR"),
                     help="no GPU: summarise three rocprofv3 --pmc runs of --attn-only N "
                          "--calib-copy M (FETCH_SIZE; WRITE_SIZE; TCC_EA0_RDREQ 32B/64B/128B) "
@@ -253,6 +355,9 @@ def main():
         sys.exit(2)
     if args.attn_config:
         attn_config(args.attn_config)
+        return
+    if args.streaming:
+        streaming(args)
         return
     import torch
 
