@@ -10,7 +10,9 @@ import ctypes as C
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkvq.so")
+# KVQ_LIB selects another build of the same sources (the host-sanitizer test);
+# a missing library raises like the default one
+LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(HERE, "libkvq.so")
 
 KVQ_OK, KVQ_EINVAL, KVQ_ECAPACITY, KVQ_ESTATE, KVQ_EDEVICE, KVQ_ESCRATCH = 0, -1, -2, -3, -4, -5
 NOALLOC_SCRATCH_BYTES, NOALLOC_COUNTER_BYTES = 8 << 20, 64 << 10

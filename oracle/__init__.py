@@ -19,7 +19,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvqref.c")
-_LIB = os.path.join(_HERE, "libkvqref.so")
+# KVQREF_LIB selects another build of the same source (the sanitizer test)
+_LIB = os.environ.get("KVQREF_LIB") or os.path.join(_HERE, "libkvqref.so")
 
 PATTERN, KVARN, NSN = 0, 1, 2
 IN_F32, IN_BF16 = 0, 1
@@ -37,6 +38,17 @@ def build(force: bool = True) -> str:
         subprocess.run(cmd, check=True)
         os.replace(_LIB + ".tmp", _LIB)
     return _LIB
+
+
+def build_sanitized(out: str) -> str:
+    """Compile the oracle with AddressSanitizer and UndefinedBehaviorSanitizer
+    (any report aborts), for a run under the ASan runtime (LD_PRELOAD)."""
+    cmd = ["gcc", "-O1", "-g", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+           "-fno-unsafe-math-optimizations", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+           "-shared", "-fPIC", "-o", out, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
 
 
 class _Cfg(C.Structure):
