@@ -395,16 +395,24 @@ __device__ __forceinline__ void km_load16(const void* x, int64_t idx, int bf16, 
 }
 
 // LDS layout of the block-parallel k-means for n rows and k patterns (bytes):
-// centroids [k rounded up to KF_PC][D] binary64, then per row its assignment
-// and its rank in its chunk (one byte each), the member lists (uint16), per
-// chunk counts / prefixes [n/64][k] (uint16) and the cluster offsets and
-// counts.  It serves any (n, k) whose total fits a compute unit's LDS.
-struct KfLds { int cent, a, rank, mem, pre, off, cnt, changed, total; };
+// centroids [k rounded up to KF_PC][D] binary64; their binary32 copies for
+// the matrix cores [k rounded up to 16][KF_CSTRIDE] with binary64 squared
+// norms and binary32 norms; then per row its assignment and its rank in its
+// chunk (one byte each), the member lists (uint16), per chunk counts /
+// prefixes [n/64][k] (uint16) and the cluster offsets and counts.  The list
+// of rows whose nearest centroid the matrix-core distances leave open
+// (uint16) shares the rank and member-list bytes, which serve only the
+// update.  It serves any (n, k) whose total fits a compute unit's LDS.
+constexpr int KF_CSTRIDE = D + 4;   // floats per binary32 centroid row (bank shift)
+struct KfLds { int cent, c32, cc, cn, a, rank, mem, pre, off, cnt, changed, namb, total; };
 __host__ __device__ inline KfLds kf_lds(int n, int k) {
   KfLds L;
-  const int kr = (k + KF_PC - 1) / KF_PC * KF_PC, nch = (n + 63) / 64;
+  const int kr = (k + KF_PC - 1) / KF_PC * KF_PC, k16 = (k + 15) / 16 * 16, nch = (n + 63) / 64;
   int o = 0;
   L.cent = o; o += kr * D * 8;
+  L.c32 = o; o += k16 * KF_CSTRIDE * 4;
+  L.cc = o; o += k16 * 8;
+  L.cn = o; o += (k16 * 4 + 15) / 16 * 16;
   L.a = o; o += (n + 15) / 16 * 16;
   L.rank = o; o += (n + 15) / 16 * 16;
   L.mem = o; o += (2 * n + 15) / 16 * 16;
@@ -412,10 +420,31 @@ __host__ __device__ inline KfLds kf_lds(int n, int k) {
   L.off = o; o += 4 * KM_MAXK;
   L.cnt = o; o += 4 * KM_MAXK;
   L.changed = o; o += 16;
+  L.namb = o; o += 16;
   L.total = o;
   return L;
 }
 
+// 32 consecutive channels of an input row (16-byte aligned) as fp32
+__device__ __forceinline__ void km_load32(const void* x, int64_t idx, int bf16, float (&o)[32]) {
+  float a[16], b[16];
+  km_load16(x, idx, bf16, a);
+  km_load16(x, idx + 16, bf16, b);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) { o[i] = a[i]; o[16 + i] = b[i]; }
+}
+
+// minimum over the 16 lanes of a row of a wave
+__device__ __forceinline__ float km_rowmin16(float v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+typedef float km_f32x4 __attribute__((ext_vector_type(4)));
+
+// NCB: column blocks of 16 patterns in the matrix-core distances (k <= 16 NCB)
+template <int NCB>
 __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk, const void* xv,
                                                                   int bf16, int n_tok, int groups,
                                                                   int64_t gstride, int k,
@@ -432,6 +461,10 @@ __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk,
   const int kr = (k + KF_PC - 1) / KF_PC * KF_PC;
   const KfLds Lo = kf_lds(n, k);
   double (*cent)[D] = (double (*)[D])(km_raw + Lo.cent);   // [kr][D]
+  float* s_c32 = (float*)(km_raw + Lo.c32);                  // [k16][KF_CSTRIDE]
+  double* s_cc = (double*)(km_raw + Lo.cc);                  // [k16] |c|^2
+  float* s_cn = (float*)(km_raw + Lo.cn);                    // [k16] |c| rounded up
+  int* s_namb = (int*)(km_raw + Lo.namb);
   uint8_t* s_a = km_raw + Lo.a;                              // [n]
   uint8_t* s_rank = km_raw + Lo.rank;                        // [n]
   uint16_t* s_mem = (uint16_t*)(km_raw + Lo.mem);            // [n]
@@ -439,6 +472,8 @@ __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk,
   int* s_off = (int*)(km_raw + Lo.off);
   int* s_cnt = (int*)(km_raw + Lo.cnt);
   int* s_changed = (int*)(km_raw + Lo.changed);
+  uint16_t* s_amb = (uint16_t*)(km_raw + Lo.rank);           // [n], assignment only
+  const int k16 = (k + 15) / 16 * 16;
 
   for (int i = tid; i < kr * D; i += KF_THREADS) {
     const int j = i / D, d = i % D;
@@ -447,42 +482,172 @@ __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk,
   }
   __syncthreads();
   for (int it = 0; it < KM_ITERS; ++it) {
-    if (tid == 0) *s_changed = 0;
+    // ---- assignment (Eq 4's nearest centroid, Euclidean).  The matrix cores
+    // give every row's binary32 dot products with binary32 copies of the
+    // centroids, so each distance |x|^2 + |c|^2 - 2 x.c (binary64) is known
+    // to within E = 2 (D + 3) 2^-24 |x| |c| (the dot over D channels in
+    // binary32 from the rounded centroid) plus a small binary64 term.  A row
+    // whose intervals leave one centroid below every other takes it: the
+    // binary64 distances of the other centroids exceed its own, so the
+    // oracle's loop picks it too.  Any other row is listed and its distances
+    // are recomputed exactly as the oracle computes them.
+    for (int i = tid; i < k16 * D; i += KF_THREADS) {
+      const int j = i / D, d = i % D;
+      s_c32[j * KF_CSTRIDE + d] = j < k ? (float)cent[j][d] : 0.0f;
+    }
+    if (tid < k16) {
+      double acc = 0.0;
+      if (tid < k)
+        for (int d = 0; d < D; ++d) acc = __builtin_fma(cent[tid][d], cent[tid][d], acc);
+      s_cc[tid] = acc;
+      s_cn[tid] = (float)(__builtin_sqrt(acc) * (1.0 + 0x1p-40));   // |c| rounded up
+    }
+    if (tid == 0) { *s_changed = 0; *s_namb = 0; }
     __syncthreads();
     int changed = 0;
-    for (int t = tid; t < n; t += KF_THREADS) {
-      const int64_t row = km_row(u, t, n_tok, gstride) * D;
-      int best = 0;
-      double bd = INFINITY;
-      for (int p0 = 0; p0 < k; p0 += KF_PC) {
-        double dist[KF_PC];
+    {
+      const int li = lane & 15, lk = lane >> 4;
+      // E = e1 |x| |c| + e2 (|x|^2 + |c|^2 + 2 |x| |c|): the binary32 dot over D
+      // channels from the rounded centroid, and (e2) the binary64 roundings
+      const float e1f = 2.0f * (D + 3) * 0x1p-24f * (1.0f + 0x1p-20f), e2f = 0x1p-40f;
+      // A: row 16 rb + li; half h of the channels, 16 per lane: channels
+      // 64 h + 16 lk .. + 15 (B uses the same order).  The next half (of this
+      // row block or the next) is loaded while one is used.
+      const int nrb = (n + 15) / 16;
+      float xn[16];
+      auto load_half = [&](int rb, int h) {
+        km_load16(x, km_row(u, min(16 * rb + li, n - 1), n_tok, gstride) * D + 64 * h + 16 * lk, bf16, xn);
+      };
+      if (wave < nrb) load_half(wave, 0);
+      for (int rb = wave; rb < nrb; rb += KF_THREADS / 64) {
+        km_f32x4 acc[NCB];
 #pragma unroll
-        for (int q = 0; q < KF_PC; ++q) dist[q] = 0.0;
-        // channels in blocks of 16; the next block's loads are in flight
-        // while this one is used
-        float xb[16], xn[16];
-        km_load16(x, row, bf16, xb);
-        for (int d0 = 0; d0 < D; d0 += 16) {
-          if (d0 + 16 < D) km_load16(x, row + d0 + 16, bf16, xn);
+        for (int cb = 0; cb < NCB; ++cb) acc[cb] = km_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        double xx = 0.0;
 #pragma unroll
-          for (int dd = 0; dd < 16; ++dd) {
-            const double xd = (double)xb[dd];
+        for (int h = 0; h < 2; ++h) {
+          float xa[16];
 #pragma unroll
-            for (int q = 0; q < KF_PC; ++q) {
-              const double diff = xd - cent[p0 + q][d0 + dd];
-              dist[q] = dist[q] + diff * diff;
+          for (int i = 0; i < 16; ++i) xa[i] = xn[i];
+          if (h == 0) load_half(rb, 1);
+          else if (rb + KF_THREADS / 64 < nrb) load_half(rb + KF_THREADS / 64, 0);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) xx = __builtin_fma((double)xa[i], (double)xa[i], xx);
+          // the pattern blocks' accumulation chains interleaved
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4) {
+            float4 cv[NCB];
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+              cv[cb] = *(const float4*)(s_c32 + (16 * cb + li) * KF_CSTRIDE + 64 * h + 16 * lk + 4 * s4);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+              acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[4 * s4], cv[cb].x, acc[cb], 0, 0, 0);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+              acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[4 * s4 + 1], cv[cb].y, acc[cb], 0, 0, 0);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+              acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[4 * s4 + 2], cv[cb].z, acc[cb], 0, 0, 0);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+              acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[4 * s4 + 3], cv[cb].w, acc[cb], 0, 0, 0);
+          }
+        }
+        // |x|^2 of row li: the four lanes holding it add their parts
+        xx += __shfl_xor(xx, 16, 64);
+        xx += __shfl_xor(xx, 32, 64);
+        // output slot r of this lane: row 16 rb + 4 lk + r, centroid 16 cb + li
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * rb + 4 * lk + r;
+          const double xr = __shfl(xx, 4 * lk + r, 64);
+          // |x| rounded up (binary32 sqrt of the rounded square, widened)
+          const float xrf = (float)xr;
+          const float xn = __builtin_sqrtf(xrf) * (1.0f + 0x1p-19f);
+          float lo[NCB], hi[NCB];
+          float U = INFINITY;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            const int j = 16 * cb + li;
+            lo[cb] = hi[cb] = INFINITY;
+            if (j < k) {
+              const double ap = (xr + s_cc[j]) - 2.0 * (double)acc[cb][r];
+              // the bound in binary32, widened by 2^-19 for its own roundings
+              const float cn = s_cn[j], apf = (float)ap;
+              const float E = (e1f * xn * cn + e2f * (xrf + (float)s_cc[j] + 2.0f * xn * cn)) * (1.0f + 0x1p-19f)
+                              + fabsf(apf) * 0x1p-22f + 0x1p-100f;
+              lo[cb] = apf - E;
+              hi[cb] = apf + E;
+            }
+            U = fminf(U, hi[cb]);
+          }
+          U = km_rowmin16(U);
+          int count = 0, first = -1;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            const uint64_t bal = __ballot(lo[cb] <= U);
+            const uint32_t bits = (uint32_t)(bal >> (16 * lk)) & 0xFFFFu;
+            count += __popc(bits);
+            if (first < 0 && bits) first = 16 * cb + __ffs(bits) - 1;
+          }
+          if (li == 0 && row < n) {
+            if (count == 1) {
+              if (it == 0 || s_a[row] != (uint8_t)first) changed = 1;
+              s_a[row] = (uint8_t)first;
+            } else {
+              s_amb[atomicAdd(s_namb, 1)] = (uint16_t)row;
             }
           }
-#pragma unroll
-          for (int dd = 0; dd < 16; ++dd) xb[dd] = xn[dd];
         }
-        // strict '<' in pattern order keeps the lowest index
-#pragma unroll
-        for (int q = 0; q < KF_PC; ++q)
-          if (p0 + q < k && dist[q] < bd) { bd = dist[q]; best = p0 + q; }
       }
-      if (it == 0 || s_a[t] != (uint8_t)best) changed = 1;
-      s_a[t] = (uint8_t)best;
+    }
+    __syncthreads();
+    // the listed rows: one wave per row, lane j sums centroid j's squared
+    // differences in channel order as the oracle does (binary64); the
+    // smallest distance, lowest index on ties, is the pattern the oracle's
+    // loop (strict '<' in pattern order) keeps
+    const int namb = *s_namb;
+    for (int i = wave; i < namb; i += KF_THREADS / 64) {
+      const int t = s_amb[i];
+      const int64_t row = km_row(u, t, n_tok, gstride) * D;
+      double dist[KM_MAXK / 64 + 1];
+      int best = 0;
+      double bd = INFINITY;
+#pragma unroll
+      for (int h = 0; h * 64 < KM_MAXK; ++h) {
+        const int j = h * 64 + lane;
+        double acc = 0.0;
+        if (j < k) {
+          float xb[16];
+          for (int d0 = 0; d0 < D; d0 += 16) {
+            km_load16(x, row + d0, bf16, xb);
+#pragma unroll
+            for (int dd = 0; dd < 16; ++dd) {
+              const double diff = (double)xb[dd] - cent[j][d0 + dd];
+              acc = acc + diff * diff;
+            }
+          }
+        }
+        dist[h] = j < k ? acc : INFINITY;
+      }
+      // lexicographic minimum of (distance, index) over the wave
+#pragma unroll
+      for (int h = 0; h * 64 < KM_MAXK; ++h) {
+        double dv = dist[h];
+        int jv = h * 64 + lane;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const double od = __shfl_xor(dv, o, 64);
+          const int oj = __shfl_xor(jv, o, 64);
+          if (od < dv || (od == dv && oj < jv)) { dv = od; jv = oj; }
+        }
+        if (dv < bd) { bd = dv; best = jv; }
+      }
+      if (lane == 0) {
+        if (it == 0 || s_a[t] != (uint8_t)best) changed = 1;
+        s_a[t] = (uint8_t)best;
+      }
     }
     if (changed) atomicOr(s_changed, 1);
     __syncthreads();
@@ -520,23 +685,49 @@ __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk,
       s_mem[s_off[j] + s_pre[(t >> 6) * k + j] + s_rank[t]] = (uint16_t)t;
     }
     __syncthreads();
-    // centroid = member sum in token order / member count; empty keeps its centroid
-    for (int i = tid; i < k * D; i += KF_THREADS) {
-      const int j = i / D, d = i % D, c = s_cnt[j];
+    // centroid = member sum in token order / member count; empty keeps its
+    // centroid.  Thread (j, q) sums channels 4 q .. 4 q + 3 of cluster j's
+    // members in token order (one accumulator per channel), with the loads
+    // of 8 members in flight; the threads of a cluster read whole rows.
+    for (int i = tid; i < k * (D / 4); i += KF_THREADS) {
+      const int j = i / (D / 4), d0 = 4 * (i % (D / 4)), c = s_cnt[j];
       if (c == 0) continue;
       const uint16_t* m = s_mem + s_off[j];
-      // members in blocks of 8 (their loads issued together), summed in order
-      double acc = 0.0;
-      int e = 0;
-      for (; e + 8 <= c; e += 8) {
-        float v[8];
+      double acc[4] = {0.0, 0.0, 0.0, 0.0};
+      if (bf16) {
+        // raw bfloat16 words of 16 members in flight
+        for (int e = 0; e < c; e += 16) {
+          uint2 w[16];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = load_in(x, km_row(u, m[e + i], n_tok, gstride) * D + d, bf16);
+          for (int i2 = 0; i2 < 16; ++i2)
+            w[i2] = *(const uint2*)((const uint16_t*)x + km_row(u, m[min(e + i2, c - 1)], n_tok, gstride) * D + d0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc = acc + (double)v[i];
+          for (int i2 = 0; i2 < 16; ++i2)
+            if (e + i2 < c) {
+              acc[0] = acc[0] + (double)bf16_to_f32((uint16_t)(w[i2].x & 0xFFFFu));
+              acc[1] = acc[1] + (double)bf16_to_f32((uint16_t)(w[i2].x >> 16));
+              acc[2] = acc[2] + (double)bf16_to_f32((uint16_t)(w[i2].y & 0xFFFFu));
+              acc[3] = acc[3] + (double)bf16_to_f32((uint16_t)(w[i2].y >> 16));
+            }
+        }
+      } else {
+        for (int e = 0; e < c; e += 8) {
+          float4 f[8];
+#pragma unroll
+          for (int i2 = 0; i2 < 8; ++i2)
+            f[i2] = *(const float4*)((const float*)x + km_row(u, m[min(e + i2, c - 1)], n_tok, gstride) * D + d0);
+#pragma unroll
+          for (int i2 = 0; i2 < 8; ++i2)
+            if (e + i2 < c) {
+              acc[0] = acc[0] + (double)f[i2].x;
+              acc[1] = acc[1] + (double)f[i2].y;
+              acc[2] = acc[2] + (double)f[i2].z;
+              acc[3] = acc[3] + (double)f[i2].w;
+            }
+        }
       }
-      for (; e < c; ++e) acc = acc + (double)load_in(x, km_row(u, m[e], n_tok, gstride) * D + d, bf16);
-      cent[j][d] = acc / (double)c;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) cent[j][d0 + q] = acc[q] / (double)c;
     }
     __syncthreads();
   }
@@ -549,15 +740,28 @@ hipError_t launch_kmeans_pair(const void* xk, const void* xv, int bf16, int n_to
   const int64_t n = (int64_t)groups * n_tok;
   if (n <= KF_MAXN && k <= KM_MAXK && kf_lds((int)n, k).total <= KF_LDS_MAX) {
     const int lds = kf_lds((int)n, k).total;
-    static int fast_attr = 0;
-    if (lds > fast_attr) {
-      hipError_t e = hipFuncSetAttribute((const void*)kmeans_fast_kernel,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    const int ncb = (k + 15) / 16;
+    const void* fn = ncb <= 1 ? (const void*)kmeans_fast_kernel<1>
+                   : ncb == 2 ? (const void*)kmeans_fast_kernel<2>
+                   : ncb == 3 ? (const void*)kmeans_fast_kernel<3> : (const void*)kmeans_fast_kernel<4>;
+    static int fast_attr[5] = {0, 0, 0, 0, 0};
+    if (lds > fast_attr[ncb]) {
+      hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
       if (e != hipSuccess) return e;
-      fast_attr = lds;
+      fast_attr[ncb] = lds;
     }
-    hipLaunchKernelGGL(kmeans_fast_kernel, dim3(units, 2), dim3(KF_THREADS), lds, s, xk, xv, bf16,
-                       n_tok, groups, gstride, k, tab_k, tab_v, max_pat);
+    if (ncb <= 1)
+      hipLaunchKernelGGL(kmeans_fast_kernel<1>, dim3(units, 2), dim3(KF_THREADS), lds, s, xk, xv, bf16,
+                         n_tok, groups, gstride, k, tab_k, tab_v, max_pat);
+    else if (ncb == 2)
+      hipLaunchKernelGGL(kmeans_fast_kernel<2>, dim3(units, 2), dim3(KF_THREADS), lds, s, xk, xv, bf16,
+                         n_tok, groups, gstride, k, tab_k, tab_v, max_pat);
+    else if (ncb == 3)
+      hipLaunchKernelGGL(kmeans_fast_kernel<3>, dim3(units, 2), dim3(KF_THREADS), lds, s, xk, xv, bf16,
+                         n_tok, groups, gstride, k, tab_k, tab_v, max_pat);
+    else
+      hipLaunchKernelGGL(kmeans_fast_kernel<4>, dim3(units, 2), dim3(KF_THREADS), lds, s, xk, xv, bf16,
+                         n_tok, groups, gstride, k, tab_k, tab_v, max_pat);
     return hipGetLastError();
   }
   size_t lds = sizeof(KmShared);
