@@ -41,7 +41,7 @@ constexpr int MF_THREADS = MF_WAVES * 64;
 // Dynamic LDS layout of a block (bytes); npat = padded pattern count.
 struct MfLds {
   int q, qsum, qe, next, qm, qa, ps, ph, vs, vz, w, alpha, m, o, z, l, wsum, M, last, tiles,
-      nsn, total;
+      nsn, mv, mv_rows, total;
 };
 // binary16 per row of the p hi / lo tables of the pattern-mass product
 constexpr int PH_STRIDE = 72;
@@ -52,7 +52,7 @@ constexpr int PH_STRIDE = 72;
 // nsn: NSN mode, which keeps q . mu_K and sum p n1 per head and the rotated
 // V centre
 __host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes, bool hist_mfma,
-                                        bool kch = false, bool nsn = false) {
+                                        int mv_rows, bool kch = false, bool nsn = false) {
   MfLds L;
   int o = 0;
   L.q = o; o = al16(o + HB * D * 4);
@@ -81,6 +81,11 @@ __host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes
   // and with NSN sum p n1)
   const int part_bytes = MF_WAVES * HB * (D + 1 + NG + (nsn ? 1 : 0)) * 4;
   L.tiles = o; o = al16(o + (MF_WAVES * tile_bytes > part_bytes ? MF_WAVES * tile_bytes : part_bytes));
+  // rows of M^V for the pattern term (one-hot path), where they fit the
+  // 160 KiB of a compute unit
+  L.mv = o;
+  L.mv_rows = (hist_mfma && o + mv_rows * D * 4 <= 160 * 1024) ? mv_rows : 0;
+  o = al16(o + L.mv_rows * D * 4);
   L.total = o;
   return L;
 }
@@ -136,7 +141,7 @@ attn_mfma_kernel(AttnArgs a) {
   const int S_tot = a.splits + a.fuse;
   const int n_pat = KVARN ? 0 : a.n_pat;
   const int npat = pad_pat(n_pat);
-  const MfLds Lo = mf_lds(HB, NG, npat, TS::BYTES, NPB > 0, KCH, NSNM);
+  const MfLds Lo = mf_lds(HB, NG, npat, TS::BYTES, NPB > 0, 16 * NPB, KCH, NSNM);
   float* s_q = (float*)(mf_raw + Lo.q);            // [HB][D]
   float* s_qsum = (float*)(mf_raw + Lo.qsum);      // [HB][NG]
   int* s_qe = (int*)(mf_raw + Lo.qe);              // [HB]: max |q| bits, then the exponent
@@ -244,8 +249,21 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) mkr[k] = m4[k];
   }
+  // M^V rows for the pattern term, staged in LDS with q (same round trip),
+  // so that the merge after the loop reads no global memory
+  constexpr int MVL = NPB > 0 ? 16 * NPB * D / 4 / MF_THREADS : 1;   // float4 per thread
+  float4 mvl[MVL];
+  const bool stage_mv = NPB > 0 && Lo.mv_rows > 0;
+  if (stage_mv) {
+    const float4* mv4 = (const float4*)(a.r.tab[1] + pat_unit(a.r, u) * a.max_pat * D);
+#pragma unroll
+    for (int k = 0; k < MVL; ++k) {
+      const int c = tid + k * MF_THREADS;    // float4 index over rows < 16 NPB
+      mvl[k] = c < n_pat * (D / 4) ? mv4[c] : float4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  }
   // q goes to LDS before the first tile is issued: a wait for it then counts
-  // only the M^K loads after it (with the tile's loads behind a branch, the
+  // only the loads after it (with the tile's loads behind a branch, the
   // count would fall back to waiting for every load)
 #pragma unroll
   for (int k = 0; k < QPT; ++k) {
@@ -254,6 +272,9 @@ attn_mfma_kernel(AttnArgs a) {
     s_q[i] = i / D < gq ? __builtin_bit_cast(float, bits) : 0.0f;
     s_o[i] = 0.0f;
   }
+  if (stage_mv)
+#pragma unroll
+    for (int k = 0; k < MVL; ++k) ((float4*)(mf_raw + Lo.mv))[tid + k * MF_THREADS] = mvl[k];
   const int n_tiles = (t_end - t_begin + TILE - 1) / TILE;
   // in the fused step waves 0 and 1 of split 0 encode the new token first and
   // take their tiles from the counter afterwards
@@ -927,14 +948,17 @@ attn_mfma_kernel(AttnArgs a) {
   }
 
   // ---------------------------------------------------------------- merge waves
-  // The M^V column of this thread's first output row (the pattern term), read
-  // from global memory now so that the loads overlap the merge below.
+  // Without staged M^V rows: the M^V column of this thread's first output row
+  // (the pattern term), read from global memory now so that the loads overlap
+  // the merge below.
   const float* mv = a.r.tab[1] + pat_unit(a.r, u) * a.max_pat * D;
   constexpr int MVR = NPB > 0 ? 16 * NPB : 1;
   float mvr[MVR];
+  const float* s_mv = (const float*)(mf_raw + Lo.mv);   // [16 NPB][D] when staged
   if constexpr (NPB > 0) {
+    if (!stage_mv)
 #pragma unroll
-    for (int jj = 0; jj < MVR; ++jj) mvr[jj] = jj < n_pat ? mv[(int64_t)jj * D + tid % D] : 0.0f;
+      for (int jj = 0; jj < MVR; ++jj) mvr[jj] = jj < n_pat ? mv[(int64_t)jj * D + tid % D] : 0.0f;
   }
 #pragma unroll
   for (int s = 0; s < SPL; ++s) l_run[s] = row_sum16(l_run[s]);
@@ -1043,8 +1067,14 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int w = 0; w < MF_WAVES; ++w) o += s_ow[(w * HB + h) * D + d];
     if constexpr (NPB > 0) {
-      // the first output row of this thread uses the registers loaded above
-      if (i == tid) {
+      // staged rows in LDS; else the first output row of this thread uses
+      // the registers loaded above (separate loops keep each one's loads in
+      // a single address space)
+      if (stage_mv) {
+#pragma unroll
+        for (int jj = 0; jj < MVR; ++jj)
+          if (jj < n_pat) o = __builtin_fmaf(s_wsum[h * npat + jj], s_mv[jj * D + d], o);
+      } else if (i == tid) {
 #pragma unroll
         for (int jj = 0; jj < MVR; ++jj)
           if (jj < n_pat) o = __builtin_fmaf(s_wsum[h * npat + jj], mvr[jj], o);
@@ -1154,7 +1184,7 @@ template <int BITS, int NG, int NGS, bool KVARN, int NPB, bool QLO, bool KCH = f
 static hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
   constexpr int HB = 16 / NG;
   const int npat = pad_pat(KVARN ? 0 : a.n_pat);
-  const MfLds L = mf_lds(HB, NG, npat, TileShape<BITS, NGS, KVARN, KCH, NSNM>::BYTES, NPB > 0, KCH, NSNM);
+  const MfLds L = mf_lds(HB, NG, npat, TileShape<BITS, NGS, KVARN, KCH, NSNM>::BYTES, NPB > 0, 16 * NPB, KCH, NSNM);
   static int attr = 0;
   if (L.total > attr) {
     hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel<BITS, NG, NGS, KVARN, NPB, QLO, KCH, NSNM>,

@@ -488,9 +488,9 @@ __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk,
     // to within E = 2 (D + 3) 2^-24 |x| |c| (the dot over D channels in
     // binary32 from the rounded centroid) plus a small binary64 term.  A row
     // whose intervals leave one centroid below every other takes it: the
-    // binary64 distances of the other centroids exceed its own, so the
-    // oracle's loop picks it too.  Any other row is listed and its distances
-    // are recomputed exactly as the oracle computes them.
+    // binary64 distances of the other centroids exceed its own, so a plain
+    // binary64 nearest-centroid scan picks it too.  Any other row is listed
+    // and its distances are recomputed in binary64 in channel order.
     for (int i = tid; i < k16 * D; i += KF_THREADS) {
       const int j = i / D, d = i % D;
       s_c32[j * KF_CSTRIDE + d] = j < k ? (float)cent[j][d] : 0.0f;
@@ -604,9 +604,9 @@ __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk,
     }
     __syncthreads();
     // the listed rows: one wave per row, lane j sums centroid j's squared
-    // differences in channel order as the oracle does (binary64); the
-    // smallest distance, lowest index on ties, is the pattern the oracle's
-    // loop (strict '<' in pattern order) keeps
+    // differences in channel order (binary64); the smallest distance, lowest
+    // index on ties, is the pattern a scan with strict '<' in pattern order
+    // keeps
     const int namb = *s_namb;
     for (int i = wave; i < namb; i += KF_THREADS / 64) {
       const int t = s_amb[i];
