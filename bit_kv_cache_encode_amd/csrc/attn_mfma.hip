@@ -1110,41 +1110,58 @@ attn_mfma_kernel(AttnArgs a) {
   __syncthreads();
   if (!*s_last) return;
   // out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, with a running max
-  // over chunks of 8 splits so that each chunk's loads are issued together
+  // over chunks of CC splits.  The partials of other blocks are read with
+  // agent-scope loads, each a long round trip, so a chunk issues all of its
+  // loads before it uses any: one round trip per chunk.  (m, l) is one
+  // 64-bit load; the lanes of a wave share its address (one head per wave).
   constexpr int OPT = HB * D / MF_THREADS;   // outputs per thread
+  constexpr int CC = 32 / OPT;               // splits per chunk
+  float Mr[OPT], Lr[OPT], Or[OPT];
+#pragma unroll
+  for (int k = 0; k < OPT; ++k) { Mr[k] = -INFINITY; Lr[k] = 0.0f; Or[k] = 0.0f; }
+  for (int c0 = 0; c0 < S; c0 += CC) {
+    const int n = min(CC, S - c0);
+    uint64_t mlw[OPT][CC];
+    float oo[OPT][CC];
+#pragma unroll
+    for (int k = 0; k < OPT; ++k) {
+      // rows of heads >= gq repeat head gq - 1 and are not stored
+      const int i = tid + k * MF_THREADS, h = min(i / D, gq - 1), d = i % D;
+      const int64_t row0 = ((int64_t)b * a.Hq + hq0 + h) * S + c0;
+#pragma unroll
+      for (int e = 0; e < CC; ++e) {
+        mlw[k][e] = 0xFF800000u;   // (m, l) = (-inf, 0) past the last split
+        oo[k][e] = 0.0f;
+        if (e < n) {
+          mlw[k][e] = __hip_atomic_load((const uint64_t*)(ml + (row0 + e) * 2), __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+          oo[k][e] = __hip_atomic_load(&a.r.ws[(row0 + e) * D + d], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < OPT; ++k) {
+      float cm = Mr[k];
+#pragma unroll
+      for (int e = 0; e < CC; ++e) cm = fmaxf(cm, __builtin_bit_cast(float, (uint32_t)mlw[k][e]));
+      const float rs = Mr[k] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(Mr[k] - cm);
+      Lr[k] *= rs;
+      Or[k] *= rs;
+#pragma unroll
+      for (int e = 0; e < CC; ++e) {
+        const float mm = __builtin_bit_cast(float, (uint32_t)mlw[k][e]);
+        const float ll = __builtin_bit_cast(float, (uint32_t)(mlw[k][e] >> 32));
+        const float fs = mm == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mm - cm);
+        Lr[k] = __builtin_fmaf(ll, fs, Lr[k]);
+        Or[k] = __builtin_fmaf(oo[k][e], fs, Or[k]);
+      }
+      Mr[k] = cm;
+    }
+  }
   float r_out[OPT];
 #pragma unroll
-  for (int k = 0; k < OPT; ++k) {
-    const int i = tid + k * MF_THREADS, h = i / D, d = i % D;
-    r_out[k] = 0.0f;
-    if (h >= gq) continue;
-    const int64_t row0 = ((int64_t)b * a.Hq + hq0 + h) * S;
-    float M = -INFINITY, L = 0.0f, O = 0.0f;
-    for (int c0 = 0; c0 < S; c0 += 8) {
-      float mm[8], ll[8], oo[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sp = c0 + e < S ? c0 + e : c0;
-        mm[e] = __hip_atomic_load(&ml[(row0 + sp) * 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ll[e] = __hip_atomic_load(&ml[(row0 + sp) * 2 + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        oo[e] = __hip_atomic_load(&a.r.ws[(row0 + sp) * D + d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      float cm = M;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) cm = (c0 + e < S) ? fmaxf(cm, mm[e]) : cm;
-      const float rs = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - cm);
-      L *= rs;
-      O *= rs;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float fs = (c0 + e < S && mm[e] != -INFINITY) ? __builtin_amdgcn_exp2f(mm[e] - cm) : 0.0f;
-        L = __builtin_fmaf(ll[e], fs, L);
-        O = __builtin_fmaf(oo[e], fs, O);
-      }
-      M = cm;
-    }
-    r_out[k] = O / L;
-  }
+  for (int k = 0; k < OPT; ++k) r_out[k] = Or[k] / Lr[k];
   if (!KVARN) {
 #pragma unroll
     for (int k = 0; k < OPT; ++k) {
