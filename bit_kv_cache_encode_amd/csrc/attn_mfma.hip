@@ -1069,15 +1069,19 @@ attn_mfma_kernel(AttnArgs a) {
     if constexpr (NPB > 0) {
       // staged rows in LDS; else the first output row of this thread uses
       // the registers loaded above (separate loops keep each one's loads in
-      // a single address space)
+      // a single address space).  Both hold zeros in the rows from n_pat up
+      // to 16 NPB, so these loops run to 16 NPB without a test per row (a
+      // branch per row would make each LDS read wait for the previous one);
+      // past the padded pattern count the weight index is clamped, and the
+      // finite weight times the zero row adds +-0.
       if (stage_mv) {
 #pragma unroll
         for (int jj = 0; jj < MVR; ++jj)
-          if (jj < n_pat) o = __builtin_fmaf(s_wsum[h * npat + jj], s_mv[jj * D + d], o);
+          o = __builtin_fmaf(s_wsum[h * npat + min(jj, npat - 1)], s_mv[jj * D + d], o);
       } else if (i == tid) {
 #pragma unroll
         for (int jj = 0; jj < MVR; ++jj)
-          if (jj < n_pat) o = __builtin_fmaf(s_wsum[h * npat + jj], mvr[jj], o);
+          o = __builtin_fmaf(s_wsum[h * npat + min(jj, npat - 1)], mvr[jj], o);
       } else {
 #pragma unroll
         for (int jj = 0; jj < MVR; ++jj)
