@@ -17,6 +17,8 @@ LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(HERE, "libkvq.so")
 KVQ_OK, KVQ_EINVAL, KVQ_ECAPACITY, KVQ_ESTATE, KVQ_EDEVICE, KVQ_ESCRATCH = 0, -1, -2, -3, -4, -5
 NOALLOC_SCRATCH_BYTES, NOALLOC_COUNTER_BYTES = 8 << 20, 64 << 10
 ATTN_AUTO, ATTN_VALU = 0, 1
+KV_LIMIT, Q_LIMIT = 4096.0, 2.0 ** 96
+DOMAIN_KV, DOMAIN_Q = 1, 2
 MODE_PATTERN, MODE_KVARN, MODE_NSN = 0, 1, 2
 F32, BF16 = 0, 1
 INDEX_NONE = 0xFF
@@ -24,7 +26,7 @@ VTILE = 32
 
 EXPORTS = ("kvq_layout_of", "kvq_cache_init", "kvq_init_patterns", "kvq_set_patterns",
            "kvq_encode_append", "kvq_attn_decode", "kvq_attn_decode_noalloc", "kvq_decode_step",
-           "kvq_dequant", "kvq_strerror",
+           "kvq_dequant", "kvq_cache_status", "kvq_strerror",
            "kvq_last_device_error")
 
 
@@ -45,7 +47,7 @@ class kvq_layout(C.Structure):
         "ws_bytes", "cnt_bytes", "total")] + [(n, C.c_int32) for n in (
         "token_cap", "n_groups", "record_bytes", "max_splits")] + [
         (n, C.c_uint64) for n in ("k_bsz", "k_tail", "bsz_bytes", "tail_bytes", "k_t2", "v_t2",
-                                  "t2_bytes")]
+                                  "t2_bytes", "status")]
 
 
 class kvq_cache(C.Structure):
@@ -86,6 +88,7 @@ def lib():
             "kvq_attn_decode_noalloc": (I, [C.POINTER(kvq_cache), P, P, C.c_float, P]),
             "kvq_decode_step": (I, [C.POINTER(kvq_cache), P, P, P, P, C.c_float, C.c_int32, P]),
             "kvq_dequant": (I, [C.POINTER(kvq_cache), I, I, I, P, P]),
+            "kvq_cache_status": (I, [C.POINTER(kvq_cache), C.POINTER(C.c_uint32), I, P]),
             "kvq_strerror": (C.c_char_p, [I]),
             "kvq_last_device_error": (I, []),
         }
@@ -139,6 +142,10 @@ def kvq_decode_step(cache, k_ptr, v_ptr, q_ptr, out_ptr, sm_scale, update_patter
 
 def kvq_dequant(cache, which, tok0, n, out_ptr, stream) -> int:
     return lib().kvq_dequant(C.byref(cache), which, tok0, n, out_ptr, stream)
+
+
+def kvq_cache_status(cache, flags_ref, clear, stream) -> int:
+    return lib().kvq_cache_status(C.byref(cache), flags_ref, clear, stream)
 
 
 def kvq_strerror(status: int) -> str:

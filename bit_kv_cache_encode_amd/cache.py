@@ -154,6 +154,14 @@ class KVCache:
                                              _stream(self.device)))
         return out
 
+    def status(self, clear: bool = True) -> int:
+        """Input-domain flags (DOMAIN_KV | DOMAIN_Q bits) set by the kernels
+        since init or the last clearing read; synchronises the stream."""
+        flags = C.c_uint32(0)
+        B.check("kvq_cache_status", B.kvq_cache_status(self.c, C.byref(flags), int(clear),
+                                                       _stream(self.device)))
+        return int(flags.value)
+
     # ------------------------------------------------------------- state
     @property
     def n_tokens(self) -> int:

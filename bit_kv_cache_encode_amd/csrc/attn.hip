@@ -63,7 +63,9 @@ __global__ void __launch_bounds__(AT_THREADS) attn_split_kernel(AttnArgs a) {
   // ---- prologue: scaled queries, per-group sums, q . M^K table
   for (int i = tid; i < a.gq * D; i += AT_THREADS) {
     int h = i / D, d = i % D;
-    sh.q[h][d] = load_in(a.q, ((int64_t)b * a.Hq + hq0 + h) * D + d, a.bf16);
+    const float qv = load_in(a.q, ((int64_t)b * a.Hq + hq0 + h) * D + d, a.bf16);
+    flag_domain(a.r.status, !(fabsf(qv) * a.qscale < KVQ_Q_LIMIT * 1.4426950408889634f), KVQ_DOMAIN_Q);
+    sh.q[h][d] = qv;
   }
   __syncthreads();
   if (nsn) {

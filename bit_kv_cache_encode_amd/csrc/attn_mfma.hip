@@ -265,13 +265,17 @@ attn_mfma_kernel(AttnArgs a) {
   // q goes to LDS before the first tile is issued: a wait for it then counts
   // only the loads after it (with the tile's loads behind a branch, the
   // count would fall back to waiting for every load)
+  bool q_bad = false;   // an element outside the query domain
 #pragma unroll
   for (int k = 0; k < QPT; ++k) {
     const int i = tid + k * MF_THREADS;
     const uint32_t bits = !a.bf16 ? qraw[k] : (i & 1) ? (qraw[k] & 0xFFFF0000u) : (qraw[k] << 16);
-    s_q[i] = i / D < gq ? __builtin_bit_cast(float, bits) : 0.0f;
+    const float qv = __builtin_bit_cast(float, bits);
+    q_bad |= !(fabsf(qv) * a.qscale < KVQ_Q_LIMIT * 1.4426950408889634f);
+    s_q[i] = i / D < gq ? qv : 0.0f;
     s_o[i] = 0.0f;
   }
+  flag_domain(a.r.status, q_bad, KVQ_DOMAIN_Q);
   if (stage_mv)
 #pragma unroll
     for (int k = 0; k < MVL; ++k) ((float4*)(mf_raw + Lo.mv))[tid + k * MF_THREADS] = mvl[k];

@@ -214,6 +214,13 @@ encode_lane_kernel(EncodeArgs a) {
         x[i] = v.x; x[i + 1] = v.y; x[i + 2] = v.z; x[i + 3] = v.w;
       }
     }
+    {
+      // input domain: the largest |x| bit pattern (NaN and inf included)
+      uint32_t mb = 0;
+#pragma unroll
+      for (int i = 0; i < D; ++i) mb = max(mb, __builtin_bit_cast(uint32_t, x[i]) & 0x7FFFFFFFu);
+      flag_domain(a.r.status, valid && mb >= __builtin_bit_cast(uint32_t, KVQ_KV_LIMIT), KVQ_DOMAIN_KV);
+    }
     // nearest pattern under d_mm, lowest index on ties (Eq 6)
     int kbest = KVQ_INDEX_NONE;
     float best = INFINITY;

@@ -212,6 +212,7 @@ __device__ __forceinline__ void encode_vector(const EncodeArgs& a, int kind, int
                                               uint32_t& w0, uint32_t& w1, int& kidx,
                                               uint32_t& t16) {
   const float* tab = a.r.tab[kind] + (a.mode == KVQ_MODE_PATTERN ? pat_unit(a.r, u) * a.max_pat * D : u * D);
+  flag_domain(a.r.status, kv_out_of_domain(x0) || kv_out_of_domain(x1), KVQ_DOMAIN_KV);
   kidx = KVQ_INDEX_NONE;
   t16 = 0;
   if (a.mode == KVQ_MODE_PATTERN) {

@@ -142,6 +142,7 @@ Regions regions_of(const kvq_cache* c, const kvq_layout& L) {
   r.kch = c->cfg.k_per_channel;
   r.kbsz = (uint32_t*)(base + L.k_bsz);
   r.ktail = (uint16_t*)(base + L.k_tail);
+  r.status = (uint32_t*)(base + L.status);
   return r;
 }
 
@@ -223,6 +224,7 @@ int kvq_layout_of(const kvq_config* cfg, kvq_layout* out) {
   L.t2_bytes = cfg->mode == KVQ_MODE_NSN ? U * tcap * 2 : 0;
   L.k_t2 = place(L.t2_bytes);
   L.v_t2 = place(L.t2_bytes);
+  L.status = place(256);
   L.total = off;
   *out = L;
   return KVQ_OK;
@@ -245,6 +247,7 @@ int kvq_cache_init(kvq_cache* cache, const kvq_config* cfg, void* base, uint64_t
   hipStream_t s = (hipStream_t)stream;
   Regions r = regions_of(cache, L);
   hipError_t ec = launch_fill((float*)r.cnt, 0.0f, (int64_t)(L.cnt_bytes / 4), s);
+  if (ec == hipSuccess) ec = launch_fill((float*)r.status, 0.0f, 1, s);
   if (ec != hipSuccess) return dev_fail(ec);
   if (cfg->mode == KVQ_MODE_PATTERN) {
     hipError_t e = launch_window_reset(r.win[0], r.win[1], (int)pattern_units(*cfg),
@@ -307,7 +310,8 @@ int kvq_init_patterns(kvq_cache* cache, const void* k, const void* v, int32_t n_
   Regions r = regions_of(cache, L);
   const int units = c.batch * c.n_kv_heads;
   const int bf16 = c.in_dtype == KVQ_BF16;
-  hipError_t e;
+  hipError_t e = launch_domain_check(k, v, (int64_t)units * n_tok * D, bf16, r.status, s);
+  if (e != hipSuccess) return dev_fail(e);
   if (pattern) {
     if (n_patterns > 0) {
       // shared tables: per kv-head over its prefixes in every sequence,
@@ -638,6 +642,20 @@ int kvq_dequant(const kvq_cache* cache, int32_t which, int32_t tok0, int32_t n, 
   a.n_closed = cache->n_tokens / KBLOCK * KBLOCK;
   hipError_t e = launch_dequant(a, c.batch * c.n_kv_heads, (hipStream_t)stream);
   if (e != hipSuccess) return dev_fail(e);
+  return KVQ_OK;
+}
+
+int kvq_cache_status(kvq_cache* cache, uint32_t* flags, int32_t clear, void* stream) {
+  kvq_layout L;
+  if (!cache || !cache->base || !flags || kvq_layout_of(&cache->cfg, &L) != KVQ_OK) return KVQ_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t* dev = (uint32_t*)((uint8_t*)cache->base + L.status);
+  uint32_t h = 0;
+  hipError_t e = hipMemcpyAsync(&h, dev, 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess && clear) e = launch_fill((float*)dev, 0.0f, 1, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return dev_fail(e);
+  *flags = h;
   return KVQ_OK;
 }
 

@@ -86,7 +86,15 @@ struct Regions {
   int kch;              // K quantized per channel over KVQ_KBLOCK-token blocks
   uint32_t* kbsz;       // kch: [U][tcap / KBLOCK][D] packed (s | z << 16)
   uint16_t* ktail;      // kch: [U][KBLOCK][D] binary16 residuals of the open block
+  uint32_t* status;     // sticky input-domain flags (KVQ_DOMAIN_*)
 };
+
+// Input domain: a lane that holds an offending element ORs its flag into the
+// cache's status word (a vector atomic, issued only on a violation).
+__device__ __forceinline__ bool kv_out_of_domain(float x) { return !(fabsf(x) < KVQ_KV_LIMIT); }
+__device__ __forceinline__ void flag_domain(uint32_t* status, bool bad, uint32_t bit) {
+  if (bad) __hip_atomic_fetch_or(status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 constexpr int KBLOCK = KVQ_KBLOCK;
 // K blocks per unit (token capacity rounded up to whole blocks)
@@ -165,6 +173,8 @@ struct KchArgs {
 // has read the buffer) the open block's residuals.
 hipError_t launch_kch_append(const KchArgs& a, int units, hipStream_t s);
 hipError_t launch_fill(float* p, float value, int64_t n, hipStream_t s);
+hipError_t launch_domain_check(const void* xk, const void* xv, int64_t n, int bf16, uint32_t* status,
+                               hipStream_t s);
 // (lo, hi) = (+inf, -inf) for `units` windows, as binary32 or (keys != 0) as
 // order keys
 hipError_t launch_window_reset(float* win_k, float* win_v, int units, int keys, hipStream_t s);

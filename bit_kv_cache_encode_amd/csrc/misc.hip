@@ -23,6 +23,27 @@ hipError_t launch_fill(float* p, float value, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Input-domain check of a pair of inputs (k and v, n elements each) for the
+// init calls, whose mining kernels read them several times: any element
+// outside |x| < KVQ_KV_LIMIT (or not finite) sets KVQ_DOMAIN_KV.
+__global__ void domain_check_kernel(const void* xk, const void* xv, int64_t n, int bf16,
+                                    uint32_t* status) {
+  bool bad = false;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    bad |= kv_out_of_domain(load_in(xk, i, bf16)) || kv_out_of_domain(load_in(xv, i, bf16));
+  flag_domain(status, bad, KVQ_DOMAIN_KV);
+}
+
+hipError_t launch_domain_check(const void* xk, const void* xv, int64_t n, int bf16, uint32_t* status,
+                               hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t want = (n + 255) / 256;
+  int blocks = (int)(want < 2048 ? want : 2048);
+  hipLaunchKernelGGL(domain_check_kernel, dim3(blocks), dim3(256), 0, s, xk, xv, n, bf16, status);
+  return hipGetLastError();
+}
+
 // Window state [U][2][D]: min row = +inf, max row = -inf.
 __global__ void window_reset_kernel(float* wk, float* wv, int units, int keys) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;

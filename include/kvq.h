@@ -17,7 +17,8 @@
  *    contiguous in the shapes stated.  Inputs are binary32 (KVQ_F32) or
  *    bfloat16 (KVQ_BF16) as the cache's in_dtype says; outputs are binary32.
  *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
- *    work on it and never synchronise or copy device data to the host.
+ *    work on it and never synchronise or copy device data to the host, with
+ *    one exception: kvq_cache_status, which exists to read a device word.
  *  - A cache must not be used from two streams or two threads at once.
  *  - The library never allocates device memory: the caller owns one device
  *    buffer per cache (kvq_layout_of().total bytes, 256-byte aligned) and
@@ -27,9 +28,13 @@
  *    multiple of n_kv_heads with at most 8 q-heads per kv-head, or at most 16
  *    where bits is 2 or 4 and group is 32 or 64 (served by the matrix-core
  *    attention).  shared_patterns and k_per_channel are PATTERN-mode options.
- *  - Domain: finite K/V inputs with |x| < 4096 and queries with
- *    |q| * sm_scale < 40.  Outside it results are unspecified (no error is
- *    raised; checking would need a device sync).
+ *  - Domain: finite K/V inputs with |x| < KVQ_KV_LIMIT (4096: binary16
+ *    scales of residuals stay below 2^13, which the attention's binary16
+ *    p * s operands assume) and finite queries with |q| * sm_scale <
+ *    KVQ_Q_LIMIT (2^96: scores stay finite in binary32).  Results computed
+ *    from inputs outside it are unspecified; the kernels that read an input
+ *    flag such elements in a sticky word in the cache buffer (no host sync),
+ *    which kvq_cache_status reads.
  *
  * Stored format (per (batch, kv-head) "unit", for K and for V alike unless
  * noted; T = token capacity, max_tokens rounded up to a multiple of 64):
@@ -89,6 +94,10 @@ extern "C" {
 #define KVQ_INDEX_NONE 0xFF
 #define KVQ_VTILE 32
 #define KVQ_KBLOCK 128      /* tokens per K block with k_per_channel */
+#define KVQ_KV_LIMIT 4096.0f        /* K/V domain: |x| < KVQ_KV_LIMIT */
+#define KVQ_Q_LIMIT 0x1p96f         /* query domain: |q| * sm_scale < KVQ_Q_LIMIT */
+#define KVQ_DOMAIN_KV 1u    /* status bit: a K/V input element outside its domain */
+#define KVQ_DOMAIN_Q 2u     /* status bit: a query element outside its domain */
 
 typedef struct {
   int32_t batch;          /* B */
@@ -135,6 +144,8 @@ typedef struct {
   uint64_t bsz_bytes, tail_bytes;   /* 0 without k_per_channel */
   uint64_t k_t2, v_t2;    /* NSN: binary16 second norm n2 [U][token_cap] */
   uint64_t t2_bytes;      /* 0 outside NSN mode */
+  uint64_t status;        /* uint32 domain flags (KVQ_DOMAIN_*), sticky; 256 bytes
+                             reserved, after every other region */
 } kvq_layout;
 
 typedef struct {
@@ -274,6 +285,19 @@ int kvq_decode_step(kvq_cache* cache, const void* k_new, const void* v_new, cons
  * KVQ_EINVAL on a bad `which` or a span outside [0, n_tokens). */
 int kvq_dequant(const kvq_cache* cache, int32_t which, int32_t tok0, int32_t n, float* out,
                 void* stream);
+
+/* Input-domain flags of the cache: *flags receives the KVQ_DOMAIN_* bits set
+ * since kvq_cache_init or the last clearing read.  KVQ_DOMAIN_KV: an element
+ * of k / v given to kvq_encode_append, kvq_decode_step or kvq_init_patterns
+ * was not finite or had |x| >= KVQ_KV_LIMIT.  KVQ_DOMAIN_Q: an element of a
+ * query given to an attention call was not finite or had |q| * sm_scale >=
+ * KVQ_Q_LIMIT.  The flags are set by the kernels that read the inputs (an
+ * atomic OR by each offending lane, nothing on the normal path), so work
+ * enqueued before this call is covered.  clear != 0 resets the word after
+ * the read.  This call synchronises `stream` (it copies the word to the
+ * host) and therefore cannot be captured in a graph.  KVQ_EINVAL on a null
+ * cache or flags. */
+int kvq_cache_status(kvq_cache* cache, uint32_t* flags, int32_t clear, void* stream);
 
 /* Message for a status code (static storage). */
 const char* kvq_strerror(int status);

@@ -37,11 +37,12 @@ def test_struct_layout_matches_c(tmp_path):
 #include <stddef.h>
 #include "{HEADER}"
 int main(void) {{
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(kvq_config),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(kvq_config),
          sizeof(kvq_layout), sizeof(kvq_cache), offsetof(kvq_cache, base),
          offsetof(kvq_cache, rho), offsetof(kvq_layout, total), offsetof(kvq_config, max_splits),
          offsetof(kvq_config, shared_patterns), offsetof(kvq_config, k_per_channel),
-         offsetof(kvq_layout, k_bsz), offsetof(kvq_layout, tail_bytes));
+         offsetof(kvq_layout, k_bsz), offsetof(kvq_layout, tail_bytes),
+         offsetof(kvq_layout, status));
   return 0;
 }}''')
     exe = tmp_path / "probe"
@@ -52,7 +53,7 @@ int main(void) {{
             B.kvq_cache.base.offset, B.kvq_cache.rho.offset, B.kvq_layout.total.offset,
             B.kvq_config.max_splits.offset, B.kvq_config.shared_patterns.offset,
             B.kvq_config.k_per_channel.offset, B.kvq_layout.k_bsz.offset,
-            B.kvq_layout.tail_bytes.offset]
+            B.kvq_layout.tail_bytes.offset, B.kvq_layout.status.offset]
     assert got == want
 
 
@@ -96,6 +97,10 @@ def test_layout_regions():
     assert L1.codes_bytes == U * T * 16 and L1.n_groups == 16
     L0 = B.kvq_layout_of(_cfg(max_tokens=4000))
     assert all(getattr(Lc, n) == getattr(L0, n) for n in ("k_codes", "v_codes", "k_sz", "ws", "cnt"))
+    # the domain-flag word comes last in every mode
+    for Lx in (L, Lk, L4, Ls, Lc, Ln, L1):
+        assert Lx.status % 256 == 0 and Lx.status + 4 <= Lx.total
+        assert Lx.status >= max(Lx.v_t2 + Lx.t2_bytes, Lx.k_tail + Lx.tail_bytes, Lx.cnt + Lx.cnt_bytes)
 
 
 @pytest.mark.parametrize("bad", [
@@ -159,6 +164,11 @@ def test_error_paths_fail_before_launch():
                               None) == B.KVQ_EINVAL
     for s in (0, -1, -2, -3, -4, -5, -99):
         assert B.kvq_strerror(s)
+    flags = C.c_uint32(7)
+    assert lib.kvq_cache_status(None, C.byref(flags), 1, None) == B.KVQ_EINVAL
+    assert lib.kvq_cache_status(C.byref(c), None, 1, None) == B.KVQ_EINVAL
+    assert lib.kvq_cache_status(C.byref(B.kvq_cache()), C.byref(flags), 1, None) == B.KVQ_EINVAL
+    assert flags.value == 7                                     # untouched on failure
 
 
 def test_noalloc_error_paths_fail_before_launch():
