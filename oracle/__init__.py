@@ -173,8 +173,10 @@ class RefCache:
         self.nblk = (self.tcap + KBLOCK - 1) // KBLOCK
 
     def __del__(self):
+        # at interpreter exit the module globals may already be gone; the
+        # process then releases the memory anyway
         h = getattr(self, "_h", None)
-        if h:
+        if h and lib is not None:
             lib().kvqref_free(h)
             self._h = None
 
