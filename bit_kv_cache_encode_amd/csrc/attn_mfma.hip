@@ -17,7 +17,7 @@
 //  V pattern mass  w_j = sum_t p_t [k*_t = j]  is a third product: rows =
 //       (head, part) with part 0/1 = binary16 hi/lo of p, columns = 16
 //       patterns, reduction = 32 tokens, B = the one-hot matrix of the
-//       tokens' pattern indices.  For more than 64 patterns it falls back to
+//       tokens' pattern indices.  For more than 80 patterns it falls back to
 //       LDS atomics.
 //
 // Codes enter the MFMA as binary16 subnormals: a 2-bit (4-bit) field masked
@@ -380,7 +380,7 @@ attn_mfma_kernel(AttnArgs a) {
   // q' . M^K_j: four threads per pattern j (32 channels each), all heads;
   // patterns beyond the first MF_THREADS / 4 take further passes
   if (!KVARN && n_pat > 0) {
-    // with the one-hot path (at most 64 patterns) one pass covers the table
+    // with the one-hot path (at most 80 patterns) one pass covers the table
     const int passes = NPB > 0 ? 1 : (n_pat + MF_THREADS / 4 - 1) / (MF_THREADS / 4);
     for (int pass = 0; pass < passes; ++pass) {
       const int j0 = pass * (MF_THREADS / 4);
@@ -1229,6 +1229,8 @@ static hipError_t launch_pattern(const AttnArgs& a, hipStream_t s) {
   if (a.n_pat <= 16) return launch_one<BITS, NG, NGS, false, 1, QLO>(a, s);
   if (a.n_pat <= 32) return launch_one<BITS, NG, NGS, false, 2, QLO>(a, s);
   if (a.n_pat <= 64) return launch_one<BITS, NG, NGS, false, 4, QLO>(a, s);
+  // 64 prefill patterns plus up to 16 Chebyshev-window centres
+  if (a.n_pat <= 80) return launch_one<BITS, NG, NGS, false, 5, QLO>(a, s);
   return launch_one<BITS, NG, NGS, false, 0, QLO>(a, s);
 }
 
@@ -1239,6 +1241,7 @@ static hipError_t launch_kch(const AttnArgs& a, hipStream_t s) {
   if (a.n_pat <= 16) return launch_one<BITS, NG, NGS, false, 1, true, true>(a, s);
   if (a.n_pat <= 32) return launch_one<BITS, NG, NGS, false, 2, true, true>(a, s);
   if (a.n_pat <= 64) return launch_one<BITS, NG, NGS, false, 4, true, true>(a, s);
+  if (a.n_pat <= 80) return launch_one<BITS, NG, NGS, false, 5, true, true>(a, s);
   return launch_one<BITS, NG, NGS, false, 0, true, true>(a, s);
 }
 

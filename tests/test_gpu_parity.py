@@ -72,7 +72,13 @@ def test_llama_shape_encode_attend(T):
 
 
 @pytest.mark.parametrize("bits,group,gq,npat", [(4, 64, 4, 64), (2, 32, 7, 64), (2, 64, 1, 16),
-                                                 (4, 32, 2, 0), (2, 128, 8, 255)])
+                                                 (4, 32, 2, 0), (2, 128, 8, 255),
+                                                 # one-hot pattern mass over five blocks of 16
+                                                 # (64 prefill patterns plus window centres;
+                                                 # 4-bit at 80 also leaves M^V unstaged), then
+                                                 # the first count past it (LDS atomics)
+                                                 (2, 32, 4, 72), (2, 32, 7, 66), (4, 64, 4, 80),
+                                                 (2, 32, 4, 81)])
 def test_shape_variants(bits, group, gq, npat):
     B, H, T = 1, 2, 333
     gpu, ref, dt = make_pair(B, gq * H, H, 400, bits=bits, group=group, max_patterns=max(npat, 1))
