@@ -657,20 +657,25 @@ attn_mfma_kernel(AttnArgs a) {
           for (int q = 0; q < KW; ++q) kw[q] = w[q];
         }
       };
-      uint32_t kw[4][KW];
+      // two column blocks at a time: their K words (2 KW dwords) are live
+      // through the chunk loop, and the two accumulator chains alternate
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        load_kw(nb, kw[nb]);
-        C[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      }
+      for (int np = 0; np < 4; np += 2) {
+        uint32_t kw[2][KW];
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const u32x4 B = unpack_k<BITS>(kw[nb], c);
-          C[nb] = mfma16(aq_hi[c], B, C[nb]);
-          if constexpr (QLO) C[nb] = mfma16(aq_lo[QLO ? c : 0], B, C[nb]);
+        for (int e = 0; e < 2; ++e) {
+          load_kw(np + e, kw[e]);
+          C[np + e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const u32x4 B = unpack_k<BITS>(kw[e], c);
+            C[np + e] = mfma16(aq_hi[c], B, C[np + e]);
+            if constexpr (QLO) C[np + e] = mfma16(aq_lo[QLO ? c : 0], B, C[np + e]);
+          }
+      }
     }
     float sc[4][SPL];
 #pragma unroll
