@@ -182,6 +182,10 @@ attn_mfma_kernel(AttnArgs a) {
   const uint8_t* vt2_src = (const uint8_t*)(a.r.t2[1] + (int64_t)u * a.tcap);
 
   // ---------------------------------------------------------------- tile copy
+  // K and V (s, z) words of a tile take 16-byte pieces P_KS and P_VS; where
+  // both fit one 64-lane pass (groups of 64 channels) they share registers
+  constexpr int P_VS = TILE * NGS * 4 / 16;
+  constexpr bool SZ_PAIR = !KCH && TS::P_KS + P_VS <= 64;
   u32x4 rkc[TS::R_KC], rvc[TS::R_VC], rks, rvs, rix;
   auto issue = [&](int tile) {
     const u32x4* kc = (const u32x4*)(kcodes + (int64_t)tile * TS::KREC);
@@ -190,13 +194,19 @@ attn_mfma_kernel(AttnArgs a) {
     for (int r = 0; r < TS::R_KC; ++r) rkc[r] = kc[lane + 64 * r];
 #pragma unroll
     for (int r = 0; r < TS::R_VC; ++r) rvc[r] = vc[lane + 64 * r];
-    if (lane < TS::P_KS) {
-      // K per channel: the words of the tile's block (a tile never straddles
-      // a block); those of an open block are not read
-      rks = KCH ? ((const u32x4*)(a.r.kbsz + ((int64_t)u * kch_blocks(a.tcap) + tile / KBLOCK) * D))[lane]
-                : ((const u32x4*)(ksz + (int64_t)tile * NGS * 4))[lane];
+    if constexpr (SZ_PAIR) {
+      // K scales in lanes [0, P_KS), V scales in the lanes after them
+      if (lane < TS::P_KS) rks = ((const u32x4*)(ksz + (int64_t)tile * NGS * 4))[lane];
+      else if (lane < TS::P_KS + P_VS) rks = ((const u32x4*)(vsz + (int64_t)tile * NGS * 4))[lane - TS::P_KS];
+    } else {
+      if (lane < TS::P_KS) {
+        // K per channel: the words of the tile's block (a tile never straddles
+        // a block); those of an open block are not read
+        rks = KCH ? ((const u32x4*)(a.r.kbsz + ((int64_t)u * kch_blocks(a.tcap) + tile / KBLOCK) * D))[lane]
+                  : ((const u32x4*)(ksz + (int64_t)tile * NGS * 4))[lane];
+      }
+      if (lane < P_VS) rvs = ((const u32x4*)(vsz + (int64_t)tile * NGS * 4))[lane];
     }
-    if (lane < TILE * NGS * 4 / 16) rvs = ((const u32x4*)(vsz + (int64_t)tile * NGS * 4))[lane];
     const int ix_bytes = KVARN ? 2 : 1;
     if (NSNM) {
       // [K t16 | K t2 | V t16 | V t2], 8 pieces each (one fixed source per
@@ -219,8 +229,13 @@ attn_mfma_kernel(AttnArgs a) {
     for (int r = 0; r < TS::R_KC; ++r) t4[TS::O_KC / 16 + kpiece<BITS>(lane + 64 * r)] = rkc[r];
 #pragma unroll
     for (int r = 0; r < TS::R_VC; ++r) t4[TS::O_VC / 16 + vpiece(lane + 64 * r)] = rvc[r];
-    if (lane < TS::P_KS) t4[TS::O_KS / 16 + lane] = rks;
-    if (lane < TILE * NGS * 4 / 16) t4[TS::O_VS / 16 + lane] = rvs;
+    if constexpr (SZ_PAIR) {
+      if (lane < TS::P_KS) t4[TS::O_KS / 16 + lane] = rks;
+      else if (lane < TS::P_KS + P_VS) t4[TS::O_VS / 16 + lane - TS::P_KS] = rks;
+    } else {
+      if (lane < TS::P_KS) t4[TS::O_KS / 16 + lane] = rks;
+      if (lane < P_VS) t4[TS::O_VS / 16 + lane] = rvs;
+    }
     if (lane < 2 * TS::P_IX) t4[TS::O_KI / 16 + lane] = rix;
   };
 
