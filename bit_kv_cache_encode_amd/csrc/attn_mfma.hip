@@ -388,8 +388,13 @@ attn_mfma_kernel(AttnArgs a) {
     const int h = tid >> 5, c0 = (tid & 31) * 4;
     float s = 0.0f;
     if (h < HB) s = (s_q[h * D + c0] + s_q[h * D + c0 + 1]) + (s_q[h * D + c0 + 2] + s_q[h * D + c0 + 3]);
-#pragma unroll
-    for (int o = 1; o < G / 4; o <<= 1) s += __shfl_xor(s, o, 64);
+    // sum over the G / 4 (8 or 16) aligned lanes of a group: DPP quad swaps,
+    // then the half-row and row mirrors
+    static_assert(G / 4 == 8 || G / 4 == 16, "groups of 32 or 64 channels");
+    s += dpp_f<0xB1>(s);
+    s += dpp_f<0x4E>(s);
+    s += dpp_f<0x141>(s);
+    if (G / 4 == 16) s += dpp_f<0x140>(s);
     if (h < HB && ((tid & 31) % (G / 4)) == 0) s_qsum[h * NG + c0 / G] = s * a.qscale;
   }
   // q' . M^K_j: four threads per pattern j (32 channels each), all heads;
@@ -409,20 +414,28 @@ attn_mfma_kernel(AttnArgs a) {
           for (int k = 0; k < 8; ++k) mkr[k] = m4[k];
         }
       }
+      // a wave holds patterns j0 + 16 wave .. + 15: waves past the table skip
+      // the pass (a wave64 FMA takes its SIMD four cycles, live rows or not).
+      // Every head row (rows of heads >= gq are zero and not stored), so the
+      // heads' LDS reads and FMAs interleave; two FMA chains per dot, then
+      // the four threads of a pattern sum with DPP quad swaps
+      if (j0 + 16 * wave >= n_pat) continue;
 #pragma unroll
       for (int h = 0; h < HB; ++h) {
-        if (h >= gq) break;
-        const float* qh = s_q + h * D + qm_part * 32;
-        float sdot = 0.0f;
+        const float4* qh = (const float4*)(s_q + h * D + qm_part * 32);
+        float sd[2] = {0.0f, 0.0f};
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          sdot = __builtin_fmaf(qh[4 * k], mkr[k].x, sdot);
-          sdot = __builtin_fmaf(qh[4 * k + 1], mkr[k].y, sdot);
-          sdot = __builtin_fmaf(qh[4 * k + 2], mkr[k].z, sdot);
-          sdot = __builtin_fmaf(qh[4 * k + 3], mkr[k].w, sdot);
+          const float4 qv = qh[k];
+          float& acc = sd[k & 1];
+          acc = __builtin_fmaf(qv.x, mkr[k].x, acc);
+          acc = __builtin_fmaf(qv.y, mkr[k].y, acc);
+          acc = __builtin_fmaf(qv.z, mkr[k].z, acc);
+          acc = __builtin_fmaf(qv.w, mkr[k].w, acc);
         }
-        sdot += __shfl_xor(sdot, 1, 64);
-        sdot += __shfl_xor(sdot, 2, 64);
+        float sdot = sd[0] + sd[1];
+        sdot += dpp_f<0xB1>(sdot);
+        sdot += dpp_f<0x4E>(sdot);
         if (qm_part == 0 && jj < n_pat) s_qm[h * 256 + jj] = sdot * a.qscale;
       }
     }
