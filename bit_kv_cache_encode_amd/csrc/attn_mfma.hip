@@ -1286,6 +1286,13 @@ static hipError_t launch_bits_group(const AttnArgs& a, hipStream_t s) {
   return a.bf16 ? launch_pattern<BITS, NG, NGS, false>(a, s) : launch_pattern<BITS, NG, NGS, true>(a, s);
 }
 
+// q-head blocks per unit: 4 heads per row block, 8 at G = 64 beyond 4 q-heads
+// per kv-head (the row layouts the launch below picks)
+int mfma_head_blocks(int group, int gq) {
+  const int hb = (group == 64 && gq > 4) ? 8 : 4;
+  return (gq + hb - 1) / hb;
+}
+
 bool mfma_attention_supported(int bits, int group, int gq) {
   if (bits != 2 && bits != 4) return false;
   // q-heads beyond one row block (4 at G = 32, 8 at G = 64) take further

@@ -453,10 +453,13 @@ static AttnKernel attn_setup(const kvq_cache* cache, const kvq_layout& L, const 
   const bool valu_ok = a.gq <= MAX_GQ;
   const AttnKernel k = (!mfma_ok || (valu_ok && cache->attn_kernel == KVQ_ATTN_VALU)) ? ATTN_VALU
                                                                                      : ATTN_MFMA;
-  // one 8-wave MFMA block per compute unit
+  // one 8-wave MFMA block per compute unit; the MFMA kernel's blocks are
+  // (unit, q-head block, split), so a unit with several q-head blocks takes
+  // fewer splits (one round of blocks, fewer partials to combine)
   int target = k == ATTN_VALU ? ATTN_TARGET_BLOCKS : 256;
   if (cache->attn_blocks > 0) target = cache->attn_blocks;
-  int want = (target + units - 1) / units;
+  const int per_split = units * (k == ATTN_MFMA ? mfma_head_blocks(c.group, a.gq) : 1);
+  int want = (target + per_split - 1) / per_split;
   if (want > L.max_splits - reserve) want = L.max_splits - reserve;
   if (want < 1) want = 1;
   // split 0 is `lead` tokens shorter (at least one chunk unit long)

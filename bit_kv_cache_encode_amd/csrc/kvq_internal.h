@@ -186,6 +186,7 @@ hipError_t launch_dequant(const DequantArgs& a, int units, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_combine(const AttnArgs& a, hipStream_t s);
 bool mfma_attention_supported(int bits, int group, int gq);
+int mfma_head_blocks(int group, int gq);
 hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t s);
 // k-means per (unit, kind) over `groups` * n_tok rows: row i of unit u is
 // input row (i / n_tok) * group_stride + u * n_tok + i % n_tok.
