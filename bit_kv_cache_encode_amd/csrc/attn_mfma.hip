@@ -550,7 +550,7 @@ attn_mfma_kernel(AttnArgs a) {
     const float x0 = load_in(e.src[kind], uu * D + lane, e.bf16);
     const float x1 = load_in(e.src[kind], uu * D + lane + 64, e.bf16);
     float wl0 = 0.0f, wl1 = 0.0f, wh0 = 0.0f, wh1 = 0.0f;
-    if (e.win_update && !e.r.pat_h) {
+    if (e.win_update && !e.r.pat_h && hb == 0) {
       const float* win = e.r.win[kind] + uu * 2 * D;
       wl0 = win[lane]; wl1 = win[lane + 64];
       wh0 = win[D + lane]; wh1 = win[D + lane + 64];
@@ -560,7 +560,11 @@ attn_mfma_kernel(AttnArgs a) {
     uint32_t t16;
     float* sx = (float*)tb;   // this wave's tile buffer is idle until its first tile
     encode_vector<true>(e, kind, uu, x0, x1, lane, sx, nullptr, uu, c0, c1, w0, w1, kidx, t16);
-    token_append(e, kind, uu, e.t0, lane, x0, x1, wl0, wl1, wh0, wh1, c0, c1, w0, w1, kidx, t16);
+    // with several q-head blocks per unit, each block of split 0 appends the
+    // token (the same bytes) for its own heads' partials; the first owns the
+    // window's read-modify-write and closure
+    token_append(e, kind, uu, e.t0, lane, x0, x1, wl0, wl1, wh0, wh1, c0, c1, w0, w1, kidx, t16,
+                 hb == 0);
     float m0 = 0.0f, m1 = 0.0f;
     if (kidx != KVQ_INDEX_NONE) {
       const float* mrow = e.r.tab[kind] + (pat_unit(e.r, uu) * e.max_pat + kidx) * D;

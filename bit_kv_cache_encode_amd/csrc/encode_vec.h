@@ -370,10 +370,13 @@ __device__ __forceinline__ void store_token(const EncodeArgs& a, int kind, int64
 // Chebyshev window update (Eq 5) with the window's (lo, hi) state as loaded.
 // A batch-shared window is folded into with atomic min / max of order keys
 // instead; its closure is a separate launch once every unit has folded in.
+// own_window: this caller updates (and closes) the Chebyshev window; another
+// caller appending the same token (identical record writes) leaves it alone
 __device__ __forceinline__ void token_append(const EncodeArgs& a, int kind, int64_t u, int t,
                                              int lane, float x0, float x1, float wl0, float wl1,
                                              float wh0, float wh1, uint32_t c0, uint32_t c1,
-                                             uint32_t w0, uint32_t w1, int kidx, uint32_t t16) {
+                                             uint32_t w0, uint32_t w1, int kidx, uint32_t t16,
+                                             bool own_window = true) {
   float* win = a.r.win[kind] + pat_unit(a.r, u) * 2 * D;
   store_token(a, kind, u, t, lane, c0, c1, w0, w1, kidx, t16);
   if (kind == 1) {
@@ -391,13 +394,13 @@ __device__ __forceinline__ void token_append(const EncodeArgs& a, int kind, int6
       if (c1) atomicOr(&tile_out[wi * D + lane + 64], c1 << bit);
     }
   }
-  if (a.win_update && a.r.pat_h) {
+  if (a.win_update && own_window && a.r.pat_h) {
     int* wk = (int*)win;
     atomicMin(&wk[lane], f32_order_key(x0));
     atomicMin(&wk[lane + 64], f32_order_key(x1));
     atomicMax(&wk[D + lane], f32_order_key(x0));
     atomicMax(&wk[D + lane + 64], f32_order_key(x1));
-  } else if (a.win_update) {
+  } else if (a.win_update && own_window) {
     // Chebyshev window (Eq 5) over this token
     const float lo0 = fminf(wl0, x0), lo1 = fminf(wl1, x1);
     const float hi0 = fmaxf(wh0, x0), hi1 = fmaxf(wh1, x1);

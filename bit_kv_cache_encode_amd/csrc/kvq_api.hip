@@ -565,11 +565,10 @@ int kvq_decode_step(kvq_cache* cache, const void* k_new, const void* v_new, cons
                            ? attn_setup(cache, L, q, out, sm_scale, cache->n_tokens, 1, a)
                            : ATTN_VALU;
   // The fused launch covers the MFMA kernel (PatternKV and KVarN modes) with
-  // a non-empty cache and one q-head block per unit; anything else is the two
-  // calls in sequence.
+  // a non-empty cache; anything else is the two calls in sequence.
   // K per channel: a token that completes its block needs the block kernel
   const bool kch_close = c.k_per_channel && (cache->n_tokens + 1) % KBLOCK == 0;
-  if (k != ATTN_MFMA || a.gq > 16 / (D / c.group) || kch_close || c.mode == KVQ_MODE_NSN) {
+  if (k != ATTN_MFMA || kch_close || c.mode == KVQ_MODE_NSN) {
     int st = kvq_encode_append(cache, k_new, v_new, 1, update_patterns, stream);
     if (st != KVQ_OK) return st;
     return kvq_attn_decode(cache, q, out, sm_scale, stream);

@@ -118,10 +118,21 @@ def test_decode_step_group64_gqa4():
     _run(2, 8, 2, 350, 8, group=64, P=20, W=4, seed_off=11)
 
 
-def test_decode_step_gqa7_two_calls():
-    """7 q-heads per kv-head at group 32 (two q-head blocks) takes the
-    two-call path; results as the separate calls."""
-    _run(2, 14, 2, 400, 6, P=20, W=4, seed_off=9)
+@pytest.mark.parametrize("Hq,group,blocks", [(14, 32, None), (14, 32, 4096), (24, 64, None),
+                                             (32, 32, 40)])
+def test_decode_step_several_head_blocks(Hq, group, blocks):
+    """More q-heads per kv-head than one MFMA row block holds (7 and 16 at
+    group 32, 12 at group 64): every q-head block of split 0 appends the new
+    token (the same bytes) for its own heads' partials and the first alone
+    updates and closes the Chebyshev window; results and cache bytes equal
+    the separate calls over window closures, from one split per unit to
+    many."""
+    _run(2, Hq, 2, 400, 6, group=group, P=20, W=4, blocks=blocks, seed_off=9)
+
+
+def test_decode_step_kvarn_head_blocks():
+    """KVarN mode with two q-head blocks per unit in one launch."""
+    _run(2, 12, 2, 300, 6, mode="kvarn", P=0, W=0, seed_off=13)
 
 
 @pytest.mark.parametrize("group,bf16", [(32, True), (64, False)])
