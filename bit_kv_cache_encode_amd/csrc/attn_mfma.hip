@@ -24,10 +24,11 @@
 // in place (K) or rotated near the top of the mantissa first (V) is the
 // integer code times 2^-24 times a power of two fixed by its position; the
 // other operand carries the inverse power, so unpacking a pair of codes is
-// one AND (plus a rotate per V word).  p*s
-// is split into binary16 hi + lo parts (two MFMAs), so products keep about 22
-// bits; q is one binary16 operand when it comes in bfloat16 (exact, see the
-// exponent choice) and hi + lo otherwise; accumulation is fp32.
+// one AND (plus a rotate per V word).  p*s is one binary16 operand in
+// PatternKV mode and binary16 hi + lo parts (two MFMAs, about 22 bits) in the
+// rotated modes, where the V sums cancel against the zero-point sums; q is one
+// binary16 operand when it comes in bfloat16 (exact, see the exponent choice)
+// and hi + lo otherwise; accumulation is fp32.
 #include <type_traits>
 
 #include "attn_mfma_common.h"

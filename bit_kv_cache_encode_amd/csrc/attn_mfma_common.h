@@ -14,7 +14,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int TILE = 64;         // tokens per wave iteration (4 QK column blocks, 2 V tiles)
-constexpr int EQ = 10;           // q operand carries 2^EQ (paired kernel)
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a),

@@ -263,14 +263,15 @@ int kvq_attn_decode_noalloc(kvq_cache* cache, const void* q, float* out, float s
  * [B][Hkv][1][D], encoded exactly as kvq_encode_append with n_new = 1) and
  * attend with q over all n_tokens + 1 tokens (as kvq_attn_decode after the
  * append).  The new token's own attention term is computed from its freshly
- * dequantized K and V by the block that encodes it, while the other blocks
- * attend over the earlier tokens; the split-K combine merges both (the
- * decode-stage fusion of PatternKV section 3.4 extended to the append).
- * Cache contents afterwards are identical to the two separate calls; `out`
- * agrees with them to floating-point rounding.  Falls back to the two calls
- * in sequence where the fused launch does not apply (an empty cache, more
- * q-heads per kv-head than one MFMA row block, shapes served by the VALU
- * kernel, NSN mode, a k_per_channel token that completes its block).
+ * dequantized K and V by the block that encodes it (each q-head block of the
+ * unit where one MFMA row block holds fewer q-heads than the unit has), while
+ * the other blocks attend over the earlier tokens; the split-K combine merges
+ * both (the decode-stage fusion of PatternKV section 3.4 extended to the
+ * append).  Cache contents afterwards are identical to the two separate
+ * calls; `out` agrees with them to floating-point rounding.  Falls back to
+ * the two calls in sequence where the fused launch does not apply (an empty
+ * cache, shapes served by the VALU kernel, NSN mode, a k_per_channel token
+ * that completes its block).
  * Errors as kvq_encode_append (n_new = 1) and kvq_attn_decode; nothing is
  * written when a check fails. */
 int kvq_decode_step(kvq_cache* cache, const void* k_new, const void* v_new, const void* q,
