@@ -72,11 +72,11 @@ def attn_config(name):
     del k, v
     q = synth.device_queries(B, Hq, D, device=dev)
     out = torch.empty((B, Hq, D), device=dev)
-    for _ in range(3):
+    for _ in range(10):
         cache.attn_decode(q, out=out)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n = 10
+    n = 50
     e0.record()
     for _ in range(n):
         cache.attn_decode(q, out=out)

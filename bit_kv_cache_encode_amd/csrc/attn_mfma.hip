@@ -265,19 +265,6 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) mkr[k] = m4[k];
   }
-  // M^V rows for the pattern term, staged in LDS with q (same round trip),
-  // so that the merge after the loop reads no global memory
-  constexpr int MVL = NPB > 0 ? 16 * NPB * D / 4 / MF_THREADS : 1;   // float4 per thread
-  float4 mvl[MVL];
-  const bool stage_mv = NPB > 0 && Lo.mv_rows > 0;
-  if (stage_mv) {
-    const float4* mv4 = (const float4*)(a.r.tab[1] + pat_unit(a.r, u) * a.max_pat * D);
-#pragma unroll
-    for (int k = 0; k < MVL; ++k) {
-      const int c = tid + k * MF_THREADS;    // float4 index over rows < 16 NPB
-      mvl[k] = c < n_pat * (D / 4) ? mv4[c] : float4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-  }
   // q goes to LDS before the first tile is issued: a wait for it then counts
   // only the loads after it (with the tile's loads behind a branch, the
   // count would fall back to waiting for every load)
@@ -292,9 +279,6 @@ attn_mfma_kernel(AttnArgs a) {
     s_o[i] = 0.0f;
   }
   flag_domain(a.r.status, q_bad, KVQ_DOMAIN_Q);
-  if (stage_mv)
-#pragma unroll
-    for (int k = 0; k < MVL; ++k) ((float4*)(mf_raw + Lo.mv))[tid + k * MF_THREADS] = mvl[k];
   const int n_tiles = (t_end - t_begin + TILE - 1) / TILE;
   // in the fused step waves 0 and 1 of split 0 encode the new token first and
   // take their tiles from the counter afterwards
@@ -303,6 +287,20 @@ attn_mfma_kernel(AttnArgs a) {
   const int first = !fuse_here ? (KCH ? 2 * wave : wave)
                                 : (wave < 2 ? n_tiles : (KCH ? 2 * (wave - 2) : wave - 2));
   if (first < n_tiles) issue(t_begin + TILE * first);
+  // M^V rows for the pattern term go to LDS before the loop, so that the
+  // merge after it reads no global memory.  They are loaded after the first
+  // tile: the prologue's first round trip then carries only q and M^K.
+  constexpr int MVL = NPB > 0 ? 16 * NPB * D / 4 / MF_THREADS : 1;   // float4 per thread
+  float4 mvl[MVL];
+  const bool stage_mv = NPB > 0 && Lo.mv_rows > 0;
+  if (stage_mv) {
+    const float4* mv4 = (const float4*)(a.r.tab[1] + pat_unit(a.r, u) * a.max_pat * D);
+#pragma unroll
+    for (int k = 0; k < MVL; ++k) {
+      const int c = tid + k * MF_THREADS;    // float4 index over rows < 16 NPB
+      mvl[k] = c < n_pat * (D / 4) ? mv4[c] : float4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  }
 
   // ---------------------------------------------------------------- prologue
   for (int i = tid; i < MF_WAVES * HB * npat; i += MF_THREADS) s_w[i] = 0.0f;
@@ -534,6 +532,10 @@ attn_mfma_kernel(AttnArgs a) {
   // claims its next one from the block counter while the current one is
   // computed, so the waves of the block finish together whatever their
   // issue priority.
+  // (the wait for these rows falls with the wait for the first tile)
+  if (stage_mv)
+#pragma unroll
+    for (int k = 0; k < MVL; ++k) ((float4*)(mf_raw + Lo.mv))[tid + k * MF_THREADS] = mvl[k];
   int cur = first;
   // K per channel: block whose q * s operand and z sums are in registers
   int kch_built = -1;
