@@ -347,16 +347,15 @@ attn_mfma_kernel(AttnArgs a) {
       __syncthreads();
     }
   }
-  {
+  if constexpr (KVARN) {
     const float isd = (float)(1.0 / __builtin_sqrt(128.0));
     const float* ck = a.r.tab[0] + (int64_t)u * D;
     for (int i = tid; i < HB * D; i += MF_THREADS) {
-      float v = s_q[i];
-      if (KVARN) v = NSNM ? v * isd : v * isd * ck[i % D];
-      s_q[i] = v;
+      const float v = s_q[i];
+      s_q[i] = NSNM ? v * isd : v * isd * ck[i % D];
     }
+    __syncthreads();
   }
-  __syncthreads();
   // Per-head binary exponent e_h that puts max_d |q_hd| 2^e_h in [2^14, 2^15).
   // The QK A operand is q 2^(e_h - shift) in binary16 (shift <= 6): a
   // bfloat16 q (8 significant bits) is exact there except for elements below
@@ -789,24 +788,26 @@ attn_mfma_kernel(AttnArgs a) {
       }
     }
 
-    // ---- online softmax (log2 domain); rescale only when a max grows
-    float mnew[SPL];
+    // ---- online softmax (log2 domain); rescale only when a max grows.  A
+    // max grows exactly when one of its lanes holds a larger score, so a
+    // vote over the lanes' own maxima decides, and the row maxima are
+    // reduced across lanes only then
+    float lmax[SPL];
     bool grow = false;
 #pragma unroll
     for (int s = 0; s < SPL; ++s) {
-      float mt = fmaxf(fmaxf(sc[0][s], sc[1][s]), fmaxf(sc[2][s], sc[3][s]));
-      mt = row_max16(mt);
-      mnew[s] = fmaxf(m_run[s], mt);
-      grow |= mnew[s] > m_run[s];
+      lmax[s] = fmaxf(fmaxf(sc[0][s], sc[1][s]), fmaxf(sc[2][s], sc[3][s]));
+      grow |= lmax[s] > m_run[s];
     }
     if (__any(grow)) {
       float al[SPL];
 #pragma unroll
       for (int s = 0; s < SPL; ++s) {
-        al[s] = __builtin_amdgcn_exp2f(m_run[s] - mnew[s]);
+        const float mnew = fmaxf(m_run[s], row_max16(lmax[s]));
+        al[s] = __builtin_amdgcn_exp2f(m_run[s] - mnew);
         l_run[s] *= al[s];
         if constexpr (NSNM) s1_run[s] *= al[s];
-        m_run[s] = mnew[s];
+        m_run[s] = mnew;
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) zacc[r] *= al[r / NG];
