@@ -25,7 +25,6 @@ _LIB = os.environ.get("KVQREF_LIB") or os.path.join(_HERE, "libkvqref.so")
 PATTERN, KVARN, NSN = 0, 1, 2
 IN_F32, IN_BF16 = 0, 1
 NONE = 0xFF
-VTILE = 32
 KBLOCK = 128
 
 
@@ -169,7 +168,7 @@ class RefCache:
             raise ValueError("invalid oracle configuration")
         self.U = batch * n_kv_heads
         self.PU = n_kv_heads if shared_patterns else self.U   # pattern-table units
-        self.tcap = (max_tokens + VTILE - 1) // VTILE * VTILE
+        self.tcap = max_tokens
         self.nblk = (self.tcap + KBLOCK - 1) // KBLOCK
 
     def __del__(self):
@@ -296,17 +295,13 @@ def attn_exact(k, v, q, n_q_heads, sm_scale=0.0):
     return out
 
 
-def unpack_codes(packed: np.ndarray, which: int, T: int, D: int, bits: int) -> np.ndarray:
-    """Codes [U][T][D] from the stored byte layout (K token-major; V 32-token
-    tiles of 32-bit words, word-major then channel).  Pure index arithmetic."""
+def unpack_codes(packed: np.ndarray, T: int, D: int, bits: int) -> np.ndarray:
+    """Codes [U][T][D] from the oracle's records (K and V alike: one record
+    per token, channel d at bit bits * d, little-endian)."""
     U = packed.shape[0]
     per = 8 // bits
     mask = (1 << bits) - 1
     b = packed.reshape(U, -1)
     sh = (np.arange(per) * bits).astype(np.uint8)
     vals = ((b[..., None] >> sh) & mask).reshape(U, -1)   # code stream in bit order
-    if which == 0:
-        return vals.reshape(U, -1, D)[:, :T]
-    per_word = 32 // bits
-    tiles = vals.reshape(U, -1, bits, D, per_word)        # [U][tile][word][d][k]
-    return tiles.transpose(0, 1, 2, 4, 3).reshape(U, -1, D)[:, :T]
+    return vals.reshape(U, -1, D)[:, :T]

@@ -48,11 +48,10 @@
  *  R14 Attention: softmax(sm_scale * q.k^) v^ over every cached token, q-head
  *      hq reading kv-head hq / (Hq/Hkv), evaluated in binary64 over the
  *      dequantised cache and rounded to fp32.
- *  R15 Code layout: K codes token-major, channel d at bit n*d of the token's
- *      record (little-endian); V codes in tiles of 32 tokens made of 32-bit
- *      words, each holding 32/n consecutive tokens of one channel (token k of
- *      the word at bit n*k); word w of channel d sits at (w*D + d)*4 bytes
- *      of the tile (all channels' first words, then their second words...).
+ *  R15 Code layout (the pages fix none): K and V codes alike, one record of
+ *      D*n/8 bytes per token, tokens in order, channel d at bit n*d of the
+ *      record (little-endian).  The GPU library keeps V in another order;
+ *      the tests map its bytes to these records before comparing.
  *  R16 Batch-shared tables (shared_patterns, PATTERN mode): the pattern
  *      memory estimate of PatternKV's memory analysis carries no batch factor
  *      (its share of the KV memory falls as 1/B) and one decode pattern per
@@ -109,7 +108,7 @@
 
 struct kvqref_cache {
   kvqref_cfg cfg;
-  int32_t D, U, PU, NG, tcap, kbytes, vtile;   /* PU: pattern-table units */
+  int32_t D, U, PU, NG, tcap, kbytes;   /* PU: pattern-table units */
   int32_t n_tokens, n_patterns, win_count, dropped;
   int32_t thr_on;
   float rho;
@@ -379,9 +378,8 @@ kvqref_cache* kvqref_new(const kvqref_cfg* cfg) {
   c->U = cfg->batch * cfg->n_kv_heads;
   c->PU = cfg->shared_patterns ? cfg->n_kv_heads : c->U;
   c->NG = cfg->head_dim / cfg->group;
-  c->tcap = (cfg->max_tokens + KVQREF_VTILE - 1) / KVQREF_VTILE * KVQREF_VTILE;
+  c->tcap = cfg->max_tokens;
   c->kbytes = c->D * cfg->bits / 8;
-  c->vtile = c->D * 4 * cfg->bits;
   c->thr_on = cfg->v_alpha > 0.0;
   c->rho = c->thr_on ? kvqref_rho_star_f32(c->D, cfg->v_alpha) : 0.0f;
   int64_t U = c->U, T = c->tcap, D = c->D;
@@ -419,17 +417,10 @@ void kvqref_free(kvqref_cache* c) {
 
 static int64_t code_byte(const kvqref_cache* c, int kind, int64_t u, int32_t t, int32_t d,
                          int* shift) {
-  int bits = c->cfg.bits;
-  if (kind == 0) {
-    int64_t bit = (int64_t)d * bits;
-    *shift = (int)(bit & 7);
-    return (u * c->tcap + t) * c->kbytes + bit / 8;
-  }
-  int64_t tile = t / KVQREF_VTILE, i = t % KVQREF_VTILE;
-  int64_t per_word = 32 / bits;              /* tokens per 32-bit word */
-  int64_t word = i / per_word, bit = (i % per_word) * bits;
+  (void)kind;   /* K and V records share the layout (R15) */
+  int64_t bit = (int64_t)d * c->cfg.bits;
   *shift = (int)(bit & 7);
-  return (u * (c->tcap / KVQREF_VTILE) + tile) * c->vtile + (word * c->D + d) * 4 + bit / 8;
+  return (u * c->tcap + t) * c->kbytes + bit / 8;
 }
 
 static void put_code(kvqref_cache* c, int kind, int64_t u, int32_t t, int32_t d, unsigned q) {

@@ -33,7 +33,6 @@ extern "C" {
 enum { KVQREF_PATTERN = 0, KVQREF_KVARN = 1, KVQREF_NSN = 2 };
 enum { KVQREF_IN_F32 = 0, KVQREF_IN_BF16 = 1 };
 enum { KVQREF_NONE = 0xFF };      /* stored pattern index meaning "raw" */
-enum { KVQREF_VTILE = 32 };       /* tokens per V code tile */
 enum { KVQREF_KBLOCK = 128 };     /* tokens per K block with k_per_channel */
 
 typedef struct {

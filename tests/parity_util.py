@@ -50,12 +50,30 @@ def gpu_t16(cache, which: int) -> np.ndarray:
     return cache.region("kv"[which] + "_t16").cpu().numpy().view(np.uint16).reshape(-1, L.token_cap)
 
 
+def unpack_gpu_codes(packed: np.ndarray, which: int, T: int, D: int, bits: int) -> np.ndarray:
+    """Codes [U][T][D] from the library's byte layout, which the oracle does
+    not share.  K: one record per token, channel d at bit bits * d (the
+    oracle's order).  V: 32-token tiles of 32-bit words; a word holds 32 /
+    bits consecutive tokens of one channel (token k at bit bits * k), and
+    word w of channel d sits at byte (w * D + d) * 4 of the tile."""
+    U = packed.shape[0]
+    per = 8 // bits
+    mask = (1 << bits) - 1
+    sh = (np.arange(per) * bits).astype(np.uint8)
+    vals = ((packed.reshape(U, -1)[..., None] >> sh) & mask).reshape(U, -1)   # code stream
+    if which == 0:
+        return vals.reshape(U, -1, D)[:, :T]
+    per_word = 32 // bits
+    tiles = vals.reshape(U, -1, bits, D, per_word)        # [U][tile][word][d][k]
+    return tiles.transpose(0, 1, 2, 4, 3).reshape(U, -1, D)[:, :T]
+
+
 def gpu_codes(cache, which: int, T: int, units=None) -> np.ndarray:
     c = cache.cfg
     packed = cache.region("kv"[which] + "_codes").cpu().numpy().reshape(c.batch * c.n_kv_heads, -1)
     if units is not None:
         packed = packed[list(units)]
-    return O.unpack_codes(packed, which, T, c.head_dim, c.bits)
+    return unpack_gpu_codes(packed, which, T, c.head_dim, c.bits)
 
 
 def gpu_tab(cache, which: int) -> np.ndarray:
@@ -78,7 +96,7 @@ def assert_same_encode(ref: "O.RefCache", cache, T: int, units=None, ref_units=N
     ref_units = units if ref_units is None else list(ref_units)
     for which in (0, 1):
         gc = gpu_codes(cache, which, T, units)
-        rc = O.unpack_codes(ref.codes(which)[ref_units], which, T, c.head_dim, c.bits)
+        rc = O.unpack_codes(ref.codes(which)[ref_units], T, c.head_dim, c.bits)
         bad = gc != rc
         assert not bad.any(), (f"{'KV'[which]} codes differ at {np.argwhere(bad)[:5]} "
                                f"(ties there: {ref.ties(which)[ref_units][:, :T][bad][:5]})")
@@ -113,7 +131,7 @@ def assert_same_kch(ref: "O.RefCache", cache, T: int, units=None, ref_units=None
     assert np.array_equal(gi, ri), f"K idx differ at {np.argwhere(gi != ri)[:5]}"
     if closed:
         gc = gpu_codes(cache, 0, closed, units)
-        rc = O.unpack_codes(ref.codes(0)[ref_units], 0, closed, D, c.bits)
+        rc = O.unpack_codes(ref.codes(0)[ref_units], closed, D, c.bits)
         bad = (gc != rc) & (ref.ties(0)[ref_units, :closed] == 0)
         assert not bad.any(), f"K codes differ at {np.argwhere(bad)[:5]}"
         gb = cache.region("k_bsz").cpu().numpy().view(np.uint16).reshape(U, -1, D, 2)[units, :nblk]
@@ -124,7 +142,7 @@ def assert_same_kch(ref: "O.RefCache", cache, T: int, units=None, ref_units=None
         gt, rt = gt[units, :T % O.KBLOCK], ref.k_tail()[ref_units, :T % O.KBLOCK]
         assert np.array_equal(gt, rt), f"K residuals differ at {np.argwhere(gt != rt)[:5]}"
     gc = gpu_codes(cache, 1, T, units)
-    rc = O.unpack_codes(ref.codes(1)[ref_units], 1, T, D, c.bits)
+    rc = O.unpack_codes(ref.codes(1)[ref_units], T, D, c.bits)
     assert np.array_equal(gc, rc), f"V codes differ at {np.argwhere(gc != rc)[:5]}"
     assert np.array_equal(gpu_sz(cache, 1)[units, :T], ref.sz(1)[ref_units, :T]), "V scales differ"
     assert np.array_equal(gpu_idx(cache, 1)[units, :T], ref.idx(1)[ref_units, :T]), "V idx differ"

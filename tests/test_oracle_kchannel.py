@@ -60,7 +60,7 @@ def test_complete_blocks_match_numpy_per_channel_quantiser(ref, bits):
     k, v = _kv(B, H, T, off=bits)
     c = O.RefCache(B, 2 * H, H, D, 320, bits=bits, max_patterns=0, k_per_channel=True)
     assert c.encode_append(k, v) == 0
-    codes = O.unpack_codes(c.codes(0), 0, T, D, bits)
+    codes = O.unpack_codes(c.codes(0), T, D, bits)
     bsz = c.block_sz()
     ties = c.ties(0)
     for u in range(B * H):

@@ -63,7 +63,7 @@ def test_reconstruction_within_quantiser_bound(ref, bits, group):
         scale = np.abs(X).max() + 1
         assert np.all(err <= n1 * n2 * ybound * (1 + 1e-3) + 1e-4 * scale * np.sqrt(D)), (w, bits)
         # codes within range
-        codes = O.unpack_codes(c.codes(w), w, T, D, bits)
+        codes = O.unpack_codes(c.codes(w), T, D, bits)
         assert codes.max() <= (1 << bits) - 1
 
 
