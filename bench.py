@@ -52,7 +52,38 @@ ATTN_CONFIGS = {
 }
 
 
-def attn_config(name):
+def calib_kernels(mib, dev):
+    """Plain kernels of known HBM traffic on `mib` MiB (4 reads: sum; 4 writes:
+    fill; 4 copies: negation), whose counters calibrate an attention run's."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        src.sum()
+    for _ in range(4):
+        dst.fill_(2.0)
+    for _ in range(4):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(f"calib-copy: {mib} MiB x 4 reads, 4 writes, 4 copies")
+
+
+def attn_config_bytes(c):
+    """Algorithmic bytes of one attention call on an ATTN_CONFIGS shape."""
+    D, B, Hq, H, T = 128, c["B"], c["Hq"], c["H"], c["T"]
+    idx = 2 if c["mode"] == "kvarn" else 4 if c["mode"] == "nsn" else 1
+    rec = D * c["bits"] // 8 + (D // c["group"]) * 4 + idx
+    if c.get("kch"):
+        # K: codes + index per token, one (s, z) word per channel and complete
+        # block, binary16 residuals of the open block; V per token as usual
+        closed = T // 128 * 128
+        k_bytes = T * (D * c["bits"] // 8 + 1) + closed // 128 * D * 4 + (T - closed) * D * 2
+        return B * H * (k_bytes + T * rec) + 2 * B * H * c["P"] * D * 4 + B * Hq * D * 6
+    return 2 * B * H * T * rec + 2 * B * H * c["P"] * D * 4 + B * Hq * D * 6
+
+
+def attn_config(name, calib_mib=0):
     import torch
 
     from bit_kv_cache_encode_amd import KVCache, synth
@@ -83,15 +114,11 @@ def attn_config(name):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / n
-    rec = cache.layout.record_bytes
-    if kch:
-        # K: codes + index per token, one (s, z) word per channel and complete
-        # block, binary16 residuals of the open block; V per token as usual
-        closed = T // 128 * 128
-        k_bytes = T * (D * c["bits"] // 8 + 1) + closed // 128 * D * 4 + (T - closed) * D * 2
-        nbytes = B * H * (k_bytes + T * rec) + 2 * B * H * c["P"] * D * 4 + B * Hq * D * 6
-    else:
-        nbytes = 2 * B * H * T * rec + 2 * B * H * c["P"] * D * 4 + B * Hq * D * 6
+    if not kch:
+        assert cache.layout.record_bytes == (D * c["bits"] // 8 + (D // c["group"]) * 4
+                                             + (2 if c["mode"] == "kvarn" else
+                                                4 if c["mode"] == "nsn" else 1))
+    nbytes = attn_config_bytes(c)
     res = {"attn_config": name, "shape": c, "us_per_call": round(us, 2),
            "algorithmic_bytes": nbytes, "effective_GBs": round(nbytes / us / 1e3, 1),
            "frac_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
@@ -107,6 +134,8 @@ def attn_config(name):
         torch.cuda.synchronize()
         res["decode_step_us"] = round(e0.elapsed_time(e1) * 1e3 / steps, 2)
     print(json.dumps(res))
+    if calib_mib:
+        calib_kernels(calib_mib, dev)
 
 
 def streaming(args):
@@ -326,6 +355,20 @@ def traffic_summary(args):
         "dispatches": len(f_attn),
         "raw_read_requests": raw, "raw_read_bytes_per_launch": raw_bytes,
     }
+    if args.attn_config:
+        # a secondary workload: its attention calls (10 warm-up + 50 timed)
+        name = args.attn_config
+        out["kernel"] = f"attention (split + combine), {name} workload"
+        out["workload"] = ATTN_CONFIGS[name]
+        out["algorithmic_bytes_per_launch"] = attn_config_bytes(ATTN_CONFIGS[name])
+        out["ratio_to_algorithmic"] = round(out["bytes_per_launch"] / out["algorithmic_bytes_per_launch"], 4)
+        out["commands"] = [c.replace("--attn-only 16", f"--attn-config {name}")
+                           .replace("--traffic-from", f"--attn-config {name} --traffic-from")
+                           for c in out["commands"]]
+        dst = os.path.join(ROOT, "profiles", f"traffic_attn_{name}.json")
+        json.dump(out, open(dst, "w"), indent=1)
+        print(json.dumps(out))
+        return
     if not args.split_step:
         # one-launch step over context + 1 tokens: attention bytes plus the
         # new token's encode (K/V in, records out, the two pattern tables)
@@ -354,7 +397,7 @@ def main():
               "one GPU's throughput is measured at its real per-GPU shape)", file=sys.stderr)
         sys.exit(2)
     if args.attn_config:
-        attn_config(args.attn_config)
+        attn_config(args.attn_config, args.calib_copy)
         return
     if args.streaming:
         streaming(args)
@@ -434,17 +477,7 @@ def main():
         torch.cuda.synchronize()
         print(f"attn-only: {args.attn_only} calls done")
         if args.calib_copy:
-            n = args.calib_copy * (1 << 20) // 4
-            src = torch.ones(n, dtype=torch.float32, device=dev)
-            dst = torch.empty_like(src)
-            for _ in range(4):
-                src.sum()
-            for _ in range(4):
-                dst.fill_(2.0)
-            for _ in range(4):
-                torch.neg(src, out=dst)
-            torch.cuda.synchronize()
-            print(f"calib-copy: {args.calib_copy} MiB x 4 reads, 4 writes, 4 copies")
+            calib_kernels(args.calib_copy, dev)
         return
 
     rec = base.layout.record_bytes
