@@ -303,7 +303,8 @@ constexpr int KM_ITERS = 50;
 // Input row of row i of unit u's k-means rows: the unit's own prefix
 // (groups = 1), or the prefixes of its kv-head in every sequence pooled
 // batch-major (group stride Hkv * n_tok).
-__device__ __forceinline__ int64_t km_row(int64_t u, int i, int n_tok, int64_t gstride) {
+__device__ __forceinline__ int64_t km_row(int64_t u, int i, int n_tok, int64_t gstride, int groups) {
+  if (groups == 1) return u * n_tok + i;
   const int g = i / n_tok;
   return g * gstride + u * n_tok + (i - g * n_tok);
 }
@@ -332,7 +333,7 @@ __global__ void __launch_bounds__(KM_THREADS) kmeans_kernel(const void* xk, cons
   for (int i = threadIdx.x; i < k * D; i += KM_THREADS) {
     int j = i / D, d = i % D;
     int64_t row = (int64_t)j * n / k;
-    sh.cent[j][d] = (double)load_in(x, km_row(u, (int)row, n_tok, gstride) * D + d, bf16);
+    sh.cent[j][d] = (double)load_in(x, km_row(u, (int)row, n_tok, gstride, groups) * D + d, bf16);
   }
   __syncthreads();
   for (int it = 0; it < KM_ITERS; ++it) {
@@ -341,7 +342,7 @@ __global__ void __launch_bounds__(KM_THREADS) kmeans_kernel(const void* xk, cons
     int changed = 0;
     for (int t = threadIdx.x; t < n; t += KM_THREADS) {
       float xr[D];
-      const int64_t xr0 = km_row(u, t, n_tok, gstride) * D;
+      const int64_t xr0 = km_row(u, t, n_tok, gstride, groups) * D;
       for (int d = 0; d < D; ++d) xr[d] = load_in(x, xr0 + d, bf16);
       int best = 0;
       double bd = INFINITY;
@@ -368,7 +369,7 @@ __global__ void __launch_bounds__(KM_THREADS) kmeans_kernel(const void* xk, cons
       const int d = threadIdx.x;
       for (int t = 0; t < n; ++t) {
         int j = a[t];
-        sh.sums[j][d] = sh.sums[j][d] + (double)load_in(x, km_row(u, t, n_tok, gstride) * D + d, bf16);
+        sh.sums[j][d] = sh.sums[j][d] + (double)load_in(x, km_row(u, t, n_tok, gstride, groups) * D + d, bf16);
         if (d == 0) sh.cnt[j] += 1;
       }
     }
@@ -425,13 +426,17 @@ __device__ __forceinline__ void km_load16(const void* x, int64_t idx, int bf16, 
 // (uint16) shares the rank and member-list bytes, which serve only the
 // update.  It serves any (n, k) whose total fits a compute unit's LDS.
 constexpr int KF_CSTRIDE = D + 4;   // floats per binary32 centroid row (bank shift)
+// bfloat16 input: two bfloat16 parts of each binary32 centroid, [2][k16][KB_STRIDE]
+// (a 16-byte shift per row keeps the 16-byte operand reads conflict-free)
+constexpr int KB_STRIDE = D + 8;
+constexpr int KF_CBYTES = (2 * KB_STRIDE * 2 > KF_CSTRIDE * 4) ? 2 * KB_STRIDE * 2 : KF_CSTRIDE * 4;
 struct KfLds { int cent, c32, cc, cn, a, rank, mem, pre, off, cnt, changed, namb, total; };
 __host__ __device__ inline KfLds kf_lds(int n, int k) {
   KfLds L;
   const int kr = (k + KF_PC - 1) / KF_PC * KF_PC, k16 = (k + 15) / 16 * 16, nch = (n + 63) / 64;
   int o = 0;
   L.cent = o; o += kr * D * 8;
-  L.c32 = o; o += k16 * KF_CSTRIDE * 4;
+  L.c32 = o; o += k16 * KF_CBYTES;
   L.cc = o; o += k16 * 8;
   L.cn = o; o += (k16 * 4 + 15) / 16 * 16;
   L.a = o; o += (n + 15) / 16 * 16;
@@ -464,8 +469,18 @@ __device__ __forceinline__ float km_rowmin16(float v) {
 
 typedef float km_f32x4 __attribute__((ext_vector_type(4)));
 
+// binary32 -> bfloat16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t km_bf16_rne(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+typedef __bf16 km_bf16x8 __attribute__((ext_vector_type(8)));
+
 // NCB: column blocks of 16 patterns in the matrix-core distances (k <= 16 NCB)
-template <int NCB>
+// BF: bfloat16 input rows, whose products with the centroids run on the
+// bfloat16 matrix cores (see the assignment)
+template <int NCB, bool BF>
 __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk, const void* xv,
                                                                   int bf16, int n_tok, int groups,
                                                                   int64_t gstride, int k,
@@ -498,8 +513,45 @@ __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk,
 
   for (int i = tid; i < kr * D; i += KF_THREADS) {
     const int j = i / D, d = i % D;
-    cent[j][d] = j < k ? (double)load_in(x, km_row(u, (int)((int64_t)j * n / k), n_tok, gstride) * D + d, bf16)
+    cent[j][d] = j < k ? (double)load_in(x, km_row(u, (int)((int64_t)j * n / k), n_tok, gstride, groups) * D + d, bf16)
                        : 0.0;
+  }
+  // bfloat16 rows: are binary64 member sums exact in any order?  Every value
+  // is an integer multiple of 2^(e_min - 7), e_min the smallest exponent of
+  // a nonzero value (subnormals count as -126), and a sum of at most n
+  // values is below n 2^(e_max + 1).  With e_max - e_min + ceil(log2 n) <=
+  // 45 every partial sum, in whatever order, is a multiple of 2^(e_min - 7)
+  // below 2^(e_min + 46): exactly representable in binary64, so every
+  // addition is exact and any order gives the exact sum, which the
+  // token-order sum also is.  The update then spreads a cluster's members
+  // over several threads.
+  bool exact_sums = false;
+  if constexpr (BF) {
+    int* s_fr = s_namb + 1;   // [min, max] exponent field of the nonzero values
+    if (tid == 0) { s_fr[0] = 255; s_fr[1] = 0; }
+    __syncthreads();
+    int fmn = 255, fmx = 0;
+    for (int i = tid; i < n * (D / 8); i += KF_THREADS) {
+      const int r = i / (D / 8), c8 = i % (D / 8);
+      const uint4 w = *(const uint4*)((const uint16_t*)x + km_row(u, r, n_tok, gstride, groups) * D + 8 * c8);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int h = 0; h < 8; ++h) {
+        const uint32_t a = (ws[h >> 1] >> (16 * (h & 1))) & 0x7FFFu;
+        const int f = (int)(a >> 7);
+        if (a) { fmn = min(fmn, max(f, 1)); fmx = max(fmx, f); }
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      fmn = min(fmn, __shfl_xor(fmn, o, 64));
+      fmx = max(fmx, __shfl_xor(fmx, o, 64));
+    }
+    if (lane == 0) { atomicMin(&s_fr[0], fmn); atomicMax(&s_fr[1], fmx); }
+    __syncthreads();
+    int lg = 0;
+    while ((1 << lg) < n) ++lg;
+    exact_sums = s_fr[1] < 255 && (s_fr[1] == 0 || s_fr[1] - s_fr[0] + lg <= 45);
   }
   __syncthreads();
   for (int it = 0; it < KM_ITERS; ++it) {
@@ -512,9 +564,23 @@ __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk,
     // binary64 distances of the other centroids exceed its own, so a plain
     // binary64 nearest-centroid scan picks it too.  Any other row is listed
     // and its distances are recomputed in binary64 in channel order.
-    for (int i = tid; i < k16 * D; i += KF_THREADS) {
-      const int j = i / D, d = i % D;
-      s_c32[j * KF_CSTRIDE + d] = j < k ? (float)cent[j][d] : 0.0f;
+    if constexpr (BF) {
+      // c = (binary32) centroid = c1 + c2 + r: c1 = bf16(c), c2 = bf16(c - c1)
+      // (c - c1 is exact: the two are within a factor of two), |r| <= 2^-18 |c|
+      uint16_t* s_cb = (uint16_t*)s_c32;
+      for (int i = tid; i < k16 * D; i += KF_THREADS) {
+        const int j = i / D, d = i % D;
+        const float c = j < k ? (float)cent[j][d] : 0.0f;
+        const uint32_t h1 = km_bf16_rne(c);
+        const uint32_t h2 = km_bf16_rne(c - __builtin_bit_cast(float, h1 << 16));
+        s_cb[j * KB_STRIDE + d] = (uint16_t)h1;
+        s_cb[(k16 + j) * KB_STRIDE + d] = (uint16_t)h2;
+      }
+    } else {
+      for (int i = tid; i < k16 * D; i += KF_THREADS) {
+        const int j = i / D, d = i % D;
+        s_c32[j * KF_CSTRIDE + d] = j < k ? (float)cent[j][d] : 0.0f;
+      }
     }
     if (tid < k16) {
       double acc = 0.0;
@@ -526,7 +592,107 @@ __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk,
     if (tid == 0) { *s_changed = 0; *s_namb = 0; }
     __syncthreads();
     int changed = 0;
-    {
+    if constexpr (BF) {
+      // bfloat16 rows are exact operands.  Products x . c1 and x . c2 are
+      // exact in the matrix cores; their sums over 2 x 128 channels carry at
+      // most a few binary32 roundings (or truncations below the largest
+      // product) of partial sums bounded by sum |x_d| |c_d| <= |x| |c|: the
+      // bound takes 2^-13 |x| |c|, far above that, plus 2^-18 |x| |c| for
+      // the part r the two bfloat16 parts leave out and 2^-24 |x| |c| for
+      // the binary32 centroid.  The distance |x|^2 + |c|^2 - 2 x.c is then
+      // formed in binary32 (|x|^2 of a bfloat16 row summed in binary32 to
+      // within 2^-17, |c|^2 rounded once, two operations): 2^-16 (|x|^2 +
+      // |c|^2 + 2 |x| |c|) covers those roundings and the binary64 scan's own.
+      // As above, a row whose intervals single out one centroid takes it;
+      // the others are recomputed in binary64.
+      const int li = lane & 15, lk = lane >> 4;
+      const uint16_t* s_cb = (const uint16_t*)s_c32;
+      const float e1f = 0x1p-13f + 0x1p-18f + 0x1p-24f, e2f = 0x1p-16f;
+      // A: row 16 rb + li; chunk c holds channels 32 c + 8 lk .. + 7 (B the same)
+      const int nrb = (n + 15) / 16;
+      uint4 xn[4];
+      auto load_row = [&](int rb) {
+        const uint4* p = (const uint4*)((const uint16_t*)x +
+                                        km_row(u, min(16 * rb + li, n - 1), n_tok, gstride, groups) * D + 8 * lk);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) xn[c] = p[4 * c];
+      };
+      if (wave < nrb) load_row(wave);
+      for (int rb = wave; rb < nrb; rb += KF_THREADS / 64) {
+        uint4 xa[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) xa[c] = xn[c];
+        if (rb + KF_THREADS / 64 < nrb) load_row(rb + KF_THREADS / 64);
+        km_f32x4 acc[NCB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) acc[cb] = km_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int part = 0; part < 2; ++part)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+              const uint4 bw = *(const uint4*)(s_cb + ((part * k16 + 16 * cb + li) * KB_STRIDE + 32 * c + 8 * lk));
+              acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(km_bf16x8, xa[c]),
+                                                                __builtin_bit_cast(km_bf16x8, bw), acc[cb], 0, 0, 0);
+            }
+        // |x|^2 of row li in binary32: this lane's 32 channels, then the
+        // four lanes holding the row
+        float xx = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t w[4] = {xa[c].x, xa[c].y, xa[c].z, xa[c].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float lo = __builtin_bit_cast(float, w[i] << 16), hi = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+            xx = __builtin_fmaf(lo, lo, xx);
+            xx = __builtin_fmaf(hi, hi, xx);
+          }
+        }
+        xx += __shfl_xor(xx, 16, 64);
+        xx += __shfl_xor(xx, 32, 64);
+        // output slot r of this lane: row 16 rb + 4 lk + r, centroid 16 cb + li
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * rb + 4 * lk + r;
+          const float xr = __shfl(xx, 4 * lk + r, 64);
+          const float xnr = __builtin_sqrtf(xr) * (1.0f + 0x1p-19f);   // |x| rounded up
+          float lo[NCB], hi[NCB];
+          float U = INFINITY;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            const int j = 16 * cb + li;
+            lo[cb] = hi[cb] = INFINITY;
+            if (j < k) {
+              const float cc = (float)s_cc[j], cn = s_cn[j];
+              const float ap = __builtin_fmaf(-2.0f, acc[cb][r], xr + cc);
+              const float E = (e1f * xnr * cn + e2f * (xr + cc + 2.0f * xnr * cn)) * (1.0f + 0x1p-19f)
+                              + fabsf(ap) * 0x1p-22f + 0x1p-100f;
+              lo[cb] = ap - E;
+              hi[cb] = ap + E;
+            }
+            U = fminf(U, hi[cb]);
+          }
+          U = km_rowmin16(U);
+          int count = 0, first = -1;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            const uint64_t bal = __ballot(lo[cb] <= U);
+            const uint32_t bits = (uint32_t)(bal >> (16 * lk)) & 0xFFFFu;
+            count += __popc(bits);
+            if (first < 0 && bits) first = 16 * cb + __ffs(bits) - 1;
+          }
+          if (li == 0 && row < n) {
+            if (count == 1) {
+              if (it == 0 || s_a[row] != (uint8_t)first) changed = 1;
+              s_a[row] = (uint8_t)first;
+            } else {
+              s_amb[atomicAdd(s_namb, 1)] = (uint16_t)row;
+            }
+          }
+        }
+      }
+    } else {
       const int li = lane & 15, lk = lane >> 4;
       // E = e1 |x| |c| + e2 (|x|^2 + |c|^2 + 2 |x| |c|): the binary32 dot over D
       // channels from the rounded centroid, and (e2) the binary64 roundings
@@ -537,7 +703,7 @@ __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk,
       const int nrb = (n + 15) / 16;
       float xn[16];
       auto load_half = [&](int rb, int h) {
-        km_load16(x, km_row(u, min(16 * rb + li, n - 1), n_tok, gstride) * D + 64 * h + 16 * lk, bf16, xn);
+        km_load16(x, km_row(u, min(16 * rb + li, n - 1), n_tok, gstride, groups) * D + 64 * h + 16 * lk, bf16, xn);
       };
       if (wave < nrb) load_half(wave, 0);
       for (int rb = wave; rb < nrb; rb += KF_THREADS / 64) {
@@ -631,7 +797,7 @@ __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk,
     const int namb = *s_namb;
     for (int i = wave; i < namb; i += KF_THREADS / 64) {
       const int t = s_amb[i];
-      const int64_t row = km_row(u, t, n_tok, gstride) * D;
+      const int64_t row = km_row(u, t, n_tok, gstride, groups) * D;
       double dist[KM_MAXK / 64 + 1];
       int best = 0;
       double bd = INFINITY;
@@ -707,23 +873,77 @@ __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk,
     }
     __syncthreads();
     // centroid = member sum in token order / member count; empty keeps its
-    // centroid.  Thread (j, q) sums channels 4 q .. 4 q + 3 of cluster j's
-    // members in token order (one accumulator per channel), with the loads
-    // of 8 members in flight; the threads of a cluster read whole rows.
+    // centroid.
+    if (BF && exact_sums) {
+      // Exact sums (see above): the member list, grouped by cluster, is cut
+      // into 32 equal segments; thread (segment, q) sums channels 4 q .. 4 q
+      // + 3 over its segment's run of each cluster and adds the run's sum to
+      // the cluster's row of `cent` (zeroed first) with an LDS atomic add,
+      // every addition exact.  Then each row is divided by its count.
+      for (int i = tid; i < k * D; i += KF_THREADS)
+        if (s_cnt[i / D] > 0) cent[i / D][i % D] = 0.0;
+      __syncthreads();
+      const int q = tid & 31, seg = tid >> 5;
+      const int e0 = (int)((int64_t)seg * n / (KF_THREADS / 32));
+      const int e1 = (int)((int64_t)(seg + 1) * n / (KF_THREADS / 32));
+      double acc[4] = {0.0, 0.0, 0.0, 0.0};
+      int cj = -1;
+      constexpr int MF = 16;
+      for (int e = e0; e < e1; e += MF) {
+        uint2 w[MF];
+        int jm[MF];
+#pragma unroll
+        for (int i2 = 0; i2 < MF; ++i2) {
+          const int t = s_mem[min(e + i2, e1 - 1)];
+          jm[i2] = s_a[t];
+          w[i2] = *(const uint2*)((const uint16_t*)x + km_row(u, t, n_tok, gstride, groups) * D + 4 * q);
+        }
+#pragma unroll
+        for (int i2 = 0; i2 < MF; ++i2)
+          if (e + i2 < e1) {
+            if (jm[i2] != cj) {
+              if (cj >= 0)
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) atomicAdd(&cent[cj][4 * q + qq], acc[qq]);
+              cj = jm[i2];
+#pragma unroll
+              for (int qq = 0; qq < 4; ++qq) acc[qq] = 0.0;
+            }
+            acc[0] = acc[0] + (double)bf16_to_f32((uint16_t)(w[i2].x & 0xFFFFu));
+            acc[1] = acc[1] + (double)bf16_to_f32((uint16_t)(w[i2].x >> 16));
+            acc[2] = acc[2] + (double)bf16_to_f32((uint16_t)(w[i2].y & 0xFFFFu));
+            acc[3] = acc[3] + (double)bf16_to_f32((uint16_t)(w[i2].y >> 16));
+          }
+      }
+      if (cj >= 0)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) atomicAdd(&cent[cj][4 * q + qq], acc[qq]);
+      __syncthreads();
+      for (int i = tid; i < k * D; i += KF_THREADS) {
+        const int j = i / D, c = s_cnt[j];
+        if (c > 0) cent[j][i % D] = cent[j][i % D] / (double)c;
+      }
+      __syncthreads();
+      continue;
+    }
+    // Thread (j, q) sums channels 4 q .. 4 q + 3 of cluster j's members in
+    // token order (one accumulator per channel), with the loads of several
+    // members in flight; the threads of a cluster read whole rows.
     for (int i = tid; i < k * (D / 4); i += KF_THREADS) {
       const int j = i / (D / 4), d0 = 4 * (i % (D / 4)), c = s_cnt[j];
       if (c == 0) continue;
       const uint16_t* m = s_mem + s_off[j];
       double acc[4] = {0.0, 0.0, 0.0, 0.0};
-      if (bf16) {
+      if constexpr (BF) {
         // raw bfloat16 words of 16 members in flight
-        for (int e = 0; e < c; e += 16) {
-          uint2 w[16];
+        constexpr int MF = 16;
+        for (int e = 0; e < c; e += MF) {
+          uint2 w[MF];
 #pragma unroll
-          for (int i2 = 0; i2 < 16; ++i2)
-            w[i2] = *(const uint2*)((const uint16_t*)x + km_row(u, m[min(e + i2, c - 1)], n_tok, gstride) * D + d0);
+          for (int i2 = 0; i2 < MF; ++i2)
+            w[i2] = *(const uint2*)((const uint16_t*)x + km_row(u, m[min(e + i2, c - 1)], n_tok, gstride, groups) * D + d0);
 #pragma unroll
-          for (int i2 = 0; i2 < 16; ++i2)
+          for (int i2 = 0; i2 < MF; ++i2)
             if (e + i2 < c) {
               acc[0] = acc[0] + (double)bf16_to_f32((uint16_t)(w[i2].x & 0xFFFFu));
               acc[1] = acc[1] + (double)bf16_to_f32((uint16_t)(w[i2].x >> 16));
@@ -736,7 +956,7 @@ __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk,
           float4 f[8];
 #pragma unroll
           for (int i2 = 0; i2 < 8; ++i2)
-            f[i2] = *(const float4*)((const float*)x + km_row(u, m[min(e + i2, c - 1)], n_tok, gstride) * D + d0);
+            f[i2] = *(const float4*)((const float*)x + km_row(u, m[min(e + i2, c - 1)], n_tok, gstride, groups) * D + d0);
 #pragma unroll
           for (int i2 = 0; i2 < 8; ++i2)
             if (e + i2 < c) {
@@ -755,6 +975,32 @@ __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk,
   for (int i = tid; i < k * D; i += KF_THREADS) tab[i] = (float)cent[i / D][i % D];
 }
 
+template <int NCB, bool BF>
+static hipError_t launch_kmeans_fast(const void* xk, const void* xv, int bf16, int n_tok, int groups,
+                                     int64_t gstride, int k, float* tab_k, float* tab_v, int max_pat,
+                                     int units, int lds, hipStream_t s) {
+  static int attr = 0;
+  if (lds > attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)kmeans_fast_kernel<NCB, BF>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    attr = lds;
+  }
+  hipLaunchKernelGGL((kmeans_fast_kernel<NCB, BF>), dim3(units, 2), dim3(KF_THREADS), lds, s, xk, xv, bf16,
+                     n_tok, groups, gstride, k, tab_k, tab_v, max_pat);
+  return hipGetLastError();
+}
+
+template <bool BF>
+static hipError_t launch_kmeans_ncb(int ncb, const void* xk, const void* xv, int bf16, int n_tok, int groups,
+                                    int64_t gstride, int k, float* tab_k, float* tab_v, int max_pat,
+                                    int units, int lds, hipStream_t s) {
+  if (ncb <= 1) return launch_kmeans_fast<1, BF>(xk, xv, bf16, n_tok, groups, gstride, k, tab_k, tab_v, max_pat, units, lds, s);
+  if (ncb == 2) return launch_kmeans_fast<2, BF>(xk, xv, bf16, n_tok, groups, gstride, k, tab_k, tab_v, max_pat, units, lds, s);
+  if (ncb == 3) return launch_kmeans_fast<3, BF>(xk, xv, bf16, n_tok, groups, gstride, k, tab_k, tab_v, max_pat, units, lds, s);
+  return launch_kmeans_fast<4, BF>(xk, xv, bf16, n_tok, groups, gstride, k, tab_k, tab_v, max_pat, units, lds, s);
+}
+
 hipError_t launch_kmeans_pair(const void* xk, const void* xv, int bf16, int n_tok, int groups,
                               int64_t gstride, int k, float* tab_k, float* tab_v, int max_pat,
                               int units, uint8_t* assign, hipStream_t s) {
@@ -762,28 +1008,8 @@ hipError_t launch_kmeans_pair(const void* xk, const void* xv, int bf16, int n_to
   if (n <= KF_MAXN && k <= KM_MAXK && kf_lds((int)n, k).total <= KF_LDS_MAX) {
     const int lds = kf_lds((int)n, k).total;
     const int ncb = (k + 15) / 16;
-    const void* fn = ncb <= 1 ? (const void*)kmeans_fast_kernel<1>
-                   : ncb == 2 ? (const void*)kmeans_fast_kernel<2>
-                   : ncb == 3 ? (const void*)kmeans_fast_kernel<3> : (const void*)kmeans_fast_kernel<4>;
-    static int fast_attr[5] = {0, 0, 0, 0, 0};
-    if (lds > fast_attr[ncb]) {
-      hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-      if (e != hipSuccess) return e;
-      fast_attr[ncb] = lds;
-    }
-    if (ncb <= 1)
-      hipLaunchKernelGGL(kmeans_fast_kernel<1>, dim3(units, 2), dim3(KF_THREADS), lds, s, xk, xv, bf16,
-                         n_tok, groups, gstride, k, tab_k, tab_v, max_pat);
-    else if (ncb == 2)
-      hipLaunchKernelGGL(kmeans_fast_kernel<2>, dim3(units, 2), dim3(KF_THREADS), lds, s, xk, xv, bf16,
-                         n_tok, groups, gstride, k, tab_k, tab_v, max_pat);
-    else if (ncb == 3)
-      hipLaunchKernelGGL(kmeans_fast_kernel<3>, dim3(units, 2), dim3(KF_THREADS), lds, s, xk, xv, bf16,
-                         n_tok, groups, gstride, k, tab_k, tab_v, max_pat);
-    else
-      hipLaunchKernelGGL(kmeans_fast_kernel<4>, dim3(units, 2), dim3(KF_THREADS), lds, s, xk, xv, bf16,
-                         n_tok, groups, gstride, k, tab_k, tab_v, max_pat);
-    return hipGetLastError();
+    return bf16 ? launch_kmeans_ncb<true>(ncb, xk, xv, bf16, n_tok, groups, gstride, k, tab_k, tab_v, max_pat, units, lds, s)
+                : launch_kmeans_ncb<false>(ncb, xk, xv, bf16, n_tok, groups, gstride, k, tab_k, tab_v, max_pat, units, lds, s);
   }
   size_t lds = sizeof(KmShared);
   static bool attr_set = false;
