@@ -460,11 +460,17 @@ __device__ __forceinline__ void km_load32(const void* x, int64_t idx, int bf16, 
   for (int i = 0; i < 16; ++i) { o[i] = a[i]; o[16 + i] = b[i]; }
 }
 
-// minimum over the 16 lanes of a row of a wave
+// minimum over the 16 lanes of a DPP row (lanes 16r .. 16r+15) on an
+// integer key that orders like the binary32 values (no NaN): swap
+// neighbours, swap pairs, mirror halves, mirror the row
 __device__ __forceinline__ float km_rowmin16(float v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v = fminf(v, __shfl_xor(v, o, 64));
-  return v;
+  const int b = __builtin_bit_cast(int, v);
+  int key = b ^ ((b >> 31) & 0x7FFFFFFF);
+  key = min(key, __builtin_amdgcn_update_dpp(key, key, 0xB1, 0xF, 0xF, true));
+  key = min(key, __builtin_amdgcn_update_dpp(key, key, 0x4E, 0xF, 0xF, true));
+  key = min(key, __builtin_amdgcn_update_dpp(key, key, 0x141, 0xF, 0xF, true));
+  key = min(key, __builtin_amdgcn_update_dpp(key, key, 0x140, 0xF, 0xF, true));
+  return __builtin_bit_cast(float, key ^ ((key >> 31) & 0x7FFFFFFF));
 }
 
 typedef float km_f32x4 __attribute__((ext_vector_type(4)));
@@ -610,6 +616,16 @@ __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk,
       const float e1f = 0x1p-13f + 0x1p-18f + 0x1p-24f, e2f = 0x1p-16f;
       // A: row 16 rb + li; chunk c holds channels 32 c + 8 lk .. + 7 (B the same)
       const int nrb = (n + 15) / 16;
+      // per centroid 16 cb + li: |c|^2 rounded to binary32 and the bound's
+      // centroid terms (e1 + 2 e2) |c| and e2 |c|^2
+      float ccf[NCB], ca[NCB], cbv[NCB];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int j = min(16 * cb + li, k16 - 1);
+        ccf[cb] = (float)s_cc[j];
+        ca[cb] = (e1f + 2.0f * e2f) * s_cn[j];
+        cbv[cb] = e2f * ccf[cb];
+      }
       uint4 xn[4];
       auto load_row = [&](int rb) {
         const uint4* p = (const uint4*)((const uint16_t*)x +
@@ -664,10 +680,11 @@ __global__ void __launch_bounds__(KF_THREADS) kmeans_fast_kernel(const void* xk,
             const int j = 16 * cb + li;
             lo[cb] = hi[cb] = INFINITY;
             if (j < k) {
-              const float cc = (float)s_cc[j], cn = s_cn[j];
-              const float ap = __builtin_fmaf(-2.0f, acc[cb][r], xr + cc);
-              const float E = (e1f * xnr * cn + e2f * (xr + cc + 2.0f * xnr * cn)) * (1.0f + 0x1p-19f)
-                              + fabsf(ap) * 0x1p-22f + 0x1p-100f;
+              // e1 |x| |c| + e2 (|x|^2 + |c|^2 + 2 |x| |c|), widened for its
+              // own roundings
+              const float ap = __builtin_fmaf(-2.0f, acc[cb][r], xr + ccf[cb]);
+              const float E = __builtin_fmaf(xnr, ca[cb], cbv[cb] + e2f * xr) * (1.0f + 0x1p-19f)
+                              + __builtin_fmaf(fabsf(ap), 0x1p-22f, 0x1p-100f);
               lo[cb] = ap - E;
               hi[cb] = ap + E;
             }
