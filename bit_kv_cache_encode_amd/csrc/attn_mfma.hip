@@ -39,6 +39,13 @@ namespace kvq {
 constexpr int MF_WAVES = 8;
 constexpr int MF_THREADS = MF_WAVES * 64;
 
+// A 16-byte tile load, non-temporal (the line is not kept for reuse) or not
+template <bool NT>
+__device__ __forceinline__ u32x4 tile_ld(const u32x4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
 // Dynamic LDS layout of a block (bytes); npat = padded pattern count.
 struct MfLds {
   int q, qsum, qe, next, qm, qa, ps, ph, vs, vz, w, alpha, m, o, z, l, wsum, M, last, tiles,
@@ -188,17 +195,25 @@ attn_mfma_kernel(AttnArgs a) {
   constexpr int P_VS = TILE * NGS * 4 / 16;
   constexpr bool SZ_PAIR = !KCH && TS::P_KS + P_VS <= 64;
   u32x4 rkc[TS::R_KC], rvc[TS::R_VC], rks, rvs, rix;
-  auto issue = [&](int tile) {
+  // The tile words are read once: non-temporal loads where they measured
+  // faster (2-bit codes, K per token: 4-6% per call).  The 4-bit and the
+  // K-per-channel variants keep ordinary loads, which time faster there, and
+  // so do units with several q-head blocks, whose blocks after the first
+  // read the unit's tiles from L2 (non-temporal lines leave it early).
+  constexpr bool NT_OK = BITS == 2 && !KCH;
+  const bool nt = NT_OK && n_hb == 1;
+  auto issue_t = [&](int tile, auto nt_tag) {
+    constexpr bool NT = decltype(nt_tag)::value;
     const u32x4* kc = (const u32x4*)(kcodes + (int64_t)tile * TS::KREC);
     const u32x4* vc = (const u32x4*)(vcodes + (int64_t)(tile >> 5) * VTB);
 #pragma unroll
-    for (int r = 0; r < TS::R_KC; ++r) rkc[r] = kc[lane + 64 * r];
+    for (int r = 0; r < TS::R_KC; ++r) rkc[r] = tile_ld<NT>(&kc[lane + 64 * r]);
 #pragma unroll
-    for (int r = 0; r < TS::R_VC; ++r) rvc[r] = vc[lane + 64 * r];
+    for (int r = 0; r < TS::R_VC; ++r) rvc[r] = tile_ld<NT>(&vc[lane + 64 * r]);
     if constexpr (SZ_PAIR) {
       // K scales in lanes [0, P_KS), V scales in the lanes after them
-      if (lane < TS::P_KS) rks = ((const u32x4*)(ksz + (int64_t)tile * NGS * 4))[lane];
-      else if (lane < TS::P_KS + P_VS) rks = ((const u32x4*)(vsz + (int64_t)tile * NGS * 4))[lane - TS::P_KS];
+      if (lane < TS::P_KS) rks = tile_ld<NT>(&((const u32x4*)(ksz + (int64_t)tile * NGS * 4))[lane]);
+      else if (lane < TS::P_KS + P_VS) rks = tile_ld<NT>(&((const u32x4*)(vsz + (int64_t)tile * NGS * 4))[lane - TS::P_KS]);
     } else {
       if (lane < TS::P_KS) {
         // K per channel: the words of the tile's block (a tile never straddles
@@ -206,7 +221,7 @@ attn_mfma_kernel(AttnArgs a) {
         rks = KCH ? ((const u32x4*)(a.r.kbsz + ((int64_t)u * kch_blocks(a.tcap) + tile / KBLOCK) * D))[lane]
                   : ((const u32x4*)(ksz + (int64_t)tile * NGS * 4))[lane];
       }
-      if (lane < P_VS) rvs = ((const u32x4*)(vsz + (int64_t)tile * NGS * 4))[lane];
+      if (lane < P_VS) rvs = tile_ld<NT>(&((const u32x4*)(vsz + (int64_t)tile * NGS * 4))[lane]);
     }
     const int ix_bytes = KVARN ? 2 : 1;
     if (NSNM) {
@@ -214,15 +229,19 @@ attn_mfma_kernel(AttnArgs a) {
       // lane range: a select over the four would become a private table)
       constexpr int Q = TS::P_IX / 2;
       const int64_t o = (int64_t)tile * ix_bytes;
-      if (lane < Q) rix = ((const u32x4*)(kix_src + o))[lane];
-      else if (lane < 2 * Q) rix = ((const u32x4*)(kt2_src + o))[lane - Q];
-      else if (lane < 3 * Q) rix = ((const u32x4*)(vix_src + o))[lane - 2 * Q];
-      else if (lane < 4 * Q) rix = ((const u32x4*)(vt2_src + o))[lane - 3 * Q];
+      if (lane < Q) rix = tile_ld<NT>(&((const u32x4*)(kix_src + o))[lane]);
+      else if (lane < 2 * Q) rix = tile_ld<NT>(&((const u32x4*)(kt2_src + o))[lane - Q]);
+      else if (lane < 3 * Q) rix = tile_ld<NT>(&((const u32x4*)(vix_src + o))[lane - 2 * Q]);
+      else if (lane < 4 * Q) rix = tile_ld<NT>(&((const u32x4*)(vt2_src + o))[lane - 3 * Q]);
     } else if (lane < TS::P_IX) {
-      rix = ((const u32x4*)(kix_src + (int64_t)tile * ix_bytes))[lane];
+      rix = tile_ld<NT>(&((const u32x4*)(kix_src + (int64_t)tile * ix_bytes))[lane]);
     } else if (lane < 2 * TS::P_IX) {
-      rix = ((const u32x4*)(vix_src + (int64_t)tile * ix_bytes))[lane - TS::P_IX];
+      rix = tile_ld<NT>(&((const u32x4*)(vix_src + (int64_t)tile * ix_bytes))[lane - TS::P_IX]);
     }
+  };
+  auto issue = [&](int tile) {
+    if (NT_OK && nt) issue_t(tile, std::true_type{});
+    else issue_t(tile, std::false_type{});
   };
   auto commit = [&]() {
     u32x4* t4 = (u32x4*)tb;
