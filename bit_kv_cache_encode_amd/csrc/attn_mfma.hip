@@ -107,7 +107,8 @@ __host__ __device__ inline MfLds mf_lds(int HB, int NG, int npat, int tile_bytes
 // word (s (q_a . c_a + q_b . c_b) = s q_a . c_a + s q_b . c_b, and likewise
 // for z and for p s, p z on the V side), which fills the 16 MFMA rows with
 // 4 q-heads at G = 64 instead of leaving half of an 8-head row block idle.
-template <int BITS, int NG, int NGS, bool KVARN, int NPB, bool QLO, bool KCH, bool NSNM>
+// NTL: the tile copy takes non-temporal loads (chosen per launch).
+template <int BITS, int NG, int NGS, bool KVARN, int NPB, bool QLO, bool KCH, bool NSNM, bool NTL>
 __global__ void __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_mfma_kernel(AttnArgs a) {
   static_assert(!(KVARN && NPB), "KVarN has no pattern term");
@@ -195,15 +196,10 @@ attn_mfma_kernel(AttnArgs a) {
   constexpr int P_VS = TILE * NGS * 4 / 16;
   constexpr bool SZ_PAIR = !KCH && TS::P_KS + P_VS <= 64;
   u32x4 rkc[TS::R_KC], rvc[TS::R_VC], rks, rvs, rix;
-  // The tile words are read once: non-temporal loads where they measured
-  // faster (2-bit codes, K per token: 4-6% per call).  The 4-bit and the
-  // K-per-channel variants keep ordinary loads, which time faster there, and
-  // so do units with several q-head blocks, whose blocks after the first
-  // read the unit's tiles from L2 (non-temporal lines leave it early).
-  constexpr bool NT_OK = BITS == 2 && !KCH;
-  const bool nt = NT_OK && n_hb == 1;
-  auto issue_t = [&](int tile, auto nt_tag) {
-    constexpr bool NT = decltype(nt_tag)::value;
+  // The tile words are read once: non-temporal loads where the launch asks
+  // for them (see launch_one)
+  constexpr bool NT = NTL;
+  auto issue = [&](int tile) {
     const u32x4* kc = (const u32x4*)(kcodes + (int64_t)tile * TS::KREC);
     const u32x4* vc = (const u32x4*)(vcodes + (int64_t)(tile >> 5) * VTB);
 #pragma unroll
@@ -238,10 +234,6 @@ attn_mfma_kernel(AttnArgs a) {
     } else if (lane < 2 * TS::P_IX) {
       rix = tile_ld<NT>(&((const u32x4*)(vix_src + (int64_t)tile * ix_bytes))[lane - TS::P_IX]);
     }
-  };
-  auto issue = [&](int tile) {
-    if (NT_OK && nt) issue_t(tile, std::true_type{});
-    else issue_t(tile, std::false_type{});
   };
   auto commit = [&]() {
     u32x4* t4 = (u32x4*)tb;
@@ -1265,22 +1257,36 @@ attn_mfma_kernel(AttnArgs a) {
   if (tid == 0) __hip_atomic_store(&a.r.cnt[cu], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int BITS, int NG, int NGS, bool KVARN, int NPB, bool QLO, bool KCH = false, bool NSNM = false>
-static hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
+template <int BITS, int NG, int NGS, bool KVARN, int NPB, bool QLO, bool KCH, bool NSNM, bool NTL>
+static hipError_t launch_impl(const AttnArgs& a, hipStream_t s) {
+  using K = void (*)(AttnArgs);
+  const K fn = attn_mfma_kernel<BITS, NG, NGS, KVARN, NPB, QLO, KCH, NSNM, NTL>;
   constexpr int HB = 16 / NG;
   const int npat = pad_pat(KVARN ? 0 : a.n_pat);
   const MfLds L = mf_lds(HB, NG, npat, TileShape<BITS, NGS, KVARN, KCH, NSNM>::BYTES, NPB > 0, 16 * NPB, KCH, NSNM);
   static int attr = 0;
   if (L.total > attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel<BITS, NG, NGS, KVARN, NPB, QLO, KCH, NSNM>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, L.total);
+    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, L.total);
     if (e != hipSuccess) return e;
     attr = L.total;
   }
   const int n_hb = (a.gq + HB - 1) / HB;
-  hipLaunchKernelGGL((attn_mfma_kernel<BITS, NG, NGS, KVARN, NPB, QLO, KCH, NSNM>),
-                     dim3(a.B * a.Hkv * a.splits * n_hb), dim3(MF_THREADS), L.total, s, a);
+  hipLaunchKernelGGL(fn, dim3(a.B * a.Hkv * a.splits * n_hb), dim3(MF_THREADS), L.total, s, a);
   return hipGetLastError();
+}
+
+// Non-temporal tile loads where they measured faster: 2-bit codes with K per
+// token (4-6% per call).  The 4-bit and K-per-channel variants keep ordinary
+// loads, which time faster there, and so do units with several q-head blocks,
+// whose blocks after the first read the unit's tiles from L2 (non-temporal
+// lines leave it early: 1.18x the algorithmic HBM bytes at 7 q-heads per
+// kv-head, against 1.0035x with ordinary loads).
+template <int BITS, int NG, int NGS, bool KVARN, int NPB, bool QLO, bool KCH = false, bool NSNM = false>
+static hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
+  if constexpr (BITS == 2 && !KCH) {
+    if (a.gq <= 16 / NG) return launch_impl<BITS, NG, NGS, KVARN, NPB, QLO, KCH, NSNM, true>(a, s);
+  }
+  return launch_impl<BITS, NG, NGS, KVARN, NPB, QLO, KCH, NSNM, false>(a, s);
 }
 
 template <int BITS, int NG, int NGS, bool QLO>
