@@ -278,7 +278,7 @@ def _used_regions(cache):
     return out
 
 
-@pytest.mark.parametrize("shape", ["llama8b_ctx32k_2bit", "long_ctx128k_4bit"])
+@pytest.mark.parametrize("shape", ["llama8b_ctx32k_2bit", "llama8b_ctx4k_2bit", "long_ctx128k_4bit"])
 def test_decode_step_fullsize(shape):
     """The kernel the benchmark times: the one-launch decode step
     (kvq_decode_step, default grid) at full size, 130 steps with the
@@ -289,11 +289,15 @@ def test_decode_step_fullsize(shape):
     copy of the cache driven by the two separate calls; the two caches' used
     contents must stay byte-identical and their outputs within 2e-3.  The
     oracle reproduces sampled units at steps 0, 126, 127 (the closing step),
-    128 and 129."""
+    128 and 129.  The Llama shape runs at 32768 and at 4096 cached tokens."""
     dev = torch.device("cuda", 0)
     if shape == "llama8b_ctx32k_2bit":
         B, Hq, H, T0, bits, group, P = 8, 32, 8, 32768, 2, 32, 32
         samples = [(0, 0), (3, 5), (7, 7)]
+    elif shape == "llama8b_ctx4k_2bit":
+        # the single-layer Llama-3-8B decode shape at 4096 tokens
+        B, Hq, H, T0, bits, group, P = 8, 32, 8, 4096, 2, 32, 32
+        samples = [(0, 3), (6, 1)]
     else:
         B, Hq, H, T0, bits, group, P = 1, 32, 8, 131072, 4, 64, 64
         samples = [(0, 1), (0, 6)]
